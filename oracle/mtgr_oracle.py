@@ -1,0 +1,198 @@
+"""CPU oracle for the MTGR HSTU encoder forward pass -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import this module.  The
+product path (the HIP library and its binding) never imports it, and it imports nothing from the
+product path.  It is plain numpy in float64, written from the pages' definitions, step by step,
+with no blocking, fusion or reordering beyond what the definitions state.
+
+Page keys used in citations:
+  [P1] chenhuiyu blog "生成式推荐 18: MTGR" (Chinese)      [P2] the same blog post in English
+  [P3] marovi.ai "MTGR: Industrial-Scale Generative Recommendation Framework in Meituan/zh"
+  [P4] intelliparadigm article on MTGR hybrid modeling      [P5] fun-rec mdbook §7.3
+       "MTGR: Hybrid Paradigm Modeling"
+
+Definitions followed (all exact; the method has no approximation, heuristic or iteration):
+  * sample layout D = [U, S, R, [C,I]_1..K], one sample per user      [P3 方法, eq. D; P5 7.3.1]
+  * block: X~ = GroupLN(X); project X~ to Q, K, V, U;
+           V~ = silu(K^T Q)/(N_U+N_S+N_R+N_I) masked by M, times V;
+           X <- MLP(GroupLN(V~ (.) U)) + X                              [P3 方法, update equations]
+  * mask M: rule 1 U and S keys visible to every query; rule 2 an R key is visible to a later
+    R or C query (strictly earlier timestamp); rule 3 a candidate is visible only to itself
+                                                    [P3 方法, mask paragraph; P5 7.3.4, Rules 1-3]
+  * GroupLN: LayerNorm statistics of each token over its features, with affine parameters chosen
+    by the token's group                                              [P5 7.3.3, GLN equation]
+  * head: candidate hidden states -> MLP -> (CTR, CTCVR) logits      [P1/P2 token section; P5 7.3.1]
+
+Readings where the pages are silent or garbled (each listed with its reason in the design notes):
+  R1 the garbled silu(K^T Q) M V is read token-wise: v~_i = sum_j M[i,j] silu(q_i.k_j)/N v_j,
+     with M applied elementwise; no 1/sqrt(d_h) scale and no relative bias.
+  R2 N is the user's total token count (N_U+N_S+N_R+K), not the count of visible keys.
+  R3 R-key visibility uses strict '<' on float32 seconds; equal timestamps are invisible, except a
+     token to itself.  U and S queries never see R keys; R, U and S queries never see C keys.
+  R4 GroupLN statistics are per token (biased variance, eps=1e-5); gamma/beta per group.
+  R5 Q, K, V, U projections are affine with no activation; heads split Q, K, V into
+     contiguous d_h-wide slices; U gates the concatenated heads elementwise.
+  R6 MLP is d -> h -> d with SiLU and biases; head is d -> d/2 -> 2 with SiLU, raw logits.
+
+parity pins: every function below is pinned by tests/test_oracle_pins.py (worked mask examples
+from [P1] and [P5], GroupLN invariants and torch layer_norm, closed forms and library reductions
+of the attention, permutation/independence/isolation/temporal-replay invariants).  The readings
+R1-R6 themselves are pinned only by construction (the pages do not fix them).
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+G_U, G_S, G_R, G_C = 0, 1, 2, 3
+
+
+# ----------------------------------------------------------------------------------------------
+# Mask  [P3 方法, mask paragraph; P5 7.3.4 Rules 1-3]
+# ----------------------------------------------------------------------------------------------
+def mask(groups: np.ndarray, times: np.ndarray) -> np.ndarray:
+    """Dynamic mask of one user's tokens, by enumeration of every (query i, key j) pair.
+
+    Returns uint8 [n, n]; rows are queries, columns keys; 1 = key visible to query.
+    Token order is irrelevant: the rules look only at group ids and timestamps.
+    """
+    g = np.asarray(groups, dtype=np.int64)
+    t = np.asarray(times, dtype=np.float32)
+    n = g.shape[0]
+    gi = g[:, None]            # query group, broadcast over keys
+    gj = g[None, :]            # key group, broadcast over queries
+    ti = t[:, None]
+    tj = t[None, :]
+    same = np.eye(n, dtype=bool)
+    rule1_static = (gj == G_U) | (gj == G_S)                        # static keys: all queries
+    rule2_causal = (gj == G_R) & ((gi == G_R) | (gi == G_C)) & (tj < ti)   # earlier R events
+    rule3_self = same                                                # every token sees itself
+    return (rule1_static | rule2_causal | rule3_self).astype(np.uint8)
+
+
+def visible_pairs(groups: np.ndarray, times: np.ndarray) -> int:
+    """Number of (query, key) pairs the mask lets through for one user."""
+    return int(mask(groups, times).sum(dtype=np.int64))
+
+
+# ----------------------------------------------------------------------------------------------
+# Group-Layer Normalization  [P5 7.3.3, GLN equation; P3 方法, GLN paragraph]
+# ----------------------------------------------------------------------------------------------
+def group_layer_norm(x: np.ndarray, groups: np.ndarray, gamma: np.ndarray, beta: np.ndarray,
+                     eps: float = 1e-5) -> np.ndarray:
+    """x [n, d]; groups [n] in 0..3; gamma, beta [4, d].  Per-token mean and biased variance over
+    the d features, then the affine parameters of the token's group."""
+    x = np.asarray(x, dtype=np.float64)
+    g = np.asarray(groups, dtype=np.int64)
+    d = x.shape[1]
+    mu = x.sum(axis=1, keepdims=True) / d
+    xc = x - mu
+    var = (xc * xc).sum(axis=1, keepdims=True) / d
+    xhat = xc / np.sqrt(var + eps)
+    gam = np.asarray(gamma, dtype=np.float64)[g]
+    bet = np.asarray(beta, dtype=np.float64)[g]
+    return xhat * gam + bet
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    """silu(z) = z * sigmoid(z) = z / (1 + exp(-z)), evaluated without overflow warnings."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = z[pos] / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = z[~pos] * ez / (1.0 + ez)
+    return out
+
+
+def linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
+    """y = x W^T + b, W in [out, in] layout."""
+    y = np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+    if b is not None:
+        y = y + np.asarray(b, dtype=np.float64)
+    return y
+
+
+# ----------------------------------------------------------------------------------------------
+# Masked SiLU attention with the U gate  [P3 方法, update equations]
+# ----------------------------------------------------------------------------------------------
+def hstu_attention(qkvu: np.ndarray, groups: np.ndarray, times: np.ndarray,
+                   num_heads: int) -> np.ndarray:
+    """One user's attention.  qkvu [n, 4d] = [Q | K | V | U]; returns V~ (.) U  [n, d].
+
+    For head h (feature slice h*d_h:(h+1)*d_h of Q, K, V):
+        V~_h = (silu(Q_h K_h^T) / N  *elementwise*  M) @ V_h,   N = n (the user's token count).
+    """
+    qkvu = np.asarray(qkvu, dtype=np.float64)
+    n, four_d = qkvu.shape
+    d = four_d // 4
+    dh = d // num_heads
+    if n == 0:
+        return np.zeros((0, d))
+    Q, K, V, U = qkvu[:, :d], qkvu[:, d:2 * d], qkvu[:, 2 * d:3 * d], qkvu[:, 3 * d:]
+    M = mask(groups, times).astype(np.float64)
+    N = float(n)
+    vt = np.empty((n, d))
+    for h in range(num_heads):
+        sl = slice(h * dh, (h + 1) * dh)
+        S = Q[:, sl] @ K[:, sl].T                    # S[i, j] = q_i . k_j
+        A = silu(S) / N * M
+        vt[:, sl] = A @ V[:, sl]
+    return vt * U
+
+
+# ----------------------------------------------------------------------------------------------
+# HSTU block, encoder, head
+# ----------------------------------------------------------------------------------------------
+def block_forward(x: np.ndarray, groups: np.ndarray, times: np.ndarray, layer: Dict[str, np.ndarray],
+                  num_heads: int, eps: float = 1e-5, return_parts: bool = False):
+    """One HSTU block for one user [P3 方法, update equations]."""
+    x = np.asarray(x, dtype=np.float64)
+    xt = group_layer_norm(x, groups, layer["gln1_gamma"], layer["gln1_beta"], eps)
+    qkvu = linear(xt, layer["w_qkvu"], layer.get("b_qkvu"))
+    y = hstu_attention(qkvu, groups, times, num_heads)
+    z = group_layer_norm(y, groups, layer["gln2_gamma"], layer["gln2_beta"], eps)
+    hid = silu(linear(z, layer["w_mlp1"], layer.get("b_mlp1")))
+    out = linear(hid, layer["w_mlp2"], layer.get("b_mlp2")) + x
+    if return_parts:
+        return out, dict(xt=xt, qkvu=qkvu, y=y, z=z, hid=hid)
+    return out
+
+
+def head_forward(x_cand: np.ndarray, head: Dict[str, np.ndarray]) -> np.ndarray:
+    """Candidate readout: logits = W_h2 silu(W_h1 x + b_h1) + b_h2, columns (CTR, CTCVR)."""
+    hid = silu(linear(x_cand, head["w_head1"], head.get("b_head1")))
+    return linear(hid, head["w_head2"], head.get("b_head2"))
+
+
+def encoder_forward(offsets: np.ndarray, groups: np.ndarray, times: np.ndarray, x: np.ndarray,
+                    layers: Sequence[Dict[str, np.ndarray]], head: Optional[Dict[str, np.ndarray]],
+                    num_heads: int, eps: float = 1e-5) -> Tuple[np.ndarray, np.ndarray]:
+    """L blocks over every user of a packed batch, then the head at candidate tokens.
+
+    Users are processed one at a time (no cross-user attention, [P1/P2] sequence packing).
+    Returns (hidden [T, d], logits [C, 2]) with candidates in packed order.
+    """
+    offsets = np.asarray(offsets, dtype=np.int64)
+    x = np.asarray(x, dtype=np.float64)
+    hidden = np.empty_like(x)
+    for b in range(offsets.shape[0] - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        xb = x[lo:hi]
+        for layer in layers:
+            xb = block_forward(xb, groups[lo:hi], times[lo:hi], layer, num_heads, eps)
+        hidden[lo:hi] = xb
+    cand = np.asarray(groups) == G_C
+    logits = head_forward(hidden[cand], head) if head is not None else np.zeros((int(cand.sum()), 2))
+    return hidden, logits
+
+
+def params_layers(params) -> List[Dict[str, np.ndarray]]:
+    """float64 copies of a generated parameter set's layers (values unchanged)."""
+    return [{k: np.asarray(v, dtype=np.float64) for k, v in lay.items()} for lay in params.layers]
+
+
+def params_head(params) -> Dict[str, np.ndarray]:
+    return {k: np.asarray(v, dtype=np.float64) for k, v in params.head.items()}

@@ -1,0 +1,362 @@
+"""Pins of the CPU oracle against things other than itself (runs without a GPU).
+
+Each test checks the oracle against a fact the pages or the mathematics fix: hand-built masks for
+the pages' worked examples, the block structure the pages describe, GroupLN invariants and torch's
+layer_norm, closed forms and library reductions of the attention, and invariants the method must
+satisfy (candidate permutation equivariance, candidate independence, user isolation, no temporal
+leakage).  A plausible slip in the oracle (a wrong comparison, a transposed product, a dropped 1/N,
+a wrong group index) fails at least one of them.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mtgr_oracle as O
+from generative_recommendation_ranking_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_golden_mask(name):
+    rows, groups, times = [], None, None
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            if line.startswith("groups"):
+                groups = np.array([int(v) for v in line.split()[1:]], dtype=np.uint8)
+            elif line.startswith("times"):
+                times = np.array([float(v) for v in line.split()[1:]], dtype=np.float32)
+            else:
+                rows.append([int(v) for v in line.split()])
+    return groups, times, np.array(rows, dtype=np.uint8)
+
+
+# ------------------------------------------------------------------------------------------
+# Mask: worked examples and block structure ([P1] eight-item example, [P5] 7.3.4)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["mask_toy8.txt", "mask_temporal_abc.txt"])
+def test_mask_golden(name):
+    g, t, expected = _read_golden_mask(name)
+    assert expected.shape == (g.shape[0], g.shape[0])
+    np.testing.assert_array_equal(O.mask(g, t), expected)
+
+
+def test_mask_p5_layout_blocks():
+    # [P5] 7.3.3 layout: [Age, Gender, City, Seq_1..100, RT_1..10, Cand_1..3]
+    n_u, n_s, n_r, k = 3, 100, 10, 3
+    g = np.array([0] * n_u + [1] * n_s + [2] * n_r + [3] * k, dtype=np.uint8)
+    t_r = np.arange(n_r, dtype=np.float32) * 60.0            # distinct, increasing
+    t_c = np.array([-1.0, 270.0, 10_000.0], dtype=np.float32)  # before all, mid, after all
+    t = np.concatenate([np.full(n_u + n_s, -np.inf, np.float32), t_r, t_c])
+    M = O.mask(g, t)
+    s = n_u + n_s
+    r0, r1 = s, s + n_r
+    assert (M[:, :s] == 1).all()                       # rule 1: U/S columns all ones
+    assert (M[:s, s:] == 0).all()                      # static rows see no R and no C
+    np.testing.assert_array_equal(M[r0:r1, r0:r1], np.tril(np.ones((n_r, n_r), np.uint8)))  # rule 2
+    np.testing.assert_array_equal(M[r1:, r1:], np.eye(k, dtype=np.uint8))  # rule 3: diagonal
+    assert (M[r0:r1, r1:] == 0).all()                  # R rows never see candidates
+    # candidate -> R by exposure time
+    np.testing.assert_array_equal(M[r1 + 0, r0:r1], np.zeros(n_r, np.uint8))
+    np.testing.assert_array_equal(M[r1 + 1, r0:r1], (t_r < 270.0).astype(np.uint8))
+    np.testing.assert_array_equal(M[r1 + 2, r0:r1], np.ones(n_r, np.uint8))
+
+
+def test_mask_ties_and_order_agnostic():
+    rng = np.random.default_rng(7)
+    # equal timestamps: invisible to each other (strict), visible to self
+    g = np.array([0, 2, 2, 3], np.uint8)
+    t = np.array([-np.inf, 5.0, 5.0, 5.0], np.float32)
+    M = O.mask(g, t)
+    np.testing.assert_array_equal(M, np.array([[1, 0, 0, 0], [1, 1, 0, 0], [1, 0, 1, 0], [1, 0, 0, 1]], np.uint8))
+    # permuting the tokens permutes the mask (the rules are type-based, not position-based)
+    g = np.array([0] * 3 + [1] * 5 + [2] * 6 + [3] * 4, np.uint8)
+    t = np.concatenate([np.full(8, -np.inf), rng.uniform(0, 10, 10)]).astype(np.float32)
+    perm = rng.permutation(g.shape[0])
+    np.testing.assert_array_equal(O.mask(g[perm], t[perm]), O.mask(g, t)[np.ix_(perm, perm)])
+
+
+def test_mask_empty_segments():
+    # a user with only candidates, a user with only static tokens, an empty user
+    np.testing.assert_array_equal(O.mask(np.array([3, 3, 3], np.uint8), np.array([1, 1, 1], np.float32)),
+                                  np.eye(3, dtype=np.uint8))
+    np.testing.assert_array_equal(O.mask(np.array([0, 1, 1], np.uint8), np.full(3, -np.inf, np.float32)),
+                                  np.ones((3, 3), np.uint8))
+    assert O.mask(np.zeros(0, np.uint8), np.zeros(0, np.float32)).shape == (0, 0)
+
+
+def test_visible_pair_closed_form():
+    # sorted distinct R: pairs = n*n_static + n_R(n_R+1)/2 + sum_c #{R: t_r < t_c} + K
+    rng = np.random.default_rng(3)
+    for _ in range(5):
+        n_u, n_s, n_r, k = [int(v) for v in rng.integers(0, 20, 4)]
+        t_r = np.sort(rng.permutation(1000)[:n_r].astype(np.float32))
+        t_c = rng.uniform(0, 1000, k).astype(np.float32)
+        g = np.array([0] * n_u + [1] * n_s + [2] * n_r + [3] * k, np.uint8)
+        t = np.concatenate([np.full(n_u + n_s, -np.inf, np.float32), t_r, t_c])
+        n = g.shape[0]
+        expect = n * (n_u + n_s) + n_r * (n_r + 1) // 2 + sum(int((t_r < c).sum()) for c in t_c) + k
+        assert O.visible_pairs(g, t) == expect
+
+
+# ------------------------------------------------------------------------------------------
+# GroupLN ([P5] 7.3.3): per-token statistics, per-group affine
+# ------------------------------------------------------------------------------------------
+def test_groupln_matches_layer_norm_per_group():
+    rng = np.random.default_rng(11)
+    n, d = 40, 48
+    x = rng.standard_normal((n, d)) * rng.uniform(0.1, 5, (n, 1)) + rng.uniform(-3, 3, (n, 1))
+    g = rng.integers(0, 4, n).astype(np.uint8)
+    gamma = rng.uniform(0.5, 1.5, (4, d))
+    beta = rng.uniform(-0.1, 0.1, (4, d))
+    y = O.group_layer_norm(x, g, gamma, beta, 1e-5)
+    for grp in range(4):
+        rows = g == grp
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(x[rows]), (d,),
+                                             torch.from_numpy(gamma[grp]), torch.from_numpy(beta[grp]), 1e-5)
+        np.testing.assert_allclose(y[rows], ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_groupln_invariants():
+    rng = np.random.default_rng(12)
+    n, d = 64, 32
+    x = rng.standard_normal((n, d)) * 3.0 + 1.0
+    g = np.repeat(np.arange(4, dtype=np.uint8), n // 4)
+    ones, zeros = np.ones((4, d)), np.zeros((4, d))
+    y = O.group_layer_norm(x, g, ones, zeros, 1e-5)
+    var = x.var(axis=1)
+    np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-12)
+    np.testing.assert_allclose(y.var(axis=1), var / (var + 1e-5), rtol=1e-12)
+    # per-group pooled mean 0 / variance ~1 follows from the per-token statistics
+    for grp in range(4):
+        assert abs(y[g == grp].mean()) < 1e-12
+        assert abs(y[g == grp].var() - 1.0) < 1e-5
+    # invariant to a positive per-token scale (the groups' x1/x0.5/x2/x4 input scales), up to eps
+    s = np.array([1.0, 0.5, 2.0, 4.0])[g][:, None]
+    np.testing.assert_allclose(O.group_layer_norm(x * s, g, ones, zeros, 0.0),
+                               O.group_layer_norm(x, g, ones, zeros, 0.0), atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------------
+# Attention: library reductions and closed forms ([P3] update equation for V~)
+# ------------------------------------------------------------------------------------------
+def _qkvu(rng, n, d):
+    return rng.standard_normal((n, 4 * d)) * 0.7
+
+
+def _torch_silu_attention(q, k, v, u, maskmat, n):
+    # dense silu attention with a given 0/1 mask, torch fp64
+    q, k, v, u, m = (torch.from_numpy(a) for a in (q, k, v, u, maskmat))
+    return ((torch.nn.functional.silu(q @ k.T) / n * m) @ v * u).numpy()
+
+
+@pytest.mark.parametrize("H", [1, 2, 4])
+def test_attention_all_static_is_dense_silu_attention(H):
+    rng = np.random.default_rng(20 + H)
+    n, d = 37, 32
+    qkvu = _qkvu(rng, n, d)
+    g = np.array([0] * 5 + [1] * (n - 5), np.uint8)
+    t = np.full(n, -np.inf, np.float32)
+    y = O.hstu_attention(qkvu, g, t, H)
+    dh = d // H
+    for h in range(H):
+        sl = slice(h * dh, (h + 1) * dh)
+        q, k, v = qkvu[:, sl], qkvu[:, d:2 * d][:, sl], qkvu[:, 2 * d:3 * d][:, sl]
+        u = qkvu[:, 3 * d:][:, sl]
+        ref = _torch_silu_attention(q, k, v, u, np.ones((n, n)), n)
+        np.testing.assert_allclose(y[:, sl], ref, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_sorted_realtime_is_causal_tril():
+    rng = np.random.default_rng(30)
+    n, d = 29, 16
+    qkvu = _qkvu(rng, n, d)
+    g = np.full(n, 2, np.uint8)
+    t = np.sort(rng.permutation(10_000)[:n]).astype(np.float32)   # strictly increasing
+    y = O.hstu_attention(qkvu, g, t, 1)
+    q, k, v, u = qkvu[:, :d], qkvu[:, d:2 * d], qkvu[:, 2 * d:3 * d], qkvu[:, 3 * d:]
+    ref = _torch_silu_attention(q, k, v, u, torch.tril(torch.ones(n, n, dtype=torch.float64)).numpy(), n)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_attention_all_candidates_closed_form():
+    rng = np.random.default_rng(31)
+    K, d, H = 9, 24, 3
+    qkvu = _qkvu(rng, K, d)
+    g = np.full(K, 3, np.uint8)
+    t = rng.uniform(0, 100, K).astype(np.float32)
+    y = O.hstu_attention(qkvu, g, t, H)
+    dh = d // H
+    for i in range(K):
+        for h in range(H):
+            sl = slice(h * dh, (h + 1) * dh)
+            q, k = qkvu[i, :d][sl], qkvu[i, d:2 * d][sl]
+            v, u = qkvu[i, 2 * d:3 * d][sl], qkvu[i, 3 * d:][sl]
+            s = float(q @ k)
+            expect = s / (1.0 + np.exp(-s)) / K * v * u
+            np.testing.assert_allclose(y[i, sl], expect, rtol=1e-12, atol=1e-15)
+
+
+def test_attention_normaliser_is_total_token_count():
+    # one static token and extra candidates: the static row's output scales as 1/N (N = all tokens)
+    rng = np.random.default_rng(32)
+    d = 8
+    qkvu1 = _qkvu(rng, 1, d)
+    g1 = np.array([0], np.uint8)
+    y1 = O.hstu_attention(qkvu1, g1, np.array([-np.inf], np.float32), 1)
+    extra = _qkvu(rng, 3, d)
+    y4 = O.hstu_attention(np.concatenate([qkvu1, extra]), np.array([0, 3, 3, 3], np.uint8),
+                          np.array([-np.inf, 1, 2, 3], np.float32), 1)
+    np.testing.assert_allclose(y4[0], y1[0] / 4.0, rtol=1e-13)
+
+
+# ------------------------------------------------------------------------------------------
+# Block and encoder: closed forms and invariants
+# ------------------------------------------------------------------------------------------
+def _small_model(seed, L=2, d=32, H=2, h=64, scale_bias=0.0):
+    rng = np.random.default_rng(seed)
+    p = synth.make_params(rng, L, d, H, h, "f32")
+    layers = O.params_layers(p)
+    if scale_bias:
+        for lay in layers:
+            for key in ("b_qkvu", "b_mlp1", "b_mlp2"):
+                lay[key] = rng.uniform(-scale_bias, scale_bias, lay[key].shape)
+    head = O.params_head(p)
+    return rng, layers, head
+
+
+def _small_batch(rng, d, lengths):
+    n_u, n_s, n_r, k = zip(*lengths)
+    return synth.batch_from_lengths(n_u, n_s, n_r, k, d, rng, "f32")
+
+
+def test_block_mlp_residual_closed_form():
+    rng, layers, _ = _small_model(40, L=1, scale_bias=0.3)
+    lay = dict(layers[0])
+    lay["w_mlp1"] = np.zeros_like(lay["w_mlp1"])
+    lay["b_mlp1"] = np.zeros_like(lay["b_mlp1"])
+    b = _small_batch(rng, 32, [(2, 5, 4, 3)])
+    out = O.block_forward(b.x, b.group_ids, b.timestamps, lay, 2)
+    np.testing.assert_allclose(out, b.x.astype(np.float64) + lay["b_mlp2"], rtol=0, atol=1e-14)
+
+
+def test_block_gate_closed_form():
+    # U projection zero => gated attention is zero => GLN2 returns beta of the token's group
+    rng, layers, _ = _small_model(41, L=1, scale_bias=0.3)
+    lay = dict(layers[0])
+    d = 32
+    w = lay["w_qkvu"].copy()
+    w[3 * d:] = 0.0
+    bq = lay["b_qkvu"].copy()
+    bq[3 * d:] = 0.0
+    lay["w_qkvu"], lay["b_qkvu"] = w, bq
+    b = _small_batch(rng, d, [(2, 5, 4, 3)])
+    out = O.block_forward(b.x, b.group_ids, b.timestamps, lay, 2)
+    z = lay["gln2_beta"][b.group_ids.astype(np.int64)]
+    hid = O.silu(z @ lay["w_mlp1"].T + lay["b_mlp1"])
+    np.testing.assert_allclose(out, b.x + hid @ lay["w_mlp2"].T + lay["b_mlp2"], rtol=1e-12, atol=1e-13)
+
+
+def _encode(b, layers, head, H=2):
+    return O.encoder_forward(b.offsets, b.group_ids, b.timestamps, b.x, layers, head, H)
+
+
+def test_candidate_permutation_equivariance():
+    rng, layers, head = _small_model(50)
+    b = _small_batch(rng, 32, [(3, 6, 5, 7)])
+    hid, logit = _encode(b, layers, head)
+    c0 = 3 + 6 + 5
+    perm = np.concatenate([np.arange(c0), c0 + rng.permutation(7)])
+    b2 = synth.Batch(b.offsets, b.group_ids[perm], b.timestamps[perm], b.x[perm], b.n_u, b.n_s, b.n_r, b.k)
+    hid2, logit2 = _encode(b2, layers, head)
+    np.testing.assert_allclose(hid2, hid[perm], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(logit2, logit[perm[c0:] - c0], rtol=0, atol=1e-12)
+
+
+def test_candidate_independence_and_duplicates():
+    rng, layers, head = _small_model(51)
+    b = _small_batch(rng, 32, [(3, 6, 5, 6)])
+    c0 = 3 + 6 + 5
+    b.x[c0 + 4] = b.x[c0 + 1]                  # candidates 1 and 4 identical (same features, time)
+    b.timestamps[c0 + 4] = b.timestamps[c0 + 1]
+    hid, logit = _encode(b, layers, head)
+    np.testing.assert_allclose(logit[4], logit[1], rtol=0, atol=1e-13)
+    x2 = b.x.copy()
+    t2 = b.timestamps.copy()
+    x2[c0 + 2] = rng.standard_normal(32) * 4
+    t2[c0 + 2] = 1e6
+    b2 = synth.Batch(b.offsets, b.group_ids, t2, x2, b.n_u, b.n_s, b.n_r, b.k)
+    hid2, logit2 = _encode(b2, layers, head)
+    others = np.array([i for i in range(b.num_tokens) if i != c0 + 2])
+    np.testing.assert_allclose(hid2[others], hid[others], rtol=0, atol=1e-13)
+    assert np.abs(hid2[c0 + 2] - hid[c0 + 2]).max() > 1e-3
+
+
+def test_user_isolation_and_packing():
+    rng, layers, head = _small_model(52)
+    b = _small_batch(rng, 32, [(2, 4, 3, 2), (1, 9, 0, 5), (4, 0, 6, 0), (2, 3, 3, 3)])
+    hid, logit = _encode(b, layers, head)
+    for u in range(b.num_users):
+        s = synth.subset(b, [u])
+        hs, ls = _encode(s, layers, head)
+        np.testing.assert_allclose(hs, hid[synth.user_rows(b, [u])], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(ls, logit[synth.candidate_rows(b, [u])], rtol=0, atol=1e-13)
+    # perturbing user 1 leaves the other users unchanged
+    x2 = b.x.copy()
+    rows1 = synth.user_rows(b, [1])
+    x2[rows1] = rng.standard_normal((rows1.shape[0], 32))
+    b2 = synth.Batch(b.offsets, b.group_ids, b.timestamps, x2, b.n_u, b.n_s, b.n_r, b.k)
+    hid2, _ = _encode(b2, layers, head)
+    keep = synth.user_rows(b, [0, 2, 3])
+    np.testing.assert_allclose(hid2[keep], hid[keep], rtol=0, atol=1e-13)
+
+
+def test_temporal_replay_no_leak():
+    # [P1] failure mode 3: an R event at time tau must not influence any token with t <= tau
+    # (other than itself) nor any U/S token, through all layers.
+    rng, layers, head = _small_model(53, L=3)
+    b = _small_batch(rng, 32, [(2, 5, 12, 10)])
+    hid, _ = _encode(b, layers, head)
+    r0 = 2 + 5
+    p = r0 + 6                                   # the 7th real-time event
+    tau = b.timestamps[p]
+    x2 = b.x.copy()
+    x2[p] = rng.standard_normal(32) * 2.0     # (a constant shift would be removed by GroupLN)
+    b2 = synth.Batch(b.offsets, b.group_ids, b.timestamps, x2, b.n_u, b.n_s, b.n_r, b.k)
+    hid2, _ = _encode(b2, layers, head)
+    unaffected = [i for i in range(b.num_tokens) if i != p and b.timestamps[i] <= tau]
+    assert len(unaffected) > 7
+    np.testing.assert_allclose(hid2[unaffected], hid[unaffected], rtol=0, atol=1e-13)
+    later = [i for i in range(b.num_tokens) if b.timestamps[i] > tau]
+    assert np.abs(hid2[later] - hid[later]).max() > 1e-6
+
+
+# ------------------------------------------------------------------------------------------
+# Generator
+# ------------------------------------------------------------------------------------------
+def test_round_to_bf16_matches_torch():
+    rng = np.random.default_rng(60)
+    a = (rng.standard_normal(100_000) * np.exp(rng.uniform(-20, 20, 100_000))).astype(np.float32)
+    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(synth.round_to_bf16(a), ref)
+
+
+def test_generator_deterministic_and_shapes():
+    b1, p1 = synth.make_workload("tiny-fp32")
+    b2, p2 = synth.make_workload("tiny-fp32")
+    np.testing.assert_array_equal(b1.x, b2.x)
+    np.testing.assert_array_equal(b1.timestamps, b2.timestamps)
+    np.testing.assert_array_equal(p1.layers[0]["w_qkvu"], p2.layers[0]["w_qkvu"])
+    assert b1.num_users == 4 and b1.num_tokens == 4 * 56
+    assert p1.layers[0]["w_qkvu"].shape == (256, 64)
+    # group order U, S, R, C within each user; R sorted; U/S at -inf
+    for u in range(4):
+        g = b1.group_ids[b1.offsets[u]:b1.offsets[u + 1]]
+        assert (np.diff(g.astype(int)) >= 0).all()
+        t = b1.timestamps[b1.offsets[u]:b1.offsets[u + 1]]
+        assert np.isneginf(t[g < 2]).all()
+        assert (np.diff(t[g == 2]) >= 0).all()
