@@ -1,0 +1,418 @@
+// C ABI of libmtgr.so: argument validation, workspace planning and launch sequencing for the
+// MTGR HSTU encoder forward (marovi.ai MTGR page, 方法: GroupLN -> QKVU -> masked silu
+// attention / N -> U gate -> GroupLN -> MLP + residual, L times; candidate head after the last
+// block).  Every check runs on the host before the first launch.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+
+#include "../../include/mtgr.h"
+#include "kernels.h"
+
+using namespace mtgr;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline int esize(int dtype) { return dtype == MTGR_BF16 ? 2 : 4; }
+
+struct Plan {
+  size_t seg = 0, order = 0, tile_off = 0, cand_off = 0, cand_idx = 0, flags = 0;
+  size_t xt = 0, big = 0, y = 0, xres = 0, hin = 0, hhid = 0;
+  size_t total = 0;
+};
+
+struct Sizes {
+  int64_t B = 0, T = 0, C = 0;
+  int d = 0, h = 0, hh = 0, dtype = MTGR_F32;
+  bool need_xres = false, need_head = false, need_acts = false;
+};
+
+Plan make_plan(const Sizes& z) {
+  Plan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  const size_t es = esize(z.dtype);
+  p.flags = take(4 * sizeof(int32_t));
+  p.seg = take((size_t)z.B * sizeof(UserSeg));
+  p.order = take((size_t)z.B * sizeof(int32_t));
+  p.tile_off = take((size_t)(z.B + 1) * sizeof(int32_t));
+  p.cand_off = take((size_t)(z.B + 1) * sizeof(int64_t));
+  p.cand_idx = take((size_t)z.C * sizeof(int64_t));
+  if (z.need_acts) {
+    p.xt = take((size_t)z.T * z.d * es);
+    p.big = take((size_t)z.T * std::max(4 * z.d, z.h) * es);
+    p.y = take((size_t)z.T * z.d * es);
+  }
+  if (z.need_xres) p.xres = take((size_t)z.T * z.d * sizeof(float));
+  if (z.need_head) {
+    p.hin = take((size_t)z.C * z.d * es);
+    p.hhid = take((size_t)z.C * z.hh * es);
+  }
+  p.total = off;
+  return p;
+}
+
+template <typename T>
+inline T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+mtgr_status check_batch(const mtgr_batch* b) {
+  if (!b) return MTGR_ERR_NULL_ARG;
+  if (b->num_users < 0 || b->num_tokens < 0 || b->num_candidates < 0) return MTGR_ERR_BAD_BATCH;
+  if (b->num_users == 0) return (b->num_tokens == 0 && b->num_candidates == 0) ? MTGR_OK : MTGR_ERR_BAD_BATCH;
+  if (!b->offsets_host || !b->offsets) return MTGR_ERR_NULL_ARG;
+  if (b->num_tokens > 0 && (!b->group_ids || !b->timestamps)) return MTGR_ERR_NULL_ARG;
+  const int64_t* o = b->offsets_host;
+  if (o[0] != 0) return MTGR_ERR_BAD_BATCH;
+  for (int32_t i = 0; i < b->num_users; ++i) {
+    if (o[i + 1] < o[i]) return MTGR_ERR_BAD_BATCH;
+    if (o[i + 1] - o[i] > (int64_t)(1 << 30)) return MTGR_ERR_BAD_BATCH;
+  }
+  if (o[b->num_users] != b->num_tokens) return MTGR_ERR_BAD_BATCH;
+  if (b->num_candidates > b->num_tokens) return MTGR_ERR_BAD_BATCH;
+  return MTGR_OK;
+}
+
+int64_t total_tiles(const mtgr_batch* b, int q_tile) {
+  int64_t t = 0;
+  for (int32_t i = 0; i < b->num_users; ++i) {
+    const int64_t n = b->offsets_host[i + 1] - b->offsets_host[i];
+    t += (n + q_tile - 1) / q_tile;
+  }
+  return t;
+}
+
+bool dh_ok(int dtype, int dh) {
+  if (dtype == MTGR_BF16) return dh == 64 || dh == 128;
+  return dh == 32 || dh == 64 || dh == 128;
+}
+
+mtgr_status check_attn_shape(int32_t d, int32_t H, int32_t dtype) {
+  if (dtype != MTGR_F32 && dtype != MTGR_BF16) return MTGR_ERR_UNSUPPORTED;
+  if (d <= 0 || H <= 0 || d % H != 0 || d > 1024) return MTGR_ERR_BAD_SHAPE;
+  if (!dh_ok(dtype, d / H)) return MTGR_ERR_BAD_SHAPE;
+  return MTGR_OK;
+}
+
+mtgr_status check_block(const mtgr_block_params* p) {
+  if (!p) return MTGR_ERR_NULL_ARG;
+  mtgr_status st = check_attn_shape(p->d_model, p->num_heads, p->dtype);
+  if (st != MTGR_OK) return st;
+  const int mult = p->dtype == MTGR_BF16 ? 64 : 8;
+  if (p->d_model % mult != 0 || p->mlp_hidden <= 0 || p->mlp_hidden % mult != 0 ||
+      p->mlp_hidden > 8192)
+    return MTGR_ERR_BAD_SHAPE;
+  if (!(p->ln_eps >= 0.f) || !std::isfinite(p->ln_eps)) return MTGR_ERR_BAD_SHAPE;
+  if (!p->gln1_gamma || !p->gln1_beta || !p->w_qkvu || !p->gln2_gamma || !p->gln2_beta ||
+      !p->w_mlp1 || !p->w_mlp2)
+    return MTGR_ERR_NULL_ARG;
+  return MTGR_OK;
+}
+
+mtgr_status check_encoder(const mtgr_encoder_params* p) {
+  if (!p || !p->layers) return MTGR_ERR_NULL_ARG;
+  if (p->num_layers < 1) return MTGR_ERR_BAD_SHAPE;
+  for (int32_t l = 0; l < p->num_layers; ++l) {
+    mtgr_status st = check_block(&p->layers[l]);
+    if (st != MTGR_OK) return st;
+    if (p->layers[l].d_model != p->layers[0].d_model ||
+        p->layers[l].num_heads != p->layers[0].num_heads ||
+        p->layers[l].dtype != p->layers[0].dtype)
+      return MTGR_ERR_BAD_SHAPE;
+  }
+  const int mult = p->layers[0].dtype == MTGR_BF16 ? 32 : 8;
+  if (p->head_hidden <= 0 || p->head_hidden % mult != 0 || p->head_hidden > 8192)
+    return MTGR_ERR_BAD_SHAPE;
+  if (!p->w_head1 || !p->w_head2) return MTGR_ERR_NULL_ARG;
+  return MTGR_OK;
+}
+
+Sizes sizes_for(const mtgr_batch* b, int d, int h, int hh, int dtype) {
+  Sizes z;
+  z.B = b->num_users;
+  z.T = b->num_tokens;
+  z.C = b->num_candidates;
+  z.d = d;
+  z.h = h;
+  z.hh = hh;
+  z.dtype = dtype;
+  return z;
+}
+
+PrepBufs prep_bufs(void* ws, const Plan& p) {
+  PrepBufs pb;
+  pb.seg = at<UserSeg>(ws, p.seg);
+  pb.order = at<int32_t>(ws, p.order);
+  pb.tile_off = at<int32_t>(ws, p.tile_off);
+  pb.cand_off = at<int64_t>(ws, p.cand_off);
+  pb.cand_idx = at<int64_t>(ws, p.cand_idx);
+  pb.flags = at<int32_t>(ws, p.flags);
+  return pb;
+}
+
+inline int q_tile_for(int dtype) { return dtype == MTGR_BF16 ? kAttnQTileBf16 : kAttnQTileF32; }
+
+mtgr_status hip_status(hipError_t e) { return e == hipSuccess ? MTGR_OK : MTGR_ERR_HIP; }
+
+#define MTGR_TRY(expr)                           \
+  do {                                           \
+    hipError_t _e = (expr);                      \
+    if (_e != hipSuccess) return MTGR_ERR_HIP;   \
+  } while (0)
+
+hipError_t linear(int64_t M, int N, int K, int dtype, int epi, const void* a, const void* w,
+                  const void* bias, const float* resid, void* out, hipStream_t s) {
+  if (dtype == MTGR_BF16)
+    return launch_gemm_bf16(M, N, K, epi, static_cast<const bf16*>(a), static_cast<const bf16*>(w),
+                            static_cast<const bf16*>(bias), resid, out, s);
+  return launch_gemm_f32(M, N, K, epi, static_cast<const float*>(a), static_cast<const float*>(w),
+                         static_cast<const float*>(bias), resid, static_cast<float*>(out), s);
+}
+
+hipError_t attention(const mtgr_batch* b, int d, int H, int dtype, const PrepBufs& pb,
+                     const void* qkvu, void* y, hipStream_t s) {
+  const int64_t tiles = total_tiles(b, q_tile_for(dtype));
+  if (dtype == MTGR_BF16)
+    return launch_attention_bf16(b->num_users, tiles, d, H, b->offsets, pb.seg, pb.order,
+                                 pb.tile_off, b->timestamps, static_cast<const bf16*>(qkvu),
+                                 static_cast<bf16*>(y), s);
+  return launch_attention_f32(b->num_users, tiles, d, H, b->offsets, pb.seg, pb.order,
+                              pb.tile_off, b->timestamps, static_cast<const float*>(qkvu),
+                              static_cast<float*>(y), s);
+}
+
+// One block: x_out = x_in + MLP(GLN2(attn(GLN1(x_in)) (.) U)); x_out may alias x_in.
+hipError_t run_block(const mtgr_block_params* p, const mtgr_batch* b, const PrepBufs& pb,
+                     const Plan& pl, void* ws, const float* x_in, float* x_out, hipStream_t s) {
+  const int64_t T = b->num_tokens;
+  const int d = p->d_model, h = p->mlp_hidden, dt = p->dtype;
+  const int act = dt == MTGR_BF16 ? 1 : 0;
+  void* xt = at<void>(ws, pl.xt);
+  void* big = at<void>(ws, pl.big);
+  void* y = at<void>(ws, pl.y);
+  hipError_t e;
+  e = launch_groupln(T, d, 0, act, act, x_in, b->group_ids, p->gln1_gamma, p->gln1_beta,
+                     p->ln_eps, xt, s);
+  if (e != hipSuccess) return e;
+  e = linear(T, 4 * d, d, dt, MTGR_EPI_STORE, xt, p->w_qkvu, p->b_qkvu, nullptr, big, s);
+  if (e != hipSuccess) return e;
+  e = attention(b, d, p->num_heads, dt, pb, big, y, s);
+  if (e != hipSuccess) return e;
+  e = launch_groupln(T, d, act, act, act, y, b->group_ids, p->gln2_gamma, p->gln2_beta,
+                     p->ln_eps, xt, s);
+  if (e != hipSuccess) return e;
+  e = linear(T, h, d, dt, MTGR_EPI_SILU, xt, p->w_mlp1, p->b_mlp1, nullptr, big, s);
+  if (e != hipSuccess) return e;
+  return linear(T, d, h, dt, MTGR_EPI_RESIDUAL_F32, big, p->w_mlp2, p->b_mlp2, x_in, x_out, s);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t mtgr_abi_version(void) { return MTGR_ABI_VERSION; }
+
+const char* mtgr_status_str(int32_t status) {
+  switch (status) {
+    case MTGR_OK: return "ok";
+    case MTGR_ERR_NULL_ARG: return "a required pointer is NULL";
+    case MTGR_ERR_BAD_SHAPE: return "unsupported or inconsistent shape";
+    case MTGR_ERR_BAD_BATCH: return "malformed batch (offsets, token or candidate counts)";
+    case MTGR_ERR_UNSUPPORTED: return "unsupported dtype or option";
+    case MTGR_ERR_WORKSPACE: return "workspace missing or too small";
+    case MTGR_ERR_HIP: return "HIP launch or copy failed";
+    default: return "unknown status";
+  }
+}
+
+mtgr_status mtgr_encoder_workspace_size(const mtgr_encoder_params* p, const mtgr_batch* b,
+                                        size_t* bytes) {
+  if (!bytes) return MTGR_ERR_NULL_ARG;
+  mtgr_status st = check_encoder(p);
+  if (st != MTGR_OK) return st;
+  if ((st = check_batch(b)) != MTGR_OK) return st;
+  Sizes z = sizes_for(b, p->layers[0].d_model, 0, p->head_hidden, p->layers[0].dtype);
+  for (int32_t l = 0; l < p->num_layers; ++l) z.h = std::max(z.h, (int)p->layers[l].mlp_hidden);
+  z.need_acts = z.need_xres = z.need_head = true;
+  *bytes = make_plan(z).total;
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_block_workspace_size(const mtgr_block_params* p, const mtgr_batch* b,
+                                      size_t* bytes) {
+  if (!bytes) return MTGR_ERR_NULL_ARG;
+  mtgr_status st = check_block(p);
+  if (st != MTGR_OK) return st;
+  if ((st = check_batch(b)) != MTGR_OK) return st;
+  Sizes z = sizes_for(b, p->d_model, p->mlp_hidden, 0, p->dtype);
+  z.need_acts = true;
+  *bytes = make_plan(z).total;
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_attention_workspace_size(const mtgr_batch* b, int32_t d, int32_t num_heads,
+                                          size_t* bytes) {
+  if (!bytes) return MTGR_ERR_NULL_ARG;
+  mtgr_status st = check_batch(b);
+  if (st != MTGR_OK) return st;
+  if (d <= 0 || num_heads <= 0 || d % num_heads != 0) return MTGR_ERR_BAD_SHAPE;
+  Sizes z = sizes_for(b, d, 0, 0, MTGR_F32);
+  *bytes = make_plan(z).total;
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_encoder_fwd(const mtgr_encoder_params* p, const mtgr_batch* b, const float* x_in,
+                             float* hidden_out, float* logits, void* ws, size_t ws_bytes,
+                             void* stream) {
+  size_t need = 0;
+  mtgr_status st = mtgr_encoder_workspace_size(p, b, &need);
+  if (st != MTGR_OK) return st;
+  if (b->num_tokens > 0 && !x_in) return MTGR_ERR_NULL_ARG;
+  if (b->num_candidates > 0 && !logits) return MTGR_ERR_NULL_ARG;
+  if (!ws || ws_bytes < need) return MTGR_ERR_WORKSPACE;
+  if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int dt = p->layers[0].dtype;
+  Sizes z = sizes_for(b, p->layers[0].d_model, 0, p->head_hidden, dt);
+  for (int32_t l = 0; l < p->num_layers; ++l) z.h = std::max(z.h, (int)p->layers[l].mlp_hidden);
+  z.need_acts = z.need_xres = z.need_head = true;
+  const Plan pl = make_plan(z);
+  const PrepBufs pb = prep_bufs(ws, pl);
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dt), pb, true, s));
+  float* xr = hidden_out ? hidden_out : at<float>(ws, pl.xres);
+  for (int32_t l = 0; l < p->num_layers; ++l) {
+    const float* src = (l == 0) ? x_in : xr;
+    MTGR_TRY(run_block(&p->layers[l], b, pb, pl, ws, src, xr, s));
+  }
+  const int64_t C = b->num_candidates;
+  if (C > 0) {
+    const int d = z.d, hh = p->head_hidden;
+    const int act = dt == MTGR_BF16 ? 1 : 0;
+    void* hin = at<void>(ws, pl.hin);
+    void* hhid = at<void>(ws, pl.hhid);
+    MTGR_TRY(launch_gather_rows(C, b->num_tokens, d, xr, pb.cand_idx, act, hin, s));
+    MTGR_TRY(linear(C, hh, d, dt, MTGR_EPI_SILU, hin, p->w_head1, p->b_head1, nullptr, hhid, s));
+    MTGR_TRY(launch_head_out(C, hh, act, hhid, p->w_head2, p->b_head2, logits, s));
+  }
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_block_fwd(const mtgr_block_params* p, const mtgr_batch* b, const float* x_in,
+                           float* x_out, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  mtgr_status st = mtgr_block_workspace_size(p, b, &need);
+  if (st != MTGR_OK) return st;
+  if (b->num_tokens > 0 && (!x_in || !x_out)) return MTGR_ERR_NULL_ARG;
+  if (!ws || ws_bytes < need) return MTGR_ERR_WORKSPACE;
+  if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Sizes z = sizes_for(b, p->d_model, p->mlp_hidden, 0, p->dtype);
+  z.need_acts = true;
+  const Plan pl = make_plan(z);
+  const PrepBufs pb = prep_bufs(ws, pl);
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(p->dtype), pb, false, s));
+  MTGR_TRY(run_block(p, b, pb, pl, ws, x_in, x_out, s));
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_groupln_fwd(const mtgr_batch* b, int32_t d, int32_t in_dtype, int32_t out_dtype,
+                             int32_t param_dtype, const void* gamma, const void* beta, float eps,
+                             const void* x, void* y, void* stream) {
+  mtgr_status st = check_batch(b);
+  if (st != MTGR_OK) return st;
+  if (d <= 0 || d % 8 != 0 || d > 1024) return MTGR_ERR_BAD_SHAPE;
+  auto ok_dt = [](int32_t v) { return v == MTGR_F32 || v == MTGR_BF16; };
+  if (!ok_dt(in_dtype) || !ok_dt(out_dtype) || !ok_dt(param_dtype)) return MTGR_ERR_UNSUPPORTED;
+  if (in_dtype == MTGR_BF16 && out_dtype == MTGR_F32) return MTGR_ERR_UNSUPPORTED;
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return MTGR_ERR_BAD_SHAPE;
+  if (b->num_tokens == 0) return MTGR_OK;
+  if (!gamma || !beta || !x || !y) return MTGR_ERR_NULL_ARG;
+  return hip_status(launch_groupln(b->num_tokens, d, in_dtype, out_dtype, param_dtype, x,
+                                   b->group_ids, gamma, beta, eps, y,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int32_t epilogue,
+                            const void* a, const void* w, const void* bias, const float* resid,
+                            void* out, void* stream) {
+  if (dtype != MTGR_F32 && dtype != MTGR_BF16) return MTGR_ERR_UNSUPPORTED;
+  if (epilogue < MTGR_EPI_STORE || epilogue > MTGR_EPI_RESIDUAL_F32) return MTGR_ERR_UNSUPPORTED;
+  if (M < 0 || N <= 0 || K <= 0 || N > (1 << 20)) return MTGR_ERR_BAD_SHAPE;
+  if (dtype == MTGR_BF16 && K % 64 != 0) return MTGR_ERR_BAD_SHAPE;
+  if (dtype == MTGR_F32 && K % 4 != 0) return MTGR_ERR_BAD_SHAPE;
+  if (M == 0) return MTGR_OK;
+  if (!a || !w || !out) return MTGR_ERR_NULL_ARG;
+  if (epilogue == MTGR_EPI_RESIDUAL_F32 && !resid) return MTGR_ERR_NULL_ARG;
+  return hip_status(linear(M, N, K, dtype, epilogue, a, w, bias, resid, out,
+                           static_cast<hipStream_t>(stream)));
+}
+
+mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
+                               const void* qkvu, void* y_gated, void* ws, size_t ws_bytes,
+                               void* stream) {
+  size_t need = 0;
+  mtgr_status st = mtgr_attention_workspace_size(b, d, num_heads, &need);
+  if (st != MTGR_OK) return st;
+  if ((st = check_attn_shape(d, num_heads, dtype)) != MTGR_OK) return st;
+  if (!ws || ws_bytes < need) return MTGR_ERR_WORKSPACE;
+  if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;
+  if (!qkvu || !y_gated) return MTGR_ERR_NULL_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Sizes z = sizes_for(b, d, 0, 0, MTGR_F32);
+  const Plan pl = make_plan(z);
+  const PrepBufs pb = prep_bufs(ws, pl);
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), pb, false, s));
+  MTGR_TRY(attention(b, d, num_heads, dtype, pb, qkvu, y_gated, s));
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_validate_batch(const mtgr_batch* b, void* ws, size_t ws_bytes, void* stream,
+                                int32_t* flags_out) {
+  if (!flags_out) return MTGR_ERR_NULL_ARG;
+  *flags_out = 0;
+  mtgr_status st = check_batch(b);
+  if (st != MTGR_OK) return st;
+  Sizes z = sizes_for(b, 8, 0, 0, MTGR_F32);
+  const Plan pl = make_plan(z);
+  if (!ws || ws_bytes < pl.total) return MTGR_ERR_WORKSPACE;
+  if (b->num_users == 0) return MTGR_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* flags = at<int32_t>(ws, pl.flags);
+  int32_t host[4] = {0, 0, 0, 0};
+  MTGR_TRY(hipMemsetAsync(flags, 0, 4 * sizeof(int32_t), s));
+  MTGR_TRY(launch_validate(b->num_users, b->offsets, b->group_ids, b->timestamps, flags, s));
+  MTGR_TRY(hipMemcpyAsync(host, flags, 4 * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  MTGR_TRY(hipStreamSynchronize(s));
+  int32_t f = host[0];
+  if ((int64_t)host[1] != b->num_candidates) f |= 8;
+  *flags_out = f;
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, uint8_t* mask_dev, void* ws,
+                            size_t ws_bytes, void* stream) {
+  mtgr_status st = check_batch(b);
+  if (st != MTGR_OK) return st;
+  if (user < 0 || user >= b->num_users) return MTGR_ERR_BAD_SHAPE;
+  Sizes z = sizes_for(b, 8, 0, 0, MTGR_F32);
+  const Plan pl = make_plan(z);
+  if (!ws || ws_bytes < pl.total) return MTGR_ERR_WORKSPACE;
+  const int64_t n = b->offsets_host[user + 1] - b->offsets_host[user];
+  if (n == 0) return MTGR_OK;
+  if (!mask_dev) return MTGR_ERR_NULL_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const PrepBufs pb = prep_bufs(ws, pl);
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, kAttnQTileF32, pb, false, s));
+  MTGR_TRY(launch_debug_mask(user, b->offsets, pb.seg, b->timestamps, n, mask_dev, s));
+  return MTGR_OK;
+}
+
+}  // extern "C"

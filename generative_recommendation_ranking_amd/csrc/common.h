@@ -1,0 +1,62 @@
+// Device-side helpers shared by the gfx950 kernels of libmtgr.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mtgr {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }  // RNE
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// silu(z) = z * sigmoid(z) = z / (1 + e^-z).  __expf maps to the hardware exp2 with a
+// log2(e) pre-scale; for z < -88 the exponential overflows to +inf and the quotient is -0,
+// which is the correctly rounded limit.
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// Visibility of key j to query i inside one user whose tokens are ordered U, S, R, C, with
+// n_static = N_U + N_S and rc_end = N_U + N_S + N_R.  Rules of the dynamic mask (fun-rec
+// "MTGR: Hybrid Paradigm Modeling" 7.3.4 Rules 1-3; marovi.ai MTGR page, 方法): static keys
+// are visible to every query; every token sees itself; a real-time key is visible to a
+// real-time or candidate query with a strictly later timestamp; candidate keys are visible
+// to nobody else.  Used by every attention kernel and by the debug mask dump.
+__device__ __forceinline__ bool mtgr_visible(int i, int j, int n_static, int rc_end, float ti,
+                                             float tj) {
+  if (j < n_static) return true;
+  if (i == j) return true;
+  return (i >= n_static) && (j < rc_end) && (tj < ti);
+}
+
+// Per-user segment record written by the batch-prep kernel.
+struct UserSeg {
+  int32_t n_u, n_s, n_r, k;
+};
+
+}  // namespace mtgr

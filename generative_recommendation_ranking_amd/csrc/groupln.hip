@@ -1,0 +1,127 @@
+// Group-Layer Normalization on gfx950.
+//
+// Definition (fun-rec "MTGR: Hybrid Paradigm Modeling" 7.3.3, GLN equation; marovi.ai MTGR
+// page, 方法): LayerNorm statistics of one token over its d features, then the affine
+// parameters gamma[g], beta[g] of the token's group g in {U, S, R, C}:
+//     y_f = (x_f - mean) / sqrt(var + eps) * gamma[g][f] + beta[g][f],  var biased (1/d).
+//
+// Mapping: one 64-lane wavefront per token row, four rows per 256-thread workgroup.  Each lane
+// holds up to two 8-element chunks of the row in registers (d <= 1024), so the row is read from
+// HBM once; mean and variance are two wavefront reductions over registers (two-pass, fp32).
+// The kernel is HBM-bound: it moves (in_bytes + out_bytes) * d per token.
+#include "kernels.h"
+
+namespace mtgr {
+
+namespace {
+
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[i + 4] = b[i]; }
+}
+__device__ __forceinline__ void load8(const bf16* p, float v[8]) {
+  bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[i + 4]; }
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+__device__ __forceinline__ void store8(bf16* p, const float v[8]) {
+  bf16x8 a;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x8*>(p) = a;
+}
+
+template <typename Tin, typename Tout, typename Tp>
+__global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __restrict__ x,
+                                                 const uint8_t* __restrict__ g,
+                                                 const Tp* __restrict__ gamma,
+                                                 const Tp* __restrict__ beta, float eps,
+                                                 Tout* __restrict__ y) {
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= T) return;
+  const int nch = d >> 3;
+  const Tin* xr = x + row * d;
+  float v[2][8];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+      load8(xr + ch * 8, v[c]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s += v[c][i];
+    }
+  }
+  const float inv_d = 1.0f / (float)d;
+  const float mean = wave_sum(s) * inv_d;
+  float q = 0.f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float e = v[c][i] - mean;
+        q += e * e;
+      }
+    }
+  }
+  const float var = wave_sum(q) * inv_d;
+  const float rstd = 1.0f / sqrtf(var + eps);
+  const int grp = g[row] & 3;  // ids outside 0..3 are rejected by validation; stay in bounds
+  const Tp* gr = gamma + (int64_t)grp * d;
+  const Tp* br = beta + (int64_t)grp * d;
+  Tout* yr = y + row * d;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+      float ga[8], be[8], o[8];
+      load8(gr + ch * 8, ga);
+      load8(br + ch * 8, be);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] = (v[c][i] - mean) * rstd * ga[i] + be[i];
+      store8(yr + ch * 8, o);
+    }
+  }
+}
+
+template <typename Tin, typename Tout, typename Tp>
+hipError_t run(int64_t T, int d, const void* x, const uint8_t* g, const void* gamma,
+               const void* beta, float eps, void* y, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int64_t blocks = (T + 3) / 4;
+  k_groupln<Tin, Tout, Tp><<<(unsigned)blocks, 256, 0, s>>>(
+      T, d, static_cast<const Tin*>(x), g, static_cast<const Tp*>(gamma),
+      static_cast<const Tp*>(beta), eps, static_cast<Tout*>(y));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_groupln(int64_t T, int d, int in_kind, int out_kind, int param_kind,
+                          const void* x, const uint8_t* group_ids, const void* gamma,
+                          const void* beta, float eps, void* y, hipStream_t s) {
+  const int key = in_kind * 4 + out_kind * 2 + param_kind;
+  switch (key) {
+    case 0: return run<float, float, float>(T, d, x, group_ids, gamma, beta, eps, y, s);
+    case 1: return run<float, float, bf16>(T, d, x, group_ids, gamma, beta, eps, y, s);
+    case 2: return run<float, bf16, float>(T, d, x, group_ids, gamma, beta, eps, y, s);
+    case 3: return run<float, bf16, bf16>(T, d, x, group_ids, gamma, beta, eps, y, s);
+    case 6: return run<bf16, bf16, float>(T, d, x, group_ids, gamma, beta, eps, y, s);
+    case 7: return run<bf16, bf16, bf16>(T, d, x, group_ids, gamma, beta, eps, y, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace mtgr

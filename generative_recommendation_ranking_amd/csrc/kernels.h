@@ -1,0 +1,64 @@
+// Internal launchers of libmtgr.so (host side).  Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace mtgr {
+
+// ---- batch prep (prep.hip) ----------------------------------------------------------------
+// Segment counts per user, LPT user order (longest users first), q-tile offsets in that order,
+// candidate offsets per user and the packed-order candidate token index list.
+struct PrepBufs {
+  UserSeg* seg;        // [B]
+  int32_t* order;      // [B]   users sorted by token count, descending (ties by index)
+  int32_t* tile_off;   // [B+1] exclusive prefix of ceil(n_b / q_tile) in `order`
+  int64_t* cand_off;   // [B+1] exclusive prefix of K_b in user order
+  int64_t* cand_idx;   // [C]   token row of each candidate, packed order
+  int32_t* flags;      // [4]   validation flags / counters
+};
+hipError_t launch_prep(int32_t B, int64_t C, const int64_t* offsets, const uint8_t* group_ids,
+                       int q_tile, const PrepBufs& pb, bool want_cand_idx, hipStream_t s);
+hipError_t launch_validate(int32_t B, const int64_t* offsets, const uint8_t* group_ids,
+                           const float* timestamps, int32_t* flags, hipStream_t s);
+hipError_t launch_debug_mask(int32_t user, const int64_t* offsets, const UserSeg* seg,
+                             const float* timestamps, int64_t n_user, uint8_t* mask,
+                             hipStream_t s);
+
+// ---- GroupLN (groupln.hip) ---------------------------------------------------------------
+// in_kind/out_kind/param_kind: 0 = float, 1 = bf16
+hipError_t launch_groupln(int64_t T, int d, int in_kind, int out_kind, int param_kind,
+                          const void* x, const uint8_t* group_ids, const void* gamma,
+                          const void* beta, float eps, void* y, hipStream_t s);
+
+// ---- GEMMs (gemm.hip) ----------------------------------------------------------------------
+// out[M][N] = epi(a[M][K] w[N][K]^T + bias); epi as MTGR_EPI_*.
+hipError_t launch_gemm_bf16(int64_t M, int N, int K, int epi, const bf16* a, const bf16* w,
+                            const bf16* bias, const float* resid, void* out, hipStream_t s);
+hipError_t launch_gemm_f32(int64_t M, int N, int K, int epi, const float* a, const float* w,
+                           const float* bias, const float* resid, float* out, hipStream_t s);
+
+// ---- attention (attention.hip) -------------------------------------------------------------
+constexpr int kAttnQTileBf16 = 128;
+constexpr int kAttnQTileF32 = 64;
+hipError_t launch_attention_bf16(int32_t B, int64_t total_tiles, int d, int H,
+                                 const int64_t* offsets, const UserSeg* seg, const int32_t* order,
+                                 const int32_t* tile_off, const float* timestamps,
+                                 const bf16* qkvu, bf16* y, hipStream_t s);
+hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H,
+                                const int64_t* offsets, const UserSeg* seg, const int32_t* order,
+                                const int32_t* tile_off, const float* timestamps,
+                                const float* qkvu, float* y, hipStream_t s);
+
+// ---- head (head.hip) -----------------------------------------------------------------------
+// rows[c] = (out_kind) x[cand_idx[c]]  (fp32 hidden state -> head input dtype)
+hipError_t launch_gather_rows(int64_t C, int64_t T, int d, const float* x,
+                              const int64_t* cand_idx, int out_kind, void* rows, hipStream_t s);
+// logits[c][o] = sum_k hid[c][k] w2[o][k] + b2[o]  (o in {0,1})
+hipError_t launch_head_out(int64_t C, int hh, int kind, const void* hid, const void* w2,
+                           const void* b2, float* logits, hipStream_t s);
+
+}  // namespace mtgr

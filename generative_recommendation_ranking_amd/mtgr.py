@@ -1,0 +1,246 @@
+"""Thin ctypes binding over libmtgr.so (declared in include/mtgr.h).
+
+Functions carry the C names and only marshal arguments: torch tensors become device pointers,
+the current torch stream becomes the hipStream_t.  Every step of the forward pass runs in the
+library's HIP kernels; there is no fallback.  Loading fails loudly when libmtgr.so is missing.
+
+The helper classes `DeviceBatch` and `DeviceModel` copy a synthetic batch / parameter set to the
+GPU with torch (memory only) and build the C structs that point at those tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import List, Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmtgr.so")
+
+MTGR_OK = 0
+MTGR_F32, MTGR_BF16 = 0, 1
+MTGR_EPI_STORE, MTGR_EPI_SILU, MTGR_EPI_RESIDUAL_F32 = 0, 1, 2
+STATUS_NAMES = {0: "MTGR_OK", 1: "MTGR_ERR_NULL_ARG", 2: "MTGR_ERR_BAD_SHAPE",
+                3: "MTGR_ERR_BAD_BATCH", 4: "MTGR_ERR_UNSUPPORTED", 5: "MTGR_ERR_WORKSPACE",
+                6: "MTGR_ERR_HIP"}
+
+# every symbol include/mtgr.h declares
+EXPORTED = [
+    "mtgr_abi_version", "mtgr_status_str", "mtgr_encoder_workspace_size",
+    "mtgr_block_workspace_size", "mtgr_attention_workspace_size", "mtgr_encoder_fwd",
+    "mtgr_block_fwd", "mtgr_groupln_fwd", "mtgr_linear_fwd", "mtgr_attention_fwd",
+    "mtgr_validate_batch", "mtgr_debug_mask",
+]
+
+c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class MtgrBatch(ctypes.Structure):
+    _fields_ = [("num_users", c_i32), ("num_tokens", c_i64), ("num_candidates", c_i64),
+                ("offsets_host", c_vp), ("offsets", c_vp), ("group_ids", c_vp),
+                ("timestamps", c_vp)]
+
+
+class MtgrBlockParams(ctypes.Structure):
+    _fields_ = [("d_model", c_i32), ("num_heads", c_i32), ("mlp_hidden", c_i32), ("dtype", c_i32),
+                ("ln_eps", c_f32), ("gln1_gamma", c_vp), ("gln1_beta", c_vp), ("w_qkvu", c_vp),
+                ("b_qkvu", c_vp), ("gln2_gamma", c_vp), ("gln2_beta", c_vp), ("w_mlp1", c_vp),
+                ("b_mlp1", c_vp), ("w_mlp2", c_vp), ("b_mlp2", c_vp)]
+
+
+class MtgrEncoderParams(ctypes.Structure):
+    _fields_ = [("num_layers", c_i32), ("layers", ctypes.POINTER(MtgrBlockParams)),
+                ("head_hidden", c_i32), ("w_head1", c_vp), ("b_head1", c_vp),
+                ("w_head2", c_vp), ("b_head2", c_vp)]
+
+
+class MtgrError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {STATUS_NAMES.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmtgr.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m generative_recommendation_ranking_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        L.mtgr_abi_version.restype = c_i32
+        L.mtgr_status_str.restype = ctypes.c_char_p
+        L.mtgr_status_str.argtypes = [c_i32]
+        L.mtgr_encoder_workspace_size.argtypes = [P(MtgrEncoderParams), P(MtgrBatch), P(c_sz)]
+        L.mtgr_block_workspace_size.argtypes = [P(MtgrBlockParams), P(MtgrBatch), P(c_sz)]
+        L.mtgr_attention_workspace_size.argtypes = [P(MtgrBatch), c_i32, c_i32, P(c_sz)]
+        L.mtgr_encoder_fwd.argtypes = [P(MtgrEncoderParams), P(MtgrBatch), c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+        L.mtgr_block_fwd.argtypes = [P(MtgrBlockParams), P(MtgrBatch), c_vp, c_vp, c_vp, c_sz, c_vp]
+        L.mtgr_groupln_fwd.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32,
+                                       c_vp, c_vp, c_vp]
+        L.mtgr_linear_fwd.argtypes = [c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
+        L.mtgr_attention_fwd.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]
+        L.mtgr_validate_batch.argtypes = [P(MtgrBatch), c_vp, c_sz, c_vp, P(c_i32)]
+        L.mtgr_debug_mask.argtypes = [P(MtgrBatch), c_i32, c_vp, c_vp, c_sz, c_vp]
+        for name in EXPORTED[2:]:
+            getattr(L, name).restype = c_i32
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != MTGR_OK:
+        raise MtgrError(fn, status)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+# ---------------------------------------------------------------------------------------------
+# device-side containers (torch supplies memory only)
+# ---------------------------------------------------------------------------------------------
+class DeviceBatch:
+    """A packed batch on the GPU plus its C description."""
+
+    def __init__(self, batch, device="cuda", x_dtype=None):
+        import torch
+        self.host_offsets = np.ascontiguousarray(batch.offsets, dtype=np.int64)
+        self.offsets = torch.from_numpy(self.host_offsets).to(device)
+        self.group_ids = torch.from_numpy(np.ascontiguousarray(batch.group_ids)).to(device)
+        self.timestamps = torch.from_numpy(np.ascontiguousarray(batch.timestamps)).to(device)
+        self.x = torch.from_numpy(np.ascontiguousarray(batch.x, dtype=np.float32)).to(device)
+        self.num_users = batch.num_users
+        self.num_tokens = batch.num_tokens
+        self.num_candidates = int((batch.group_ids == 3).sum())
+        self.c = MtgrBatch(self.num_users, self.num_tokens, self.num_candidates,
+                           self.host_offsets.ctypes.data, self.offsets.data_ptr(),
+                           self.group_ids.data_ptr(), self.timestamps.data_ptr())
+
+
+class DeviceModel:
+    """Encoder parameters on the GPU in the storage dtype, plus their C description."""
+
+    def __init__(self, params, device="cuda"):
+        import torch
+        self.dtype = MTGR_BF16 if params.dtype == "bf16" else MTGR_F32
+        tdt = torch.bfloat16 if self.dtype == MTGR_BF16 else torch.float32
+        self.d, self.H, self.h = params.d, params.H, params.h
+        self._keep: List = []
+
+        def dev(a):
+            t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device).to(tdt)
+            self._keep.append(t)
+            return t
+
+        self.layers = []
+        blocks = (MtgrBlockParams * params.num_layers)()
+        for i, lay in enumerate(params.layers):
+            t = {k: dev(v) for k, v in lay.items()}
+            self.layers.append(t)
+            blocks[i] = MtgrBlockParams(params.d, params.H, params.h, self.dtype, params.ln_eps,
+                                        _ptr(t["gln1_gamma"]), _ptr(t["gln1_beta"]), _ptr(t["w_qkvu"]),
+                                        _ptr(t["b_qkvu"]), _ptr(t["gln2_gamma"]), _ptr(t["gln2_beta"]),
+                                        _ptr(t["w_mlp1"]), _ptr(t["b_mlp1"]), _ptr(t["w_mlp2"]),
+                                        _ptr(t["b_mlp2"]))
+        self.blocks = blocks
+        self.head = {k: dev(v) for k, v in params.head.items()}
+        self.head_hidden = int(params.head["w_head1"].shape[0])
+        self.c = MtgrEncoderParams(params.num_layers, blocks, self.head_hidden,
+                                   _ptr(self.head["w_head1"]), _ptr(self.head["b_head1"]),
+                                   _ptr(self.head["w_head2"]), _ptr(self.head["b_head2"]))
+
+
+# ---------------------------------------------------------------------------------------------
+# C entry points (same names as include/mtgr.h)
+# ---------------------------------------------------------------------------------------------
+def mtgr_abi_version() -> int:
+    return int(lib().mtgr_abi_version())
+
+
+def mtgr_status_str(status: int) -> str:
+    return lib().mtgr_status_str(status).decode()
+
+
+def mtgr_encoder_workspace_size(model: DeviceModel, batch: DeviceBatch) -> int:
+    n = c_sz(0)
+    _check("mtgr_encoder_workspace_size",
+           lib().mtgr_encoder_workspace_size(ctypes.byref(model.c), ctypes.byref(batch.c), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mtgr_block_workspace_size(block: MtgrBlockParams, batch: DeviceBatch) -> int:
+    n = c_sz(0)
+    _check("mtgr_block_workspace_size",
+           lib().mtgr_block_workspace_size(ctypes.byref(block), ctypes.byref(batch.c), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mtgr_attention_workspace_size(batch: DeviceBatch, d: int, num_heads: int) -> int:
+    n = c_sz(0)
+    _check("mtgr_attention_workspace_size",
+           lib().mtgr_attention_workspace_size(ctypes.byref(batch.c), d, num_heads, ctypes.byref(n)))
+    return int(n.value)
+
+
+def workspace(nbytes: int, device="cuda"):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def mtgr_encoder_fwd(model: DeviceModel, batch: DeviceBatch, x_in, hidden_out, logits, ws,
+                     stream=None):
+    _check("mtgr_encoder_fwd", lib().mtgr_encoder_fwd(
+        ctypes.byref(model.c), ctypes.byref(batch.c), _ptr(x_in), _ptr(hidden_out), _ptr(logits),
+        _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def mtgr_block_fwd(block: MtgrBlockParams, batch: DeviceBatch, x_in, x_out, ws, stream=None):
+    _check("mtgr_block_fwd", lib().mtgr_block_fwd(
+        ctypes.byref(block), ctypes.byref(batch.c), _ptr(x_in), _ptr(x_out), _ptr(ws), ws.numel(),
+        _stream(stream)))
+
+
+def mtgr_groupln_fwd(batch: DeviceBatch, d: int, in_dtype: int, out_dtype: int, param_dtype: int,
+                     gamma, beta, eps: float, x, y, stream=None):
+    _check("mtgr_groupln_fwd", lib().mtgr_groupln_fwd(
+        ctypes.byref(batch.c), d, in_dtype, out_dtype, param_dtype, _ptr(gamma), _ptr(beta), eps,
+        _ptr(x), _ptr(y), _stream(stream)))
+
+
+def mtgr_linear_fwd(M: int, N: int, K: int, dtype: int, epilogue: int, a, w, bias, resid, out,
+                    stream=None):
+    _check("mtgr_linear_fwd", lib().mtgr_linear_fwd(
+        M, N, K, dtype, epilogue, _ptr(a), _ptr(w), _ptr(bias), _ptr(resid), _ptr(out),
+        _stream(stream)))
+
+
+def mtgr_attention_fwd(batch: DeviceBatch, d: int, num_heads: int, dtype: int, qkvu, y_gated, ws,
+                       stream=None):
+    _check("mtgr_attention_fwd", lib().mtgr_attention_fwd(
+        ctypes.byref(batch.c), d, num_heads, dtype, _ptr(qkvu), _ptr(y_gated), _ptr(ws), ws.numel(),
+        _stream(stream)))
+
+
+def mtgr_validate_batch(batch: DeviceBatch, ws, stream=None) -> int:
+    flags = c_i32(0)
+    _check("mtgr_validate_batch", lib().mtgr_validate_batch(
+        ctypes.byref(batch.c), _ptr(ws), ws.numel(), _stream(stream), ctypes.byref(flags)))
+    return int(flags.value)
+
+
+def mtgr_debug_mask(batch: DeviceBatch, user: int, mask_dev, ws, stream=None):
+    _check("mtgr_debug_mask", lib().mtgr_debug_mask(
+        ctypes.byref(batch.c), user, _ptr(mask_dev), _ptr(ws), ws.numel(), _stream(stream)))

@@ -19,8 +19,9 @@ Draw order (fixed, per workload seed = 250518654 + seed_offset, numpy PCG64):
   1. lengths: N_S for all users, then (large workload only) the long-tail users from one
      permutation, then N_R for all users, then K for all users (N_U is fixed);
   2. timestamps user by user: R = sort(uniform[0,3600)), C = uniform[0,3600) unsorted;
-  3. embeddings N(0,1) [T,d] float32 in token order, times the group scale (U 1, S 0.5, R 2, C 4);
-     bf16 workloads round them to bf16 (round to nearest even);
+  3. embeddings N(0,1) [T,d] float32 in token order (rows in chunks of 65536, chunk c from the
+     PCG64 state jumped c+1 times), times the group scale (U 1, S 0.5, R 2, C 4); bf16 workloads
+     round them to bf16 (round to nearest even);
   4. parameters layer by layer: GLN1 gamma~U(0.5,1.5) [4,d], beta~U(-0.1,0.1) [4,d];
      W_qkvu [4d,d] Xavier-uniform per d x d block; GLN2 gamma, beta; W1 [h,d]; W2 [d,h]
      (Xavier-uniform); biases 0; then the head W_h1 [d/2,d], W_h2 [2,d/2] (Xavier-uniform,
@@ -102,19 +103,37 @@ class Params:
 
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
-    """float32 -> nearest bf16 (ties to even) -> float32; pure storage encoding."""
-    a = np.ascontiguousarray(a, dtype=np.float32)
-    u = a.view(np.uint32).astype(np.uint64)
-    lsb = (u >> 16) & 1
-    r = ((u + 0x7FFF + lsb) >> 16) << 16
-    out = r.astype(np.uint32).view(np.float32)
-    # NaN stays NaN (not produced by this generator); inf stays inf
-    return np.where(np.isfinite(a), out, a).astype(np.float32)
+    """float32 -> nearest bf16 (ties to even) -> float32; pure storage encoding (torch's RNE cast,
+    multithreaded).  Returns a new array."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float32).numpy()
 
 
 def _encode(a: np.ndarray, dtype: str) -> np.ndarray:
     a = np.ascontiguousarray(a, dtype=np.float32)
     return round_to_bf16(a) if dtype == "bf16" else a
+
+
+ROW_CHUNK = 65536
+
+
+def _normal_rows(rng: np.random.Generator, T: int, d: int) -> np.ndarray:
+    """N(0,1) float32 [T, d].  Rows come in chunks of ROW_CHUNK; chunk c is drawn from the
+    caller's PCG64 state jumped c+1 times (independent streams, filled in parallel threads).
+    The caller's own generator is not advanced."""
+    import concurrent.futures
+    x = np.empty((T, d), dtype=np.float32)
+    chunks = [(c, s, min(s + ROW_CHUNK, T)) for c, s in enumerate(range(0, T, ROW_CHUNK))]
+
+    def fill(job):
+        c, lo, hi = job
+        g = np.random.Generator(rng.bit_generator.jumped(c + 1))
+        g.standard_normal((hi - lo, d), dtype=np.float32, out=x[lo:hi])
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        list(ex.map(fill, chunks))
+    return x
 
 
 def batch_from_lengths(n_u: Sequence[int], n_s: Sequence[int], n_r: Sequence[int],
@@ -143,7 +162,7 @@ def batch_from_lengths(n_u: Sequence[int], n_s: Sequence[int], n_r: Sequence[int
         timestamps[o:s0] = -np.inf
         timestamps[s0:s0 + segs[2]] = np.sort(rng.uniform(0.0, 3600.0, segs[2])).astype(np.float32)
         timestamps[s0 + segs[2]:p] = rng.uniform(0.0, 3600.0, segs[3]).astype(np.float32)
-    x = rng.standard_normal((T, d), dtype=np.float32)
+    x = _normal_rows(rng, T, d)
     scale = np.asarray(GROUP_SCALE, dtype=np.float32)[group_ids]
     x *= scale[:, None]
     x = _encode(x, dtype)

@@ -1,0 +1,178 @@
+/*
+ * mtgr.h -- C ABI of libmtgr.so: forward pass of the MTGR HSTU encoder on one MI355X (gfx950).
+ *
+ * Page keys used in the citations below:
+ *   [P1]/[P2] chenhuiyu blog post "MTGR" (Chinese / English)
+ *   [P3] marovi.ai "MTGR: Industrial-Scale Generative Recommendation Framework in Meituan/zh"
+ *   [P5] fun-rec mdbook section 7.3 "MTGR: Hybrid Paradigm Modeling"
+ *
+ * What the library computes (one HSTU block, [P3] section 方法, the two update equations):
+ *   X~ = GroupLN1(X)                                   per-token statistics, per-group gamma/beta
+ *   [Q|K|V|U] = X~ W_qkvu^T + b_qkvu                   four d-wide affine projections
+ *   V~_h = (silu(Q_h K_h^T) / N  (.)  M) V_h           per head h; N = the user's token count;
+ *                                                      M = three-rule dynamic mask ([P5] 7.3.4)
+ *   X <- W2 silu(W1 GroupLN2(V~ (.) U) + b1) + b2 + X  residual MLP
+ * and, after L blocks, CTR/CTCVR logits at candidate tokens ([P1]/[P2] token section; [P5] 7.3.1):
+ *   logits = W_h2 silu(W_h1 x + b_h1) + b_h2.
+ *
+ * Batch format ([P3] 方法, equation for D; [P1]/[P2] sequence packing): users are packed back to
+ * back; user b owns tokens offsets[b] .. offsets[b+1]-1, in group order U, S, R, C
+ * (group id 0 = static user feature, 1 = long-term history, 2 = real-time event, 3 = candidate).
+ * Tokens of different users never attend to each other.
+ *
+ * Mask ([P5] 7.3.4 Rules 1-3, [P3] 方法): key j is visible to query i of the same user iff
+ * j is a U or S token, or j == i, or (j is an R token, i is an R or C token, t_j < t_i).
+ * Timestamps are float32 seconds; U/S timestamps are never read.
+ *
+ * Conventions
+ *   - Every buffer is owned by the caller.  "device" pointers are HIP device memory of the
+ *     current device; "host" pointers are ordinary host memory read during the call only.
+ *   - The library never allocates device memory: scratch space is a caller-provided workspace
+ *     whose size the *_workspace_size functions report.  It keeps no state between calls.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call returns
+ *     after enqueueing.  Faults inside kernels surface at the caller's next synchronisation.
+ *   - Argument and shape errors are found on the host before anything is enqueued and are
+ *     returned as a status; MTGR_ERR_HIP reports a failed launch (hipGetLastError).
+ *   - Weights use the torch Linear layout [out][in], row-major.  Row block order in W_qkvu is
+ *     Q, K, V, U; head h owns rows h*d_h .. (h+1)*d_h-1 of each block.
+ *   - Storage dtype MTGR_BF16 means bf16 weights and bf16 intermediate activations with fp32
+ *     accumulation; the residual stream x is always fp32.  MTGR_F32 keeps everything fp32.
+ *   - Supported shapes: d % H == 0; d_h = d/H in {32, 64, 128} (bf16: {64, 128});
+ *     d, h multiples of 64 (bf16) or 8 (fp32); d <= 1024; h <= 8192; head hidden multiple of 8.
+ */
+#ifndef MTGR_H
+#define MTGR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MTGR_ABI_VERSION 1
+
+typedef enum {
+  MTGR_OK = 0,
+  MTGR_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
+  MTGR_ERR_BAD_SHAPE = 2,    /* d, H, h, M, N, K out of the supported set */
+  MTGR_ERR_BAD_BATCH = 3,    /* offsets not monotone, T or C inconsistent, bad group order */
+  MTGR_ERR_UNSUPPORTED = 4,  /* dtype / epilogue / option not implemented */
+  MTGR_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the reported size */
+  MTGR_ERR_HIP = 6           /* a HIP launch or copy failed */
+} mtgr_status;
+
+typedef enum { MTGR_F32 = 0, MTGR_BF16 = 1 } mtgr_dtype;
+
+enum { MTGR_G_U = 0, MTGR_G_S = 1, MTGR_G_R = 2, MTGR_G_C = 3, MTGR_NUM_GROUPS = 4 };
+
+/* GEMM epilogues of mtgr_linear_fwd */
+enum {
+  MTGR_EPI_STORE = 0,        /* out(dtype)  = a W^T + bias              */
+  MTGR_EPI_SILU = 1,         /* out(dtype)  = silu(a W^T + bias)        */
+  MTGR_EPI_RESIDUAL_F32 = 2  /* out(float)  = a W^T + bias + resid(float); out may alias resid */
+};
+
+/* Packed jagged batch.  All device arrays are read-only for the library. */
+typedef struct mtgr_batch {
+  int32_t num_users;              /* B >= 0 */
+  int64_t num_tokens;             /* T == offsets[B] */
+  int64_t num_candidates;         /* C == number of tokens with group id 3 */
+  const int64_t* offsets_host;    /* host   [B+1], offsets_host[0] == 0, non-decreasing */
+  const int64_t* offsets;         /* device [B+1], same values */
+  const uint8_t* group_ids;       /* device [T], 0..3, non-decreasing within each user */
+  const float* timestamps;        /* device [T], seconds; R and C entries must not be NaN */
+} mtgr_batch;
+
+/* One HSTU block.  All pointers are device pointers in `dtype`; biases may be NULL (= 0). */
+typedef struct mtgr_block_params {
+  int32_t d_model;                /* d */
+  int32_t num_heads;              /* H */
+  int32_t mlp_hidden;             /* h */
+  int32_t dtype;                  /* mtgr_dtype */
+  float ln_eps;                   /* GroupLN epsilon (1e-5 in the workloads) */
+  const void* gln1_gamma;         /* [4][d] */
+  const void* gln1_beta;          /* [4][d] */
+  const void* w_qkvu;             /* [4d][d] */
+  const void* b_qkvu;             /* [4d] or NULL */
+  const void* gln2_gamma;         /* [4][d] */
+  const void* gln2_beta;          /* [4][d] */
+  const void* w_mlp1;             /* [h][d] */
+  const void* b_mlp1;             /* [h] or NULL */
+  const void* w_mlp2;             /* [d][h] */
+  const void* b_mlp2;             /* [d] or NULL */
+} mtgr_block_params;
+
+/* L blocks plus the candidate head.  `layers` is a host array of L block descriptions that
+ * must all share d, H, dtype. */
+typedef struct mtgr_encoder_params {
+  int32_t num_layers;             /* L >= 1 */
+  const mtgr_block_params* layers;/* host [L] */
+  int32_t head_hidden;            /* hh (d/2 in the workloads) */
+  const void* w_head1;            /* device [hh][d]  */
+  const void* b_head1;            /* device [hh] or NULL */
+  const void* w_head2;            /* device [2][hh]  */
+  const void* b_head2;            /* device [2] or NULL */
+} mtgr_encoder_params;
+
+/* ---- version and messages -------------------------------------------------------------- */
+int32_t mtgr_abi_version(void);
+const char* mtgr_status_str(int32_t status);
+
+/* ---- workspace sizes (host only, no HIP call) ------------------------------------------- */
+mtgr_status mtgr_encoder_workspace_size(const mtgr_encoder_params* p, const mtgr_batch* b,
+                                        size_t* bytes);
+mtgr_status mtgr_block_workspace_size(const mtgr_block_params* p, const mtgr_batch* b,
+                                      size_t* bytes);
+mtgr_status mtgr_attention_workspace_size(const mtgr_batch* b, int32_t d, int32_t num_heads,
+                                          size_t* bytes);
+
+/* ---- the hot path ----------------------------------------------------------------------- */
+/* Full encoder: L blocks over x_in (device float [T][d]) then the head at candidate tokens.
+ * hidden_out (device float [T][d], may be NULL) receives the final hidden states and may alias
+ * x_in; logits (device float [C][2]) receive (CTR, CTCVR) logits in packed candidate order
+ * (user-major, then token order within the user).  No sigmoid is applied. */
+mtgr_status mtgr_encoder_fwd(const mtgr_encoder_params* p, const mtgr_batch* b, const float* x_in,
+                             float* hidden_out, float* logits, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* One block: x_out = block(x_in), both device float [T][d]; x_out may alias x_in. */
+mtgr_status mtgr_block_fwd(const mtgr_block_params* p, const mtgr_batch* b, const float* x_in,
+                           float* x_out, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- kernel-level entries (the same kernels the block uses) ------------------------------ */
+/* GroupLN over T rows of width d: y = (x - mean) / sqrt(var + eps) * gamma[g] + beta[g].
+ * x in `in_dtype`, y in `out_dtype`, gamma/beta [4][d] in `param_dtype`.
+ * Supported (in, out): (F32, F32), (F32, BF16), (BF16, BF16). */
+mtgr_status mtgr_groupln_fwd(const mtgr_batch* b, int32_t d, int32_t in_dtype, int32_t out_dtype,
+                             int32_t param_dtype, const void* gamma, const void* beta, float eps,
+                             const void* x, void* y, void* stream);
+
+/* out = epilogue(a[M][K] W[N][K]^T + bias[N]); a, W, bias in `dtype`; see MTGR_EPI_*. */
+mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int32_t epilogue,
+                            const void* a, const void* w, const void* bias, const float* resid,
+                            void* out, void* stream);
+
+/* Masked SiLU attention with the U gate for every user and head:
+ * qkvu device [T][4d] in `dtype` -> y_gated device [T][d] in `dtype` (V~ (.) U). */
+mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
+                               const void* qkvu, void* y_gated, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* ---- test / debug ------------------------------------------------------------------------ */
+/* Device-side checks of a batch (group ids in 0..3 and non-decreasing within each user, no NaN
+ * R/C timestamp, candidate count == num_candidates).  Synchronises `stream`.  *flags_out gets
+ * a bit set per failed check (1 group range, 2 group order, 4 NaN time, 8 candidate count). */
+mtgr_status mtgr_validate_batch(const mtgr_batch* b, void* ws, size_t ws_bytes, void* stream,
+                                int32_t* flags_out);
+
+/* Writes the mask of user `user` as uint8 [n_b][n_b] (rows = queries) into mask_dev, using the
+ * same visibility predicate as the attention kernels. */
+mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, uint8_t* mask_dev, void* ws,
+                            size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MTGR_H */

@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/mtgr.h
+declares, and rejects bad arguments on the host with the documented status before any launch."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from generative_recommendation_ranking_amd import mtgr as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mtgr.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mtgr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_matches_binding_list():
+    assert _declared_functions() == sorted(M.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = M.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert M.mtgr_abi_version() == 1
+    assert M.mtgr_status_str(0) == "ok"
+    assert "workspace" in M.mtgr_status_str(5)
+
+
+def test_exported_symbols_are_plain_c():
+    # no C++ mangling for the ABI: nm lists the exact names
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", M.LIB_PATH], capture_output=True, text=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared_functions():
+        assert name in names, name
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails host validation first
+
+
+def _batch(offsets, T=None, C=0):
+    off = np.asarray(offsets, dtype=np.int64)
+    b = M.MtgrBatch(len(off) - 1, int(off[-1]) if T is None else T, C, off.ctypes.data, FAKE, FAKE, FAKE)
+    return b, off
+
+
+def _block(d=256, H=4, h=1024, dtype=M.MTGR_BF16, eps=1e-5):
+    return M.MtgrBlockParams(d, H, h, dtype, eps, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, None)
+
+
+def _ws_size(block, batch):
+    n = ctypes.c_size_t(0)
+    st = M.lib().mtgr_block_workspace_size(ctypes.byref(block), ctypes.byref(batch), ctypes.byref(n))
+    return st, n.value
+
+
+def test_block_workspace_size_and_shape_checks():
+    b, _keep = _batch([0, 10, 30])
+    st, n = _ws_size(_block(), b)
+    assert st == 0
+    T, d, h = 30, 256, 1024
+    assert n >= T * d * 2 * 2 + T * max(4 * d, h) * 2
+    assert _ws_size(_block(d=250, H=2), b)[0] == 2          # d not a multiple of 64 (bf16)
+    assert _ws_size(_block(d=256, H=3), b)[0] == 2          # d % H != 0
+    assert _ws_size(_block(d=256, H=8), b)[0] == 2          # d_h = 32 unsupported in bf16
+    assert _ws_size(_block(d=64, H=2, h=128, dtype=M.MTGR_F32), b)[0] == 0  # d_h = 32 fine in fp32
+    assert _ws_size(_block(dtype=7), b)[0] == 4             # unknown dtype
+    assert _ws_size(_block(eps=float("nan")), b)[0] == 2
+
+
+@pytest.mark.parametrize("offsets,T,code", [
+    ([0, 10, 5], None, 3),        # decreasing offsets
+    ([1, 10, 30], None, 3),       # offsets[0] != 0
+    ([0, 10, 30], 31, 3),         # T != offsets[B]
+])
+def test_bad_batches_rejected(offsets, T, code):
+    b, _keep = _batch(offsets, T)
+    assert _ws_size(_block(), b)[0] == code
+
+
+def test_fwd_rejects_small_workspace_and_nulls_without_launch():
+    b, _keep = _batch([0, 10, 30], C=4)
+    blk = _block()
+    st = M.lib().mtgr_block_fwd(ctypes.byref(blk), ctypes.byref(b), FAKE, FAKE, FAKE, 16, None)
+    assert st == 5
+    st = M.lib().mtgr_block_fwd(ctypes.byref(blk), ctypes.byref(b), None, FAKE, FAKE, 1 << 40, None)
+    assert st == 1
+    # encoder: missing head weights, zero layers
+    blocks = (M.MtgrBlockParams * 1)(blk)
+    enc = M.MtgrEncoderParams(1, blocks, 128, FAKE, None, None, None)
+    n = ctypes.c_size_t(0)
+    assert M.lib().mtgr_encoder_workspace_size(ctypes.byref(enc), ctypes.byref(b), ctypes.byref(n)) == 1
+    enc = M.MtgrEncoderParams(0, blocks, 128, FAKE, None, FAKE, None)
+    assert M.lib().mtgr_encoder_workspace_size(ctypes.byref(enc), ctypes.byref(b), ctypes.byref(n)) == 2
+    enc = M.MtgrEncoderParams(1, blocks, 128, FAKE, None, FAKE, None)
+    assert M.lib().mtgr_encoder_workspace_size(ctypes.byref(enc), ctypes.byref(b), ctypes.byref(n)) == 0
+    st = M.lib().mtgr_encoder_fwd(ctypes.byref(enc), ctypes.byref(b), FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == 1  # logits NULL with candidates present
+
+
+def test_linear_and_groupln_argument_checks():
+    L = M.lib()
+    assert L.mtgr_linear_fwd(100, 64, 100, M.MTGR_BF16, 0, FAKE, FAKE, None, None, FAKE, None) == 2
+    assert L.mtgr_linear_fwd(100, 64, 128, M.MTGR_BF16, 9, FAKE, FAKE, None, None, FAKE, None) == 4
+    assert L.mtgr_linear_fwd(100, 64, 128, M.MTGR_BF16, 2, FAKE, FAKE, None, None, FAKE, None) == 1
+    assert L.mtgr_linear_fwd(0, 64, 128, M.MTGR_BF16, 0, None, None, None, None, None, None) == 0
+    b, _keep = _batch([0, 10, 30])
+    assert L.mtgr_groupln_fwd(ctypes.byref(b), 1030, 0, 0, 0, FAKE, FAKE, ctypes.c_float(1e-5), FAKE, FAKE, None) == 2
+    assert L.mtgr_groupln_fwd(ctypes.byref(b), 64, 1, 0, 0, FAKE, FAKE, ctypes.c_float(1e-5), FAKE, FAKE, None) == 4
+    assert L.mtgr_groupln_fwd(ctypes.byref(b), 64, 0, 0, 0, None, FAKE, ctypes.c_float(1e-5), FAKE, FAKE, None) == 1
+
+
+def test_empty_batch_is_a_no_op():
+    off = np.zeros(1, np.int64)
+    b = M.MtgrBatch(0, 0, 0, off.ctypes.data, None, None, None)
+    blk = _block()
+    assert M.lib().mtgr_block_fwd(ctypes.byref(blk), ctypes.byref(b), None, None, FAKE, 1 << 20, None) == 0

@@ -338,11 +338,15 @@ def test_temporal_replay_no_leak():
 # ------------------------------------------------------------------------------------------
 # Generator
 # ------------------------------------------------------------------------------------------
-def test_round_to_bf16_matches_torch():
+def test_round_to_bf16_is_round_to_nearest_even():
+    # bit-level definition: add 0x7FFF plus the lowest kept bit, truncate the low 16 bits
     rng = np.random.default_rng(60)
     a = (rng.standard_normal(100_000) * np.exp(rng.uniform(-20, 20, 100_000))).astype(np.float32)
-    ref = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    a[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 65504.0]  # exact ties
+    u = a.view(np.uint32).astype(np.uint64)
+    ref = (((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16).astype(np.uint32).view(np.float32)
     np.testing.assert_array_equal(synth.round_to_bf16(a), ref)
+    assert synth.round_to_bf16(a[:2]).tolist() == [1.0, 1.0 + 4 * 2.0 ** -8]
 
 
 def test_generator_deterministic_and_shapes():
