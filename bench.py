@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark: MTGR HSTU encoder forward (bf16, fp32 accumulation) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large-bf16] [--no-cpu-baseline]
+
+One step = one mtgr_encoder_fwd over the whole synthetic batch (all L blocks + the candidate
+head), inputs and weights resident in HBM, workspace preallocated.  Prints ONE JSON line.
+
+Besides the headline tokens/s the line carries
+  * "roofline": the dominant kernel (the fused attention) -- algorithmic FLOPs per launch
+    (4 * d_model per visible (query, key) pair) over its average launch duration, measured with
+    HIP events on the library's stream in a replay of the per-layer kernel sequence;
+  * "mfma_util": algorithmic FLOPs of the GEMM + attention launches over their summed durations
+    and the bf16 dense MFMA peak;
+  * "cpu_baseline": the fp64 CPU oracle timed on this host on a bounded sample of users.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "encoder tokens/sec (fwd, bf16) and MFMA-util % on one MI355X"
+
+
+def visible_pairs_per_user(b) -> np.ndarray:
+    """Exact count of (query, key) pairs the dynamic mask lets through, per user: every query
+    sees the n_U+n_S static keys; R and C queries also see the strictly earlier R keys; every
+    token sees itself (static rows already count themselves among the static keys)."""
+    out = np.zeros(b.num_users, dtype=np.int64)
+    for u in range(b.num_users):
+        lo = int(b.offsets[u])
+        n = int(b.offsets[u + 1]) - lo
+        ns = int(b.n_u[u] + b.n_s[u])
+        nr = int(b.n_r[u])
+        t = b.timestamps[lo + ns:lo + n]
+        tr = np.sort(t[:nr])
+        earlier = np.searchsorted(tr, t, side="left")   # R keys strictly earlier than each R/C row
+        out[u] = n * ns + int(earlier.sum()) + (n - ns)
+    return out
+
+
+def flops_per_layer(b, d, h):
+    T = b.num_tokens
+    pairs = int(visible_pairs_per_user(b).sum())
+    return {"qkvu": 2.0 * T * d * 4 * d, "mlp1": 2.0 * T * d * h, "mlp2": 2.0 * T * h * d,
+            "attention": 4.0 * d * pairs, "pairs": pairs}
+
+
+def cpu_baseline(b, p, budget_s=12.0, max_s=30.0):
+    """The oracle (fp64 numpy, as it stands) on whole users of the same batch, in index order,
+    until at least `budget_s` seconds of work; tokens of the sample per second."""
+    from generative_recommendation_ranking_amd import synth
+    from oracle import mtgr_oracle as O
+    layers, head = O.params_layers(p), O.params_head(p)
+    done, users, t0 = 0, [], time.perf_counter()
+    for u in range(b.num_users):
+        s = synth.subset(b, [u])
+        O.encoder_forward(s.offsets, s.group_ids, s.timestamps, s.x, layers, head, p.H, p.ln_eps)
+        done += s.num_tokens
+        users.append(u)
+        el = time.perf_counter() - t0
+        if el >= budget_s or el >= max_s:
+            break
+    el = time.perf_counter() - t0
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"users {users[0]}..{users[-1]} ({len(users)} users, {done} tokens) of the "
+                      f"same batch, all {p.num_layers} blocks + head, fp64 numpy",
+            "seconds": round(el, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="large-bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--replay-steps", type=int, default=5)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); users are independent, "
+              "so more GPUs would each run their own share of users with no exchange step.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from generative_recommendation_ranking_amd import mtgr as M
+    from generative_recommendation_ranking_amd import synth
+
+    torch.cuda.set_device(0)
+    b, p = synth.make_workload(args.workload)
+    db, dm = M.DeviceBatch(b), M.DeviceModel(p)
+    ws = M.workspace(M.mtgr_encoder_workspace_size(dm, db))
+    hidden = torch.empty_like(db.x)
+    logits = torch.empty(db.num_candidates, 2, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    print(f"[bench] workload {args.workload}: users {b.num_users} tokens {b.num_tokens} "
+          f"candidates {db.num_candidates}", file=sys.stderr, flush=True)
+
+    def step():
+        M.mtgr_encoder_fwd(dm, db, db.x, hidden, logits, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = b.num_tokens * args.steps / elapsed
+    print(f"[bench] {ms_per_step:.2f} ms/step, {tokens_per_s / 1e6:.3f} M tokens/s",
+          file=sys.stderr, flush=True)
+
+    # ---- replay of one layer's kernel sequence through the kernel-level entries, timed with
+    # HIP events on the same stream (layer 0's weights; every layer has the same shapes)
+    d, H, h = p.d, p.H, p.h
+    T = b.num_tokens
+    lay = dm.layers[0]
+    bf = torch.bfloat16
+    xt = torch.empty(T, d, dtype=bf, device="cuda")
+    big = torch.empty(T, max(4 * d, h), dtype=bf, device="cuda")
+    yb = torch.empty(T, d, dtype=bf, device="cuda")
+    xo = torch.empty_like(db.x)
+    aws = M.workspace(M.mtgr_attention_workspace_size(db, d, H))
+    seq = [
+        ("gln1", lambda: M.mtgr_groupln_fwd(db, d, 0, 1, 1, lay["gln1_gamma"], lay["gln1_beta"], p.ln_eps, db.x, xt)),
+        ("qkvu", lambda: M.mtgr_linear_fwd(T, 4 * d, d, M.MTGR_BF16, M.MTGR_EPI_STORE, xt, lay["w_qkvu"], lay["b_qkvu"], None, big)),
+        ("attention", lambda: M.mtgr_attention_fwd(db, d, H, M.MTGR_BF16, big, yb, aws)),
+        ("gln2", lambda: M.mtgr_groupln_fwd(db, d, 1, 1, 1, lay["gln2_gamma"], lay["gln2_beta"], p.ln_eps, yb, xt)),
+        ("mlp1", lambda: M.mtgr_linear_fwd(T, h, d, M.MTGR_BF16, M.MTGR_EPI_SILU, xt, lay["w_mlp1"], lay["b_mlp1"], None, big)),
+        ("mlp2", lambda: M.mtgr_linear_fwd(T, d, h, M.MTGR_BF16, M.MTGR_EPI_RESIDUAL_F32, big, lay["w_mlp2"], lay["b_mlp2"], db.x, xo)),
+    ]
+    for _, fn in seq:
+        fn()
+    torch.cuda.synchronize()
+    times = {k: 0.0 for k, _ in seq}
+    for _ in range(args.replay_steps):
+        for k, fn in seq:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            times[k] += e0.elapsed_time(e1)
+    ms = {k: v / args.replay_steps for k, v in times.items()}
+    fl = flops_per_layer(b, d, h)
+    gemm_ms = ms["qkvu"] + ms["mlp1"] + ms["mlp2"]
+    gemm_fl = fl["qkvu"] + fl["mlp1"] + fl["mlp2"]
+    att_tflops = fl["attention"] / (ms["attention"] * 1e-3) / 1e12
+    util_all = (gemm_fl + fl["attention"]) / ((gemm_ms + ms["attention"]) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    norm_bytes = {"gln1": T * d * (4 + 2), "gln2": T * d * (2 + 2)}
+    kernels = {k: {"ms": round(v, 4)} for k, v in ms.items()}
+    for k in ("qkvu", "mlp1", "mlp2", "attention"):
+        kernels[k]["tflops"] = round(fl[k] / (ms[k] * 1e-3) / 1e12, 1)
+    for k, by in norm_bytes.items():
+        kernels[k]["gbs"] = round(by / (ms[k] * 1e-3) / 1e9, 1)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "users": b.num_users, "tokens": T,
+                   "candidates": db.num_candidates, "layers": p.num_layers, "d_model": d,
+                   "heads": H, "mlp_hidden": h, "visible_pairs_per_layer": fl["pairs"]},
+        "roofline": {"bound": "mfma", "kernel": "attention (fused masked silu + U gate)",
+                     "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": fl["attention"], "launch_ms": round(ms["attention"], 4)},
+        "mfma_util": {"gemm_plus_attention": round(util_all, 4),
+                      "gemm": round(gemm_fl / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                      "attention": round(att_tflops / PEAK_BF16_TFLOPS, 4)},
+        "kernels_per_layer": kernels,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample of users", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(b, p)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
