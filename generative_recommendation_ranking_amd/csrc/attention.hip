@@ -36,17 +36,6 @@ namespace {
 constexpr int BQ = kAttnQTileBf16;  // 128 query rows per work item
 constexpr int BKV = 64;             // keys per tile
 
-// Position of key k (0..63) of a tile inside a transposed V row: keys are grouped so that the
-// 8 keys feeding slot 0..7 of lane-half hh in PV k-step ks sit at ks*16 + hh*8 + slot.
-__device__ __forceinline__ int vt_pos(int k) {
-  const int mt = k >> 5, G = (k >> 3) & 3, hk = (k >> 2) & 1, c = k & 3;
-  return mt * 32 + (G >> 1) * 16 + hk * 8 + (G & 1) * 4 + c;
-}
-
-__device__ __forceinline__ float silu_fast(float z) {
-  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
-}
-
 __device__ __forceinline__ int find_slot(const int32_t* __restrict__ tile_off, int B, int item) {
   int lo = 0, hi = B;  // largest p with tile_off[p] <= item
   while (hi - lo > 1) {
@@ -64,15 +53,21 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   constexpr int KP = DH + 8;
   constexpr int VP = BKV + 8;
   constexpr int DCH = DH / 8;                    // 16-byte chunks per key row
-  constexpr int CK = BKV * DCH / 256;            // K chunks per thread
-  constexpr int VG = (BKV / 4) * DCH;            // V groups (4 keys x 8 features)
-  constexpr int CV = (VG + 255) / 256;           // V groups per thread
+  constexpr int VT = 8 * DCH;                    // V-staging threads: (8-key chunk, 8 features)
+  constexpr int KT = DH;                         // K-staging threads
+  constexpr int CK = BKV * DCH / KT;             // K chunks per K-staging thread (8)
   constexpr int NT = DH / 32;                    // output tiles of 32 features
-  static_assert(CK * 256 == BKV * DCH, "K staging mismatch");
+  static_assert(CK == 8 && VT + KT <= 256, "staging layout");
 
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][BKV][KP];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][DH][VP];
-  __shared__ __attribute__((aligned(16))) float Ts[2][BKV];
+  // One LDS arena: K and V^T tiles (double-buffered) and the tile timestamps during the key loop;
+  // reused afterwards to stage each wavefront's output rows for vectorised stores.
+  constexpr int OP = DH + 4;                                   // fp32 pitch of staged output rows
+  constexpr size_t kLoopBytes = (2 * BKV * KP + 2 * DH * VP) * sizeof(bf16) + 2 * BKV * sizeof(float);
+  constexpr size_t kEpiBytes = 4 * 32 * OP * sizeof(float) + 4 * 32 * sizeof(float);
+  __shared__ __attribute__((aligned(16))) char arena[kLoopBytes > kEpiBytes ? kLoopBytes : kEpiBytes];
+  bf16 (*Ks)[BKV][KP] = reinterpret_cast<bf16 (*)[BKV][KP]>(arena);
+  bf16 (*Vt)[DH][VP] = reinterpret_cast<bf16 (*)[DH][VP]>(arena + 2 * BKV * KP * sizeof(bf16));
+  float (*Ts)[BKV] = reinterpret_cast<float (*)[BKV]>(arena + (2 * BKV * KP + 2 * DH * VP) * sizeof(bf16));
 
   const int item = blockIdx.x;
   const int h = blockIdx.y;
@@ -121,61 +116,70 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
 
-  bf16x8 rk[CK];
-  bf16x8 rv[CV][4];
+  // Staging registers, shared by the two roles: wavefronts with tid < VT gather V, the next KT
+  // threads copy K, the rest only help with the timestamps.
+  //  * V: thread (ch, c) fetches the 8 keys that form 16-byte chunk ch of a transposed V row
+  //    (the keys lane-half hh of k-step ks consumes, ch = 2*ks + hh) at features c*8..c*8+7, then
+  //    writes one 16-byte chunk per feature.  Eight consecutive threads fill one 128-byte row,
+  //    and with the 144-byte row pitch the rows of neighbouring groups start 32 banks apart.
+  //  * K: plain 16-byte chunks, 8 per thread, row-major with a 16-byte pad.
+  bf16x8 stg[8];
   float rt = INFINITY;
+  // role is uniform per wavefront (VT and KT are multiples of 64); make that visible
+  const int role = __builtin_amdgcn_readfirstlane(tid < VT ? 0 : (tid < VT + KT ? 1 : 2));
+  const bool v_role = role == 0;
+  const bool k_role = role == 1;
+  const int v_ch = tid & 7, v_c = (tid >> 3) % DCH;
+  auto v_key = [](int ch, int jj) {  // key (0..63) feeding slot jj of chunk ch
+    const int ks = ch >> 1, h = ch & 1;
+    return (ks >> 1) * 32 + 8 * ((ks & 1) * 2 + (jj >> 2)) + 4 * h + (jj & 3);
+  };
+  // Buffer resources over this user's K (or V) rows of head h, sized to the first kend keys:
+  // keys at or past kend read as zero.  Per-lane byte offset in a VGPR, per-key step in SGPRs.
+  const uint32_t row_bytes = (uint32_t)(ld * 2);
+  const __amdgpu_buffer_rsrc_t kv_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(v_role ? Vp : Kp), (short)0, (int)((uint32_t)kend * row_bytes), 0x00020000);
+  const uint32_t v_off = (uint32_t)v_key(v_ch, 0) * row_bytes + v_c * 16;
+  const uint32_t k_off = (uint32_t)((tid - VT) / DCH) * row_bytes + ((tid - VT) % DCH) * 16;
+  const uint32_t my_off = v_role ? v_off : k_off;
 
   auto stage_load = [&](int k0) {
+    if (role < 2) {
 #pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      const int idx = tid + i * 256;
-      const int key = idx / DCH, c = idx % DCH;
-      const int j = k0 + key;
-      rk[i] = (j < kend) ? *reinterpret_cast<const bf16x8*>(Kp + j * ld + c * 8) : zero8;
-    }
-#pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int idx = tid + i * 256;
-      if (idx < VG) {
-        const int kg = idx / DCH, c = idx % DCH;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int j = k0 + kg * 4 + r;
-          rv[i][r] = (j < kend) ? *reinterpret_cast<const bf16x8*>(Vp + j * ld + c * 8) : zero8;
-        }
+      for (int jj = 0; jj < 8; ++jj) {
+        // V: keys v_key(ch, jj) = v_key(ch, 0) + 8*(jj/4) + jj%4;  K: rows (tid-VT)/DCH + jj*KT/DCH
+        const uint32_t step = v_role ? (uint32_t)(8 * (jj >> 2) + (jj & 3)) : (uint32_t)(jj * (KT / DCH));
+        stg[jj] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+            kv_rsrc, my_off, (uint32_t)(k0 + step) * row_bytes, 0));
       }
     }
     if (tid < BKV) rt = (k0 + tid < kend) ? ts[base + k0 + tid] : INFINITY;
   };
   auto stage_store = [&](int buf) {
+    if (v_role) {
 #pragma unroll
-    for (int i = 0; i < CK; ++i) {
-      const int idx = tid + i * 256;
-      const int key = idx / DCH, c = idx % DCH;
-      *reinterpret_cast<bf16x8*>(&Ks[buf][key][c * 8]) = rk[i];
-    }
+      for (int e = 0; e < 8; ++e) {
+        bf16x8 col;
 #pragma unroll
-    for (int i = 0; i < CV; ++i) {
-      const int idx = tid + i * 256;
-      if (idx < VG) {
-        const int kg = idx / DCH, c = idx % DCH;
-        const int p = vt_pos(kg * 4);
+        for (int jj = 0; jj < 8; ++jj) col[jj] = stg[jj][e];
+        *reinterpret_cast<bf16x8*>(&Vt[buf][v_c * 8 + e][v_ch * 8]) = col;
+      }
+    } else if (k_role) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          bf16x4 v4;
-          v4[0] = rv[i][0][e];
-          v4[1] = rv[i][1][e];
-          v4[2] = rv[i][2][e];
-          v4[3] = rv[i][3][e];
-          *reinterpret_cast<bf16x4*>(&Vt[buf][c * 8 + e][p]) = v4;
-        }
+      for (int i = 0; i < CK; ++i) {
+        const int idx = (tid - VT) + i * KT;
+        const int key = idx / DCH, c = idx % DCH;
+        *reinterpret_cast<bf16x8*>(&Ks[buf][key][c * 8]) = stg[i];
       }
     }
     if (tid < BKV) Ts[buf][tid] = rt;
   };
 
-  auto compute = [&](int buf, int k0) {
-    const bool tile_static = (k0 + BKV <= ns);
+  // Per key tile: the wavefront's scores S^T = K Q^T and P = mask(silu(S)) first; the next
+  // tile's global loads are issued only after that (the score accumulators are dead by then,
+  // which keeps the staging registers and the scores from being live together); then O += P V,
+  // the store of the next tile into the other LDS buffer, and one barrier.
+  auto tile_needed = [&](int buf, int k0) {
     bool need = wave_rows && (k0 < ns || (wave_rc && k0 < rc_end));
     if (need && k0 >= ns) {
       // pure R tile: skip when no key is earlier than the wavefront's latest R/C row and the
@@ -186,45 +190,56 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       const bool diag = max(wr_lo, k0) < min(wr_hi, k0 + BKV);
       if (!diag && tmin >= wave_tmax) need = false;
     }
-    if (!need) return;
-    f32x16 s[2];
+    return need;
+  };
+  bf16x8 pa[4];
+  auto scores = [&](int buf, int k0) {
+    f32x16 sc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[mt][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sc[mt][r] = 0.f;
 #pragma unroll
     for (int ks = 0; ks < DH / 16; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[buf][mt * 32 + l32][ks * 16 + hh * 8]);
-        s[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[mt], 0, 0, 0);
+        sc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[mt], 0, 0, 0);
       }
     }
-    // s[mt][r]: key k0 + mt*32 + 8*(r/4) + 4*hh + r%4, query qi
-    bf16x8 pa[4];
-    if (tile_static) {
+    // sc[mt][r]: key k0 + mt*32 + 8*(r/4) + 4*hh + r%4, query qi
+    if (k0 + BKV <= ns) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          pa[mt * 2 + (r >> 3)][r & 7] = (bf16)silu_fast(s[mt][r]);
+          pa[mt * 2 + (r >> 3)][r & 7] = (bf16)silu_rcp(sc[mt][r]);
     } else {
+      // Mask.  With jb = k0 + 4*hh this lane's keys are jb + dk, dk = mt*32 + 8*(r/4) + r%4 a
+      // compile-time constant, so the visibility rule (the same as mtgr_visible) becomes three
+      // integer compares against per-lane offsets plus one timestamp compare.  Keys at or past
+      // kend were loaded as zeros: their score and silu are 0 already.
+      const int jb = k0 + 4 * hh;
+      const int lim_static = ns - jb, lim_rc = rc_end - jb, self = qi - jb;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int kb = mt * 32 + 8 * g4 + 4 * hh;
-          const f32x4 t4 = *reinterpret_cast<const f32x4*>(&Ts[buf][kb]);
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(&Ts[buf][mt * 32 + 8 * g4 + 4 * hh]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int r = g4 * 4 + c;
-            const int j = k0 + kb + c;
-            const bool vis = (j < kend) && mtgr_visible(qi, j, ns, rc_end, tq, t4[c]);
-            pa[mt * 2 + (r >> 3)][r & 7] = (bf16)(vis ? silu_fast(s[mt][r]) : 0.f);
+            const int dk = mt * 32 + 8 * g4 + c;
+            const float p = silu_rcp(sc[mt][r]);
+            const bool vis = (dk < lim_static) | (dk == self) |
+                             (q_rc & (dk < lim_rc) & (t4[c] < tq));
+            pa[mt * 2 + (r >> 3)][r & 7] = (bf16)(vis ? p : 0.f);
           }
         }
       }
     }
+  };
+  auto accumulate = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -240,8 +255,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
     const int cur = kt & 1;
-    if (kt + 1 < nkt) stage_load((kt + 1) * BKV);
-    compute(cur, kt * BKV);
+    const int k0 = kt * BKV;
+    const bool need = tile_needed(cur, k0);
+    if (need) scores(cur, k0);
+    if (kt + 1 < nkt) stage_load(k0 + BKV);
+    if (need) accumulate(cur);
     if (kt + 1 < nkt) stage_store(cur ^ 1);
     __syncthreads();
   }
@@ -260,23 +278,44 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     }
   }
   const float s_self = part + __shfl_xor(part, 32, kWave);
-  const float p_self = q_c ? (float)(bf16)silu_fast(s_self) : 0.f;
+  const float p_self = q_c ? (float)(bf16)silu_rcp(s_self) : 0.f;
+
+  // Stage this wavefront's O rows (fp32) in LDS: element r of tile t is row 8*(r/4)+4*hh+r%4,
+  // feature t*32 + l32.  The key loop ended with a barrier, so the arena is free.
+  float* Os = reinterpret_cast<float*>(arena) + w * 32 * OP;
+  float* Ps = reinterpret_cast<float*>(arena) + 4 * 32 * OP + w * 32;
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      Os[(8 * (r >> 2) + 4 * hh + (r & 3)) * OP + t * 32 + l32] = o[t][r];
+  if (hh == 0) Ps[l32] = p_self;
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // y = (O + p_self v) / n (.) u, 8 features per lane step, 16-byte loads and stores.
   const float inv_n = 1.0f / (float)n;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int ql = 8 * (r >> 2) + 4 * hh + (r & 3);  // wavefront-local query of element r
+  for (int idx = lane; idx < 32 * DCH; idx += 64) {
+    const int ql = idx / DCH, c = idx % DCH;
     const int q = wq0 + ql;
-    const float pw = __shfl(p_self, ql, kWave);
-    if (q < n) {
+    if (q >= n) continue;
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Os[ql * OP + c * 8]);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(&Os[ql * OP + c * 8 + 4]);
+    float acc[8];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const int f = t * 32 + l32;
-        float acc = o[t][r];
-        if (pw != 0.f) acc += pw * (float)Vp[q * ld + f];
-        const float u = (float)Up[q * ld + f];
-        y[(base + q) * (int64_t)d + (int64_t)h * DH + f] = (bf16)(acc * inv_n * u);
-      }
+    for (int e = 0; e < 4; ++e) { acc[e] = a0[e]; acc[e + 4] = a1[e]; }
+    const float ps = Ps[ql];
+    if (ps != 0.f) {
+      const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(Vp + q * ld + c * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += ps * (float)v8[e];
     }
+    const bf16x8 u8 = *reinterpret_cast<const bf16x8*>(Up + q * ld + c * 8);
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (bf16)(acc[e] * inv_n * (float)u8[e]);
+    *reinterpret_cast<bf16x8*>(y + (base + q) * (int64_t)d + (int64_t)h * DH + c * 8) = out;
   }
 }
 

@@ -40,6 +40,11 @@ __device__ __forceinline__ float wave_min(float v) {
 // log2(e) pre-scale; for z < -88 the exponential overflows to +inf and the quotient is -0,
 // which is the correctly rounded limit.
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// Same function with the hardware reciprocal (about 1 ulp) in place of the IEEE division; used
+// where the result is rounded to bf16 anyway.  rcp(+inf) = 0 gives the same -0 limit.
+__device__ __forceinline__ float silu_rcp(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 // Visibility of key j to query i inside one user whose tokens are ordered U, S, R, C, with
 // n_static = N_U + N_S and rc_end = N_U + N_S + N_R.  Rules of the dynamic mask (fun-rec
@@ -49,9 +54,8 @@ __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-
 // to nobody else.  Used by every attention kernel and by the debug mask dump.
 __device__ __forceinline__ bool mtgr_visible(int i, int j, int n_static, int rc_end, float ti,
                                              float tj) {
-  if (j < n_static) return true;
-  if (i == j) return true;
-  return (i >= n_static) && (j < rc_end) && (tj < ti);
+  // non-short-circuit form: evaluates to a few compares and a select, no branches
+  return (j < n_static) | (i == j) | ((i >= n_static) & (j < rc_end) & (tj < ti));
 }
 
 // Per-user segment record written by the batch-prep kernel.

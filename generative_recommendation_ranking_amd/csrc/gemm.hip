@@ -4,12 +4,12 @@
 //
 //   out[M][N] = epi(a[M][K] . w[N][K]^T + bias[N])
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  A workgroup of 4 wavefronts owns
-// a BM x BN output tile (2 x 2 wavefronts, each (BM/2) x (BN/2) = a grid of 32x32 MFMA tiles);
-// the K loop stages BK-wide slabs of a and w through LDS (register-staged, double-buffered,
-// rows padded by 16 bytes so the 16-byte fragment reads of 32 consecutive rows spread over the
-// banks).  Both operands are K-contiguous, so every lane fetches its 8 consecutive k values of
-// a fragment with one 16-byte LDS read.
+// bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation, one persistent workgroup of 8
+// wavefronts per CU walking 256 x 256 output tiles (wavefront tile 64 x 128); the K loop stages
+// 64-wide slabs of a and w through LDS (register-staged, double-buffered, rows padded by 16 bytes
+// so 16-byte fragment reads of 32 consecutive rows hit distinct banks) and keeps one software
+// pipeline running across tile boundaries.  Both operands are K-contiguous, so every lane
+// fetches its 8 consecutive k values of a fragment with one 16-byte LDS read.
 //
 // Workgroup order: MI355X dispatches consecutive workgroup ids round-robin to its 8 XCDs, each
 // with a private L2.  Tiles are numbered so that every XCD walks its own M-tiles and, for each,
@@ -17,6 +17,8 @@
 // from HBM into one L2 only, while the small weight matrix is shared through the MALL.
 //
 // fp32 path: a plain 64x64 register-tiled VALU kernel (used by the fp32 storage mode).
+#include <algorithm>
+
 #include "../../include/mtgr.h"
 #include "kernels.h"
 
@@ -37,123 +39,196 @@ __device__ __forceinline__ void store_out(TOut* out, const float* resid, int64_t
   }
 }
 
-template <int BM, int BN, int BK, int EPI, typename TOut>
-__global__ __launch_bounds__(256, 1) void k_gemm_bf16(int64_t M, int N, int K,
-                                                      const bf16* __restrict__ A,
-                                                      const bf16* __restrict__ W,
-                                                      const bf16* __restrict__ bias,
-                                                      const float* resid, TOut* out, int nN,
-                                                      int64_t nM) {
-  constexpr int NT = 256;
-  constexpr int TM = BM / 2, TN = BN / 2;   // wavefront tile
-  constexpr int FM = TM / 32, FN = TN / 32; // MFMA tiles per wavefront
-  constexpr int LP = BK + 8;                // LDS row pitch (elements)
-  constexpr int CPR = BK / 8;               // 16-byte chunks per slab row
-  constexpr int CA = BM * CPR / NT;         // a chunks per thread
-  constexpr int CB = BN * CPR / NT;         // w chunks per thread
-  static_assert(CA * NT == BM * CPR && CB * NT == BN * CPR, "tile/thread mismatch");
+template <int EPI, typename TOut>
+__device__ __forceinline__ void store4(TOut* out, const float* resid, int64_t idx, const float v[4]) {
+  float r[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r[e] = v[e];
+  if constexpr (EPI == MTGR_EPI_SILU) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = silu_rcp(r[e]);
+  } else if constexpr (EPI == MTGR_EPI_RESIDUAL_F32) {
+    const f32x4 q = *reinterpret_cast<const f32x4*>(resid + idx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] += q[e];
+  }
+  if constexpr (sizeof(TOut) == 4) {
+    f32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = r[e];
+    *reinterpret_cast<f32x4*>(out + idx) = o;
+  } else {
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (bf16)r[e];
+    *reinterpret_cast<bf16x4*>(out + idx) = o;
+  }
+}
 
-  __shared__ __attribute__((aligned(16))) bf16 As[2][BM][LP];
-  __shared__ __attribute__((aligned(16))) bf16 Bs[2][BN][LP];
+// Persistent variant: one workgroup per CU walks its share of output tiles and streams the
+// K-slabs of consecutive tiles through one software pipeline, so the first loads of the next tile
+// are in flight while the current tile finishes and stores its results.
+//   * WM x WN wavefronts, 256 x 256 tile, BK = 64 (4 MFMA k-steps per slab), two LDS buffers.
+//   * Global loads are buffer loads whose resource starts at the tile's first row and whose size
+//     stops at M (N): rows past the end read as zero, and per-chunk offsets live in SGPRs.
+//   * Per slab: the fragments of k-step ks+1 are read before the MFMAs of k-step ks; the slab
+//     after next is written to LDS after k-step 1 and the one after that is fetched after
+//     k-step 2; the end-of-slab barrier waits for LDS traffic only.
+template <int WM, int WN, int EPI, typename TOut>
+__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
+    int64_t M, int N, int K, const bf16* __restrict__ A, const bf16* __restrict__ W,
+    const bf16* __restrict__ bias, const float* resid, TOut* out, int nN, int64_t nM) {
+  constexpr int BM = 256, BN = 256, BK = 64, NT = 64 * WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32, KS = BK / 16;
+  constexpr int LP = BK + 8, CPR = BK / 8;
+  constexpr int CA = BM * CPR / NT, CB = BN * CPR / NT;   // 8 and 8 chunks per thread
+  constexpr int RSTEP = NT / CPR;                          // rows covered by one chunk index
 
-  // XCD-aware tile decode
-  const int64_t bid = blockIdx.x;
-  const int xcd = (int)(bid % kXcd);
-  const int64_t slot = bid / kXcd;
-  const int64_t m_tile = (slot / nN) * kXcd + xcd;
-  const int n_tile = (int)(slot % nN);
-  if (m_tile >= nM) return;
-  const int64_t m0 = m_tile * BM;
-  const int n0 = n_tile * BN;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16 (*As)[BM][LP] = reinterpret_cast<bf16 (*)[BM][LP]>(smem);
+  bf16 (*Bs)[BN][LP] = reinterpret_cast<bf16 (*)[BN][LP]>(smem + 2 * BM * LP * sizeof(bf16));
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  // tile sequence of this workgroup: XCD-major slots (see the header comment)
+  const int xcd = (int)(blockIdx.x % kXcd);
+  const int gx = (int)(gridDim.x / kXcd);
+  const int64_t nMx = (nM + kXcd - 1) / kXcd;
+  const int64_t nslots = nMx * nN;
+  auto valid_slot = [&](int64_t s) { return s < nslots && (s / nN) * kXcd + xcd < nM; };
+  auto next_slot = [&](int64_t s) {  // next slot of this workgroup holding a real tile
+    s += gx;
+    while (s < nslots && !valid_slot(s)) s += gx;
+    return s;
+  };
+  int64_t first = blockIdx.x / kXcd;
+  if (!valid_slot(first)) first = next_slot(first);
+  if (first >= nslots) return;
 
+  const int nk = K / BK;
+  const uint32_t vo = (uint32_t)((tid / CPR) * K * 2 + (tid % CPR) * 16);  // byte offset in slab
+
+  // load cursor
+  int64_t ld_slot = first;
+  int ld_kt = 0;
+  __amdgpu_buffer_rsrc_t ra_rsrc, rb_rsrc;
+  auto set_load_tile = [&](int64_t slot) {
+    const int64_t m0 = ((slot / nN) * kXcd + xcd) * BM;
+    const int n0 = (int)(slot % nN) * BN;
+    const int64_t mrows = min((int64_t)BM, M - m0);
+    const int nrows = min(BN, N - n0);
+    ra_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * K), (short)0, (int)(mrows * K * 2), 0x00020000);
+    rb_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * K), (short)0, nrows * K * 2, 0x00020000);
+  };
+  set_load_tile(ld_slot);
   bf16x8 ra[CA], rb[CB];
-  const bf16x8 zero8 = {};
-
-  auto load_slab = [&](int k0) {
+  bool ld_valid = true;
+  auto issue_loads = [&]() {  // loads the slab under the load cursor, then advances it
+    const int kb = ld_kt * BK * 2;
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int idx = tid + i * NT;
-      const int r = idx / CPR, c = idx % CPR;
-      const int64_t m = m0 + r;
-      ra[i] = (m < M) ? *reinterpret_cast<const bf16x8*>(A + m * K + k0 + c * 8) : zero8;
-    }
+    for (int i = 0; i < CA; ++i)
+      ra[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, vo, i * RSTEP * K * 2 + kb, 0));
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int idx = tid + i * NT;
-      const int r = idx / CPR, c = idx % CPR;
-      const int n = n0 + r;
-      rb[i] = (n < N) ? *reinterpret_cast<const bf16x8*>(W + (int64_t)n * K + k0 + c * 8) : zero8;
+    for (int i = 0; i < CB; ++i)
+      rb[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, vo, i * RSTEP * K * 2 + kb, 0));
+    if (++ld_kt == nk) {
+      ld_kt = 0;
+      ld_slot = next_slot(ld_slot);
+      ld_valid = ld_slot < nslots;
+      if (ld_valid) set_load_tile(ld_slot);
     }
   };
   auto store_slab = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int idx = tid + i * NT;
-      const int r = idx / CPR, c = idx % CPR;
-      *reinterpret_cast<bf16x8*>(&As[buf][r][c * 8]) = ra[i];
-    }
+    for (int i = 0; i < CA; ++i)
+      *reinterpret_cast<bf16x8*>(&As[buf][tid / CPR + i * RSTEP][(tid % CPR) * 8]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < CB; ++i) {
-      const int idx = tid + i * NT;
-      const int r = idx / CPR, c = idx % CPR;
-      *reinterpret_cast<bf16x8*>(&Bs[buf][r][c * 8]) = rb[i];
-    }
+    for (int i = 0; i < CB; ++i)
+      *reinterpret_cast<bf16x8*>(&Bs[buf][tid / CPR + i * RSTEP][(tid % CPR) * 8]) = rb[i];
   };
+  bf16x8 fa[2][FM], fb[2][FN];
+  auto read_frags = [&](int buf, int ks, int slot) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[slot][i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * TM + i * 32 + l32][ks * 16 + hh * 8]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      fb[slot][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * TN + j * 32 + l32][ks * 16 + hh * 8]);
+  };
+  auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-  const int nk = K / BK;
-  load_slab(0);
+  // prologue: slab 0 into LDS buffer 0, slab 1 into registers
+  issue_loads();
   store_slab(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) load_slab((kt + 1) * BK);
+  bool have_next = ld_valid;   // registers hold a slab still to be written to LDS
+  if (have_next) issue_loads();
+  lds_barrier();
+  read_frags(0, 0, 0);
+
+  int64_t slot = first;
+  int cur = 0;
+  while (true) {
+    f32x16 acc[FM][FN];
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 fa[FM], fb[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8*>(&As[cur][wm * TM + i * 32 + l32][ks * 16 + hh * 8]);
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8*>(&Bs[cur][wn * TN + j * 32 + l32][ks * 16 + hh * 8]);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    const int64_t next = next_slot(slot);
+    for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) store_slab(cur ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue.  Accumulator element r of a 32x32 tile sits at row 8*(r/4) + 4*(lane/32) + r%4,
-  // column lane%32.
+      for (int ks = 0; ks < KS; ++ks) {
+        const int fs = ks & 1;
+        if (ks + 1 < KS) read_frags(cur, ks + 1, fs ^ 1);
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int n = n0 + wn * TN + j * 32 + l32;
-    if (n >= N) continue;
-    const float bv = bias ? (float)bias[n] : 0.f;
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t m = m0 + wm * TM + i * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (m < M) store_out<EPI, TOut>(out, resid, m * N + n, acc[i][j][r] + bv);
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fs][j], fa[fs][i], acc[i][j], 0, 0, 0);
+        if (ks == 1 && have_next) store_slab(cur ^ 1);
+        if (ks == 2) {
+          have_next = have_next && ld_valid;
+          if (have_next) issue_loads();
+        }
+      }
+      if (kt + 1 < nk || next < nslots) {
+        lds_barrier();
+        cur ^= 1;
+        read_frags(cur, 0, 0);
       }
     }
+    // epilogue of this tile: row m = l32 of the MFMA tile, columns 8g + 4hh + 0..3 (N is a
+    // multiple of 4, so a group is either wholly inside or wholly past the last column)
+    const int64_t m0 = ((slot / nN) * kXcd + xcd) * BM;
+    const int n0 = (int)(slot % nN) * BN;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t m = m0 + wm * TM + i * 32 + l32;
+      if (m >= M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int n = n0 + wn * TN + j * 32 + 8 * g + 4 * hh;
+          if (n >= N) continue;
+          float v[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
+          if (bias) {
+            const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(bias + n);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] += (float)b4[e];
+          }
+          store4<EPI, TOut>(out, resid, m * N + n, v);
+        }
+      }
+    }
+    if (next >= nslots) break;
+    slot = next;
   }
 }
 
@@ -210,16 +285,25 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int64_t M, int N, int K,
   }
 }
 
-template <int BM, int BN, int EPI, typename TOut>
-hipError_t run_bf16(int64_t M, int N, int K, const bf16* a, const bf16* w, const bf16* bias,
-                    const float* resid, void* out, hipStream_t s) {
-  constexpr int BK = 64;
-  const int nN = (N + BN - 1) / BN;
-  const int64_t nM = (M + BM - 1) / BM;
-  const int64_t nMpad = (nM + kXcd - 1) / kXcd * kXcd;
-  const int64_t blocks = nMpad * nN;
-  k_gemm_bf16<BM, BN, BK, EPI, TOut><<<(unsigned)blocks, 256, 0, s>>>(
-      M, N, K, a, w, bias, resid, static_cast<TOut*>(out), nN, nM);
+template <int WM, int WN, int EPI, typename TOut>
+hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf16* w,
+                               const bf16* bias, const float* resid, void* out, hipStream_t s) {
+  constexpr size_t lds = 2 * (size_t)(256 + 256) * (64 + 8) * sizeof(bf16);
+  auto kern = k_gemm_bf16_persistent<WM, WN, EPI, TOut>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int nN = (N + 255) / 256;
+  const int64_t nM = (M + 255) / 256;
+  const int64_t tiles_pad = (nM + kXcd - 1) / kXcd * kXcd * nN;
+  const int64_t grid = std::min<int64_t>(tiles_pad, (int64_t)cus / kXcd * kXcd);
+  kern<<<(unsigned)grid, 64 * WM * WN, lds, s>>>(M, N, K, a, w, bias, resid, static_cast<TOut*>(out), nN, nM);
   return hipGetLastError();
 }
 
@@ -229,10 +313,10 @@ hipError_t launch_gemm_bf16(int64_t M, int N, int K, int epi, const bf16* a, con
                             const bf16* bias, const float* resid, void* out, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   switch (epi) {
-    case MTGR_EPI_STORE: return run_bf16<128, 128, MTGR_EPI_STORE, bf16>(M, N, K, a, w, bias, resid, out, s);
-    case MTGR_EPI_SILU: return run_bf16<128, 128, MTGR_EPI_SILU, bf16>(M, N, K, a, w, bias, resid, out, s);
+    case MTGR_EPI_STORE: return run_bf16_persistent<4, 2, MTGR_EPI_STORE, bf16>(M, N, K, a, w, bias, resid, out, s);
+    case MTGR_EPI_SILU: return run_bf16_persistent<4, 2, MTGR_EPI_SILU, bf16>(M, N, K, a, w, bias, resid, out, s);
     case MTGR_EPI_RESIDUAL_F32:
-      return run_bf16<128, 128, MTGR_EPI_RESIDUAL_F32, float>(M, N, K, a, w, bias, resid, out, s);
+      return run_bf16_persistent<4, 2, MTGR_EPI_RESIDUAL_F32, float>(M, N, K, a, w, bias, resid, out, s);
     default: return hipErrorInvalidValue;
   }
 }
