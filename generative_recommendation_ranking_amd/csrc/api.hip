@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <vector>
 
 #include "../../include/mtgr.h"
 #include "kernels.h"
@@ -19,14 +20,14 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 inline int esize(int dtype) { return dtype == MTGR_BF16 ? 2 : 4; }
 
 struct Plan {
-  size_t seg = 0, order = 0, tile_off = 0, cand_off = 0, cand_idx = 0, flags = 0;
+  size_t seg = 0, order = 0, tile_off = 0, cand_off = 0, cand_idx = 0, flags = 0, xcd_off = 0;
   size_t xt = 0, big = 0, y = 0, xres = 0, hin = 0, hhid = 0;
   size_t total = 0;
 };
 
 struct Sizes {
   int64_t B = 0, T = 0, C = 0;
-  int d = 0, h = 0, hh = 0, dtype = MTGR_F32;
+  int d = 0, h = 0, hh = 0, dtype = MTGR_F32, H = 0;
   bool need_xres = false, need_head = false, need_acts = false;
 };
 
@@ -45,6 +46,8 @@ Plan make_plan(const Sizes& z) {
   p.tile_off = take((size_t)(z.B + 1) * sizeof(int32_t));
   p.cand_off = take((size_t)(z.B + 1) * sizeof(int64_t));
   p.cand_idx = take((size_t)z.C * sizeof(int64_t));
+  const int64_t rounds = (z.B * z.H + kXcdCount - 1) / kXcdCount;
+  p.xcd_off = take((size_t)kXcdCount * (rounds + 1) * sizeof(int32_t));
   if (z.need_acts) {
     p.xt = take((size_t)z.T * z.d * es);
     p.big = take((size_t)z.T * std::max(4 * z.d, z.h) * es);
@@ -88,6 +91,24 @@ int64_t total_tiles(const mtgr_batch* b, int q_tile) {
     t += (n + q_tile - 1) / q_tile;
   }
   return t;
+}
+
+// Host replica of the device-side placement (k_prep_users' LPT order, k_prep_xcd's snake deal):
+// the largest per-XCD q-tile count, which sizes the attention grid.
+int64_t xcd_grid_slots(const mtgr_batch* b, int H, int q_tile) {
+  const int32_t B = b->num_users;
+  std::vector<int32_t> order(B);
+  for (int32_t i = 0; i < B; ++i) order[i] = i;
+  auto len = [&](int32_t u) { return b->offsets_host[u + 1] - b->offsets_host[u]; };
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return len(x) > len(y); });
+  const int64_t G = (int64_t)B * H;
+  int64_t tot[kXcdCount] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t g = 0; g < G; ++g) {
+    const int64_t k = g / kXcdCount, r = g % kXcdCount;
+    const int x = (int)((k & 1) ? (kXcdCount - 1 - r) : r);
+    tot[x] += (len(order[g / H]) + q_tile - 1) / q_tile;
+  }
+  return *std::max_element(tot, tot + kXcdCount);
 }
 
 bool dh_ok(int dtype, int dh) {
@@ -135,8 +156,9 @@ mtgr_status check_encoder(const mtgr_encoder_params* p) {
   return MTGR_OK;
 }
 
-Sizes sizes_for(const mtgr_batch* b, int d, int h, int hh, int dtype) {
+Sizes sizes_for(const mtgr_batch* b, int d, int h, int hh, int dtype, int H) {
   Sizes z;
+  z.H = H;
   z.B = b->num_users;
   z.T = b->num_tokens;
   z.C = b->num_candidates;
@@ -155,6 +177,7 @@ PrepBufs prep_bufs(void* ws, const Plan& p) {
   pb.cand_off = at<int64_t>(ws, p.cand_off);
   pb.cand_idx = at<int64_t>(ws, p.cand_idx);
   pb.flags = at<int32_t>(ws, p.flags);
+  pb.xcd_off = at<int32_t>(ws, p.xcd_off);
   return pb;
 }
 
@@ -179,11 +202,11 @@ hipError_t linear(int64_t M, int N, int K, int dtype, int epi, const void* a, co
 
 hipError_t attention(const mtgr_batch* b, int d, int H, int dtype, const PrepBufs& pb,
                      const void* qkvu, void* y, hipStream_t s) {
-  const int64_t tiles = total_tiles(b, q_tile_for(dtype));
   if (dtype == MTGR_BF16)
-    return launch_attention_bf16(b->num_users, tiles, d, H, b->offsets, pb.seg, pb.order,
-                                 pb.tile_off, b->timestamps, static_cast<const bf16*>(qkvu),
-                                 static_cast<bf16*>(y), s);
+    return launch_attention_bf16(b->num_users, xcd_grid_slots(b, H, kAttnQTileBf16), d, H,
+                                 b->offsets, pb.seg, pb.order, pb.xcd_off, b->timestamps,
+                                 static_cast<const bf16*>(qkvu), static_cast<bf16*>(y), s);
+  const int64_t tiles = total_tiles(b, kAttnQTileF32);
   return launch_attention_f32(b->num_users, tiles, d, H, b->offsets, pb.seg, pb.order,
                               pb.tile_off, b->timestamps, static_cast<const float*>(qkvu),
                               static_cast<float*>(y), s);
@@ -239,7 +262,8 @@ mtgr_status mtgr_encoder_workspace_size(const mtgr_encoder_params* p, const mtgr
   mtgr_status st = check_encoder(p);
   if (st != MTGR_OK) return st;
   if ((st = check_batch(b)) != MTGR_OK) return st;
-  Sizes z = sizes_for(b, p->layers[0].d_model, 0, p->head_hidden, p->layers[0].dtype);
+  Sizes z = sizes_for(b, p->layers[0].d_model, 0, p->head_hidden, p->layers[0].dtype,
+                      p->layers[0].num_heads);
   for (int32_t l = 0; l < p->num_layers; ++l) z.h = std::max(z.h, (int)p->layers[l].mlp_hidden);
   z.need_acts = z.need_xres = z.need_head = true;
   *bytes = make_plan(z).total;
@@ -252,7 +276,7 @@ mtgr_status mtgr_block_workspace_size(const mtgr_block_params* p, const mtgr_bat
   mtgr_status st = check_block(p);
   if (st != MTGR_OK) return st;
   if ((st = check_batch(b)) != MTGR_OK) return st;
-  Sizes z = sizes_for(b, p->d_model, p->mlp_hidden, 0, p->dtype);
+  Sizes z = sizes_for(b, p->d_model, p->mlp_hidden, 0, p->dtype, p->num_heads);
   z.need_acts = true;
   *bytes = make_plan(z).total;
   return MTGR_OK;
@@ -264,7 +288,7 @@ mtgr_status mtgr_attention_workspace_size(const mtgr_batch* b, int32_t d, int32_
   mtgr_status st = check_batch(b);
   if (st != MTGR_OK) return st;
   if (d <= 0 || num_heads <= 0 || d % num_heads != 0) return MTGR_ERR_BAD_SHAPE;
-  Sizes z = sizes_for(b, d, 0, 0, MTGR_F32);
+  Sizes z = sizes_for(b, d, 0, 0, MTGR_F32, num_heads);
   *bytes = make_plan(z).total;
   return MTGR_OK;
 }
@@ -281,12 +305,12 @@ mtgr_status mtgr_encoder_fwd(const mtgr_encoder_params* p, const mtgr_batch* b, 
   if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int dt = p->layers[0].dtype;
-  Sizes z = sizes_for(b, p->layers[0].d_model, 0, p->head_hidden, dt);
+  Sizes z = sizes_for(b, p->layers[0].d_model, 0, p->head_hidden, dt, p->layers[0].num_heads);
   for (int32_t l = 0; l < p->num_layers; ++l) z.h = std::max(z.h, (int)p->layers[l].mlp_hidden);
   z.need_acts = z.need_xres = z.need_head = true;
   const Plan pl = make_plan(z);
   const PrepBufs pb = prep_bufs(ws, pl);
-  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dt), pb, true, s));
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dt), z.H, pb, true, s));
   float* xr = hidden_out ? hidden_out : at<float>(ws, pl.xres);
   for (int32_t l = 0; l < p->num_layers; ++l) {
     const float* src = (l == 0) ? x_in : xr;
@@ -314,11 +338,11 @@ mtgr_status mtgr_block_fwd(const mtgr_block_params* p, const mtgr_batch* b, cons
   if (!ws || ws_bytes < need) return MTGR_ERR_WORKSPACE;
   if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Sizes z = sizes_for(b, p->d_model, p->mlp_hidden, 0, p->dtype);
+  Sizes z = sizes_for(b, p->d_model, p->mlp_hidden, 0, p->dtype, p->num_heads);
   z.need_acts = true;
   const Plan pl = make_plan(z);
   const PrepBufs pb = prep_bufs(ws, pl);
-  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(p->dtype), pb, false, s));
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(p->dtype), z.H, pb, false, s));
   MTGR_TRY(run_block(p, b, pb, pl, ws, x_in, x_out, s));
   return MTGR_OK;
 }
@@ -366,10 +390,10 @@ mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads
   if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;
   if (!qkvu || !y_gated) return MTGR_ERR_NULL_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  Sizes z = sizes_for(b, d, 0, 0, MTGR_F32);
+  Sizes z = sizes_for(b, d, 0, 0, MTGR_F32, num_heads);
   const Plan pl = make_plan(z);
   const PrepBufs pb = prep_bufs(ws, pl);
-  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), pb, false, s));
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), num_heads, pb, false, s));
   MTGR_TRY(attention(b, d, num_heads, dtype, pb, qkvu, y_gated, s));
   return MTGR_OK;
 }
@@ -380,7 +404,7 @@ mtgr_status mtgr_validate_batch(const mtgr_batch* b, void* ws, size_t ws_bytes, 
   *flags_out = 0;
   mtgr_status st = check_batch(b);
   if (st != MTGR_OK) return st;
-  Sizes z = sizes_for(b, 8, 0, 0, MTGR_F32);
+  Sizes z = sizes_for(b, 8, 0, 0, MTGR_F32, 0);
   const Plan pl = make_plan(z);
   if (!ws || ws_bytes < pl.total) return MTGR_ERR_WORKSPACE;
   if (b->num_users == 0) return MTGR_OK;
@@ -402,7 +426,7 @@ mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, uint8_t* mask_dev
   mtgr_status st = check_batch(b);
   if (st != MTGR_OK) return st;
   if (user < 0 || user >= b->num_users) return MTGR_ERR_BAD_SHAPE;
-  Sizes z = sizes_for(b, 8, 0, 0, MTGR_F32);
+  Sizes z = sizes_for(b, 8, 0, 0, MTGR_F32, 0);
   const Plan pl = make_plan(z);
   if (!ws || ws_bytes < pl.total) return MTGR_ERR_WORKSPACE;
   const int64_t n = b->offsets_host[user + 1] - b->offsets_host[user];
@@ -410,7 +434,7 @@ mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, uint8_t* mask_dev
   if (!mask_dev) return MTGR_ERR_NULL_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const PrepBufs pb = prep_bufs(ws, pl);
-  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, kAttnQTileF32, pb, false, s));
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, kAttnQTileF32, 0, pb, false, s));
   MTGR_TRY(launch_debug_mask(user, b->offsets, pb.seg, b->timestamps, n, mask_dev, s));
   return MTGR_OK;
 }

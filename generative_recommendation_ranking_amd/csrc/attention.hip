@@ -34,6 +34,8 @@ namespace mtgr {
 namespace {
 
 constexpr int BQ = kAttnQTileBf16;  // 128 query rows per work item
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int BKV = 64;             // keys per tile
 
 __device__ __forceinline__ int find_slot(const int32_t* __restrict__ tile_off, int B, int item) {
@@ -47,33 +49,39 @@ __device__ __forceinline__ int find_slot(const int32_t* __restrict__ tile_off, i
 
 template <int DH>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(
-    int32_t B, int d, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
-    const int32_t* __restrict__ order, const int32_t* __restrict__ tile_off,
+    int32_t B, int H, int d, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ xcd_off,
     const float* __restrict__ ts, const bf16* __restrict__ qkvu, bf16* __restrict__ y) {
-  constexpr int KP = DH + 8;
-  constexpr int VP = BKV + 8;
+  constexpr int KP = DH + 8;                     // K row pitch: 16-byte reads of 16 rows hit distinct banks
+  constexpr int VP = DH + 16;                    // V row pitch: the 4 rows of a transposing read too
   constexpr int DCH = DH / 8;                    // 16-byte chunks per key row
-  constexpr int VT = 8 * DCH;                    // V-staging threads: (8-key chunk, 8 features)
-  constexpr int KT = DH;                         // K-staging threads
-  constexpr int CK = BKV * DCH / KT;             // K chunks per K-staging thread (8)
+  constexpr int CH = BKV * DCH / 256;            // K (and V) chunks per thread per tile
   constexpr int NT = DH / 32;                    // output tiles of 32 features
-  static_assert(CK == 8 && VT + KT <= 256, "staging layout");
+  static_assert(CH * 256 == BKV * DCH && CH <= 4, "staging layout");
 
   // One LDS arena: K and V^T tiles (double-buffered) and the tile timestamps during the key loop;
   // reused afterwards to stage each wavefront's output rows for vectorised stores.
   constexpr int OP = DH + 4;                                   // fp32 pitch of staged output rows
-  constexpr size_t kLoopBytes = (2 * BKV * KP + 2 * DH * VP) * sizeof(bf16) + 2 * BKV * sizeof(float);
+  constexpr size_t kLoopBytes = (2 * BKV * KP + 2 * BKV * VP) * sizeof(bf16) + 2 * BKV * sizeof(float);
   constexpr size_t kEpiBytes = 4 * 32 * OP * sizeof(float) + 4 * 32 * sizeof(float);
   __shared__ __attribute__((aligned(16))) char arena[kLoopBytes > kEpiBytes ? kLoopBytes : kEpiBytes];
   bf16 (*Ks)[BKV][KP] = reinterpret_cast<bf16 (*)[BKV][KP]>(arena);
-  bf16 (*Vt)[DH][VP] = reinterpret_cast<bf16 (*)[DH][VP]>(arena + 2 * BKV * KP * sizeof(bf16));
-  float (*Ts)[BKV] = reinterpret_cast<float (*)[BKV]>(arena + (2 * BKV * KP + 2 * DH * VP) * sizeof(bf16));
+  bf16 (*Vs)[BKV][VP] = reinterpret_cast<bf16 (*)[BKV][VP]>(arena + 2 * BKV * KP * sizeof(bf16));
+  float (*Ts)[BKV] = reinterpret_cast<float (*)[BKV]>(arena + (2 * BKV * KP + 2 * BKV * VP) * sizeof(bf16));
 
-  const int item = blockIdx.x;
-  const int h = blockIdx.y;
-  const int slot = find_slot(tile_off, B, item);
-  const int b = order[slot];
-  const int qt = item - tile_off[slot];
+  // Work decode: workgroup ids go round-robin to the XCDs, so id % 8 is the XCD and id / 8 the
+  // position in that XCD's queue; the queue lists its (user, head) groups' q-tiles back to back,
+  // so all q-tiles of a group run on one XCD, together, and share its L2 while they sweep K/V.
+  const int xcd = (int)(blockIdx.x % kXcdCount);
+  const int pos = (int)(blockIdx.x / kXcdCount);
+  const int R = (int)(((int64_t)B * H + kXcdCount - 1) / kXcdCount);
+  const int32_t* xo = xcd_off + (int64_t)xcd * (R + 1);
+  if (pos >= xo[R]) return;
+  const int round = find_slot(xo, R, pos);
+  const int64_t grp = (int64_t)round * kXcdCount + ((round & 1) ? (kXcdCount - 1 - xcd) : xcd);
+  const int b = order[grp / H];
+  const int h = (int)(grp % H);
+  const int qt = pos - xo[round];
   const int64_t base = offsets[b];
   const int n = (int)(offsets[b + 1] - base);
   const UserSeg sg = seg[b];
@@ -116,69 +124,38 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
 
-  // Staging registers, shared by the two roles: wavefronts with tid < VT gather V, the next KT
-  // threads copy K, the rest only help with the timestamps.
-  //  * V: thread (ch, c) fetches the 8 keys that form 16-byte chunk ch of a transposed V row
-  //    (the keys lane-half hh of k-step ks consumes, ch = 2*ks + hh) at features c*8..c*8+7, then
-  //    writes one 16-byte chunk per feature.  Eight consecutive threads fill one 128-byte row,
-  //    and with the 144-byte row pitch the rows of neighbouring groups start 32 banks apart.
-  //  * K: plain 16-byte chunks, 8 per thread, row-major with a 16-byte pad.
-  bf16x8 stg[8];
+  // Staging: every thread copies CH 16-byte chunks of the K tile and CH of the V tile (both kept
+  // row-major in LDS), through buffer loads over this user's rows of head h sized to the first
+  // kend keys, so keys at or past kend read as zero.  Per-lane byte offset in a VGPR, the tile
+  // offset in an SGPR.
+  bf16x8 stg[2 * CH];
   float rt = INFINITY;
-  // role is uniform per wavefront (VT and KT are multiples of 64); make that visible
-  const int role = __builtin_amdgcn_readfirstlane(tid < VT ? 0 : (tid < VT + KT ? 1 : 2));
-  const bool v_role = role == 0;
-  const bool k_role = role == 1;
-  const int v_ch = tid & 7, v_c = (tid >> 3) % DCH;
-  auto v_key = [](int ch, int jj) {  // key (0..63) feeding slot jj of chunk ch
-    const int ks = ch >> 1, h = ch & 1;
-    return (ks >> 1) * 32 + 8 * ((ks & 1) * 2 + (jj >> 2)) + 4 * h + (jj & 3);
-  };
-  // Buffer resources over this user's K (or V) rows of head h, sized to the first kend keys:
-  // keys at or past kend read as zero.  Per-lane byte offset in a VGPR, per-key step in SGPRs.
   const uint32_t row_bytes = (uint32_t)(ld * 2);
-  const __amdgpu_buffer_rsrc_t kv_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(v_role ? Vp : Kp), (short)0, (int)((uint32_t)kend * row_bytes), 0x00020000);
-  const uint32_t v_off = (uint32_t)v_key(v_ch, 0) * row_bytes + v_c * 16;
-  const uint32_t k_off = (uint32_t)((tid - VT) / DCH) * row_bytes + ((tid - VT) % DCH) * 16;
-  const uint32_t my_off = v_role ? v_off : k_off;
+  const int nbytes = (int)((uint32_t)kend * row_bytes);
+  const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kp, (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vp, (short)0, nbytes, 0x00020000);
+  const int st_key = tid / DCH, st_c = tid % DCH;             // chunk i: key st_key + i*(256/DCH)
+  constexpr int KSTEP = 256 / DCH;
+  const uint32_t st_off = (uint32_t)st_key * row_bytes + st_c * 16;
 
   auto stage_load = [&](int k0) {
-    if (role < 2) {
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        // V: keys v_key(ch, jj) = v_key(ch, 0) + 8*(jj/4) + jj%4;  K: rows (tid-VT)/DCH + jj*KT/DCH
-        const uint32_t step = v_role ? (uint32_t)(8 * (jj >> 2) + (jj & 3)) : (uint32_t)(jj * (KT / DCH));
-        stg[jj] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
-            kv_rsrc, my_off, (uint32_t)(k0 + step) * row_bytes, 0));
-      }
+    for (int i = 0; i < CH; ++i) {
+      const uint32_t so = (uint32_t)(k0 + i * KSTEP) * row_bytes;
+      stg[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, st_off, so, 0));
+      stg[CH + i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, st_off, so, 0));
     }
     if (tid < BKV) rt = (k0 + tid < kend) ? ts[base + k0 + tid] : INFINITY;
   };
   auto stage_store = [&](int buf) {
-    if (v_role) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x8 col;
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) col[jj] = stg[jj][e];
-        *reinterpret_cast<bf16x8*>(&Vt[buf][v_c * 8 + e][v_ch * 8]) = col;
-      }
-    } else if (k_role) {
-#pragma unroll
-      for (int i = 0; i < CK; ++i) {
-        const int idx = (tid - VT) + i * KT;
-        const int key = idx / DCH, c = idx % DCH;
-        *reinterpret_cast<bf16x8*>(&Ks[buf][key][c * 8]) = stg[i];
-      }
+    for (int i = 0; i < CH; ++i) {
+      *reinterpret_cast<bf16x8*>(&Ks[buf][st_key + i * KSTEP][st_c * 8]) = stg[i];
+      *reinterpret_cast<bf16x8*>(&Vs[buf][st_key + i * KSTEP][st_c * 8]) = stg[CH + i];
     }
     if (tid < BKV) Ts[buf][tid] = rt;
   };
 
-  // Per key tile: the wavefront's scores S^T = K Q^T and P = mask(silu(S)) first; the next
-  // tile's global loads are issued only after that (the score accumulators are dead by then,
-  // which keeps the staging registers and the scores from being live together); then O += P V,
-  // the store of the next tile into the other LDS buffer, and one barrier.
   auto tile_needed = [&](int buf, int k0) {
     bool need = wave_rows && (k0 < ns || (wave_rc && k0 < rc_end));
     if (need && k0 >= ns) {
@@ -244,7 +221,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(&Vt[buf][t * 32 + l32][ks * 16 + hh * 8]);
+        // B fragment (keys x features) of PV k-step ks: slot jj of lane-half hh is key
+        // kb + 4*hh + jj%4 (+8 for jj >= 4), kb = (ks/2)*32 + (ks%2)*16, feature t*32 + lane%32.
+        // ds_read_b64_tr_b16 hands lane i of a 16-lane group element i%4 of the 4-element rows
+        // addressed by lanes i/4 + 4e: point lane s at row kb + 4*hh + s/4, features
+        // t*32 + 16*(group%2) + 4*(s%4), and each read returns 4 keys of one feature column.
+        const int kb = (ks >> 1) * 32 + (ks & 1) * 16 + 4 * hh + (lane & 15) / 4;
+        const int fc = t * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&Vs[buf][kb][fc]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&Vs[buf][kb + 8][fc]));
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], vf, o[t], 0, 0, 0);
       }
     }
@@ -364,17 +350,17 @@ __global__ __launch_bounds__(64) void k_attn_f32(
 
 }  // namespace
 
-hipError_t launch_attention_bf16(int32_t B, int64_t total_tiles, int d, int H,
+hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H,
                                  const int64_t* offsets, const UserSeg* seg, const int32_t* order,
-                                 const int32_t* tile_off, const float* timestamps,
+                                 const int32_t* xcd_off, const float* timestamps,
                                  const bf16* qkvu, bf16* y, hipStream_t s) {
-  if (total_tiles == 0) return hipSuccess;
+  if (grid_slots == 0) return hipSuccess;
   const int dh = d / H;
-  dim3 grid((unsigned)total_tiles, (unsigned)H);
+  const unsigned grid = (unsigned)(grid_slots * kXcdCount);
   if (dh == 128)
-    k_attn_bf16<128><<<grid, 256, 0, s>>>(B, d, offsets, seg, order, tile_off, timestamps, qkvu, y);
+    k_attn_bf16<128><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y);
   else if (dh == 64)
-    k_attn_bf16<64><<<grid, 256, 0, s>>>(B, d, offsets, seg, order, tile_off, timestamps, qkvu, y);
+    k_attn_bf16<64><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -19,9 +19,12 @@ struct PrepBufs {
   int64_t* cand_off;   // [B+1] exclusive prefix of K_b in user order
   int64_t* cand_idx;   // [C]   token row of each candidate, packed order
   int32_t* flags;      // [4]   validation flags / counters
+  int32_t* xcd_off;    // [8][R+1] per-XCD q-tile prefix over (user, head) groups, R = ceil(B*H/8)
 };
+constexpr int kXcdCount = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin by id
 hipError_t launch_prep(int32_t B, int64_t C, const int64_t* offsets, const uint8_t* group_ids,
-                       int q_tile, const PrepBufs& pb, bool want_cand_idx, hipStream_t s);
+                       int q_tile, int heads, const PrepBufs& pb, bool want_cand_idx,
+                       hipStream_t s);
 hipError_t launch_validate(int32_t B, const int64_t* offsets, const uint8_t* group_ids,
                            const float* timestamps, int32_t* flags, hipStream_t s);
 hipError_t launch_debug_mask(int32_t user, const int64_t* offsets, const UserSeg* seg,
@@ -44,9 +47,10 @@ hipError_t launch_gemm_f32(int64_t M, int N, int K, int epi, const float* a, con
 // ---- attention (attention.hip) -------------------------------------------------------------
 constexpr int kAttnQTileBf16 = 128;
 constexpr int kAttnQTileF32 = 64;
-hipError_t launch_attention_bf16(int32_t B, int64_t total_tiles, int d, int H,
+// grid_slots = max over XCDs of that XCD's q-tile count (the host replica of k_prep_xcd)
+hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H,
                                  const int64_t* offsets, const UserSeg* seg, const int32_t* order,
-                                 const int32_t* tile_off, const float* timestamps,
+                                 const int32_t* xcd_off, const float* timestamps,
                                  const bf16* qkvu, bf16* y, hipStream_t s);
 hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H,
                                 const int64_t* offsets, const UserSeg* seg, const int32_t* order,

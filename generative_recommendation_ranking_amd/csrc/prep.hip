@@ -98,6 +98,30 @@ __global__ __launch_bounds__(1024) void k_prep_scan(int32_t B, int q_tile,
   }
 }
 
+// XCD placement of attention work: groups g = (LPT position p, head h) = p*H + h are dealt to the
+// 8 XCDs in snake order (round k = g / 8 holds groups 8k..8k+7; XCD x takes 8k + x in even rounds
+// and 8k + 7 - x in odd ones).  xo[x][k] = q-tiles of XCD x's groups in rounds before k, so XCD x
+// runs its groups one after another and all q-tiles of a group share that XCD's L2.
+__global__ void k_prep_xcd(int32_t B, int H, int q_tile, const int64_t* __restrict__ offsets,
+                           const int32_t* __restrict__ order, int32_t* __restrict__ xo) {
+  const int x = threadIdx.x;
+  if (x >= kXcdCount) return;
+  const int64_t G = (int64_t)B * H;
+  const int R = (int)((G + kXcdCount - 1) / kXcdCount);
+  int32_t* row = xo + (int64_t)x * (R + 1);
+  int32_t acc = 0;
+  for (int k = 0; k < R; ++k) {
+    row[k] = acc;
+    const int64_t g = (int64_t)k * kXcdCount + ((k & 1) ? (kXcdCount - 1 - x) : x);
+    if (g < G) {
+      const int b = order[g / H];
+      const int64_t n = offsets[b + 1] - offsets[b];
+      acc += (int32_t)((n + q_tile - 1) / q_tile);
+    }
+  }
+  row[R] = acc;
+}
+
 __global__ void k_prep_cand(int32_t B, int64_t C, const int64_t* __restrict__ offsets,
                             const UserSeg* __restrict__ seg, const int64_t* __restrict__ cand_off,
                             int64_t* __restrict__ cand_idx) {
@@ -147,11 +171,13 @@ __global__ void k_debug_mask(const int64_t* __restrict__ offsets, const UserSeg*
 }  // namespace
 
 hipError_t launch_prep(int32_t B, int64_t C, const int64_t* offsets, const uint8_t* group_ids,
-                       int q_tile, const PrepBufs& pb, bool want_cand_idx, hipStream_t s) {
+                       int q_tile, int heads, const PrepBufs& pb, bool want_cand_idx,
+                       hipStream_t s) {
   if (B <= 0) return hipSuccess;
   k_prep_users<<<(B + 255) / 256, 256, 0, s>>>(B, offsets, group_ids, pb.seg, pb.order);
   k_prep_scan<<<1, 1024, 0, s>>>(B, q_tile, offsets, pb.seg, pb.order, pb.tile_off, pb.cand_off);
   if (want_cand_idx) k_prep_cand<<<B, 256, 0, s>>>(B, C, offsets, pb.seg, pb.cand_off, pb.cand_idx);
+  if (pb.xcd_off && heads > 0) k_prep_xcd<<<1, 64, 0, s>>>(B, heads, q_tile, offsets, pb.order, pb.xcd_off);
   return hipGetLastError();
 }
 
