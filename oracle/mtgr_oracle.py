@@ -23,21 +23,24 @@ Definitions followed (all exact; the method has no approximation, heuristic or i
     by the token's group                                              [P5 7.3.3, GLN equation]
   * head: candidate hidden states -> MLP -> (CTR, CTCVR) logits      [P1/P2 token section; P5 7.3.1]
 
-Readings where the pages are silent or garbled (each listed with its reason in the design notes):
+Readings where the pages are silent or garbled (the same numbering as the design notes):
   R1 the garbled silu(K^T Q) M V is read token-wise: v~_i = sum_j M[i,j] silu(q_i.k_j)/N v_j,
-     with M applied elementwise; no 1/sqrt(d_h) scale and no relative bias.
+     with M applied elementwise.
   R2 N is the user's total token count (N_U+N_S+N_R+K), not the count of visible keys.
-  R3 R-key visibility uses strict '<' on float32 seconds; equal timestamps are invisible, except a
-     token to itself.  U and S queries never see R keys; R, U and S queries never see C keys.
-  R4 GroupLN statistics are per token (biased variance, eps=1e-5); gamma/beta per group.
-  R5 Q, K, V, U projections are affine with no activation; heads split Q, K, V into
-     contiguous d_h-wide slices; U gates the concatenated heads elementwise.
-  R6 MLP is d -> h -> d with SiLU and biases; head is d -> d/2 -> 2 with SiLU, raw logits.
+  R3 no scale and no relative bias inside silu.
+  R4 R-key visibility uses strict '<' on float32 seconds; equal timestamps are invisible, except a
+     token to itself.  R5: U and S queries never see R keys.  R6: candidates see only themselves
+     among candidates; R, U and S queries never see C keys.
+  R7 GroupLN statistics are per token (biased variance, eps=1e-5); gamma/beta per group.
+  R8 Q, K, V, U projections are affine with no activation; heads split Q, K, V into contiguous
+     d_h-wide slices; U gates the concatenated heads elementwise.
+  R9 MLP is d -> h -> d with SiLU and biases.  R10: the head is d -> d/2 -> 2 with SiLU, raw logits.
 
 parity pins: every function below is pinned by tests/test_oracle_pins.py (worked mask examples
 from [P1] and [P5], GroupLN invariants and torch layer_norm, closed forms and library reductions
-of the attention, permutation/independence/isolation/temporal-replay invariants).  The readings
-R1-R6 themselves are pinned only by construction (the pages do not fix them).
+of the attention, silu against torch, a special case of the head, and permutation / independence /
+isolation / temporal-replay invariants).  The readings R3, R8, R9 and R10 are parity unpinned with
+respect to the paper: the pages never fix them, so they are pinned only by construction.
 """
 from __future__ import annotations
 

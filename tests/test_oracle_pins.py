@@ -364,3 +364,23 @@ def test_generator_deterministic_and_shapes():
         t = b1.timestamps[b1.offsets[u]:b1.offsets[u + 1]]
         assert np.isneginf(t[g < 2]).all()
         assert (np.diff(t[g == 2]) >= 0).all()
+
+
+def test_silu_matches_torch_and_limits():
+    z = np.concatenate([np.linspace(-50, 50, 2001), [-1000.0, 1000.0, 0.0]])
+    ref = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    np.testing.assert_allclose(O.silu(z), ref, rtol=1e-15, atol=1e-300)
+    assert O.silu(np.array([-1000.0]))[0] == 0.0 and O.silu(np.array([1000.0]))[0] == 1000.0
+
+
+def test_head_special_case():
+    # W_h1 picks features 0..3 of x, W_h2 sums the first two / the last two, biases shift:
+    # logits = (silu(x0)+silu(x1)+b0, silu(x2)+silu(x3)+b1), computed with torch's silu
+    rng = np.random.default_rng(70)
+    x = rng.standard_normal((5, 8)) * 3
+    w1 = np.zeros((4, 8)); w1[np.arange(4), np.arange(4)] = 1.0
+    w2 = np.array([[1.0, 1.0, 0.0, 0.0], [0.0, 0.0, 1.0, 1.0]])
+    head = {"w_head1": w1, "b_head1": np.zeros(4), "w_head2": w2, "b_head2": np.array([0.5, -0.25])}
+    s = torch.nn.functional.silu(torch.from_numpy(x[:, :4])).numpy()
+    expect = np.stack([s[:, 0] + s[:, 1] + 0.5, s[:, 2] + s[:, 3] - 0.25], axis=1)
+    np.testing.assert_allclose(O.head_forward(x, head), expect, rtol=1e-14, atol=1e-14)
