@@ -131,6 +131,8 @@ mtgr_status check_block(const mtgr_block_params* p) {
   if (p->d_model % mult != 0 || p->mlp_hidden <= 0 || p->mlp_hidden % mult != 0 ||
       p->mlp_hidden > 8192)
     return MTGR_ERR_BAD_SHAPE;
+  if (p->dtype == MTGR_BF16 && (p->d_model < 128 || p->mlp_hidden < 128))
+    return MTGR_ERR_BAD_SHAPE;   // the bf16 GEMM pipeline needs at least two 64-wide K slabs
   if (!(p->ln_eps >= 0.f) || !std::isfinite(p->ln_eps)) return MTGR_ERR_BAD_SHAPE;
   if (!p->gln1_gamma || !p->gln1_beta || !p->w_qkvu || !p->gln2_gamma || !p->gln2_beta ||
       !p->w_mlp1 || !p->w_mlp2)
@@ -370,7 +372,7 @@ mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int3
   if (dtype != MTGR_F32 && dtype != MTGR_BF16) return MTGR_ERR_UNSUPPORTED;
   if (epilogue < MTGR_EPI_STORE || epilogue > MTGR_EPI_RESIDUAL_F32) return MTGR_ERR_UNSUPPORTED;
   if (M < 0 || N <= 0 || K <= 0 || N > (1 << 20)) return MTGR_ERR_BAD_SHAPE;
-  if (dtype == MTGR_BF16 && (K % 64 != 0 || N % 4 != 0)) return MTGR_ERR_BAD_SHAPE;
+  if (dtype == MTGR_BF16 && (K % 64 != 0 || K < 128 || N % 4 != 0)) return MTGR_ERR_BAD_SHAPE;
   if (dtype == MTGR_F32 && K % 4 != 0) return MTGR_ERR_BAD_SHAPE;
   if (M == 0) return MTGR_OK;
   if (!a || !w || !out) return MTGR_ERR_NULL_ARG;

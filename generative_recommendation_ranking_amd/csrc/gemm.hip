@@ -77,9 +77,9 @@ __device__ __forceinline__ void store4(TOut* out, const float* resid, int64_t id
 template <int WM, int WN, int EPI, typename TOut>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     int64_t M, int N, int K, const bf16* __restrict__ A, const bf16* __restrict__ W,
-    const bf16* __restrict__ bias, const float* resid, TOut* out, int nN, int64_t nM) {
+    const bf16* __restrict__ bias, const float* resid, TOut* out, int nN, int64_t nM, int nb) {
   constexpr int BM = 256, BN = 256, BK = 64, NT = 64 * WM * WN;
-  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32, KS = BK / 16;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int LP = BK + 8, CPR = BK / 8;
   constexpr int CA = BM * CPR / NT, CB = BN * CPR / NT;   // 8 and 8 chunks per thread
   constexpr int RSTEP = NT / CPR;                          // rows covered by one chunk index
@@ -93,12 +93,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   const int wm = wave / WN, wn = wave % WN;
   const int l32 = lane & 31, hh = lane >> 5;
 
-  // tile sequence of this workgroup: XCD-major slots (see the header comment)
+  // Tile sequence.  Workgroup ids reach the XCDs round-robin; XCD x owns M-tiles x, x+8, ...
+  // and walks N in chunks of nb tiles (outer) and its M-tiles (inner), so while a chunk is being
+  // processed only nb weight slices are live in that XCD's L2 and the activation slabs stream
+  // through once per chunk.  nb is chosen by the host from an estimate of L2-miss traffic.
   const int xcd = (int)(blockIdx.x % kXcd);
   const int gx = (int)(gridDim.x / kXcd);
   const int64_t nMx = (nM + kXcd - 1) / kXcd;
   const int64_t nslots = nMx * nN;
-  auto valid_slot = [&](int64_t s) { return s < nslots && (s / nN) * kXcd + xcd < nM; };
+  const int nchunk_full = nN / nb;                  // chunks of exactly nb tiles; the last may be short
+  auto decode = [&](int64_t s, int64_t& m_tile, int& n_tile) {
+    const int64_t per = nMx * nb;                   // slots per full chunk
+    int64_t c = s / per;
+    int64_t rem = s - c * per;
+    int w = nb;
+    if (c >= nchunk_full) { c = nchunk_full; rem = s - c * per; w = nN - nchunk_full * nb; }
+    m_tile = (rem / w) * kXcd + xcd;
+    n_tile = (int)(c * nb + rem % w);
+  };
+  auto valid_slot = [&](int64_t s) {
+    if (s >= nslots) return false;
+    int64_t m; int n; decode(s, m, n);
+    return m < nM;
+  };
   auto next_slot = [&](int64_t s) {  // next slot of this workgroup holding a real tile
     s += gx;
     while (s < nslots && !valid_slot(s)) s += gx;
@@ -108,38 +125,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   if (!valid_slot(first)) first = next_slot(first);
   if (first >= nslots) return;
 
-  const int nk = K / BK;
+  const int nk = K / BK;                 // >= 2 (checked by the host)
   const uint32_t vo = (uint32_t)((tid / CPR) * K * 2 + (tid % CPR) * 16);  // byte offset in slab
 
-  // load cursor
-  int64_t ld_slot = first;
-  int ld_kt = 0;
-  __amdgpu_buffer_rsrc_t ra_rsrc, rb_rsrc;
-  auto set_load_tile = [&](int64_t slot) {
-    const int64_t m0 = ((slot / nN) * kXcd + xcd) * BM;
-    const int n0 = (int)(slot % nN) * BN;
+  struct TileRsrc {
+    __amdgpu_buffer_rsrc_t a, w;
+  };
+  auto make_rsrc = [&](int64_t s) {
+    int64_t mt; int ntile; decode(s, mt, ntile);
+    const int64_t m0 = mt * BM;
+    const int n0 = ntile * BN;
     const int64_t mrows = min((int64_t)BM, M - m0);
     const int nrows = min(BN, N - n0);
-    ra_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * K), (short)0, (int)(mrows * K * 2), 0x00020000);
-    rb_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * K), (short)0, nrows * K * 2, 0x00020000);
+    TileRsrc r;
+    r.a = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * K), (short)0, (int)(mrows * K * 2), 0x00020000);
+    r.w = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * K), (short)0, nrows * K * 2, 0x00020000);
+    return r;
   };
-  set_load_tile(ld_slot);
   bf16x8 ra[CA], rb[CB];
-  bool ld_valid = true;
-  auto issue_loads = [&]() {  // loads the slab under the load cursor, then advances it
-    const int kb = ld_kt * BK * 2;
+  auto issue_loads = [&](const TileRsrc& r, int kt) {
+    const int kb = kt * BK * 2;
 #pragma unroll
     for (int i = 0; i < CA; ++i)
-      ra[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, vo, i * RSTEP * K * 2 + kb, 0));
+      ra[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.a, vo, i * RSTEP * K * 2 + kb, 0));
 #pragma unroll
     for (int i = 0; i < CB; ++i)
-      rb[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, vo, i * RSTEP * K * 2 + kb, 0));
-    if (++ld_kt == nk) {
-      ld_kt = 0;
-      ld_slot = next_slot(ld_slot);
-      ld_valid = ld_slot < nslots;
-      if (ld_valid) set_load_tile(ld_slot);
-    }
+      rb[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.w, vo, i * RSTEP * K * 2 + kb, 0));
   };
   auto store_slab = [&](int buf) {
 #pragma unroll
@@ -149,36 +160,45 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     for (int i = 0; i < CB; ++i)
       *reinterpret_cast<bf16x8*>(&Bs[buf][tid / CPR + i * RSTEP][(tid % CPR) * 8]) = rb[i];
   };
+  // Software pipeline over the K slabs of this workgroup's tiles, one after another: slab g is
+  // in LDS buffer g%2; the fragments of k-step ks+1 are read before the MFMAs of k-step ks; the
+  // slab after next is written to LDS after k-step 1 and the one after it fetched after k-step 2
+  // (from the next tile once this tile's slabs run out); the end-of-slab barrier waits for LDS
+  // traffic only, so global loads stay in flight.  The loads run at most two slabs ahead, so
+  // with at least two slabs per tile they only ever touch this tile or the next one.
+  constexpr int KS = BK / 16;
   bf16x8 fa[2][FM], fb[2][FN];
-  auto read_frags = [&](int buf, int ks, int slot) {
+  auto read_frags = [&](int buf, int ks, int fslot) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
-      fa[slot][i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * TM + i * 32 + l32][ks * 16 + hh * 8]);
+      fa[fslot][i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * TM + i * 32 + l32][ks * 16 + hh * 8]);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-      fb[slot][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * TN + j * 32 + l32][ks * 16 + hh * 8]);
+      fb[fslot][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * TN + j * 32 + l32][ks * 16 + hh * 8]);
   };
   auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
+  int64_t slot = first;
+  int64_t next = next_slot(slot);
+  TileRsrc r_cur = make_rsrc(slot);
+  TileRsrc r_nxt = (next < nslots) ? make_rsrc(next) : r_cur;
+
   // prologue: slab 0 into LDS buffer 0, slab 1 into registers
-  issue_loads();
+  issue_loads(r_cur, 0);
   store_slab(0);
-  bool have_next = ld_valid;   // registers hold a slab still to be written to LDS
-  if (have_next) issue_loads();
+  issue_loads(r_cur, 1);
+  bool have_next = true;   // registers hold a slab still to be written to LDS
   lds_barrier();
   read_frags(0, 0, 0);
 
-  int64_t slot = first;
   int cur = 0;
   while (true) {
     f32x16 acc[FM][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-    const int64_t next = next_slot(slot);
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+    const bool more_tiles = next < nslots;
     for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -191,11 +211,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fs][j], fa[fs][i], acc[i][j], 0, 0, 0);
         if (ks == 1 && have_next) store_slab(cur ^ 1);
         if (ks == 2) {
-          have_next = have_next && ld_valid;
-          if (have_next) issue_loads();
+          // slab kt+2 of this tile, else slab kt+2-nk of the next tile
+          const bool here = kt + 2 < nk;
+          have_next = here || more_tiles;
+          if (have_next) issue_loads(here ? r_cur : r_nxt, here ? kt + 2 : kt + 2 - nk);
         }
       }
-      if (kt + 1 < nk || next < nslots) {
+      if (kt + 1 < nk || more_tiles) {
         lds_barrier();
         cur ^= 1;
         read_frags(cur, 0, 0);
@@ -203,8 +225,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     }
     // epilogue of this tile: row m = l32 of the MFMA tile, columns 8g + 4hh + 0..3 (N is a
     // multiple of 4, so a group is either wholly inside or wholly past the last column)
-    const int64_t m0 = ((slot / nN) * kXcd + xcd) * BM;
-    const int n0 = (int)(slot % nN) * BN;
+    int64_t mt_e; int nt_e; decode(slot, mt_e, nt_e);
+    const int64_t m0 = mt_e * BM;
+    const int n0 = nt_e * BN;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int64_t m = m0 + wm * TM + i * 32 + l32;
@@ -227,8 +250,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
         }
       }
     }
-    if (next >= nslots) break;
+    if (!more_tiles) break;
     slot = next;
+    next = next_slot(slot);
+    r_cur = r_nxt;
+    if (next < nslots) r_nxt = make_rsrc(next);
   }
 }
 
@@ -303,7 +329,21 @@ hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf1
   const int64_t nM = (M + 255) / 256;
   const int64_t tiles_pad = (nM + kXcd - 1) / kXcd * kXcd * nN;
   const int64_t grid = std::min<int64_t>(tiles_pad, (int64_t)cus / kXcd * kXcd);
-  kern<<<(unsigned)grid, 64 * WM * WN, lds, s>>>(M, N, K, a, w, bias, resid, static_cast<TOut*>(out), nN, nM);
+  // N-chunk width: estimated bytes missing a 4 MB XCD L2, activations re-read once per chunk
+  // versus weights re-read once per round of concurrently running M-tiles when they do not fit.
+  const double a_bytes = (double)M * K * 2, slice = 256.0 * K * 2, l2 = 4.0 * 1024 * 1024;
+  const double wg_per_xcd = (double)grid / kXcd;
+  int nb = nN;
+  double best = 1e300;
+  for (int c = 1; c <= nN; ++c) {
+    const double chunks = (double)((nN + c - 1) / c);
+    const bool fits = c * slice <= 0.6 * l2;
+    const double rounds = (double)((nM + kXcd - 1) / kXcd) * c / std::max(1.0, wg_per_xcd);
+    const double w_traffic = fits ? kXcd * nN * slice : kXcd * rounds * c * slice * chunks;
+    const double t = a_bytes * chunks + w_traffic;
+    if (t < best * 0.98) { best = t; nb = c; }
+  }
+  kern<<<(unsigned)grid, 64 * WM * WN, lds, s>>>(M, N, K, a, w, bias, resid, static_cast<TOut*>(out), nN, nM, nb);
   return hipGetLastError();
 }
 

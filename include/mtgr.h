@@ -38,7 +38,8 @@
  *   - Storage dtype MTGR_BF16 means bf16 weights and bf16 intermediate activations with fp32
  *     accumulation; the residual stream x is always fp32.  MTGR_F32 keeps everything fp32.
  *   - Supported shapes: d % H == 0; d_h = d/H in {32, 64, 128} (bf16: {64, 128});
- *     d, h multiples of 64 (bf16) or 8 (fp32); d <= 1024; h <= 8192; head hidden multiple of 8.
+ *     d, h multiples of 64 and >= 128 (bf16) or multiples of 8 (fp32); d <= 1024; h <= 8192;
+ *     head hidden a multiple of 32 (bf16) or 8 (fp32).
  */
 #ifndef MTGR_H
 #define MTGR_H
@@ -148,7 +149,8 @@ mtgr_status mtgr_groupln_fwd(const mtgr_batch* b, int32_t d, int32_t in_dtype, i
                              int32_t param_dtype, const void* gamma, const void* beta, float eps,
                              const void* x, void* y, void* stream);
 
-/* out = epilogue(a[M][K] W[N][K]^T + bias[N]); a, W, bias in `dtype`; see MTGR_EPI_*. */
+/* out = epilogue(a[M][K] W[N][K]^T + bias[N]); a, W, bias in `dtype`; see MTGR_EPI_*.
+ * bf16: K a multiple of 64 and >= 128, N a multiple of 4.  fp32: K a multiple of 4. */
 mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int32_t epilogue,
                             const void* a, const void* w, const void* bias, const float* resid,
                             void* out, void* stream);

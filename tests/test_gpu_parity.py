@@ -141,8 +141,9 @@ def test_groupln_parity(kin, kout, d):
     assert rel_err(to_np(y), ref) < tol
 
 
-@pytest.mark.parametrize("M_,N,K,epi", [(1000, 256, 64, 0), (3001, 96, 256, 1), (777, 768, 3072, 2),
-                                        (130, 3072, 768, 0), (1, 64, 128, 1), (4097, 128, 512, 2)])
+@pytest.mark.parametrize("M_,N,K,epi", [(1000, 256, 128, 0), (3001, 96, 256, 1), (777, 768, 3072, 2),
+                                        (130, 3072, 768, 0), (1, 64, 128, 1), (4097, 128, 512, 2),
+                                        (70000, 1540, 192, 1)])
 def test_linear_bf16_parity(M_, N, K, epi):
     rng = np.random.default_rng(M_ + N + K)
     a = synth.round_to_bf16(rng.standard_normal((M_, K)).astype(np.float32))
