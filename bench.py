@@ -31,6 +31,33 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "encoder tokens/sec (fwd, bf16) and MFMA-util % on one MI355X"
+ATTN_SRC = os.path.join(ROOT, "generative_recommendation_ranking_amd", "csrc", "attention.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_large-bf16_traffic.md")
+COPY_BYTES = 1 << 30        # size of the plain copy used to calibrate the traffic counters
+
+
+def attention_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in (ATTN_SRC, os.path.join(os.path.dirname(ATTN_SRC), "common.h")):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE runs,
+    or None when the attention source changed after they were taken."""
+    try:
+        fields = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+        if fields.get("attention source sha256/16") != attention_source_hash():
+            return None
+        return float(fields["calibrated bytes per launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def visible_pairs_per_user(b) -> np.ndarray:
@@ -93,6 +120,8 @@ def main():
     ap.add_argument("--workload", default="large-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--replay-steps", type=int, default=5)
+    ap.add_argument("--profile-kernel", choices=["attention", "copy"], default=None,
+                    help="run only this kernel --steps times (for rocprofv3 counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); users are independent, "
@@ -105,6 +134,16 @@ def main():
     from generative_recommendation_ranking_amd import synth
 
     torch.cuda.set_device(0)
+    if args.profile_kernel == "copy":
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_kernel": "copy", "bytes_read": COPY_BYTES,
+                          "bytes_written": COPY_BYTES, "launches": args.steps}), flush=True)
+        return
     b, p = synth.make_workload(args.workload)
     db, dm = M.DeviceBatch(b), M.DeviceModel(p)
     ws = M.workspace(M.mtgr_encoder_workspace_size(dm, db))
@@ -116,6 +155,24 @@ def main():
 
     def step():
         M.mtgr_encoder_fwd(dm, db, db.x, hidden, logits, ws)
+
+    if args.profile_kernel == "attention":
+        # layer 0's QKVU from one real block pass, then the attention launch alone
+        d_, H_ = p.d, p.H
+        lay0 = dm.layers[0]
+        xt0 = torch.empty(b.num_tokens, d_, dtype=torch.bfloat16, device="cuda")
+        q0 = torch.empty(b.num_tokens, 4 * d_, dtype=torch.bfloat16, device="cuda")
+        y0 = torch.empty(b.num_tokens, d_, dtype=torch.bfloat16, device="cuda")
+        M.mtgr_groupln_fwd(db, d_, 0, 1, 1, lay0["gln1_gamma"], lay0["gln1_beta"], p.ln_eps, db.x, xt0)
+        M.mtgr_linear_fwd(b.num_tokens, 4 * d_, d_, M.MTGR_BF16, M.MTGR_EPI_STORE, xt0,
+                          lay0["w_qkvu"], lay0["b_qkvu"], None, q0)
+        aws0 = M.workspace(M.mtgr_attention_workspace_size(db, d_, H_))
+        for _ in range(args.steps):
+            M.mtgr_attention_fwd(db, d_, H_, M.MTGR_BF16, q0, y0, aws0)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_kernel": "attention", "launches": args.steps,
+                          "attention_source_sha256_16": attention_source_hash()}), flush=True)
+        return
 
     for _ in range(args.warmup):
         step()
@@ -192,7 +249,7 @@ def main():
                    "heads": H, "mlp_hidden": h, "visible_pairs_per_layer": fl["pairs"]},
         "roofline": {"bound": "mfma", "kernel": "attention (fused masked silu + U gate)",
                      "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
                      "flops_per_launch": fl["attention"], "launch_ms": round(ms["attention"], 4)},
         "mfma_util": {"gemm_plus_attention": round(util_all, 4),
                       "gemm": round(gemm_fl / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),

@@ -25,8 +25,8 @@
 // operand of O = P V; V is stored transposed in LDS (feature-major, keys permuted so the 8 keys
 // a lane needs are contiguous), and the B fragment is one 16-byte LDS read.
 //
-// LDS per workgroup: K 2 x 64 x (d_h+8) and V^T 2 x d_h x 72 bf16 (double-buffered,
-// register-staged global->LDS copies), ~71 KB at d_h = 128, two workgroups per CU.
+// LDS per workgroup: K 2 x 64 x (d_h+8) and V 2 x 64 x (d_h+32) bf16 (double-buffered,
+// register-staged global->LDS copies), ~75 KB at d_h = 128, two workgroups per CU.
 #include "kernels.h"
 
 namespace mtgr {
@@ -53,7 +53,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     const int32_t* __restrict__ order, const int32_t* __restrict__ xcd_off,
     const float* __restrict__ ts, const bf16* __restrict__ qkvu, bf16* __restrict__ y) {
   constexpr int KP = DH + 8;                     // K row pitch: 16-byte reads of 16 rows hit distinct banks
-  constexpr int VP = DH + 16;                    // V row pitch: the 4 rows of a transposing read too
+  // V row pitch: a transposing read by 32 lanes touches 4 rows x 2 column chunks of 32 bytes;
+  // a pitch of 16 (mod 64) dwords puts those 8 chunks on disjoint banks.
+  constexpr int VP = DH + 32;
   constexpr int DCH = DH / 8;                    // 16-byte chunks per key row
   constexpr int CH = BKV * DCH / 256;            // K (and V) chunks per thread per tile
   constexpr int NT = DH / 32;                    // output tiles of 32 features
