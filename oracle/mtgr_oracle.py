@@ -55,12 +55,27 @@ G_U, G_S, G_R, G_C = 0, 1, 2, 3
 # ----------------------------------------------------------------------------------------------
 # Mask  [P3 方法, mask paragraph; P5 7.3.4 Rules 1-3]
 # ----------------------------------------------------------------------------------------------
-def mask(groups: np.ndarray, times: np.ndarray) -> np.ndarray:
-    """Dynamic mask of one user's tokens, by enumeration of every (query i, key j) pair.
+MASK_MODES = ("dynamic", "causal", "full")
+
+
+def mask(groups: np.ndarray, times: np.ndarray, mode: str = "dynamic") -> np.ndarray:
+    """Mask of one user's tokens, by enumeration of every (query i, key j) pair.
 
     Returns uint8 [n, n]; rows are queries, columns keys; 1 = key visible to query.
-    Token order is irrelevant: the rules look only at group ids and timestamps.
+    mode "dynamic": the three rules (token order is irrelevant: they look only at group ids and
+    timestamps).  The ablation without the dynamic mask ([P1]/[P2] experiments; [P3] 结果) is read
+    as the plain causal mask over the sequence order, which the pages name as what the three rules
+    replace ([P3] 方法, mask paragraph; [P5] 7.3.4): mode "causal", key j visible iff j <= i.
+    mode "full": every token of the user sees every other.
     """
+    if mode == "causal":
+        n = np.asarray(groups).shape[0]
+        return np.tril(np.ones((n, n), dtype=np.uint8))
+    if mode == "full":
+        n = np.asarray(groups).shape[0]
+        return np.ones((n, n), dtype=np.uint8)
+    if mode != "dynamic":
+        raise ValueError(mode)
     g = np.asarray(groups, dtype=np.int64)
     t = np.asarray(times, dtype=np.float32)
     n = g.shape[0]
@@ -84,11 +99,13 @@ def visible_pairs(groups: np.ndarray, times: np.ndarray) -> int:
 # Group-Layer Normalization  [P5 7.3.3, GLN equation; P3 方法, GLN paragraph]
 # ----------------------------------------------------------------------------------------------
 def group_layer_norm(x: np.ndarray, groups: np.ndarray, gamma: np.ndarray, beta: np.ndarray,
-                     eps: float = 1e-5) -> np.ndarray:
+                     eps: float = 1e-5, shared: bool = False) -> np.ndarray:
     """x [n, d]; groups [n] in 0..3; gamma, beta [4, d].  Per-token mean and biased variance over
-    the d features, then the affine parameters of the token's group."""
+    the d features, then the affine parameters of the token's group.  shared=True is the
+    ablation without GroupLN (one shared LayerNorm, [P3] 方法, GLN paragraph): every token takes
+    the parameters of row 0."""
     x = np.asarray(x, dtype=np.float64)
-    g = np.asarray(groups, dtype=np.int64)
+    g = np.zeros(np.asarray(groups).shape[0], dtype=np.int64) if shared else np.asarray(groups, dtype=np.int64)
     d = x.shape[1]
     mu = x.sum(axis=1, keepdims=True) / d
     xc = x - mu
@@ -122,7 +139,7 @@ def linear(x: np.ndarray, w: np.ndarray, b: Optional[np.ndarray]) -> np.ndarray:
 # Masked SiLU attention with the U gate  [P3 方法, update equations]
 # ----------------------------------------------------------------------------------------------
 def hstu_attention(qkvu: np.ndarray, groups: np.ndarray, times: np.ndarray,
-                   num_heads: int) -> np.ndarray:
+                   num_heads: int, mask_mode: str = "dynamic") -> np.ndarray:
     """One user's attention.  qkvu [n, 4d] = [Q | K | V | U]; returns V~ (.) U  [n, d].
 
     For head h (feature slice h*d_h:(h+1)*d_h of Q, K, V):
@@ -135,7 +152,7 @@ def hstu_attention(qkvu: np.ndarray, groups: np.ndarray, times: np.ndarray,
     if n == 0:
         return np.zeros((0, d))
     Q, K, V, U = qkvu[:, :d], qkvu[:, d:2 * d], qkvu[:, 2 * d:3 * d], qkvu[:, 3 * d:]
-    M = mask(groups, times).astype(np.float64)
+    M = mask(groups, times, mask_mode).astype(np.float64)
     N = float(n)
     vt = np.empty((n, d))
     for h in range(num_heads):
@@ -150,13 +167,14 @@ def hstu_attention(qkvu: np.ndarray, groups: np.ndarray, times: np.ndarray,
 # HSTU block, encoder, head
 # ----------------------------------------------------------------------------------------------
 def block_forward(x: np.ndarray, groups: np.ndarray, times: np.ndarray, layer: Dict[str, np.ndarray],
-                  num_heads: int, eps: float = 1e-5, return_parts: bool = False):
+                  num_heads: int, eps: float = 1e-5, return_parts: bool = False,
+                  mask_mode: str = "dynamic", shared_norm: bool = False):
     """One HSTU block for one user [P3 方法, update equations]."""
     x = np.asarray(x, dtype=np.float64)
-    xt = group_layer_norm(x, groups, layer["gln1_gamma"], layer["gln1_beta"], eps)
+    xt = group_layer_norm(x, groups, layer["gln1_gamma"], layer["gln1_beta"], eps, shared_norm)
     qkvu = linear(xt, layer["w_qkvu"], layer.get("b_qkvu"))
-    y = hstu_attention(qkvu, groups, times, num_heads)
-    z = group_layer_norm(y, groups, layer["gln2_gamma"], layer["gln2_beta"], eps)
+    y = hstu_attention(qkvu, groups, times, num_heads, mask_mode)
+    z = group_layer_norm(y, groups, layer["gln2_gamma"], layer["gln2_beta"], eps, shared_norm)
     hid = silu(linear(z, layer["w_mlp1"], layer.get("b_mlp1")))
     out = linear(hid, layer["w_mlp2"], layer.get("b_mlp2")) + x
     if return_parts:
@@ -172,7 +190,8 @@ def head_forward(x_cand: np.ndarray, head: Dict[str, np.ndarray]) -> np.ndarray:
 
 def encoder_forward(offsets: np.ndarray, groups: np.ndarray, times: np.ndarray, x: np.ndarray,
                     layers: Sequence[Dict[str, np.ndarray]], head: Optional[Dict[str, np.ndarray]],
-                    num_heads: int, eps: float = 1e-5) -> Tuple[np.ndarray, np.ndarray]:
+                    num_heads: int, eps: float = 1e-5, mask_mode: str = "dynamic",
+                    shared_norm: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """L blocks over every user of a packed batch, then the head at candidate tokens.
 
     Users are processed one at a time (no cross-user attention, [P1/P2] sequence packing).
@@ -185,7 +204,8 @@ def encoder_forward(offsets: np.ndarray, groups: np.ndarray, times: np.ndarray, 
         lo, hi = int(offsets[b]), int(offsets[b + 1])
         xb = x[lo:hi]
         for layer in layers:
-            xb = block_forward(xb, groups[lo:hi], times[lo:hi], layer, num_heads, eps)
+            xb = block_forward(xb, groups[lo:hi], times[lo:hi], layer, num_heads, eps,
+                               mask_mode=mask_mode, shared_norm=shared_norm)
         hidden[lo:hi] = xb
     cand = np.asarray(groups) == G_C
     logits = head_forward(hidden[cand], head) if head is not None else np.zeros((int(cand.sum()), 2))

@@ -384,3 +384,40 @@ def test_head_special_case():
     s = torch.nn.functional.silu(torch.from_numpy(x[:, :4])).numpy()
     expect = np.stack([s[:, 0] + s[:, 1] + 0.5, s[:, 2] + s[:, 3] - 0.25], axis=1)
     np.testing.assert_allclose(O.head_forward(x, head), expect, rtol=1e-14, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------------------
+# Ablation variants: shared LayerNorm, causal and full masks
+# ------------------------------------------------------------------------------------------
+def test_ablation_masks_are_library_patterns():
+    g = np.array([0, 1, 1, 2, 2, 3, 3], np.uint8)
+    t = np.array([-np.inf, -np.inf, -np.inf, 1, 2, 0, 5], np.float32)
+    np.testing.assert_array_equal(O.mask(g, t, "causal"), torch.tril(torch.ones(7, 7, dtype=torch.uint8)).numpy())
+    np.testing.assert_array_equal(O.mask(g, t, "full"), np.ones((7, 7), np.uint8))
+    # the causal ablation is exactly the leak the dynamic rules remove: a later candidate sees an
+    # earlier one and an R event that happened after it ([P5] 7.3.4)
+    assert O.mask(g, t, "causal")[6, 5] == 1 and O.mask(g, t)[6, 5] == 0
+    assert O.mask(g, t, "causal")[5, 3] == 1 and O.mask(g, t)[5, 3] == 0
+
+
+def test_shared_layer_norm_is_torch_layer_norm():
+    rng = np.random.default_rng(80)
+    x = rng.standard_normal((30, 16)) * 2 + 0.5
+    g = rng.integers(0, 4, 30).astype(np.uint8)
+    gamma, beta = rng.uniform(0.5, 1.5, (4, 16)), rng.uniform(-0.1, 0.1, (4, 16))
+    ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (16,), torch.from_numpy(gamma[0]),
+                                         torch.from_numpy(beta[0]), 1e-5).numpy()
+    np.testing.assert_allclose(O.group_layer_norm(x, g, gamma, beta, 1e-5, shared=True), ref, atol=1e-12)
+
+
+def test_full_mask_attention_is_dense_and_causal_is_tril():
+    rng = np.random.default_rng(81)
+    n, d = 23, 16
+    qkvu = rng.standard_normal((n, 4 * d)) * 0.7
+    g = np.array([0] * 3 + [1] * 8 + [2] * 6 + [3] * 6, np.uint8)
+    t = np.concatenate([np.full(11, -np.inf), rng.uniform(0, 9, 12)]).astype(np.float32)
+    q, k, v, u = qkvu[:, :d], qkvu[:, d:2 * d], qkvu[:, 2 * d:3 * d], qkvu[:, 3 * d:]
+    full = _torch_silu_attention(q, k, v, u, np.ones((n, n)), n)
+    causal = _torch_silu_attention(q, k, v, u, np.tril(np.ones((n, n))), n)
+    np.testing.assert_allclose(O.hstu_attention(qkvu, g, t, 1, "full"), full, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(O.hstu_attention(qkvu, g, t, 1, "causal"), causal, rtol=1e-12, atol=1e-14)
