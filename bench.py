@@ -2,6 +2,10 @@
 """Benchmark: MTGR HSTU encoder forward (bf16, fp32 accumulation) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large-bf16] [--no-cpu-baseline]
+                    [--mask dynamic|causal|full] [--norm group|shared]
+
+--mask / --norm select the ablation variants (plain causal or full mask in place of the dynamic
+mask, one shared LayerNorm in place of GroupLN); the defaults are the method itself.
 
 One step = one mtgr_encoder_fwd over the whole synthetic batch (all L blocks + the candidate
 head), inputs and weights resident in HBM, workspace preallocated.  Prints ONE JSON line.
@@ -60,10 +64,16 @@ def recorded_traffic():
         return None
 
 
-def visible_pairs_per_user(b) -> np.ndarray:
-    """Exact count of (query, key) pairs the dynamic mask lets through, per user: every query
+def visible_pairs_per_user(b, mask="dynamic") -> np.ndarray:
+    """Exact count of (query, key) pairs the mask lets through, per user.  Dynamic: every query
     sees the n_U+n_S static keys; R and C queries also see the strictly earlier R keys; every
-    token sees itself (static rows already count themselves among the static keys)."""
+    token sees itself (static rows already count themselves among the static keys).  Causal:
+    n(n+1)/2.  Full: n^2."""
+    n_all = np.diff(np.asarray(b.offsets, dtype=np.int64))
+    if mask == "causal":
+        return n_all * (n_all + 1) // 2
+    if mask == "full":
+        return n_all * n_all
     out = np.zeros(b.num_users, dtype=np.int64)
     for u in range(b.num_users):
         lo = int(b.offsets[u])
@@ -77,14 +87,14 @@ def visible_pairs_per_user(b) -> np.ndarray:
     return out
 
 
-def flops_per_layer(b, d, h):
+def flops_per_layer(b, d, h, mask="dynamic"):
     T = b.num_tokens
-    pairs = int(visible_pairs_per_user(b).sum())
+    pairs = int(visible_pairs_per_user(b, mask).sum())
     return {"qkvu": 2.0 * T * d * 4 * d, "mlp1": 2.0 * T * d * h, "mlp2": 2.0 * T * h * d,
             "attention": 4.0 * d * pairs, "pairs": pairs}
 
 
-def cpu_baseline(b, p, budget_s=12.0, max_s=30.0):
+def cpu_baseline(b, p, mask="dynamic", norm="group", budget_s=12.0, max_s=30.0):
     """The oracle (fp64 numpy, as it stands) on whole users of the same batch, in index order,
     until at least `budget_s` seconds of work; tokens of the sample per second."""
     from generative_recommendation_ranking_amd import synth
@@ -93,7 +103,8 @@ def cpu_baseline(b, p, budget_s=12.0, max_s=30.0):
     done, users, t0 = 0, [], time.perf_counter()
     for u in range(b.num_users):
         s = synth.subset(b, [u])
-        O.encoder_forward(s.offsets, s.group_ids, s.timestamps, s.x, layers, head, p.H, p.ln_eps)
+        O.encoder_forward(s.offsets, s.group_ids, s.timestamps, s.x, layers, head, p.H, p.ln_eps,
+                          mask_mode=mask, shared_norm=(norm == "shared"))
         done += s.num_tokens
         users.append(u)
         el = time.perf_counter() - t0
@@ -119,6 +130,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="large-bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mask", choices=["dynamic", "causal", "full"], default="dynamic")
+    ap.add_argument("--norm", choices=["group", "shared"], default="group")
     ap.add_argument("--replay-steps", type=int, default=5)
     ap.add_argument("--profile-kernel", choices=["attention", "copy"], default=None,
                     help="run only this kernel --steps times (for rocprofv3 counter runs)")
@@ -145,7 +158,8 @@ def main():
                           "bytes_written": COPY_BYTES, "launches": args.steps}), flush=True)
         return
     b, p = synth.make_workload(args.workload)
-    db, dm = M.DeviceBatch(b), M.DeviceModel(p)
+    db, dm = M.DeviceBatch(b), M.DeviceModel(p, mask_mode=args.mask, norm_mode=args.norm)
+    mask_c, norm_c = M.MASK_MODES[args.mask], M.NORM_MODES[args.norm]
     ws = M.workspace(M.mtgr_encoder_workspace_size(dm, db))
     hidden = torch.empty_like(db.x)
     logits = torch.empty(db.num_candidates, 2, dtype=torch.float32, device="cuda")
@@ -163,12 +177,12 @@ def main():
         xt0 = torch.empty(b.num_tokens, d_, dtype=torch.bfloat16, device="cuda")
         q0 = torch.empty(b.num_tokens, 4 * d_, dtype=torch.bfloat16, device="cuda")
         y0 = torch.empty(b.num_tokens, d_, dtype=torch.bfloat16, device="cuda")
-        M.mtgr_groupln_fwd(db, d_, 0, 1, 1, lay0["gln1_gamma"], lay0["gln1_beta"], p.ln_eps, db.x, xt0)
+        M.mtgr_groupln_fwd(db, d_, 0, 1, 1, norm_c, lay0["gln1_gamma"], lay0["gln1_beta"], p.ln_eps, db.x, xt0)
         M.mtgr_linear_fwd(b.num_tokens, 4 * d_, d_, M.MTGR_BF16, M.MTGR_EPI_STORE, xt0,
                           lay0["w_qkvu"], lay0["b_qkvu"], None, q0)
         aws0 = M.workspace(M.mtgr_attention_workspace_size(db, d_, H_))
         for _ in range(args.steps):
-            M.mtgr_attention_fwd(db, d_, H_, M.MTGR_BF16, q0, y0, aws0)
+            M.mtgr_attention_fwd(db, d_, H_, M.MTGR_BF16, mask_c, q0, y0, aws0)
         torch.cuda.synchronize()
         print(json.dumps({"profile_kernel": "attention", "launches": args.steps,
                           "attention_source_sha256_16": attention_source_hash()}), flush=True)
@@ -199,10 +213,10 @@ def main():
     xo = torch.empty_like(db.x)
     aws = M.workspace(M.mtgr_attention_workspace_size(db, d, H))
     seq = [
-        ("gln1", lambda: M.mtgr_groupln_fwd(db, d, 0, 1, 1, lay["gln1_gamma"], lay["gln1_beta"], p.ln_eps, db.x, xt)),
+        ("gln1", lambda: M.mtgr_groupln_fwd(db, d, 0, 1, 1, norm_c, lay["gln1_gamma"], lay["gln1_beta"], p.ln_eps, db.x, xt)),
         ("qkvu", lambda: M.mtgr_linear_fwd(T, 4 * d, d, M.MTGR_BF16, M.MTGR_EPI_STORE, xt, lay["w_qkvu"], lay["b_qkvu"], None, big)),
-        ("attention", lambda: M.mtgr_attention_fwd(db, d, H, M.MTGR_BF16, big, yb, aws)),
-        ("gln2", lambda: M.mtgr_groupln_fwd(db, d, 1, 1, 1, lay["gln2_gamma"], lay["gln2_beta"], p.ln_eps, yb, xt)),
+        ("attention", lambda: M.mtgr_attention_fwd(db, d, H, M.MTGR_BF16, mask_c, big, yb, aws)),
+        ("gln2", lambda: M.mtgr_groupln_fwd(db, d, 1, 1, 1, norm_c, lay["gln2_gamma"], lay["gln2_beta"], p.ln_eps, yb, xt)),
         ("mlp1", lambda: M.mtgr_linear_fwd(T, h, d, M.MTGR_BF16, M.MTGR_EPI_SILU, xt, lay["w_mlp1"], lay["b_mlp1"], None, big)),
         ("mlp2", lambda: M.mtgr_linear_fwd(T, d, h, M.MTGR_BF16, M.MTGR_EPI_RESIDUAL_F32, big, lay["w_mlp2"], lay["b_mlp2"], db.x, xo)),
     ]
@@ -219,7 +233,7 @@ def main():
             e1.synchronize()
             times[k] += e0.elapsed_time(e1)
     ms = {k: v / args.replay_steps for k, v in times.items()}
-    fl = flops_per_layer(b, d, h)
+    fl = flops_per_layer(b, d, h, args.mask)
     gemm_ms = ms["qkvu"] + ms["mlp1"] + ms["mlp2"]
     gemm_fl = fl["qkvu"] + fl["mlp1"] + fl["mlp2"]
     att_tflops = fl["attention"] / (ms["attention"] * 1e-3) / 1e12
@@ -246,10 +260,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "users": b.num_users, "tokens": T,
                    "candidates": db.num_candidates, "layers": p.num_layers, "d_model": d,
-                   "heads": H, "mlp_hidden": h, "visible_pairs_per_layer": fl["pairs"]},
+                   "heads": H, "mlp_hidden": h, "mask": args.mask, "norm": args.norm,
+                   "visible_pairs_per_layer": fl["pairs"]},
         "roofline": {"bound": "mfma", "kernel": "attention (fused masked silu + U gate)",
                      "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic(),
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": recorded_traffic() if args.mask == "dynamic" else None,
                      "flops_per_launch": fl["attention"], "launch_ms": round(ms["attention"], 4)},
         "mfma_util": {"gemm_plus_attention": round(util_all, 4),
                       "gemm": round(gemm_fl / (gemm_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
@@ -258,7 +273,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample of users", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(b, p)
+        out["cpu_baseline"] = cpu_baseline(b, p, args.mask, args.norm)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

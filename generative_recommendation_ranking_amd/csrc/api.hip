@@ -123,10 +123,14 @@ mtgr_status check_attn_shape(int32_t d, int32_t H, int32_t dtype) {
   return MTGR_OK;
 }
 
+inline bool mask_mode_ok(int32_t m) { return m >= MTGR_MASK_DYNAMIC && m <= MTGR_MASK_FULL; }
+inline bool norm_mode_ok(int32_t m) { return m == MTGR_NORM_GROUP || m == MTGR_NORM_SHARED; }
+
 mtgr_status check_block(const mtgr_block_params* p) {
   if (!p) return MTGR_ERR_NULL_ARG;
   mtgr_status st = check_attn_shape(p->d_model, p->num_heads, p->dtype);
   if (st != MTGR_OK) return st;
+  if (!mask_mode_ok(p->mask_mode) || !norm_mode_ok(p->norm_mode)) return MTGR_ERR_UNSUPPORTED;
   const int mult = p->dtype == MTGR_BF16 ? 64 : 8;
   if (p->d_model % mult != 0 || p->mlp_hidden <= 0 || p->mlp_hidden % mult != 0 ||
       p->mlp_hidden > 8192)
@@ -202,14 +206,14 @@ hipError_t linear(int64_t M, int N, int K, int dtype, int epi, const void* a, co
                          static_cast<const float*>(bias), resid, static_cast<float*>(out), s);
 }
 
-hipError_t attention(const mtgr_batch* b, int d, int H, int dtype, const PrepBufs& pb,
-                     const void* qkvu, void* y, hipStream_t s) {
+hipError_t attention(const mtgr_batch* b, int d, int H, int dtype, int mask_mode,
+                     const PrepBufs& pb, const void* qkvu, void* y, hipStream_t s) {
   if (dtype == MTGR_BF16)
     return launch_attention_bf16(b->num_users, xcd_grid_slots(b, H, kAttnQTileBf16), d, H,
-                                 b->offsets, pb.seg, pb.order, pb.xcd_off, b->timestamps,
+                                 mask_mode, b->offsets, pb.seg, pb.order, pb.xcd_off, b->timestamps,
                                  static_cast<const bf16*>(qkvu), static_cast<bf16*>(y), s);
   const int64_t tiles = total_tiles(b, kAttnQTileF32);
-  return launch_attention_f32(b->num_users, tiles, d, H, b->offsets, pb.seg, pb.order,
+  return launch_attention_f32(b->num_users, tiles, d, H, mask_mode, b->offsets, pb.seg, pb.order,
                               pb.tile_off, b->timestamps, static_cast<const float*>(qkvu),
                               static_cast<float*>(y), s);
 }
@@ -224,14 +228,15 @@ hipError_t run_block(const mtgr_block_params* p, const mtgr_batch* b, const Prep
   void* big = at<void>(ws, pl.big);
   void* y = at<void>(ws, pl.y);
   hipError_t e;
-  e = launch_groupln(T, d, 0, act, act, x_in, b->group_ids, p->gln1_gamma, p->gln1_beta,
+  const int shared = p->norm_mode == MTGR_NORM_SHARED;
+  e = launch_groupln(T, d, 0, act, act, shared, x_in, b->group_ids, p->gln1_gamma, p->gln1_beta,
                      p->ln_eps, xt, s);
   if (e != hipSuccess) return e;
   e = linear(T, 4 * d, d, dt, MTGR_EPI_STORE, xt, p->w_qkvu, p->b_qkvu, nullptr, big, s);
   if (e != hipSuccess) return e;
-  e = attention(b, d, p->num_heads, dt, pb, big, y, s);
+  e = attention(b, d, p->num_heads, dt, p->mask_mode, pb, big, y, s);
   if (e != hipSuccess) return e;
-  e = launch_groupln(T, d, act, act, act, y, b->group_ids, p->gln2_gamma, p->gln2_beta,
+  e = launch_groupln(T, d, act, act, act, shared, y, b->group_ids, p->gln2_gamma, p->gln2_beta,
                      p->ln_eps, xt, s);
   if (e != hipSuccess) return e;
   e = linear(T, h, d, dt, MTGR_EPI_SILU, xt, p->w_mlp1, p->b_mlp1, nullptr, big, s);
@@ -350,18 +355,20 @@ mtgr_status mtgr_block_fwd(const mtgr_block_params* p, const mtgr_batch* b, cons
 }
 
 mtgr_status mtgr_groupln_fwd(const mtgr_batch* b, int32_t d, int32_t in_dtype, int32_t out_dtype,
-                             int32_t param_dtype, const void* gamma, const void* beta, float eps,
-                             const void* x, void* y, void* stream) {
+                             int32_t param_dtype, int32_t norm_mode, const void* gamma,
+                             const void* beta, float eps, const void* x, void* y, void* stream) {
   mtgr_status st = check_batch(b);
   if (st != MTGR_OK) return st;
   if (d <= 0 || d % 8 != 0 || d > 1024) return MTGR_ERR_BAD_SHAPE;
   auto ok_dt = [](int32_t v) { return v == MTGR_F32 || v == MTGR_BF16; };
   if (!ok_dt(in_dtype) || !ok_dt(out_dtype) || !ok_dt(param_dtype)) return MTGR_ERR_UNSUPPORTED;
   if (in_dtype == MTGR_BF16 && out_dtype == MTGR_F32) return MTGR_ERR_UNSUPPORTED;
+  if (!norm_mode_ok(norm_mode)) return MTGR_ERR_UNSUPPORTED;
   if (!(eps >= 0.f) || !std::isfinite(eps)) return MTGR_ERR_BAD_SHAPE;
   if (b->num_tokens == 0) return MTGR_OK;
   if (!gamma || !beta || !x || !y) return MTGR_ERR_NULL_ARG;
-  return hip_status(launch_groupln(b->num_tokens, d, in_dtype, out_dtype, param_dtype, x,
+  return hip_status(launch_groupln(b->num_tokens, d, in_dtype, out_dtype, param_dtype,
+                                   norm_mode == MTGR_NORM_SHARED, x,
                                    b->group_ids, gamma, beta, eps, y,
                                    static_cast<hipStream_t>(stream)));
 }
@@ -382,12 +389,13 @@ mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int3
 }
 
 mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
-                               const void* qkvu, void* y_gated, void* ws, size_t ws_bytes,
-                               void* stream) {
+                               int32_t mask_mode, const void* qkvu, void* y_gated, void* ws,
+                               size_t ws_bytes, void* stream) {
   size_t need = 0;
   mtgr_status st = mtgr_attention_workspace_size(b, d, num_heads, &need);
   if (st != MTGR_OK) return st;
   if ((st = check_attn_shape(d, num_heads, dtype)) != MTGR_OK) return st;
+  if (!mask_mode_ok(mask_mode)) return MTGR_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < need) return MTGR_ERR_WORKSPACE;
   if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;
   if (!qkvu || !y_gated) return MTGR_ERR_NULL_ARG;
@@ -396,7 +404,7 @@ mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads
   const Plan pl = make_plan(z);
   const PrepBufs pb = prep_bufs(ws, pl);
   MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), num_heads, pb, false, s));
-  MTGR_TRY(attention(b, d, num_heads, dtype, pb, qkvu, y_gated, s));
+  MTGR_TRY(attention(b, d, num_heads, dtype, mask_mode, pb, qkvu, y_gated, s));
   return MTGR_OK;
 }
 
@@ -423,10 +431,11 @@ mtgr_status mtgr_validate_batch(const mtgr_batch* b, void* ws, size_t ws_bytes, 
   return MTGR_OK;
 }
 
-mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, uint8_t* mask_dev, void* ws,
-                            size_t ws_bytes, void* stream) {
+mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, int32_t mask_mode,
+                            uint8_t* mask_dev, void* ws, size_t ws_bytes, void* stream) {
   mtgr_status st = check_batch(b);
   if (st != MTGR_OK) return st;
+  if (!mask_mode_ok(mask_mode)) return MTGR_ERR_UNSUPPORTED;
   if (user < 0 || user >= b->num_users) return MTGR_ERR_BAD_SHAPE;
   Sizes z = sizes_for(b, 8, 0, 0, MTGR_F32, 0);
   const Plan pl = make_plan(z);
@@ -437,7 +446,7 @@ mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, uint8_t* mask_dev
   hipStream_t s = static_cast<hipStream_t>(stream);
   const PrepBufs pb = prep_bufs(ws, pl);
   MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, kAttnQTileF32, 0, pb, false, s));
-  MTGR_TRY(launch_debug_mask(user, b->offsets, pb.seg, b->timestamps, n, mask_dev, s));
+  MTGR_TRY(launch_debug_mask(user, mask_mode, b->offsets, pb.seg, b->timestamps, n, mask_dev, s));
   return MTGR_OK;
 }
 

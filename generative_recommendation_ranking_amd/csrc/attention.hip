@@ -47,7 +47,8 @@ __device__ __forceinline__ int find_slot(const int32_t* __restrict__ tile_off, i
   return lo;
 }
 
-template <int DH>
+// MODE: kMaskDynamic (the three rules), kMaskCausal (j <= i) or kMaskFull (all keys of the user).
+template <int DH, int MODE>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     int32_t B, int H, int d, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
     const int32_t* __restrict__ order, const int32_t* __restrict__ xcd_off,
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
 #pragma unroll
   for (int ks = 0; ks < DH / 16; ++ks)
     qf[ks] = q_valid ? *reinterpret_cast<const bf16x8*>(Qp + qi * ld + ks * 16 + hh * 8) : zero8;
-  const bool q_rc = q_valid && qi >= ns;
+  const bool q_rc = MODE == kMaskDynamic && q_valid && qi >= ns;
   const float tq = q_rc ? ts[base + qi] : -INFINITY;
 
   const bool wave_rows = wq0 < n;
@@ -117,7 +118,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   const int wr_lo = max(wq0, ns), wr_hi = min(min(wq0 + 32, rc_end), n);  // wavefront's R rows
 
   const bool blk_rc = (q0 + BQ > ns);
-  const int kend = blk_rc ? rc_end : ns;
+  // keys past kend are invisible to every row of this q-tile
+  const int kend = MODE == kMaskFull ? n : MODE == kMaskCausal ? min(n, q0 + BQ) : blk_rc ? rc_end : ns;
   const int nkt = (kend + BKV - 1) / BKV;
 
   f32x16 o[NT];
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       stg[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, st_off, so, 0));
       stg[CH + i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, st_off, so, 0));
     }
-    if (tid < BKV) rt = (k0 + tid < kend) ? ts[base + k0 + tid] : INFINITY;
+    if (MODE == kMaskDynamic && tid < BKV) rt = (k0 + tid < kend) ? ts[base + k0 + tid] : INFINITY;
   };
   auto stage_store = [&](int buf) {
 #pragma unroll
@@ -155,10 +157,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       *reinterpret_cast<bf16x8*>(&Ks[buf][st_key + i * KSTEP][st_c * 8]) = stg[i];
       *reinterpret_cast<bf16x8*>(&Vs[buf][st_key + i * KSTEP][st_c * 8]) = stg[CH + i];
     }
-    if (tid < BKV) Ts[buf][tid] = rt;
+    if (MODE == kMaskDynamic && tid < BKV) Ts[buf][tid] = rt;
   };
 
   auto tile_needed = [&](int buf, int k0) {
+    if (MODE == kMaskFull) return wave_rows;
+    if (MODE == kMaskCausal) return wave_rows && k0 <= wq0 + 31;
     bool need = wave_rows && (k0 < ns || (wave_rc && k0 < rc_end));
     if (need && k0 >= ns) {
       // pure R tile: skip when no key is earlier than the wavefront's latest R/C row and the
@@ -187,7 +191,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
       }
     }
     // sc[mt][r]: key k0 + mt*32 + 8*(r/4) + 4*hh + r%4, query qi
-    if (k0 + BKV <= ns) {
+    // tiles every key of which is visible to every row of the wavefront skip the mask
+    const bool unmasked = MODE == kMaskFull || (MODE == kMaskCausal ? k0 + BKV <= wq0 + 1 : k0 + BKV <= ns);
+    if (unmasked) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -210,8 +216,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
             const int r = g4 * 4 + c;
             const int dk = mt * 32 + 8 * g4 + c;
             const float p = silu_rcp(sc[mt][r]);
-            const bool vis = (dk < lim_static) | (dk == self) |
-                             (q_rc & (dk < lim_rc) & (t4[c] < tq));
+            const bool vis = MODE == kMaskCausal
+                                 ? dk <= self
+                                 : (dk < lim_static) | (dk == self) | (q_rc & (dk < lim_rc) & (t4[c] < tq));
             pa[mt * 2 + (r >> 3)][r & 7] = (bf16)(vis ? p : 0.f);
           }
         }
@@ -254,8 +261,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
 
   if (!wave_rows) return;
 
-  // Candidate rows: their own term silu(q_i . k_i) v_i (the diagonal of the C block).
-  const bool q_c = q_valid && qi >= rc_end;
+  // Candidate rows under the dynamic mask: their own term silu(q_i . k_i) v_i (the diagonal of
+  // the C block, which the key loop stops short of).
+  const bool q_c = MODE == kMaskDynamic && q_valid && qi >= rc_end;
   float part = 0.f;
   if (q_c) {
 #pragma unroll
@@ -307,13 +315,14 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   }
 }
 
-// fp32 storage mode: the same rule set evaluated directly over every key of the user, one
+// fp32 storage mode: the same rule set (any mask mode) evaluated directly over every key of the user, one
 // thread per query row, for exact comparison with the oracle.
 template <int DH>
 __global__ __launch_bounds__(64) void k_attn_f32(
-    int32_t B, int d, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
-    const int32_t* __restrict__ order, const int32_t* __restrict__ tile_off,
-    const float* __restrict__ ts, const float* __restrict__ qkvu, float* __restrict__ y) {
+    int32_t B, int d, int mode, const int64_t* __restrict__ offsets,
+    const UserSeg* __restrict__ seg, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ tile_off, const float* __restrict__ ts,
+    const float* __restrict__ qkvu, float* __restrict__ y) {
   const int item = blockIdx.x;
   const int h = blockIdx.y;
   const int slot = find_slot(tile_off, B, item);
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(
   for (int f = 0; f < DH; ++f) { q[f] = Qp[i * ld + f]; acc[f] = 0.f; }
   const float ti = ts[base + i];
   for (int j = 0; j < n; ++j) {
-    if (!mtgr_visible(i, j, ns, rc_end, ti, ts[base + j])) continue;
+    if (!mtgr_visible_mode(mode, i, j, ns, rc_end, ti, ts[base + j])) continue;
     float s = 0.f;
 #pragma unroll
     for (int f = 0; f < DH; ++f) s = fmaf(q[f], Kp[j * ld + f], s);
@@ -352,23 +361,39 @@ __global__ __launch_bounds__(64) void k_attn_f32(
 
 }  // namespace
 
-hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H,
-                                 const int64_t* offsets, const UserSeg* seg, const int32_t* order,
-                                 const int32_t* xcd_off, const float* timestamps,
-                                 const bf16* qkvu, bf16* y, hipStream_t s) {
-  if (grid_slots == 0) return hipSuccess;
+template <int MODE>
+hipError_t attn_bf16_mode(unsigned grid, int32_t B, int d, int H, const int64_t* offsets,
+                          const UserSeg* seg, const int32_t* order, const int32_t* xcd_off,
+                          const float* timestamps, const bf16* qkvu, bf16* y, hipStream_t s) {
   const int dh = d / H;
-  const unsigned grid = (unsigned)(grid_slots * kXcdCount);
   if (dh == 128)
-    k_attn_bf16<128><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y);
+    k_attn_bf16<128, MODE><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y);
   else if (dh == 64)
-    k_attn_bf16<64><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y);
+    k_attn_bf16<64, MODE><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H,
+hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H, int mask_mode,
+                                 const int64_t* offsets, const UserSeg* seg, const int32_t* order,
+                                 const int32_t* xcd_off, const float* timestamps,
+                                 const bf16* qkvu, bf16* y, hipStream_t s) {
+  if (grid_slots == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(grid_slots * kXcdCount);
+  switch (mask_mode) {
+    case kMaskDynamic:
+      return attn_bf16_mode<kMaskDynamic>(grid, B, d, H, offsets, seg, order, xcd_off, timestamps, qkvu, y, s);
+    case kMaskCausal:
+      return attn_bf16_mode<kMaskCausal>(grid, B, d, H, offsets, seg, order, xcd_off, timestamps, qkvu, y, s);
+    case kMaskFull:
+      return attn_bf16_mode<kMaskFull>(grid, B, d, H, offsets, seg, order, xcd_off, timestamps, qkvu, y, s);
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H, int mask_mode,
                                 const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                 const int32_t* tile_off, const float* timestamps,
                                 const float* qkvu, float* y, hipStream_t s) {
@@ -376,11 +401,11 @@ hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H,
   const int dh = d / H;
   dim3 grid((unsigned)total_tiles, (unsigned)H);
   if (dh == 32)
-    k_attn_f32<32><<<grid, 64, 0, s>>>(B, d, offsets, seg, order, tile_off, timestamps, qkvu, y);
+    k_attn_f32<32><<<grid, 64, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off, timestamps, qkvu, y);
   else if (dh == 64)
-    k_attn_f32<64><<<grid, 64, 0, s>>>(B, d, offsets, seg, order, tile_off, timestamps, qkvu, y);
+    k_attn_f32<64><<<grid, 64, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off, timestamps, qkvu, y);
   else if (dh == 128)
-    k_attn_f32<128><<<grid, 64, 0, s>>>(B, d, offsets, seg, order, tile_off, timestamps, qkvu, y);
+    k_attn_f32<128><<<grid, 64, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off, timestamps, qkvu, y);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -58,6 +58,18 @@ __device__ __forceinline__ bool mtgr_visible(int i, int j, int n_static, int rc_
   return (j < n_static) | (i == j) | ((i >= n_static) & (j < rc_end) & (tj < ti));
 }
 
+// Mask modes (values of MTGR_MASK_*).  Dynamic is the method's mask; causal (key j visible iff
+// j <= i in sequence order) and full (every key of the user) are the ablation baselines: the
+// causal mask is what the dynamic rules replace (fun-rec 7.3.4; marovi.ai MTGR page, 方法).
+enum { kMaskDynamic = 0, kMaskCausal = 1, kMaskFull = 2 };
+
+__device__ __forceinline__ bool mtgr_visible_mode(int mode, int i, int j, int n_static, int rc_end,
+                                                  float ti, float tj) {
+  if (mode == kMaskCausal) return j <= i;
+  if (mode == kMaskFull) return true;
+  return mtgr_visible(i, j, n_static, rc_end, ti, tj);
+}
+
 // Per-user segment record written by the batch-prep kernel.
 struct UserSeg {
   int32_t n_u, n_s, n_r, k;

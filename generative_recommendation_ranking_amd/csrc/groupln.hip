@@ -4,6 +4,8 @@
 // page, 方法): LayerNorm statistics of one token over its d features, then the affine
 // parameters gamma[g], beta[g] of the token's group g in {U, S, R, C}:
 //     y_f = (x_f - mean) / sqrt(var + eps) * gamma[g][f] + beta[g][f],  var biased (1/d).
+// With `shared` set every token takes gamma[0], beta[0]: one plain LayerNorm, the ablation
+// without GroupLN (marovi.ai MTGR page, 方法, GLN paragraph).
 //
 // Mapping: one 64-lane wavefront per token row, four rows per 256-thread workgroup.  Each lane
 // holds up to two 8-element chunks of the row in registers (d <= 1024), so the row is read from
@@ -45,7 +47,7 @@ __global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __
                                                  const uint8_t* __restrict__ g,
                                                  const Tp* __restrict__ gamma,
                                                  const Tp* __restrict__ beta, float eps,
-                                                 Tout* __restrict__ y) {
+                                                 int gmask, Tout* __restrict__ y) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= T) return;
@@ -78,7 +80,9 @@ __global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __
   }
   const float var = wave_sum(q) * inv_d;
   const float rstd = 1.0f / sqrtf(var + eps);
-  const int grp = g[row] & 3;  // ids outside 0..3 are rejected by validation; stay in bounds
+  // gmask 3: the token's group (ids outside 0..3 are rejected by validation; this stays in
+  // bounds regardless); gmask 0: row 0 for every token
+  const int grp = g[row] & gmask;
   const Tp* gr = gamma + (int64_t)grp * d;
   const Tp* br = beta + (int64_t)grp * d;
   Tout* yr = y + row * d;
@@ -98,28 +102,29 @@ __global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __
 
 template <typename Tin, typename Tout, typename Tp>
 hipError_t run(int64_t T, int d, const void* x, const uint8_t* g, const void* gamma,
-               const void* beta, float eps, void* y, hipStream_t s) {
+               const void* beta, float eps, int gmask, void* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int64_t blocks = (T + 3) / 4;
   k_groupln<Tin, Tout, Tp><<<(unsigned)blocks, 256, 0, s>>>(
       T, d, static_cast<const Tin*>(x), g, static_cast<const Tp*>(gamma),
-      static_cast<const Tp*>(beta), eps, static_cast<Tout*>(y));
+      static_cast<const Tp*>(beta), eps, gmask, static_cast<Tout*>(y));
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_groupln(int64_t T, int d, int in_kind, int out_kind, int param_kind,
+hipError_t launch_groupln(int64_t T, int d, int in_kind, int out_kind, int param_kind, int shared,
                           const void* x, const uint8_t* group_ids, const void* gamma,
                           const void* beta, float eps, void* y, hipStream_t s) {
   const int key = in_kind * 4 + out_kind * 2 + param_kind;
+  const int gm = shared ? 0 : 3;
   switch (key) {
-    case 0: return run<float, float, float>(T, d, x, group_ids, gamma, beta, eps, y, s);
-    case 1: return run<float, float, bf16>(T, d, x, group_ids, gamma, beta, eps, y, s);
-    case 2: return run<float, bf16, float>(T, d, x, group_ids, gamma, beta, eps, y, s);
-    case 3: return run<float, bf16, bf16>(T, d, x, group_ids, gamma, beta, eps, y, s);
-    case 6: return run<bf16, bf16, float>(T, d, x, group_ids, gamma, beta, eps, y, s);
-    case 7: return run<bf16, bf16, bf16>(T, d, x, group_ids, gamma, beta, eps, y, s);
+    case 0: return run<float, float, float>(T, d, x, group_ids, gamma, beta, eps, gm, y, s);
+    case 1: return run<float, float, bf16>(T, d, x, group_ids, gamma, beta, eps, gm, y, s);
+    case 2: return run<float, bf16, float>(T, d, x, group_ids, gamma, beta, eps, gm, y, s);
+    case 3: return run<float, bf16, bf16>(T, d, x, group_ids, gamma, beta, eps, gm, y, s);
+    case 6: return run<bf16, bf16, float>(T, d, x, group_ids, gamma, beta, eps, gm, y, s);
+    case 7: return run<bf16, bf16, bf16>(T, d, x, group_ids, gamma, beta, eps, gm, y, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -27,13 +27,13 @@ hipError_t launch_prep(int32_t B, int64_t C, const int64_t* offsets, const uint8
                        hipStream_t s);
 hipError_t launch_validate(int32_t B, const int64_t* offsets, const uint8_t* group_ids,
                            const float* timestamps, int32_t* flags, hipStream_t s);
-hipError_t launch_debug_mask(int32_t user, const int64_t* offsets, const UserSeg* seg,
+hipError_t launch_debug_mask(int32_t user, int mask_mode, const int64_t* offsets, const UserSeg* seg,
                              const float* timestamps, int64_t n_user, uint8_t* mask,
                              hipStream_t s);
 
 // ---- GroupLN (groupln.hip) ---------------------------------------------------------------
-// in_kind/out_kind/param_kind: 0 = float, 1 = bf16
-hipError_t launch_groupln(int64_t T, int d, int in_kind, int out_kind, int param_kind,
+// in_kind/out_kind/param_kind: 0 = float, 1 = bf16; shared != 0: every row takes gamma[0]/beta[0]
+hipError_t launch_groupln(int64_t T, int d, int in_kind, int out_kind, int param_kind, int shared,
                           const void* x, const uint8_t* group_ids, const void* gamma,
                           const void* beta, float eps, void* y, hipStream_t s);
 
@@ -48,11 +48,12 @@ hipError_t launch_gemm_f32(int64_t M, int N, int K, int epi, const float* a, con
 constexpr int kAttnQTileBf16 = 128;
 constexpr int kAttnQTileF32 = 64;
 // grid_slots = max over XCDs of that XCD's q-tile count (the host replica of k_prep_xcd)
-hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H,
+// mask_mode: kMaskDynamic / kMaskCausal / kMaskFull
+hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H, int mask_mode,
                                  const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                  const int32_t* xcd_off, const float* timestamps,
                                  const bf16* qkvu, bf16* y, hipStream_t s);
-hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H,
+hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H, int mask_mode,
                                 const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                 const int32_t* tile_off, const float* timestamps,
                                 const float* qkvu, float* y, hipStream_t s);

@@ -155,7 +155,7 @@ __global__ void k_validate(int32_t B, const int64_t* __restrict__ offsets,
   if (ncand) atomicAdd(&flags[1], ncand);
 }
 
-__global__ void k_debug_mask(const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
+__global__ void k_debug_mask(int mode, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
                              const float* __restrict__ t, int32_t user, int64_t n,
                              uint8_t* __restrict__ mask) {
   int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -165,7 +165,7 @@ __global__ void k_debug_mask(const int64_t* __restrict__ offsets, const UserSeg*
   int n_static = sg.n_u + sg.n_s;
   int rc_end = n_static + sg.n_r;
   int64_t lo = offsets[user];
-  mask[idx] = mtgr_visible(i, j, n_static, rc_end, t[lo + i], t[lo + j]) ? 1 : 0;
+  mask[idx] = mtgr_visible_mode(mode, i, j, n_static, rc_end, t[lo + i], t[lo + j]) ? 1 : 0;
 }
 
 }  // namespace
@@ -188,13 +188,13 @@ hipError_t launch_validate(int32_t B, const int64_t* offsets, const uint8_t* gro
   return hipGetLastError();
 }
 
-hipError_t launch_debug_mask(int32_t user, const int64_t* offsets, const UserSeg* seg,
+hipError_t launch_debug_mask(int32_t user, int mask_mode, const int64_t* offsets, const UserSeg* seg,
                              const float* timestamps, int64_t n_user, uint8_t* mask,
                              hipStream_t s) {
   int64_t total = n_user * n_user;
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
-  k_debug_mask<<<(unsigned)blocks, 256, 0, s>>>(offsets, seg, timestamps, user, n_user, mask);
+  k_debug_mask<<<(unsigned)blocks, 256, 0, s>>>(mask_mode, offsets, seg, timestamps, user, n_user, mask);
   return hipGetLastError();
 }
 

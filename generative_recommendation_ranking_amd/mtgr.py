@@ -21,6 +21,10 @@ LIB_PATH = os.path.join(_PKG, "libmtgr.so")
 MTGR_OK = 0
 MTGR_F32, MTGR_BF16 = 0, 1
 MTGR_EPI_STORE, MTGR_EPI_SILU, MTGR_EPI_RESIDUAL_F32 = 0, 1, 2
+MTGR_MASK_DYNAMIC, MTGR_MASK_CAUSAL, MTGR_MASK_FULL = 0, 1, 2
+MTGR_NORM_GROUP, MTGR_NORM_SHARED = 0, 1
+MASK_MODES = {"dynamic": MTGR_MASK_DYNAMIC, "causal": MTGR_MASK_CAUSAL, "full": MTGR_MASK_FULL}
+NORM_MODES = {"group": MTGR_NORM_GROUP, "shared": MTGR_NORM_SHARED}
 STATUS_NAMES = {0: "MTGR_OK", 1: "MTGR_ERR_NULL_ARG", 2: "MTGR_ERR_BAD_SHAPE",
                 3: "MTGR_ERR_BAD_BATCH", 4: "MTGR_ERR_UNSUPPORTED", 5: "MTGR_ERR_WORKSPACE",
                 6: "MTGR_ERR_HIP"}
@@ -46,7 +50,8 @@ class MtgrBlockParams(ctypes.Structure):
     _fields_ = [("d_model", c_i32), ("num_heads", c_i32), ("mlp_hidden", c_i32), ("dtype", c_i32),
                 ("ln_eps", c_f32), ("gln1_gamma", c_vp), ("gln1_beta", c_vp), ("w_qkvu", c_vp),
                 ("b_qkvu", c_vp), ("gln2_gamma", c_vp), ("gln2_beta", c_vp), ("w_mlp1", c_vp),
-                ("b_mlp1", c_vp), ("w_mlp2", c_vp), ("b_mlp2", c_vp)]
+                ("b_mlp1", c_vp), ("w_mlp2", c_vp), ("b_mlp2", c_vp), ("mask_mode", c_i32),
+                ("norm_mode", c_i32)]
 
 
 class MtgrEncoderParams(ctypes.Structure):
@@ -81,12 +86,13 @@ def lib():
         L.mtgr_attention_workspace_size.argtypes = [P(MtgrBatch), c_i32, c_i32, P(c_sz)]
         L.mtgr_encoder_fwd.argtypes = [P(MtgrEncoderParams), P(MtgrBatch), c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
         L.mtgr_block_fwd.argtypes = [P(MtgrBlockParams), P(MtgrBatch), c_vp, c_vp, c_vp, c_sz, c_vp]
-        L.mtgr_groupln_fwd.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32,
-                                       c_vp, c_vp, c_vp]
+        L.mtgr_groupln_fwd.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp,
+                                       c_f32, c_vp, c_vp, c_vp]
         L.mtgr_linear_fwd.argtypes = [c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
-        L.mtgr_attention_fwd.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp]
+        L.mtgr_attention_fwd.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz,
+                                         c_vp]
         L.mtgr_validate_batch.argtypes = [P(MtgrBatch), c_vp, c_sz, c_vp, P(c_i32)]
-        L.mtgr_debug_mask.argtypes = [P(MtgrBatch), c_i32, c_vp, c_vp, c_sz, c_vp]
+        L.mtgr_debug_mask.argtypes = [P(MtgrBatch), c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
         for name in EXPORTED[2:]:
             getattr(L, name).restype = c_i32
         _lib = L
@@ -131,9 +137,11 @@ class DeviceBatch:
 
 
 class DeviceModel:
-    """Encoder parameters on the GPU in the storage dtype, plus their C description."""
+    """Encoder parameters on the GPU in the storage dtype, plus their C description.
+    mask_mode / norm_mode ("dynamic"|"causal"|"full", "group"|"shared") select the method or one
+    of its ablation variants in every block."""
 
-    def __init__(self, params, device="cuda"):
+    def __init__(self, params, device="cuda", mask_mode="dynamic", norm_mode="group"):
         import torch
         self.dtype = MTGR_BF16 if params.dtype == "bf16" else MTGR_F32
         tdt = torch.bfloat16 if self.dtype == MTGR_BF16 else torch.float32
@@ -154,7 +162,7 @@ class DeviceModel:
                                         _ptr(t["gln1_gamma"]), _ptr(t["gln1_beta"]), _ptr(t["w_qkvu"]),
                                         _ptr(t["b_qkvu"]), _ptr(t["gln2_gamma"]), _ptr(t["gln2_beta"]),
                                         _ptr(t["w_mlp1"]), _ptr(t["b_mlp1"]), _ptr(t["w_mlp2"]),
-                                        _ptr(t["b_mlp2"]))
+                                        _ptr(t["b_mlp2"]), MASK_MODES[mask_mode], NORM_MODES[norm_mode])
         self.blocks = blocks
         self.head = {k: dev(v) for k, v in params.head.items()}
         self.head_hidden = int(params.head["w_head1"].shape[0])
@@ -214,10 +222,10 @@ def mtgr_block_fwd(block: MtgrBlockParams, batch: DeviceBatch, x_in, x_out, ws, 
 
 
 def mtgr_groupln_fwd(batch: DeviceBatch, d: int, in_dtype: int, out_dtype: int, param_dtype: int,
-                     gamma, beta, eps: float, x, y, stream=None):
+                     norm_mode: int, gamma, beta, eps: float, x, y, stream=None):
     _check("mtgr_groupln_fwd", lib().mtgr_groupln_fwd(
-        ctypes.byref(batch.c), d, in_dtype, out_dtype, param_dtype, _ptr(gamma), _ptr(beta), eps,
-        _ptr(x), _ptr(y), _stream(stream)))
+        ctypes.byref(batch.c), d, in_dtype, out_dtype, param_dtype, norm_mode, _ptr(gamma),
+        _ptr(beta), eps, _ptr(x), _ptr(y), _stream(stream)))
 
 
 def mtgr_linear_fwd(M: int, N: int, K: int, dtype: int, epilogue: int, a, w, bias, resid, out,
@@ -227,11 +235,11 @@ def mtgr_linear_fwd(M: int, N: int, K: int, dtype: int, epilogue: int, a, w, bia
         _stream(stream)))
 
 
-def mtgr_attention_fwd(batch: DeviceBatch, d: int, num_heads: int, dtype: int, qkvu, y_gated, ws,
-                       stream=None):
+def mtgr_attention_fwd(batch: DeviceBatch, d: int, num_heads: int, dtype: int, mask_mode: int, qkvu,
+                       y_gated, ws, stream=None):
     _check("mtgr_attention_fwd", lib().mtgr_attention_fwd(
-        ctypes.byref(batch.c), d, num_heads, dtype, _ptr(qkvu), _ptr(y_gated), _ptr(ws), ws.numel(),
-        _stream(stream)))
+        ctypes.byref(batch.c), d, num_heads, dtype, mask_mode, _ptr(qkvu), _ptr(y_gated), _ptr(ws),
+        ws.numel(), _stream(stream)))
 
 
 def mtgr_validate_batch(batch: DeviceBatch, ws, stream=None) -> int:
@@ -241,6 +249,6 @@ def mtgr_validate_batch(batch: DeviceBatch, ws, stream=None) -> int:
     return int(flags.value)
 
 
-def mtgr_debug_mask(batch: DeviceBatch, user: int, mask_dev, ws, stream=None):
+def mtgr_debug_mask(batch: DeviceBatch, user: int, mask_mode: int, mask_dev, ws, stream=None):
     _check("mtgr_debug_mask", lib().mtgr_debug_mask(
-        ctypes.byref(batch.c), user, _ptr(mask_dev), _ptr(ws), ws.numel(), _stream(stream)))
+        ctypes.byref(batch.c), user, mask_mode, _ptr(mask_dev), _ptr(ws), ws.numel(), _stream(stream)))

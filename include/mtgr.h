@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define MTGR_ABI_VERSION 1
+#define MTGR_ABI_VERSION 2
 
 typedef enum {
   MTGR_OK = 0,
@@ -66,6 +66,18 @@ typedef enum {
 typedef enum { MTGR_F32 = 0, MTGR_BF16 = 1 } mtgr_dtype;
 
 enum { MTGR_G_U = 0, MTGR_G_S = 1, MTGR_G_R = 2, MTGR_G_C = 3, MTGR_NUM_GROUPS = 4 };
+
+/* Attention masks.  MTGR_MASK_DYNAMIC is the method's three-rule mask.  The other two are the
+ * baselines of the ablation without the dynamic mask ([P1]/[P2] experiments; [P3] 结果):
+ * MTGR_MASK_CAUSAL, key j visible to query i iff j <= i in the user's token order (the plain
+ * causal mask the dynamic rules replace, [P3] 方法 and [P5] 7.3.4), and MTGR_MASK_FULL, every
+ * key of the user visible. */
+enum { MTGR_MASK_DYNAMIC = 0, MTGR_MASK_CAUSAL = 1, MTGR_MASK_FULL = 2 };
+
+/* Normalisation.  MTGR_NORM_GROUP is GroupLN; MTGR_NORM_SHARED is the ablation without GroupLN
+ * ([P1]/[P2] experiments; [P3] 方法, GLN paragraph): one LayerNorm whose gamma/beta are row 0
+ * of the [4][d] parameter arrays, for every token. */
+enum { MTGR_NORM_GROUP = 0, MTGR_NORM_SHARED = 1 };
 
 /* GEMM epilogues of mtgr_linear_fwd */
 enum {
@@ -102,6 +114,8 @@ typedef struct mtgr_block_params {
   const void* b_mlp1;             /* [h] or NULL */
   const void* w_mlp2;             /* [d][h] */
   const void* b_mlp2;             /* [d] or NULL */
+  int32_t mask_mode;              /* MTGR_MASK_*; 0 (a zeroed struct) = the dynamic mask */
+  int32_t norm_mode;              /* MTGR_NORM_*; 0 = GroupLN */
 } mtgr_block_params;
 
 /* L blocks plus the candidate head.  `layers` is a host array of L block descriptions that
@@ -143,11 +157,12 @@ mtgr_status mtgr_block_fwd(const mtgr_block_params* p, const mtgr_batch* b, cons
 
 /* ---- kernel-level entries (the same kernels the block uses) ------------------------------ */
 /* GroupLN over T rows of width d: y = (x - mean) / sqrt(var + eps) * gamma[g] + beta[g].
- * x in `in_dtype`, y in `out_dtype`, gamma/beta [4][d] in `param_dtype`.
+ * x in `in_dtype`, y in `out_dtype`, gamma/beta [4][d] in `param_dtype` ([1][d] suffices with
+ * MTGR_NORM_SHARED, which uses g = 0 for every row).
  * Supported (in, out): (F32, F32), (F32, BF16), (BF16, BF16). */
 mtgr_status mtgr_groupln_fwd(const mtgr_batch* b, int32_t d, int32_t in_dtype, int32_t out_dtype,
-                             int32_t param_dtype, const void* gamma, const void* beta, float eps,
-                             const void* x, void* y, void* stream);
+                             int32_t param_dtype, int32_t norm_mode, const void* gamma,
+                             const void* beta, float eps, const void* x, void* y, void* stream);
 
 /* out = epilogue(a[M][K] W[N][K]^T + bias[N]); a, W, bias in `dtype`; see MTGR_EPI_*.
  * bf16: K a multiple of 64 and >= 128, N a multiple of 4.  fp32: K a multiple of 4. */
@@ -155,11 +170,12 @@ mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int3
                             const void* a, const void* w, const void* bias, const float* resid,
                             void* out, void* stream);
 
-/* Masked SiLU attention with the U gate for every user and head:
- * qkvu device [T][4d] in `dtype` -> y_gated device [T][d] in `dtype` (V~ (.) U). */
+/* Masked SiLU attention with the U gate for every user and head, under mask `mask_mode`
+ * (MTGR_MASK_*): qkvu device [T][4d] in `dtype` -> y_gated device [T][d] in `dtype` (V~ (.) U).
+ * The normaliser is the user's token count N in every mode. */
 mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
-                               const void* qkvu, void* y_gated, void* ws, size_t ws_bytes,
-                               void* stream);
+                               int32_t mask_mode, const void* qkvu, void* y_gated, void* ws,
+                               size_t ws_bytes, void* stream);
 
 /* ---- test / debug ------------------------------------------------------------------------ */
 /* Device-side checks of a batch (group ids in 0..3 and non-decreasing within each user, no NaN
@@ -168,10 +184,10 @@ mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads
 mtgr_status mtgr_validate_batch(const mtgr_batch* b, void* ws, size_t ws_bytes, void* stream,
                                 int32_t* flags_out);
 
-/* Writes the mask of user `user` as uint8 [n_b][n_b] (rows = queries) into mask_dev, using the
- * same visibility predicate as the attention kernels. */
-mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, uint8_t* mask_dev, void* ws,
-                            size_t ws_bytes, void* stream);
+/* Writes the mask `mask_mode` (MTGR_MASK_*) of user `user` as uint8 [n_b][n_b] (rows = queries)
+ * into mask_dev, using the same visibility predicate as the attention kernels. */
+mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, int32_t mask_mode,
+                            uint8_t* mask_dev, void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert M.mtgr_abi_version() == 1
+    assert M.mtgr_abi_version() == 2
     assert M.mtgr_status_str(0) == "ok"
     assert "workspace" in M.mtgr_status_str(5)
 
@@ -50,8 +50,9 @@ def _batch(offsets, T=None, C=0):
     return b, off
 
 
-def _block(d=256, H=4, h=1024, dtype=M.MTGR_BF16, eps=1e-5):
-    return M.MtgrBlockParams(d, H, h, dtype, eps, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, None)
+def _block(d=256, H=4, h=1024, dtype=M.MTGR_BF16, eps=1e-5, mask_mode=0, norm_mode=0):
+    return M.MtgrBlockParams(d, H, h, dtype, eps, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, None,
+                             mask_mode, norm_mode)
 
 
 def _ws_size(block, batch):
@@ -72,6 +73,10 @@ def test_block_workspace_size_and_shape_checks():
     assert _ws_size(_block(d=64, H=2, h=128, dtype=M.MTGR_F32), b)[0] == 0  # d_h = 32 fine in fp32
     assert _ws_size(_block(dtype=7), b)[0] == 4             # unknown dtype
     assert _ws_size(_block(eps=float("nan")), b)[0] == 2
+    assert _ws_size(_block(mask_mode=M.MTGR_MASK_CAUSAL, norm_mode=M.MTGR_NORM_SHARED), b)[0] == 0
+    assert _ws_size(_block(mask_mode=M.MTGR_MASK_FULL), b)[0] == 0
+    assert _ws_size(_block(mask_mode=3), b)[0] == 4          # unknown mask mode
+    assert _ws_size(_block(norm_mode=2), b)[0] == 4          # unknown norm mode
 
 
 @pytest.mark.parametrize("offsets,T,code", [
@@ -113,9 +118,14 @@ def test_linear_and_groupln_argument_checks():
     assert L.mtgr_linear_fwd(100, 64, 128, M.MTGR_BF16, 2, FAKE, FAKE, None, None, FAKE, None) == 1
     assert L.mtgr_linear_fwd(0, 64, 128, M.MTGR_BF16, 0, None, None, None, None, None, None) == 0
     b, _keep = _batch([0, 10, 30])
-    assert L.mtgr_groupln_fwd(ctypes.byref(b), 1030, 0, 0, 0, FAKE, FAKE, ctypes.c_float(1e-5), FAKE, FAKE, None) == 2
-    assert L.mtgr_groupln_fwd(ctypes.byref(b), 64, 1, 0, 0, FAKE, FAKE, ctypes.c_float(1e-5), FAKE, FAKE, None) == 4
-    assert L.mtgr_groupln_fwd(ctypes.byref(b), 64, 0, 0, 0, None, FAKE, ctypes.c_float(1e-5), FAKE, FAKE, None) == 1
+    e = ctypes.c_float(1e-5)
+    assert L.mtgr_groupln_fwd(ctypes.byref(b), 1030, 0, 0, 0, 0, FAKE, FAKE, e, FAKE, FAKE, None) == 2
+    assert L.mtgr_groupln_fwd(ctypes.byref(b), 64, 1, 0, 0, 0, FAKE, FAKE, e, FAKE, FAKE, None) == 4
+    assert L.mtgr_groupln_fwd(ctypes.byref(b), 64, 0, 0, 0, 0, None, FAKE, e, FAKE, FAKE, None) == 1
+    assert L.mtgr_groupln_fwd(ctypes.byref(b), 64, 0, 0, 0, 5, FAKE, FAKE, e, FAKE, FAKE, None) == 4
+    ws = 1 << 20
+    assert L.mtgr_attention_fwd(ctypes.byref(b), 256, 4, M.MTGR_BF16, 7, FAKE, FAKE, FAKE, ws, None) == 4
+    assert L.mtgr_debug_mask(ctypes.byref(b), 0, -1, FAKE, FAKE, ws, None) == 4
 
 
 def test_empty_batch_is_a_no_op():

@@ -75,14 +75,32 @@ def test_debug_mask_bit_exact(unsorted_r, ties):
         if n == 0:
             continue
         out = torch.full((n, n), 7, dtype=torch.uint8, device=DEV)
-        M.mtgr_debug_mask(db, u, out, ws)
+        M.mtgr_debug_mask(db, u, M.MTGR_MASK_DYNAMIC, out, ws)
         lo, hi = b.offsets[u], b.offsets[u + 1]
         expect = O.mask(b.group_ids[lo:hi], b.timestamps[lo:hi])
         np.testing.assert_array_equal(out.cpu().numpy(), expect, err_msg=f"user {u}")
 
 
-@pytest.mark.parametrize("dtype,d,H", [("bf16", 128, 2), ("bf16", 256, 2), ("f32", 64, 2)])
-def test_onehot_probe_reproduces_mask_through_fused_kernel(dtype, d, H):
+@pytest.mark.parametrize("mode", ["causal", "full"])
+def test_debug_mask_ablation_modes_bit_exact(mode):
+    b = custom_batch(EDGE_LENGTHS, 64, 1, "f32", unsorted_r=True)
+    db = M.DeviceBatch(b)
+    ws = M.workspace(M.mtgr_attention_workspace_size(db, 64, 2))
+    for u in range(b.num_users):
+        n = int(b.offsets[u + 1] - b.offsets[u])
+        if n == 0:
+            continue
+        out = torch.full((n, n), 7, dtype=torch.uint8, device=DEV)
+        M.mtgr_debug_mask(db, u, M.MASK_MODES[mode], out, ws)
+        lo, hi = b.offsets[u], b.offsets[u + 1]
+        expect = O.mask(b.group_ids[lo:hi], b.timestamps[lo:hi], mode)
+        np.testing.assert_array_equal(out.cpu().numpy(), expect, err_msg=f"user {u}")
+
+
+@pytest.mark.parametrize("dtype,d,H,mode", [("bf16", 128, 2, "dynamic"), ("bf16", 256, 2, "dynamic"),
+                                            ("f32", 64, 2, "dynamic"), ("bf16", 128, 2, "causal"),
+                                            ("bf16", 256, 2, "full"), ("f32", 64, 2, "causal")])
+def test_onehot_probe_reproduces_mask_through_fused_kernel(dtype, d, H, mode):
     """q_i = k_j = e_0 (score 1, silu(1) > 0), U = 1, and V one-hot over one chunk of d_h keys per
     run: a nonzero output feature f of row i means key (chunk*d_h + f) was added to row i."""
     lengths = [(2, 150, 70, 30), (0, 0, 3, 9), (4, 20, 0, 2)]
@@ -96,7 +114,7 @@ def test_onehot_probe_reproduces_mask_through_fused_kernel(dtype, d, H):
     for u in range(b.num_users):
         lo, hi = int(b.offsets[u]), int(b.offsets[u + 1])
         n = hi - lo
-        expect = O.mask(b.group_ids[lo:hi], b.timestamps[lo:hi])
+        expect = O.mask(b.group_ids[lo:hi], b.timestamps[lo:hi], mode)
         got = np.zeros((n, n), np.uint8)
         for c0 in range(0, n, dh):
             qkvu = torch.zeros(T, 4 * d, dtype=torch.float32)
@@ -108,7 +126,7 @@ def test_onehot_probe_reproduces_mask_through_fused_kernel(dtype, d, H):
                 qkvu[lo + j, 2 * d + (j - c0)] = 1.0    # head 0 only: v_j = e_{j-c0}
             qd = qkvu.to(DEV).to(tdt)
             y = torch.zeros(T, d, dtype=tdt, device=DEV)
-            M.mtgr_attention_fwd(db, d, H, kd, qd, y, ws)
+            M.mtgr_attention_fwd(db, d, H, kd, M.MASK_MODES[mode], qd, y, ws)
             yh = to_np(y)[lo:hi, :dh]
             cols = min(dh, n - c0)
             got[:, c0:c0 + cols] = (yh[:, :cols] != 0).astype(np.uint8)
@@ -118,8 +136,10 @@ def test_onehot_probe_reproduces_mask_through_fused_kernel(dtype, d, H):
 # ---------------------------------------------------------------------------------------------
 # kernels
 # ---------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("kin,kout,d", [(0, 0, 64), (0, 1, 256), (1, 1, 768), (0, 1, 1024), (0, 0, 40)])
-def test_groupln_parity(kin, kout, d):
+@pytest.mark.parametrize("kin,kout,d,shared", [(0, 0, 64, False), (0, 1, 256, False), (1, 1, 768, False),
+                                               (0, 1, 1024, False), (0, 0, 40, False), (0, 0, 64, True),
+                                               (0, 1, 768, True), (1, 1, 256, True)])
+def test_groupln_parity(kin, kout, d, shared):
     b = custom_batch(EDGE_LENGTHS, d, 2, "f32")
     db = M.DeviceBatch(b)
     rng = np.random.default_rng(3)
@@ -134,9 +154,10 @@ def test_groupln_parity(kin, kout, d):
     tp = torch.bfloat16 if pk else torch.float32
     xd = torch.from_numpy(x).to(DEV).to(tin)
     y = torch.zeros(b.num_tokens, d, dtype=tout, device=DEV)
-    M.mtgr_groupln_fwd(db, d, kin, kout, pk, torch.from_numpy(gamma).to(DEV).to(tp),
+    nm = M.MTGR_NORM_SHARED if shared else M.MTGR_NORM_GROUP
+    M.mtgr_groupln_fwd(db, d, kin, kout, pk, nm, torch.from_numpy(gamma).to(DEV).to(tp),
                        torch.from_numpy(beta).to(DEV).to(tp), 1e-5, xd, y)
-    ref = O.group_layer_norm(x, b.group_ids, gamma, beta, 1e-5)
+    ref = O.group_layer_norm(x, b.group_ids, gamma, beta, 1e-5, shared=shared)
     tol = TOL_F32 if kout == 0 else TOL_BF16_KERNEL
     assert rel_err(to_np(y), ref) < tol
 
@@ -177,10 +198,12 @@ def test_linear_f32_parity(M_, N, K, epi):
     assert rel_err(to_np(out), ref) < 1e-5
 
 
-@pytest.mark.parametrize("dtype,d,H,unsorted_r", [("bf16", 256, 2, False), ("bf16", 256, 4, True),
-                                                  ("bf16", 768, 6, False), ("f32", 64, 2, True),
-                                                  ("f32", 128, 2, False)])
-def test_attention_parity(dtype, d, H, unsorted_r):
+@pytest.mark.parametrize("dtype,d,H,unsorted_r,mode", [
+    ("bf16", 256, 2, False, "dynamic"), ("bf16", 256, 4, True, "dynamic"), ("bf16", 768, 6, False, "dynamic"),
+    ("f32", 64, 2, True, "dynamic"), ("f32", 128, 2, False, "dynamic"),
+    ("bf16", 256, 2, True, "causal"), ("bf16", 768, 6, False, "causal"), ("bf16", 256, 4, False, "full"),
+    ("f32", 64, 2, True, "causal"), ("f32", 128, 2, False, "full")])
+def test_attention_parity(dtype, d, H, unsorted_r, mode):
     b = custom_batch(EDGE_LENGTHS + [(8, 600, 120, 77)], d, 11, dtype, unsorted_r, ties=not unsorted_r)
     db = M.DeviceBatch(b)
     rng = np.random.default_rng(12)
@@ -192,23 +215,23 @@ def test_attention_parity(dtype, d, H, unsorted_r):
     kd = M.MTGR_BF16 if dtype == "bf16" else M.MTGR_F32
     y = torch.zeros(b.num_tokens, d, dtype=tdt, device=DEV)
     ws = M.workspace(M.mtgr_attention_workspace_size(db, d, H))
-    M.mtgr_attention_fwd(db, d, H, kd, torch.from_numpy(qkvu).to(DEV).to(tdt), y, ws)
+    M.mtgr_attention_fwd(db, d, H, kd, M.MASK_MODES[mode], torch.from_numpy(qkvu).to(DEV).to(tdt), y, ws)
     got = to_np(y)
     tol = TOL_F32 if dtype == "f32" else TOL_BF16_KERNEL
     for u in range(b.num_users):
         lo, hi = int(b.offsets[u]), int(b.offsets[u + 1])
         if hi == lo:
             continue
-        ref = O.hstu_attention(qkvu[lo:hi], b.group_ids[lo:hi], b.timestamps[lo:hi], H)
+        ref = O.hstu_attention(qkvu[lo:hi], b.group_ids[lo:hi], b.timestamps[lo:hi], H, mode)
         assert rel_err(got[lo:hi], ref) < tol, f"user {u}"
 
 
 # ---------------------------------------------------------------------------------------------
 # block and encoder
 # ---------------------------------------------------------------------------------------------
-def run_encoder(b, p):
+def run_encoder(b, p, mask="dynamic", norm="group"):
     db = M.DeviceBatch(b)
-    dm = M.DeviceModel(p)
+    dm = M.DeviceModel(p, mask_mode=mask, norm_mode=norm)
     ws = M.workspace(M.mtgr_encoder_workspace_size(dm, db))
     hidden = torch.empty(b.num_tokens, p.d, dtype=torch.float32, device=DEV)
     logits = torch.empty(max(db.num_candidates, 1), 2, dtype=torch.float32, device=DEV)
@@ -217,10 +240,11 @@ def run_encoder(b, p):
     return to_np(hidden), to_np(logits)[:db.num_candidates]
 
 
-def oracle_subset(b, p, users):
+def oracle_subset(b, p, users, mask="dynamic", norm="group"):
     s = synth.subset(b, users)
     return O.encoder_forward(s.offsets, s.group_ids, s.timestamps, s.x, O.params_layers(p),
-                             O.params_head(p), p.H, p.ln_eps)
+                             O.params_head(p), p.H, p.ln_eps, mask_mode=mask,
+                             shared_norm=(norm == "shared"))
 
 
 def test_block_fp32_parity():
@@ -243,16 +267,20 @@ def test_block_fp32_parity():
     assert rel_err(to_np(xin), ref) < TOL_F32
 
 
-def test_encoder_tiny_fp32_parity():
+@pytest.mark.parametrize("mask,norm", [("dynamic", "group"), ("causal", "group"), ("dynamic", "shared"),
+                                       ("full", "shared")])
+def test_encoder_tiny_fp32_parity(mask, norm):
     b, p = workload("tiny-fp32")
-    hid, logit = run_encoder(b, p)
+    hid, logit = run_encoder(b, p, mask, norm)
     rh, rl = O.encoder_forward(b.offsets, b.group_ids, b.timestamps, b.x, O.params_layers(p),
-                               O.params_head(p), p.H, p.ln_eps)
+                               O.params_head(p), p.H, p.ln_eps, mask_mode=mask,
+                               shared_norm=(norm == "shared"))
     assert rel_err(hid, rh) < TOL_F32
     assert rel_err(logit, rl) < TOL_F32
 
 
-def test_encoder_bf16_custom_parity_with_biases():
+@pytest.mark.parametrize("mask,norm", [("dynamic", "group"), ("causal", "shared"), ("full", "group")])
+def test_encoder_bf16_custom_parity_with_biases(mask, norm):
     rng = np.random.default_rng(21)
     b = custom_batch(EDGE_LENGTHS + [(8, 600, 120, 77)], 256, 22, "bf16", unsorted_r=True)
     p = synth.make_params(rng, 2, 256, 2, 512, "bf16")
@@ -261,9 +289,10 @@ def test_encoder_bf16_custom_parity_with_biases():
             lay[k] = synth.round_to_bf16(rng.uniform(-0.2, 0.2, lay[k].shape).astype(np.float32))
     p.head["b_head1"] = synth.round_to_bf16(rng.uniform(-0.2, 0.2, p.head["b_head1"].shape).astype(np.float32))
     p.head["b_head2"] = synth.round_to_bf16(np.array([0.3, -0.4], np.float32))
-    hid, logit = run_encoder(b, p)
+    hid, logit = run_encoder(b, p, mask, norm)
     rh, rl = O.encoder_forward(b.offsets, b.group_ids, b.timestamps, b.x, O.params_layers(p),
-                               O.params_head(p), p.H, p.ln_eps)
+                               O.params_head(p), p.H, p.ln_eps, mask_mode=mask,
+                               shared_norm=(norm == "shared"))
     assert rel_err(hid, rh) < TOL_BF16_ENCODER
     assert rel_err(logit, rl) < TOL_BF16_ENCODER
 
@@ -276,19 +305,21 @@ def _sample_users(b, k_extra):
     return sorted(set([longest, shortest] + extra))
 
 
-@pytest.mark.parametrize("name,k_extra", [("small-bf16", 3), ("medium-bf16", 1), ("large-bf16", 0),
-                                          ("inference-bf16", 1)])
-def test_encoder_workload_sampled_users(name, k_extra):
+@pytest.mark.parametrize("name,k_extra,mask,norm", [
+    ("small-bf16", 3, "dynamic", "group"), ("medium-bf16", 1, "dynamic", "group"),
+    ("large-bf16", 0, "dynamic", "group"), ("inference-bf16", 1, "dynamic", "group"),
+    ("large-bf16", 0, "causal", "shared")])
+def test_encoder_workload_sampled_users(name, k_extra, mask, norm):
     """Full-size batch on the GPU (the configuration the benchmark times); the oracle recomputes a
     few users exactly (users never interact, so a subset is exact)."""
     b, p = workload(name)
-    hid, logit = run_encoder(b, p)
+    hid, logit = run_encoder(b, p, mask, norm)
     users = _sample_users(b, k_extra)
-    rh, rl = oracle_subset(b, p, users)
+    rh, rl = oracle_subset(b, p, users, mask, norm)
     gh = hid[synth.user_rows(b, users)]
     gl = logit[synth.candidate_rows(b, users)]
     e_h, e_l = rel_err(gh, rh), rel_err(gl, rl)
-    print(f"{name}: users {users} hidden rel err {e_h:.3e} logits rel err {e_l:.3e}")
+    print(f"{name} ({mask}, {norm}): users {users} hidden rel err {e_h:.3e} logits rel err {e_l:.3e}")
     assert e_h < TOL_BF16_ENCODER
     assert e_l < TOL_BF16_ENCODER
     assert np.isfinite(hid).all() and np.isfinite(logit).all()
