@@ -379,7 +379,7 @@ mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int3
   if (dtype != MTGR_F32 && dtype != MTGR_BF16) return MTGR_ERR_UNSUPPORTED;
   if (epilogue < MTGR_EPI_STORE || epilogue > MTGR_EPI_RESIDUAL_F32) return MTGR_ERR_UNSUPPORTED;
   if (M < 0 || N <= 0 || K <= 0 || N > (1 << 20)) return MTGR_ERR_BAD_SHAPE;
-  if (dtype == MTGR_BF16 && (K % 64 != 0 || K < 128 || N % 4 != 0)) return MTGR_ERR_BAD_SHAPE;
+  if (dtype == MTGR_BF16 && (K % 64 != 0 || K < 128 || N % 8 != 0)) return MTGR_ERR_BAD_SHAPE;
   if (dtype == MTGR_F32 && K % 4 != 0) return MTGR_ERR_BAD_SHAPE;
   if (M == 0) return MTGR_OK;
   if (!a || !w || !out) return MTGR_ERR_NULL_ARG;

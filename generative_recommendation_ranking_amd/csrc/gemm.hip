@@ -27,6 +27,9 @@ namespace mtgr {
 namespace {
 
 constexpr int kXcd = 8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kBiasLds = 4096;  // bias entries staged in LDS by the persistent bf16 GEMM
 
 template <int EPI, typename TOut>
 __device__ __forceinline__ void store_out(TOut* out, const float* resid, int64_t idx, float v) {
@@ -39,41 +42,15 @@ __device__ __forceinline__ void store_out(TOut* out, const float* resid, int64_t
   }
 }
 
-template <int EPI, typename TOut>
-__device__ __forceinline__ void store4(TOut* out, const float* resid, int64_t idx, const float v[4]) {
-  float r[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) r[e] = v[e];
-  if constexpr (EPI == MTGR_EPI_SILU) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = silu_rcp(r[e]);
-  } else if constexpr (EPI == MTGR_EPI_RESIDUAL_F32) {
-    const f32x4 q = *reinterpret_cast<const f32x4*>(resid + idx);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] += q[e];
-  }
-  if constexpr (sizeof(TOut) == 4) {
-    f32x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = r[e];
-    *reinterpret_cast<f32x4*>(out + idx) = o;
-  } else {
-    bf16x4 o;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o[e] = (bf16)r[e];
-    *reinterpret_cast<bf16x4*>(out + idx) = o;
-  }
-}
-
 // Persistent variant: one workgroup per CU walks its share of output tiles and streams the
 // K-slabs of consecutive tiles through one software pipeline, so the first loads of the next tile
 // are in flight while the current tile finishes and stores its results.
 //   * WM x WN wavefronts, 256 x 256 tile, BK = 64 (4 MFMA k-steps per slab), two LDS buffers.
 //   * Global loads are buffer loads whose resource starts at the tile's first row and whose size
 //     stops at M (N): rows past the end read as zero, and per-chunk offsets live in SGPRs.
-//   * Per slab: the fragments of k-step ks+1 are read before the MFMAs of k-step ks; the slab
-//     after next is written to LDS after k-step 1 and the one after that is fetched after
-//     k-step 2; the end-of-slab barrier waits for LDS traffic only.
+//   * Per slab: the fragments of k-step ks+1 are read before the MFMAs of k-step ks; the next
+//     slab is written to LDS and the one after it fetched after k-step 1; one barrier after
+//     k-step 2 (LDS traffic only) covers both buffers.
 template <int WM, int WN, int EPI, typename TOut>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     int64_t M, int N, int K, const bf16* __restrict__ A, const bf16* __restrict__ W,
@@ -87,6 +64,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16 (*As)[BM][LP] = reinterpret_cast<bf16 (*)[BM][LP]>(smem);
   bf16 (*Bs)[BN][LP] = reinterpret_cast<bf16 (*)[BN][LP]>(smem + 2 * BM * LP * sizeof(bf16));
+  // Bias table in LDS: the whole vector when N <= kBiasLds (staged once), else the current
+  // tile's slice (staged at the start of each tile).  It seeds the accumulators.
+  bf16* Bias = reinterpret_cast<bf16*>(smem + 2 * (BM + BN) * LP * sizeof(bf16));
+  const bool bias_whole = bias != nullptr && N <= kBiasLds;
+  const bool bias_slice = bias != nullptr && N > kBiasLds;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -161,12 +143,17 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
       *reinterpret_cast<bf16x8*>(&Bs[buf][tid / CPR + i * RSTEP][(tid % CPR) * 8]) = rb[i];
   };
   // Software pipeline over the K slabs of this workgroup's tiles, one after another: slab g is
-  // in LDS buffer g%2; the fragments of k-step ks+1 are read before the MFMAs of k-step ks; the
-  // slab after next is written to LDS after k-step 1 and the one after it fetched after k-step 2
-  // (from the next tile once this tile's slabs run out); the end-of-slab barrier waits for LDS
-  // traffic only, so global loads stay in flight.  The loads run at most two slabs ahead, so
-  // with at least two slabs per tile they only ever touch this tile or the next one.
+  // in LDS buffer g%2 and the fragments of k-step ks+1 are read before the MFMAs of k-step ks.
+  // Within slab g: after the MFMAs of k-step 1 the registers holding slab g+1 are written to the
+  // other buffer and the loads of slab g+2 are issued (from the next tile once this tile's slabs
+  // run out), so a load has a whole slab of MFMAs to arrive; after the MFMAs of k-step 2 one
+  // barrier (LDS traffic only, global loads stay in flight) publishes slab g+1 and retires every
+  // read of slab g's buffer before it is overwritten; during k-step 3 the first fragments of slab
+  // g+1 are read, so the slab boundary exposes no LDS latency (at a tile boundary they are read
+  // after the epilogue instead).  The loads run at most two slabs
+  // ahead, so with at least two slabs per tile they only touch this tile or the next one.
   constexpr int KS = BK / 16;
+  static_assert(KS == 4, "the schedule below assumes four k-steps per slab");
   bf16x8 fa[2][FM], fb[2][FN];
   auto read_frags = [&](int buf, int ks, int fslot) {
 #pragma unroll
@@ -175,6 +162,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
 #pragma unroll
     for (int j = 0; j < FN; ++j)
       fb[fslot][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * TN + j * 32 + l32][ks * 16 + hh * 8]);
+    // keep the reads ahead of the MFMAs that follow (the scheduler would otherwise sink them)
+    __builtin_amdgcn_sched_barrier(0);
   };
   auto lds_barrier = [] { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
@@ -183,7 +172,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   TileRsrc r_cur = make_rsrc(slot);
   TileRsrc r_nxt = (next < nslots) ? make_rsrc(next) : r_cur;
 
-  // prologue: slab 0 into LDS buffer 0, slab 1 into registers
+  // prologue: the bias slice table, slab 0 into LDS buffer 0, slab 1 into registers
+  if (bias_whole) {
+    for (int i = tid; i < N; i += NT) Bias[i] = bias[i];
+  }
   issue_loads(r_cur, 0);
   store_slab(0);
   issue_loads(r_cur, 1);
@@ -192,69 +184,203 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   read_frags(0, 0, 0);
 
   int cur = 0;
-  while (true) {
-    f32x16 acc[FM][FN];
+  bool more_tiles = next < nslots;
+  f32x16 acc[FM][FN];
+  // The accumulators start at the bias of their columns (element r of MFMA tile j holds column
+  // j*32 + 8(r/4) + 4hh + r%4 of the wavefront tile), so the epilogue never touches the bias.
+  auto init_acc = [&] {
+    if (!bias) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+      return;
+    }
+    int64_t mt_i; int nt_i; decode(slot, mt_i, nt_i);
+    const int n0 = nt_i * BN;
+    const bf16* btab = Bias;
+    if (bias_slice) {
+      // every wavefront passed a barrier after its last read of the previous slice
+      for (int i = tid; i < BN; i += NT) Bias[i] = n0 + i < N ? bias[n0 + i] : (bf16)0.f;
+      lds_barrier();
+      btab = Bias - n0;
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // columns past N are clamped to a valid entry; their results are dropped
+        const int n = min(n0 + wn * TN + j * 32 + 8 * g + 4 * hh, N - 4);
+        const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(&btab[n]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int i = 0; i < FM; ++i) acc[i][j][4 * g + e] = (float)b4[e];
+      }
+  };
+  auto mfmas = [&](int fs) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
-    const bool more_tiles = next < nslots;
-    for (int kt = 0; kt < nk; ++kt) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int fs = ks & 1;
-        if (ks + 1 < KS) read_frags(cur, ks + 1, fs ^ 1);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fs][j], fa[fs][i], acc[i][j], 0, 0, 0);
-        if (ks == 1 && have_next) store_slab(cur ^ 1);
-        if (ks == 2) {
-          // slab kt+2 of this tile, else slab kt+2-nk of the next tile
-          const bool here = kt + 2 < nk;
-          have_next = here || more_tiles;
-          if (have_next) issue_loads(here ? r_cur : r_nxt, here ? kt + 2 : kt + 2 - nk);
-        }
-      }
-      if (kt + 1 < nk || more_tiles) {
-        lds_barrier();
-        cur ^= 1;
-        read_frags(cur, 0, 0);
-      }
+      for (int j = 0; j < FN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[fs][j], fa[fs][i], acc[i][j], 0, 0, 0);
+  };
+  auto slab = [&](int kt) {
+    const bool cont = kt + 1 < nk || more_tiles;
+    read_frags(cur, 1, 1);
+    mfmas(0);
+    read_frags(cur, 2, 0);
+    mfmas(1);
+    if (have_next) store_slab(cur ^ 1);
+    {
+      // slab kt+2 of this tile, else slab kt+2-nk of the next tile
+      const bool here = kt + 2 < nk;
+      have_next = here || more_tiles;
+      if (have_next) issue_loads(here ? r_cur : r_nxt, here ? kt + 2 : kt + 2 - nk);
     }
-    // epilogue of this tile: row m = l32 of the MFMA tile, columns 8g + 4hh + 0..3 (N is a
-    // multiple of 4, so a group is either wholly inside or wholly past the last column)
+    read_frags(cur, 3, 1);
+    mfmas(0);
+    if (cont) {
+      lds_barrier();
+      // the next tile's first fragments are read after the epilogue, which needs the registers
+      if (kt + 1 < nk) read_frags(cur ^ 1, 0, 0);
+    }
+    mfmas(1);
+    if (cont) cur ^= 1;
+  };
+
+  // Epilogue.  An MFMA tile leaves each lane 4 consecutive columns of one row, so stores straight
+  // from registers would write 16-byte pieces of 32 different rows per instruction; instead each
+  // wavefront passes its results through a private region of the LDS slab buffer that the next
+  // tile does not use yet, 32 rows at a time, and writes whole 256-byte row segments with 16-byte
+  // stores (the residual rows of the fp32 variant are read the same way).  Vector memory
+  // operations retire in order, so a wait for a load also waits for every store issued before it:
+  // the bias is already in the accumulators, the residual chunks of a pass are requested before
+  // the pass's stores, and every
+  // lane issues the same fixed number of stores whatever the tile's edges (the resource ends at
+  // the tile's last valid row; chunks past column N get an offset beyond it and are dropped), so
+  // the compiler can also count past them when it waits for the next tile's prefetched slab.
+  constexpr uint32_t kDrop = 0x80000000u;   // > any valid byte offset (N <= 2^20, 256 rows)
+  constexpr int SP = 272;                    // staging row pitch, bytes (16-byte aligned, 4-bank skew)
+  constexpr int CPS = sizeof(TOut) == 2 ? 4 : 2;   // MFMA column tiles per pass: 256 bytes of row
+  constexpr int NPASS = FM * FN / CPS;
+  constexpr int CW = 16 / (int)sizeof(TOut);       // columns per 16-byte chunk
+  static_assert(NT == 512 && WM * WN == 8 && 32 * SP <= BM * LP * (int)sizeof(bf16) / 4,
+                "each wavefront stages 32 rows in a quarter of one operand buffer");
+  // byte offset of this lane's first chunk inside a wavefront tile (row lane/16, 16-byte chunk
+  // lane%16)
+  const uint32_t lane_off =
+      ((uint32_t)(wm * TM + (lane >> 4)) * (uint32_t)N + (uint32_t)(wn * TN + (lane & 15) * CW)) * (uint32_t)sizeof(TOut);
+  auto epilogue = [&] {
     int64_t mt_e; int nt_e; decode(slot, mt_e, nt_e);
     const int64_t m0 = mt_e * BM;
     const int n0 = nt_e * BN;
+    const uint32_t rows = (uint32_t)min((int64_t)BM, M - m0);
+    const int nbytes = (int)(rows * (uint32_t)N * sizeof(TOut));
+    const __amdgpu_buffer_rsrc_t o_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(out + m0 * N), (short)0, nbytes, 0x00020000);
+    __amdgpu_buffer_rsrc_t r_rsrc = o_rsrc;
+    if constexpr (EPI == MTGR_EPI_RESIDUAL_F32)
+      r_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(resid + m0 * N), (short)0, nbytes, 0x00020000);
+    // this wavefront's staging region: a quarter of the operand buffer the last slab used
+    char* stage = (wave < 4 ? reinterpret_cast<char*>(&As[cur ^ 1][0][0])
+                            : reinterpret_cast<char*>(&Bs[cur ^ 1][0][0])) + (wave & 3) * (BM * LP * (int)sizeof(bf16) / 4);
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t m = m0 + wm * TM + i * 32 + l32;
-      if (m >= M) continue;
+    for (int p = 0; p < NPASS; ++p) {
+      const int i = p / (FN / CPS), j0 = (p % (FN / CPS)) * CPS;
+      // Chunk it of this lane covers row i*32 + it*4 + lane/16 of the wavefront tile and columns
+      // j0*32 + (lane%16)*CW .. +CW-1: a per-lane byte offset (one VGPR, or kDrop when the chunk
+      // lies past column N) plus a wavefront-uniform offset in an SGPR.
+      const bool col_ok = n0 + wn * TN + j0 * 32 + (lane & 15) * CW < N;
+      const uint32_t vo_c = col_ok ? lane_off : kDrop;
+      auto s_off = [&](int it) {
+        return (uint32_t)((i * 32 + it * 4) * N + n0 + j0 * 32) * (uint32_t)sizeof(TOut);
+      };
+      // A VALU write to the data registers of a >8-byte buffer store needs a wait state after
+      // the store; the compiler omits it when the store's SGPR offset field holds a register, but
+      // gfx950 corrupts the stored data without it, so it is inserted here.
+      auto store_chunk = [&](u32x4 c, int it) {
+        __builtin_amdgcn_raw_buffer_store_b128(c, o_rsrc, vo_c, s_off(it), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 1");
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      f32x4 rq[8];
+      if constexpr (EPI == MTGR_EPI_RESIDUAL_F32) {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
+        for (int it = 0; it < 8; ++it)
+          rq[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r_rsrc, vo_c, s_off(it), 0));
+      }
+      // registers -> LDS: row l32, columns jj*32 + 8g + 4hh .. +3 of this pass
+#pragma unroll
+      for (int jj = 0; jj < CPS; ++jj) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int n = n0 + wn * TN + j * 32 + 8 * g + 4 * hh;
-          if (n >= N) continue;
+          const int cl = jj * 32 + 8 * g + 4 * hh;
           float v[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = acc[i][j][4 * g + e];
-          if (bias) {
-            const bf16x4 b4 = *reinterpret_cast<const bf16x4*>(bias + n);
+          for (int e = 0; e < 4; ++e) v[e] = acc[i][j0 + jj][4 * g + e];
+          if constexpr (EPI == MTGR_EPI_SILU) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] += (float)b4[e];
+            for (int e = 0; e < 4; ++e) v[e] = silu_rcp(v[e]);
           }
-          store4<EPI, TOut>(out, resid, m * N + n, v);
+          char* dst = stage + l32 * SP + cl * (int)sizeof(TOut);
+          if constexpr (sizeof(TOut) == 4) {
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = v[e];
+            *reinterpret_cast<f32x4*>(dst) = o;
+          } else {
+            bf16x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (bf16)v[e];
+            *reinterpret_cast<bf16x4*>(dst) = o;
+          }
         }
       }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      // LDS -> global: 32 rows x 256 bytes = 512 chunks, 8 per lane, in two groups of four to
+      // bound the registers in flight
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        if (it == 4) __builtin_amdgcn_sched_barrier(0);
+        const int q = it * 64 + lane;
+        u32x4 c = *reinterpret_cast<const u32x4*>(stage + (q / 16) * SP + (q % 16) * 16);
+        if constexpr (EPI == MTGR_EPI_RESIDUAL_F32) {
+          f32x4 f = __builtin_bit_cast(f32x4, c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) f[e] += rq[it][e];
+          c = __builtin_bit_cast(u32x4, f);
+        }
+        store_chunk(c, it);
+      }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
+    // the next slab write reuses the staging buffer: every wavefront must be done with it
+    lds_barrier();
+  };
+
+  // The tile loop is rotated so that each epilogue runs straight into the first slab of the next
+  // tile with no control-flow merge between them (a merge would make the compiler's wait before
+  // that slab's LDS write conservative again).
+  init_acc();
+  for (int kt = 0; kt < nk; ++kt) slab(kt);
+  while (true) {
+    epilogue();
     if (!more_tiles) break;
     slot = next;
     next = next_slot(slot);
     r_cur = r_nxt;
     if (next < nslots) r_nxt = make_rsrc(next);
+    more_tiles = next < nslots;
+    init_acc();
+    read_frags(cur, 0, 0);
+    slab(0);
+    for (int kt = 1; kt < nk; ++kt) slab(kt);
   }
 }
 
@@ -314,7 +440,7 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int64_t M, int N, int K,
 template <int WM, int WN, int EPI, typename TOut>
 hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf16* w,
                                const bf16* bias, const float* resid, void* out, hipStream_t s) {
-  constexpr size_t lds = 2 * (size_t)(256 + 256) * (64 + 8) * sizeof(bf16);
+  constexpr size_t lds = 2 * (size_t)(256 + 256) * (64 + 8) * sizeof(bf16) + kBiasLds * sizeof(bf16);
   auto kern = k_gemm_bf16_persistent<WM, WN, EPI, TOut>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -324,7 +450,9 @@ hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf1
     attr_set = true;
   }
   int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
   const int nN = (N + 255) / 256;
   const int64_t nM = (M + 255) / 256;
   const int64_t tiles_pad = (nM + kXcd - 1) / kXcd * kXcd * nN;

@@ -165,7 +165,7 @@ mtgr_status mtgr_groupln_fwd(const mtgr_batch* b, int32_t d, int32_t in_dtype, i
                              const void* beta, float eps, const void* x, void* y, void* stream);
 
 /* out = epilogue(a[M][K] W[N][K]^T + bias[N]); a, W, bias in `dtype`; see MTGR_EPI_*.
- * bf16: K a multiple of 64 and >= 128, N a multiple of 4.  fp32: K a multiple of 4. */
+ * bf16: K a multiple of 64 and >= 128, N a multiple of 8.  fp32: K a multiple of 4. */
 mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int32_t epilogue,
                             const void* a, const void* w, const void* bias, const float* resid,
                             void* out, void* stream);

@@ -114,6 +114,7 @@ def test_linear_and_groupln_argument_checks():
     assert L.mtgr_linear_fwd(100, 64, 100, M.MTGR_BF16, 0, FAKE, FAKE, None, None, FAKE, None) == 2
     assert L.mtgr_linear_fwd(100, 64, 64, M.MTGR_BF16, 0, FAKE, FAKE, None, None, FAKE, None) == 2   # one K slab
     assert L.mtgr_linear_fwd(100, 66, 128, M.MTGR_BF16, 0, FAKE, FAKE, None, None, FAKE, None) == 2  # N % 4
+    assert L.mtgr_linear_fwd(100, 132, 128, M.MTGR_BF16, 0, FAKE, FAKE, None, None, FAKE, None) == 2  # N % 8
     assert L.mtgr_linear_fwd(100, 64, 128, M.MTGR_BF16, 9, FAKE, FAKE, None, None, FAKE, None) == 4
     assert L.mtgr_linear_fwd(100, 64, 128, M.MTGR_BF16, 2, FAKE, FAKE, None, None, FAKE, None) == 1
     assert L.mtgr_linear_fwd(0, 64, 128, M.MTGR_BF16, 0, None, None, None, None, None, None) == 0

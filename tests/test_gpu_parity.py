@@ -162,10 +162,13 @@ def test_groupln_parity(kin, kout, d, shared):
     assert rel_err(to_np(y), ref) < tol
 
 
-@pytest.mark.parametrize("M_,N,K,epi", [(1000, 256, 128, 0), (3001, 96, 256, 1), (777, 768, 3072, 2),
-                                        (130, 3072, 768, 0), (1, 64, 128, 1), (4097, 128, 512, 2),
-                                        (70000, 1540, 192, 1)])
-def test_linear_bf16_parity(M_, N, K, epi):
+# N > 4096 takes the per-tile bias slice path; N % 256 != 0 leaves a ragged last column tile
+@pytest.mark.parametrize("M_,N,K,epi,with_bias", [
+    (1000, 256, 128, 0, True), (3001, 96, 256, 1, True), (777, 768, 3072, 2, True),
+    (130, 3072, 768, 0, True), (1, 64, 128, 1, True), (4097, 128, 512, 2, True),
+    (70000, 1544, 192, 1, True), (3000, 4104, 128, 1, True), (600, 4352, 128, 2, True),
+    (2049, 776, 256, 0, False), (513, 392, 256, 2, False)])
+def test_linear_bf16_parity(M_, N, K, epi, with_bias):
     rng = np.random.default_rng(M_ + N + K)
     a = synth.round_to_bf16(rng.standard_normal((M_, K)).astype(np.float32))
     w = synth.round_to_bf16((rng.standard_normal((N, K)) / np.sqrt(K)).astype(np.float32))
@@ -173,9 +176,13 @@ def test_linear_bf16_parity(M_, N, K, epi):
     resid = rng.standard_normal((M_, N)).astype(np.float32)
     ad, wd, bd = (torch.from_numpy(v).to(DEV).to(torch.bfloat16) for v in (a, w, bias))
     rd = torch.from_numpy(resid).to(DEV)
-    out = torch.zeros(M_, N, dtype=torch.float32 if epi == 2 else torch.bfloat16, device=DEV)
-    M.mtgr_linear_fwd(M_, N, K, M.MTGR_BF16, epi, ad, wd, bd, rd if epi == 2 else None, out)
-    ref = O.linear(a, w, bias)
+    # a guard row past the output: nothing may be written outside out[:M_]
+    full = torch.full((M_ + 1, N), 7.0, dtype=torch.float32 if epi == 2 else torch.bfloat16, device=DEV)
+    out = full[:M_]
+    M.mtgr_linear_fwd(M_, N, K, M.MTGR_BF16, epi, ad, wd, bd if with_bias else None,
+                      rd if epi == 2 else None, out)
+    assert bool((full[M_] == 7.0).all())
+    ref = O.linear(a, w, bias if with_bias else None)
     if epi == 1:
         ref = O.silu(ref)
     if epi == 2:
