@@ -134,3 +134,11 @@ def test_empty_batch_is_a_no_op():
     b = M.MtgrBatch(0, 0, 0, off.ctypes.data, None, None, None)
     blk = _block()
     assert M.lib().mtgr_block_fwd(ctypes.byref(blk), ctypes.byref(b), None, None, FAKE, 1 << 20, None) == 0
+
+
+def test_library_has_no_undefined_internal_symbols():
+    # a kernel whose host-side launch stub was not emitted shows up as an undefined mtgr:: symbol
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", M.LIB_PATH], capture_output=True, text=True).stdout
+    bad = [line for line in out.splitlines() if "mtgr" in line]
+    assert not bad, bad
