@@ -41,6 +41,8 @@ from [P1] and [P5], GroupLN invariants and torch layer_norm, closed forms and li
 of the attention, silu against torch, a special case of the head, and permutation / independence /
 isolation / temporal-replay invariants).  The readings R3, R8, R9 and R10 are parity unpinned with
 respect to the paper: the pages never fix them, so they are pinned only by construction.
+The block backward (the chain rule of the same equations) is pinned by central finite differences
+of block_forward and by autograd of an independent torch formulation of the block.
 """
 from __future__ import annotations
 
@@ -50,6 +52,7 @@ from typing import Dict, List, Optional, Sequence, Tuple
 import numpy as np
 
 G_U, G_S, G_R, G_C = 0, 1, 2, 3
+NUM_GROUPS = 4
 
 
 # ----------------------------------------------------------------------------------------------
@@ -219,3 +222,135 @@ def params_layers(params) -> List[Dict[str, np.ndarray]]:
 
 def params_head(params) -> Dict[str, np.ndarray]:
     return {k: np.asarray(v, dtype=np.float64) for k, v in params.head.items()}
+
+
+# ----------------------------------------------------------------------------------------------
+# Backward pass of one block (the training direction of the same update equations, [P3] 方法).
+# Plain chain rule, float64, one user at a time; parameter gradients are sums over tokens.
+# ----------------------------------------------------------------------------------------------
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d silu / dz = sigma(z) (1 + z (1 - sigma(z)))."""
+    z = np.asarray(z, dtype=np.float64)
+    s = 1.0 / (1.0 + np.exp(-z))
+    return s * (1.0 + z * (1.0 - s))
+
+
+def linear_backward(x: np.ndarray, w: np.ndarray, dy: np.ndarray):
+    """y = x W^T + b  ->  (dx = dy W, dW = dy^T x, db = sum_rows dy)."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    return dy @ w, dy.T @ x, dy.sum(axis=0)
+
+
+def group_layer_norm_backward(x: np.ndarray, groups: np.ndarray, gamma: np.ndarray, dy: np.ndarray,
+                              eps: float = 1e-5, shared: bool = False):
+    """Gradients of group_layer_norm: (dx [n, d], dgamma [4, d], dbeta [4, d]).
+
+    With xhat = (x - mean) / s, s = sqrt(var + eps) (biased var over the d features):
+        dxhat = dy * gamma[g];  dx = (dxhat - mean(dxhat) - xhat * mean(dxhat * xhat)) / s.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    n, d = x.shape
+    g = np.zeros(n, dtype=np.int64) if shared else np.asarray(groups, dtype=np.int64)
+    mean = x.mean(axis=1, keepdims=True)
+    s = np.sqrt(((x - mean) ** 2).mean(axis=1, keepdims=True) + eps)
+    xhat = (x - mean) / s
+    dgamma = np.zeros((NUM_GROUPS, d))
+    dbeta = np.zeros((NUM_GROUPS, d))
+    for grp in range(NUM_GROUPS):
+        sel = g == grp
+        dgamma[grp] = (dy[sel] * xhat[sel]).sum(axis=0)
+        dbeta[grp] = dy[sel].sum(axis=0)
+    dxhat = dy * gamma[g]
+    dx = (dxhat - dxhat.mean(axis=1, keepdims=True)
+          - xhat * (dxhat * xhat).mean(axis=1, keepdims=True)) / s
+    return dx, dgamma, dbeta
+
+
+def hstu_attention_backward(qkvu: np.ndarray, groups: np.ndarray, times: np.ndarray,
+                            num_heads: int, dy: np.ndarray, mask_mode: str = "dynamic") -> np.ndarray:
+    """Gradient of hstu_attention w.r.t. qkvu [n, 4d] given dy = d loss / d (V~ (.) U).
+
+    dV~ = dy (.) U and dU = dy (.) V~; per head, with A = silu(S) / N (.) M and S = Q K^T:
+        dV = A^T dV~,  dA = dV~ V^T,  dS = dA (.) M / N (.) silu'(S),  dQ = dS K,  dK = dS^T Q.
+    """
+    qkvu = np.asarray(qkvu, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    n, four_d = qkvu.shape
+    d = four_d // 4
+    dh = d // num_heads
+    dq = np.zeros((n, four_d))
+    if n == 0:
+        return dq
+    Q, K, V, U = qkvu[:, :d], qkvu[:, d:2 * d], qkvu[:, 2 * d:3 * d], qkvu[:, 3 * d:]
+    M = mask(groups, times, mask_mode).astype(np.float64)
+    N = float(n)
+    vt = np.empty((n, d))
+    for h in range(num_heads):
+        sl = slice(h * dh, (h + 1) * dh)
+        S = Q[:, sl] @ K[:, sl].T
+        A = silu(S) / N * M
+        vt[:, sl] = A @ V[:, sl]
+        dvt = dy[:, sl] * U[:, sl]
+        dA = dvt @ V[:, sl].T
+        dS = dA * M / N * silu_grad(S)
+        dq[:, sl] = dS @ K[:, sl]
+        dq[:, d + h * dh:d + (h + 1) * dh] = dS.T @ Q[:, sl]
+        dq[:, 2 * d + h * dh:2 * d + (h + 1) * dh] = A.T @ dvt
+    dq[:, 3 * d:] = dy * vt
+    return dq
+
+
+BLOCK_PARAM_NAMES = ("gln1_gamma", "gln1_beta", "w_qkvu", "b_qkvu", "gln2_gamma", "gln2_beta",
+                     "w_mlp1", "b_mlp1", "w_mlp2", "b_mlp2")
+
+
+def block_backward(x: np.ndarray, groups: np.ndarray, times: np.ndarray, layer: Dict[str, np.ndarray],
+                   num_heads: int, dout: np.ndarray, eps: float = 1e-5, mask_mode: str = "dynamic",
+                   shared_norm: bool = False):
+    """Gradients of block_forward for one user given dout = d loss / d out.
+
+    Returns (dx [n, d], grads) with grads[name] shaped like the parameter (biases included even
+    when the layer has none).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    _, parts = block_forward(x, groups, times, layer, num_heads, eps, return_parts=True,
+                             mask_mode=mask_mode, shared_norm=shared_norm)
+    a = linear(parts["z"], layer["w_mlp1"], layer.get("b_mlp1"))     # MLP1 pre-activation
+    grads = {}
+    dhid, grads["w_mlp2"], grads["b_mlp2"] = linear_backward(parts["hid"], layer["w_mlp2"], dout)
+    da = dhid * silu_grad(a)
+    dz, grads["w_mlp1"], grads["b_mlp1"] = linear_backward(parts["z"], layer["w_mlp1"], da)
+    dy, grads["gln2_gamma"], grads["gln2_beta"] = group_layer_norm_backward(
+        parts["y"], groups, layer["gln2_gamma"], dz, eps, shared_norm)
+    dqkvu = hstu_attention_backward(parts["qkvu"], groups, times, num_heads, dy, mask_mode)
+    dxt, grads["w_qkvu"], grads["b_qkvu"] = linear_backward(parts["xt"], layer["w_qkvu"], dqkvu)
+    dx1, grads["gln1_gamma"], grads["gln1_beta"] = group_layer_norm_backward(
+        x, groups, layer["gln1_gamma"], dxt, eps, shared_norm)
+    return dout + dx1, grads
+
+
+def block_backward_batch(offsets: np.ndarray, groups: np.ndarray, times: np.ndarray, x: np.ndarray,
+                         layer: Dict[str, np.ndarray], num_heads: int, dout: np.ndarray,
+                         eps: float = 1e-5, mask_mode: str = "dynamic", shared_norm: bool = False):
+    """block_backward over a packed batch: dx per token, parameter gradients summed over users."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    x = np.asarray(x, dtype=np.float64)
+    dx = np.zeros_like(x)
+    total = None
+    for b in range(offsets.shape[0] - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if hi == lo:
+            continue
+        dxb, g = block_backward(x[lo:hi], groups[lo:hi], times[lo:hi], layer, num_heads, dout[lo:hi],
+                                eps, mask_mode, shared_norm)
+        dx[lo:hi] = dxb
+        total = g if total is None else {k: total[k] + g[k] for k in g}
+    if total is None:
+        total = {k: np.zeros_like(np.asarray(layer[k] if layer.get(k) is not None else 0.0, dtype=np.float64))
+                 for k in BLOCK_PARAM_NAMES if layer.get(k) is not None}
+    return dx, total

@@ -421,3 +421,109 @@ def test_full_mask_attention_is_dense_and_causal_is_tril():
     causal = _torch_silu_attention(q, k, v, u, np.tril(np.ones((n, n))), n)
     np.testing.assert_allclose(O.hstu_attention(qkvu, g, t, 1, "full"), full, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(O.hstu_attention(qkvu, g, t, 1, "causal"), causal, rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------------------
+# Block backward: finite differences and autograd of an independent torch formulation
+# ------------------------------------------------------------------------------------------
+def _tiny_block(seed=90, d=16, H=2, h=24, with_bias=True):
+    rng = np.random.default_rng(seed)
+    g = np.array([0, 1, 1, 1, 2, 2, 2, 2, 3, 3, 3], np.uint8)
+    n = g.shape[0]
+    t = np.concatenate([np.full(4, -np.inf), rng.uniform(0, 10, 4), rng.uniform(0, 10, 3)]).astype(np.float32)
+    x = rng.standard_normal((n, d)) * np.array([1, .5, .5, .5, 2, 2, 2, 2, 4, 4, 4])[:, None]
+    lay = {
+        "gln1_gamma": rng.uniform(0.5, 1.5, (4, d)), "gln1_beta": rng.uniform(-0.1, 0.1, (4, d)),
+        "w_qkvu": rng.standard_normal((4 * d, d)) / np.sqrt(d),
+        "b_qkvu": rng.uniform(-0.2, 0.2, 4 * d) if with_bias else None,
+        "gln2_gamma": rng.uniform(0.5, 1.5, (4, d)), "gln2_beta": rng.uniform(-0.1, 0.1, (4, d)),
+        "w_mlp1": rng.standard_normal((h, d)) / np.sqrt(d),
+        "b_mlp1": rng.uniform(-0.2, 0.2, h) if with_bias else None,
+        "w_mlp2": rng.standard_normal((d, h)) / np.sqrt(h),
+        "b_mlp2": rng.uniform(-0.2, 0.2, d) if with_bias else None,
+    }
+    lay["w_qkvu"][:2 * d] *= 2.0          # scores of order a few: the curved part of silu
+    dout = rng.standard_normal((n, d))
+    return g, t, x, lay, dout, H
+
+
+@pytest.mark.parametrize("mask_mode,shared", [("dynamic", False), ("causal", True), ("full", False)])
+def test_block_backward_matches_finite_differences(mask_mode, shared):
+    g, t, x, lay, dout, H = _tiny_block()
+    dx, grads = O.block_backward(x, g, t, lay, H, dout, mask_mode=mask_mode, shared_norm=shared)
+    rng = np.random.default_rng(91)
+
+    def loss(xx, ll):
+        return float((O.block_forward(xx, g, t, ll, H, mask_mode=mask_mode, shared_norm=shared) * dout).sum())
+
+    eps = 1e-6
+    # directional derivative along a random direction, for the input and every parameter tensor
+    for name in ("x",) + O.BLOCK_PARAM_NAMES:
+        base = x if name == "x" else lay[name]
+        v = rng.standard_normal(base.shape)
+        if name == "x":
+            fd = (loss(x + eps * v, lay) - loss(x - eps * v, lay)) / (2 * eps)
+            an = float((dx * v).sum())
+        else:
+            lp, lm = dict(lay), dict(lay)
+            lp[name], lm[name] = base + eps * v, base - eps * v
+            fd = (loss(x, lp) - loss(x, lm)) / (2 * eps)
+            an = float((grads[name] * v).sum())
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(fd)), (name, fd, an)
+
+
+def test_block_backward_matches_torch_autograd():
+    g, t, x, lay, dout, H = _tiny_block(seed=92)
+    dx, grads = O.block_backward(x, g, t, lay, H, dout)
+    # independent formulation: torch ops on the whole user, dense mask tensor built here from the
+    # three rules, per-group affine by gather, autograd for every gradient
+    T = torch.float64
+    gt = torch.from_numpy(g.astype(np.int64))
+    tt = torch.from_numpy(t.astype(np.float64))
+    n, d = x.shape
+    static_key = (gt == 0) | (gt == 1)
+    rc_query = (gt == 2) | (gt == 3)
+    r_key = gt == 2
+    vis = static_key[None, :] | torch.eye(n, dtype=torch.bool) | (
+        rc_query[:, None] & r_key[None, :] & (tt[None, :] < tt[:, None]))
+    P = {k: torch.tensor(v, dtype=T, requires_grad=True) for k, v in lay.items() if v is not None}
+    xt_ = torch.tensor(x, dtype=T, requires_grad=True)
+
+    def gln(v, gamma, beta):
+        return torch.nn.functional.layer_norm(v, (d,), eps=1e-5) * gamma[gt] + beta[gt]
+
+    a1 = gln(xt_, P["gln1_gamma"], P["gln1_beta"])
+    qkvu = a1 @ P["w_qkvu"].T + P["b_qkvu"]
+    q, k, v, u = qkvu.split(d, dim=1)
+    dh = d // H
+    heads = []
+    for hh in range(H):
+        sl = slice(hh * dh, (hh + 1) * dh)
+        s = q[:, sl] @ k[:, sl].T
+        heads.append((torch.nn.functional.silu(s) * vis / n) @ v[:, sl])
+    y = torch.cat(heads, dim=1) * u
+    z = gln(y, P["gln2_gamma"], P["gln2_beta"])
+    out = torch.nn.functional.silu(z @ P["w_mlp1"].T + P["b_mlp1"]) @ P["w_mlp2"].T + P["b_mlp2"] + xt_
+    (out * torch.from_numpy(dout)).sum().backward()
+    np.testing.assert_allclose(dx, xt_.grad.numpy(), rtol=1e-10, atol=1e-12)
+    for name, p in P.items():
+        np.testing.assert_allclose(grads[name], p.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def test_block_backward_batch_sums_users_and_isolates_them():
+    g, t, x, lay, dout, H = _tiny_block(seed=93)
+    n = g.shape[0]
+    offsets = np.array([0, n, 2 * n])
+    x2 = np.concatenate([x, x[::-1].copy()])
+    g2 = np.concatenate([g, g])
+    t2 = np.concatenate([t, t])
+    rng = np.random.default_rng(94)
+    x2[n:] = rng.standard_normal((n, x.shape[1]))
+    d2 = np.concatenate([dout, rng.standard_normal(dout.shape)])
+    dx, grads = O.block_backward_batch(offsets, g2, t2, x2, lay, H, d2)
+    dxa, ga = O.block_backward(x2[:n], g, t, lay, H, d2[:n])
+    dxb, gb = O.block_backward(x2[n:], g, t, lay, H, d2[n:])
+    np.testing.assert_array_equal(dx[:n], dxa)
+    np.testing.assert_array_equal(dx[n:], dxb)
+    for k in grads:
+        np.testing.assert_allclose(grads[k], ga[k] + gb[k], rtol=0, atol=1e-12)
