@@ -207,15 +207,17 @@ hipError_t linear(int64_t M, int N, int K, int dtype, int epi, const void* a, co
 }
 
 hipError_t attention(const mtgr_batch* b, int d, int H, int dtype, int mask_mode,
-                     const PrepBufs& pb, const void* qkvu, void* y, hipStream_t s) {
+                     const PrepBufs& pb, const void* qkvu, void* y, hipStream_t s,
+                     void* vt = nullptr) {
   if (dtype == MTGR_BF16)
     return launch_attention_bf16(b->num_users, xcd_grid_slots(b, H, kAttnQTileBf16), d, H,
                                  mask_mode, b->offsets, pb.seg, pb.order, pb.xcd_off, b->timestamps,
-                                 static_cast<const bf16*>(qkvu), static_cast<bf16*>(y), s);
+                                 static_cast<const bf16*>(qkvu), static_cast<bf16*>(y),
+                                 static_cast<bf16*>(vt), s);
   const int64_t tiles = total_tiles(b, kAttnQTileF32);
   return launch_attention_f32(b->num_users, tiles, d, H, mask_mode, b->offsets, pb.seg, pb.order,
                               pb.tile_off, b->timestamps, static_cast<const float*>(qkvu),
-                              static_cast<float*>(y), s);
+                              static_cast<float*>(y), static_cast<float*>(vt), s);
 }
 
 // One block: x_out = x_in + MLP(GLN2(attn(GLN1(x_in)) (.) U)); x_out may alias x_in.
@@ -242,6 +244,168 @@ hipError_t run_block(const mtgr_block_params* p, const mtgr_batch* b, const Prep
   e = linear(T, h, d, dt, MTGR_EPI_SILU, xt, p->w_mlp1, p->b_mlp1, nullptr, big, s);
   if (e != hipSuccess) return e;
   return linear(T, d, h, dt, MTGR_EPI_RESIDUAL_F32, big, p->w_mlp2, p->b_mlp2, x_in, x_out, s);
+}
+
+// ---- backward ----------------------------------------------------------------------------------
+// Workspace of mtgr_block_bwd after the prep buffers: the recomputed forward activations, the
+// activation gradients, transposed copies for the weight-gradient GEMMs (token axis last, padded
+// to Tp with zeros, plus a ones row whose product gives the bias gradient), one transposed weight,
+// and fp32 partial sums (split-K slices of the weight gradients, per-wavefront GroupLN slots).
+struct BwdPlan {
+  Plan prep;
+  size_t xt = 0, qkvu = 0, y = 0, vt = 0, z = 0, a = 0, hid = 0, dout = 0, dhid = 0, dz = 0;
+  size_t dqkvu = 0, ta = 0, tb = 0, wt = 0, part = 0, gpart = 0, total = 0;
+  int ks = 1;
+  int64_t Tp = 0;
+};
+
+constexpr int64_t kMaxBwdTokens = 4000000;
+
+inline int64_t tiles256(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
+
+BwdPlan make_bwd_plan(const Sizes& z) {
+  BwdPlan p;
+  p.prep = make_plan(z);
+  size_t off = p.prep.total;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  const size_t es = esize(z.dtype);
+  const size_t T = (size_t)z.T, d = (size_t)z.d, h = (size_t)z.h;
+  // split count of the weight-gradient GEMMs: enough output tiles to cover the CUs, each split at
+  // least 2048 tokens long
+  const int64_t tmin = std::min({tiles256(d, h + 8), tiles256(h, d + 8), tiles256(4 * d, d + 8)});
+  p.ks = 1;
+  while (p.ks < 32 && tmin * p.ks * 2 <= 512 && z.T >= (int64_t)p.ks * 2 * 2048) p.ks *= 2;
+  const int64_t unit = 64 * (int64_t)p.ks;
+  p.Tp = std::max((z.T + unit - 1) / unit * unit, 2 * unit);
+  p.xt = take(T * d * es);
+  p.qkvu = take(T * 4 * d * es);
+  p.y = take(T * d * es);
+  p.vt = take(T * d * es);
+  p.z = take(T * d * es);
+  p.a = take(T * h * es);
+  p.hid = take(T * h * es);
+  p.dout = take(z.dtype == MTGR_BF16 ? T * d * es : 0);
+  p.dhid = take(T * h * es);
+  p.dz = take(T * d * es);
+  p.dqkvu = take(T * 4 * d * es);
+  p.ta = take(std::max({d, h, 4 * d}) * (size_t)p.Tp * es);
+  p.tb = take((std::max(d, h) + 8) * (size_t)p.Tp * es);
+  p.wt = take(std::max(h * d, 4 * d * d) * es);
+  p.part = take((size_t)p.ks * std::max({d * (h + 8), h * (d + 8), 4 * d * (d + 8)}) * sizeof(float));
+  p.gpart = take((size_t)groupln_bwd_waves(z.T) * 8 * d * sizeof(float));
+  p.total = off;
+  return p;
+}
+
+// dW [M][K] (+ db [M]) = sum over tokens of dy^T x, from the transposed operands at and bt
+// ([M][Tp] and [K+8][Tp], the row K of bt all ones) by split-K GEMMs and a fixed-order reduction.
+hipError_t weight_grad(const BwdPlan& pl, void* ws, int dtype, int M, int K, const void* at_,
+                       const void* bt_, float* dw, float* db, hipStream_t s) {
+  float* part = at<float>(ws, pl.part);
+  const int Kx = K + 8;
+  hipError_t e;
+  if (dtype == MTGR_BF16)
+    e = launch_gemm_bf16_splitk(M, Kx, (int)pl.Tp, pl.ks, static_cast<const bf16*>(at_),
+                                static_cast<const bf16*>(bt_), part, s);
+  else
+    e = launch_gemm_f32_splitk(M, Kx, (int)pl.Tp, pl.ks, static_cast<const float*>(at_),
+                               static_cast<const float*>(bt_), part, s);
+  if (e != hipSuccess) return e;
+  return launch_reduce_wb(M, K, Kx, pl.ks, part, dw, db, s);
+}
+
+// GroupLN parameter gradients from the per-wavefront slots [waves][2][4][d].
+hipError_t gln_param_grads(int64_t T, int d, const float* gpart, float* dgamma, float* dbeta,
+                           hipStream_t s) {
+  const int waves = T > 0 ? groupln_bwd_waves(T) : 0;
+  hipError_t e = launch_reduce(4 * (int64_t)d, waves, 8 * (int64_t)d, gpart, dgamma, s);
+  if (e != hipSuccess) return e;
+  return launch_reduce(4 * (int64_t)d, waves, 8 * (int64_t)d, gpart ? gpart + 4 * d : nullptr, dbeta, s);
+}
+
+hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const BwdPlan& pl,
+                         void* ws, const float* x_in, const float* dx_out, float* dx_in,
+                         const mtgr_block_grads* g, hipStream_t s) {
+  const int64_t T = b->num_tokens;
+  const int d = p->d_model, h = p->mlp_hidden, dt = p->dtype, H = p->num_heads;
+  const int act = dt == MTGR_BF16 ? 1 : 0;
+  const int shared = p->norm_mode == MTGR_NORM_SHARED;
+  const PrepBufs pb = prep_bufs(ws, pl.prep);
+  void* xt = at<void>(ws, pl.xt);
+  void* qkvu = at<void>(ws, pl.qkvu);
+  void* y = at<void>(ws, pl.y);
+  void* vt = at<void>(ws, pl.vt);
+  void* z = at<void>(ws, pl.z);
+  void* a = at<void>(ws, pl.a);
+  void* hid = at<void>(ws, pl.hid);
+  void* dhid = at<void>(ws, pl.dhid);
+  void* dz = at<void>(ws, pl.dz);
+  void* dqkvu = at<void>(ws, pl.dqkvu);
+  void* ta = at<void>(ws, pl.ta);
+  void* tb = at<void>(ws, pl.tb);
+  void* wt = at<void>(ws, pl.wt);
+  float* gpart = at<float>(ws, pl.gpart);
+  const int q_tile = q_tile_for(dt);
+  hipError_t e;
+#define MTGR_BWD_TRY(expr)              \
+  do {                                  \
+    e = (expr);                         \
+    if (e != hipSuccess) return e;      \
+  } while (0)
+  MTGR_BWD_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile, H, pb, false, s));
+  // forward, keeping what the backward needs: GLN1 output, QKVU, V~, the gated output, GLN2
+  // output, the MLP pre-activation and its SiLU
+  MTGR_BWD_TRY(launch_groupln(T, d, 0, act, act, shared, x_in, b->group_ids, p->gln1_gamma,
+                              p->gln1_beta, p->ln_eps, xt, s));
+  MTGR_BWD_TRY(linear(T, 4 * d, d, dt, MTGR_EPI_STORE, xt, p->w_qkvu, p->b_qkvu, nullptr, qkvu, s));
+  MTGR_BWD_TRY(attention(b, d, H, dt, p->mask_mode, pb, qkvu, y, s, vt));
+  MTGR_BWD_TRY(launch_groupln(T, d, act, act, act, shared, y, b->group_ids, p->gln2_gamma,
+                              p->gln2_beta, p->ln_eps, z, s));
+  MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, z, p->w_mlp1, p->b_mlp1, nullptr, a, s));
+  MTGR_BWD_TRY(launch_silu(T * h, act, a, hid, s));
+
+  // MLP2: dhid = dout W2, dW2 = dout^T hid, db2 = sum dout
+  const void* dout = dx_out;
+  if (act) {
+    MTGR_BWD_TRY(launch_convert(T * d, act, dx_out, at<void>(ws, pl.dout), s));
+    dout = at<void>(ws, pl.dout);
+  }
+  MTGR_BWD_TRY(launch_transpose(d, h, d, 0, act, p->w_mlp2, wt, s));
+  MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, dout, wt, nullptr, nullptr, dhid, s));
+  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 0, act, dout, ta, s));
+  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp, 1, act, hid, tb, s));
+  MTGR_BWD_TRY(weight_grad(pl, ws, dt, d, h, ta, tb, g->w_mlp2, g->b_mlp2, s));
+  // MLP1: da = dhid (.) silu'(a) (in place), dz = da W1, dW1 = da^T z, db1 = sum da
+  MTGR_BWD_TRY(launch_silu_bwd(T * h, act, a, dhid, s));
+  MTGR_BWD_TRY(launch_transpose(h, d, h, 0, act, p->w_mlp1, wt, s));
+  MTGR_BWD_TRY(linear(T, d, h, dt, MTGR_EPI_STORE, dhid, wt, nullptr, nullptr, dz, s));
+  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp, 0, act, dhid, ta, s));
+  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 1, act, z, tb, s));
+  MTGR_BWD_TRY(weight_grad(pl, ws, dt, h, d, ta, tb, g->w_mlp1, g->b_mlp1, s));
+  // GLN2: dy (in place over dz) and the GLN2 parameter gradients
+  MTGR_BWD_TRY(launch_groupln_bwd(T, d, act, act, shared, y, b->group_ids, p->gln2_gamma, p->ln_eps,
+                                  dz, nullptr, dz, act, gpart, s));
+  MTGR_BWD_TRY(gln_param_grads(T, d, gpart, g->gln2_gamma, g->gln2_beta, s));
+  // gate and attention: dqkvu from qkvu, V~ and dy
+  MTGR_BWD_TRY(launch_attention_bwd_ref(b->num_users, total_tiles(b, q_tile), q_tile, d, H,
+                                        p->mask_mode, act, b->offsets, pb.seg, pb.order, pb.tile_off,
+                                        b->timestamps, qkvu, vt, dz, dqkvu, s));
+  // QKVU: dxt = dqkvu W_qkvu (over dz), dW_qkvu = dqkvu^T xt, db_qkvu = sum dqkvu
+  MTGR_BWD_TRY(launch_transpose(4 * (int64_t)d, d, 4 * (int64_t)d, 0, act, p->w_qkvu, wt, s));
+  MTGR_BWD_TRY(linear(T, d, 4 * d, dt, MTGR_EPI_STORE, dqkvu, wt, nullptr, nullptr, dz, s));
+  MTGR_BWD_TRY(launch_transpose(T, 4 * d, pl.Tp, 0, act, dqkvu, ta, s));
+  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 1, act, xt, tb, s));
+  MTGR_BWD_TRY(weight_grad(pl, ws, dt, 4 * d, d, ta, tb, g->w_qkvu, g->b_qkvu, s));
+  // GLN1 plus the residual path: dx_in = dx_out + GLN1'(x_in)^T dxt
+  MTGR_BWD_TRY(launch_groupln_bwd(T, d, 0, act, shared, x_in, b->group_ids, p->gln1_gamma, p->ln_eps,
+                                  dz, dx_out, dx_in, 0, gpart, s));
+  MTGR_BWD_TRY(gln_param_grads(T, d, gpart, g->gln1_gamma, g->gln1_beta, s));
+#undef MTGR_BWD_TRY
+  return hipSuccess;
 }
 
 }  // namespace
@@ -297,6 +461,48 @@ mtgr_status mtgr_attention_workspace_size(const mtgr_batch* b, int32_t d, int32_
   if (d <= 0 || num_heads <= 0 || d % num_heads != 0) return MTGR_ERR_BAD_SHAPE;
   Sizes z = sizes_for(b, d, 0, 0, MTGR_F32, num_heads);
   *bytes = make_plan(z).total;
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_block_bwd_workspace_size(const mtgr_block_params* p, const mtgr_batch* b,
+                                          size_t* bytes) {
+  if (!bytes) return MTGR_ERR_NULL_ARG;
+  mtgr_status st = check_block(p);
+  if (st != MTGR_OK) return st;
+  if ((st = check_batch(b)) != MTGR_OK) return st;
+  // the weight-gradient GEMMs run over the padded token axis; one 256-row slab of it must stay
+  // within a 32-bit buffer range
+  if (b->num_tokens > kMaxBwdTokens) return MTGR_ERR_BAD_SHAPE;
+  Sizes z = sizes_for(b, p->d_model, p->mlp_hidden, 0, p->dtype, p->num_heads);
+  *bytes = make_bwd_plan(z).total;
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const float* x_in,
+                           const float* dx_out, float* dx_in, const mtgr_block_grads* g, void* ws,
+                           size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  mtgr_status st = mtgr_block_bwd_workspace_size(p, b, &need);
+  if (st != MTGR_OK) return st;
+  if (!g || !g->gln1_gamma || !g->gln1_beta || !g->w_qkvu || !g->gln2_gamma || !g->gln2_beta ||
+      !g->w_mlp1 || !g->w_mlp2)
+    return MTGR_ERR_NULL_ARG;
+  if (b->num_tokens > 0 && (!x_in || !dx_out || !dx_in)) return MTGR_ERR_NULL_ARG;
+  if (!ws || ws_bytes < need) return MTGR_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int d = p->d_model, h = p->mlp_hidden;
+  if (b->num_users == 0 || b->num_tokens == 0) {
+    // no tokens: every parameter gradient is an empty sum
+    MTGR_TRY(launch_reduce_wb(d, h, h + 8, 0, nullptr, g->w_mlp2, g->b_mlp2, s));
+    MTGR_TRY(launch_reduce_wb(h, d, d + 8, 0, nullptr, g->w_mlp1, g->b_mlp1, s));
+    MTGR_TRY(launch_reduce_wb(4 * d, d, d + 8, 0, nullptr, g->w_qkvu, g->b_qkvu, s));
+    MTGR_TRY(gln_param_grads(0, d, nullptr, g->gln1_gamma, g->gln1_beta, s));
+    MTGR_TRY(gln_param_grads(0, d, nullptr, g->gln2_gamma, g->gln2_beta, s));
+    return MTGR_OK;
+  }
+  Sizes z = sizes_for(b, d, h, 0, p->dtype, p->num_heads);
+  const BwdPlan pl = make_bwd_plan(z);
+  MTGR_TRY(run_block_bwd(p, b, pl, ws, x_in, dx_out, dx_in, g, s));
   return MTGR_OK;
 }
 

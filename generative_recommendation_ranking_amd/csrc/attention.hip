@@ -52,7 +52,8 @@ template <int DH, int MODE>
 __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     int32_t B, int H, int d, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
     const int32_t* __restrict__ order, const int32_t* __restrict__ xcd_off,
-    const float* __restrict__ ts, const bf16* __restrict__ qkvu, bf16* __restrict__ y) {
+    const float* __restrict__ ts, const bf16* __restrict__ qkvu, bf16* __restrict__ y,
+    bf16* __restrict__ vt) {
   constexpr int KP = DH + 8;                     // K row pitch: 16-byte reads of 16 rows hit distinct banks
   // V row pitch: a transposing read by 32 lanes touches 4 rows x 2 column chunks of 32 bytes;
   // a pitch of 16 (mod 64) dwords puts those 8 chunks on disjoint banks.
@@ -311,6 +312,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
     bf16x8 out;
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = (bf16)(acc[e] * inv_n * (float)u8[e]);
+    if (vt) {   // the ungated V~ (kept for the backward pass)
+      bf16x8 o2;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o2[e] = (bf16)(acc[e] * inv_n);
+      *reinterpret_cast<bf16x8*>(vt + (base + q) * (int64_t)d + (int64_t)h * DH + c * 8) = o2;
+    }
     *reinterpret_cast<bf16x8*>(y + (base + q) * (int64_t)d + (int64_t)h * DH + c * 8) = out;
   }
 }
@@ -322,7 +329,7 @@ __global__ __launch_bounds__(64) void k_attn_f32(
     int32_t B, int d, int mode, const int64_t* __restrict__ offsets,
     const UserSeg* __restrict__ seg, const int32_t* __restrict__ order,
     const int32_t* __restrict__ tile_off, const float* __restrict__ ts,
-    const float* __restrict__ qkvu, float* __restrict__ y) {
+    const float* __restrict__ qkvu, float* __restrict__ y, float* __restrict__ vt) {
   const int item = blockIdx.x;
   const int h = blockIdx.y;
   const int slot = find_slot(tile_off, B, item);
@@ -357,6 +364,10 @@ __global__ __launch_bounds__(64) void k_attn_f32(
 #pragma unroll
   for (int f = 0; f < DH; ++f)
     y[(base + i) * (int64_t)d + (int64_t)h * DH + f] = acc[f] * inv_n * Up[i * ld + f];
+  if (vt) {   // the ungated V~ (kept for the backward pass)
+#pragma unroll
+    for (int f = 0; f < DH; ++f) vt[(base + i) * (int64_t)d + (int64_t)h * DH + f] = acc[f] * inv_n;
+  }
 }
 
 }  // namespace
@@ -364,12 +375,13 @@ __global__ __launch_bounds__(64) void k_attn_f32(
 template <int MODE>
 hipError_t attn_bf16_mode(unsigned grid, int32_t B, int d, int H, const int64_t* offsets,
                           const UserSeg* seg, const int32_t* order, const int32_t* xcd_off,
-                          const float* timestamps, const bf16* qkvu, bf16* y, hipStream_t s) {
+                          const float* timestamps, const bf16* qkvu, bf16* y, bf16* vt,
+                          hipStream_t s) {
   const int dh = d / H;
   if (dh == 128)
-    k_attn_bf16<128, MODE><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y);
+    k_attn_bf16<128, MODE><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y, vt);
   else if (dh == 64)
-    k_attn_bf16<64, MODE><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y);
+    k_attn_bf16<64, MODE><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y, vt);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -378,16 +390,16 @@ hipError_t attn_bf16_mode(unsigned grid, int32_t B, int d, int H, const int64_t*
 hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H, int mask_mode,
                                  const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                  const int32_t* xcd_off, const float* timestamps,
-                                 const bf16* qkvu, bf16* y, hipStream_t s) {
+                                 const bf16* qkvu, bf16* y, bf16* vt, hipStream_t s) {
   if (grid_slots == 0) return hipSuccess;
   const unsigned grid = (unsigned)(grid_slots * kXcdCount);
   switch (mask_mode) {
     case kMaskDynamic:
-      return attn_bf16_mode<kMaskDynamic>(grid, B, d, H, offsets, seg, order, xcd_off, timestamps, qkvu, y, s);
+      return attn_bf16_mode<kMaskDynamic>(grid, B, d, H, offsets, seg, order, xcd_off, timestamps, qkvu, y, vt, s);
     case kMaskCausal:
-      return attn_bf16_mode<kMaskCausal>(grid, B, d, H, offsets, seg, order, xcd_off, timestamps, qkvu, y, s);
+      return attn_bf16_mode<kMaskCausal>(grid, B, d, H, offsets, seg, order, xcd_off, timestamps, qkvu, y, vt, s);
     case kMaskFull:
-      return attn_bf16_mode<kMaskFull>(grid, B, d, H, offsets, seg, order, xcd_off, timestamps, qkvu, y, s);
+      return attn_bf16_mode<kMaskFull>(grid, B, d, H, offsets, seg, order, xcd_off, timestamps, qkvu, y, vt, s);
     default:
       return hipErrorInvalidValue;
   }
@@ -396,16 +408,16 @@ hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H, in
 hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H, int mask_mode,
                                 const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                 const int32_t* tile_off, const float* timestamps,
-                                const float* qkvu, float* y, hipStream_t s) {
+                                const float* qkvu, float* y, float* vt, hipStream_t s) {
   if (total_tiles == 0) return hipSuccess;
   const int dh = d / H;
   dim3 grid((unsigned)total_tiles, (unsigned)H);
   if (dh == 32)
-    k_attn_f32<32><<<grid, 64, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off, timestamps, qkvu, y);
+    k_attn_f32<32><<<grid, 64, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off, timestamps, qkvu, y, vt);
   else if (dh == 64)
-    k_attn_f32<64><<<grid, 64, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off, timestamps, qkvu, y);
+    k_attn_f32<64><<<grid, 64, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off, timestamps, qkvu, y, vt);
   else if (dh == 128)
-    k_attn_f32<128><<<grid, 64, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off, timestamps, qkvu, y);
+    k_attn_f32<128><<<grid, 64, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off, timestamps, qkvu, y, vt);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

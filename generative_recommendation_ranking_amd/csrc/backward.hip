@@ -1,0 +1,441 @@
+// Backward pass of one HSTU block on gfx950: the pieces that are not GEMMs (the GEMMs reuse the
+// MFMA kernels of gemm.hip on transposed copies).  The block's update equations (marovi.ai MTGR
+// page, 方法) differentiated by the chain rule:
+//   MLP:        dH = dX' W2, dA = dH (.) silu'(A), dZ = dA W1         (A = Z W1^T + b1)
+//   GroupLN:    dx = (dxh - mean(dxh) - xh mean(dxh (.) xh)) / s,  dxh = dz (.) gamma[g]
+//   gate:       dV~ = dY (.) U,  dU = dY (.) V~
+//   attention:  dS = M/N (.) silu'(S) (.) (dV~ V^T),  dQ = dS K,  dK = dS^T Q,  dV = (M/N (.) silu(S))^T dV~
+// Parameter gradients are sums over tokens; every reduction here is deterministic (fixed
+// partial-sum layout, fixed summation order).
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace mtgr {
+
+namespace {
+
+template <typename T>
+__device__ __forceinline__ T cvt(float v) { return from_f32<T>(v); }
+
+// ---- transposes -----------------------------------------------------------------------------
+// dst[c][r] = src[r][c] for r < R, c < C; dst[c][r] = 0 for R <= r < Rp; with ones_row, an extra
+// row dst[C][r] = (r < R) and rows C+1 .. C+7 zero.  dst row pitch Rp.  64 x 64 tiles via LDS.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(int64_t R, int C, int64_t Rp, int ones_row,
+                                                   const T* __restrict__ src, T* __restrict__ dst) {
+  __shared__ float tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int crows = C + (ones_row ? 8 : 0);
+  for (int i = ty; i < 64; i += 4) {
+    const int64_t r = r0 + i;
+    const int c = c0 + tx;
+    float v = 0.f;
+    if (r < R) {
+      if (c < C) v = to_f32(src[r * C + c]);
+      else if (ones_row && c == C) v = 1.f;
+    }
+    tile[i][tx] = v;
+  }
+  __syncthreads();
+  for (int i = ty; i < 64; i += 4) {
+    const int c = c0 + i;
+    const int64_t r = r0 + tx;
+    if (c < crows && r < Rp) dst[(int64_t)c * Rp + r] = cvt<T>(tile[tx][i]);
+  }
+}
+
+// ---- elementwise ----------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_silu(int64_t n, const T* __restrict__ a, T* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = cvt<T>(silu_f32(to_f32(a[i])));
+}
+
+// dh <- dh (.) silu'(a), silu'(z) = sigma(z) (1 + z (1 - sigma(z)))
+template <typename T>
+__global__ __launch_bounds__(256) void k_silu_bwd(int64_t n, const T* __restrict__ a, T* __restrict__ dh) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const float z = to_f32(a[i]);
+    const float sg = 1.0f / (1.0f + __expf(-z));
+    dh[i] = cvt<T>(to_f32(dh[i]) * sg * (1.0f + z * (1.0f - sg)));
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_convert(int64_t n, const float* __restrict__ x, T* __restrict__ y) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = cvt<T>(x[i]);
+}
+
+// ---- partial-sum reduction ------------------------------------------------------------------
+// out[i] = sum_s part[s * stride + i] (i < n), s in fixed order.
+__global__ __launch_bounds__(256) void k_reduce(int64_t n, int nsplit, int64_t stride,
+                                                const float* __restrict__ part, float* __restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) acc += part[s * stride + i];
+    out[i] = acc;
+  }
+}
+
+// Sum the nsplit split-K partials of an extended weight gradient [M][Kx] (column K = the bias
+// gradient, from the ones row appended to the transposed activations) into dW [M][K] and db [M]
+// (db may be NULL), partials added in split order.
+__global__ __launch_bounds__(256) void k_reduce_wb(int M, int K, int Kx, int nsplit, const float* __restrict__ part,
+                                                   float* __restrict__ dw, float* __restrict__ db) {
+  const int64_t n = (int64_t)M * (K + 1);
+  const int64_t stride = (int64_t)M * Kx;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / (K + 1), k = i % (K + 1);
+    if (k == K && !db) continue;
+    float acc = 0.f;
+    for (int s = 0; s < nsplit; ++s) acc += part[s * stride + m * Kx + k];
+    if (k < K) dw[m * K + k] = acc;
+    else db[m] = acc;
+  }
+}
+
+// ---- GroupLN backward -------------------------------------------------------------------------
+// One wavefront per token row, as in the forward; each wavefront takes a contiguous run of rows.
+// dx = (dxh - mean(dxh) - xh mean(dxh xh)) / s; with resid, dx += resid (the residual path of the
+// block input; dx may alias resid).  Parameter gradients: a wavefront sums dz (.) xh and dz for the
+// current group in registers and adds them into its own slot [2][4][d] of `part` whenever the group
+// changes (tokens come in group runs); only that wavefront touches the slot, in program order, and
+// k_reduce sums the slots in a fixed order, so the result is deterministic.
+template <typename Tx, typename Tdz, typename Tp, typename Tout>
+__global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t rows_per_wave,
+                                                     const Tx* __restrict__ x, const uint8_t* __restrict__ g,
+                                                     const Tp* __restrict__ gamma, float eps, int gmask,
+                                                     const Tdz* __restrict__ dz, const float* resid, Tout* dx,
+                                                     float* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nch = d >> 3;
+  float* slot = part + wave * 2 * 4 * d;            // [2][4][d]: dgamma, dbeta
+  // each lane zeroes exactly the entries it later accumulates into (same thread, program order)
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch)
+      for (int gi = 0; gi < 8; ++gi)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) slot[gi * d + ch * 8 + i] = 0.f;
+  }
+  const int64_t r0 = wave * rows_per_wave;
+  const int64_t r1 = min(T, r0 + rows_per_wave);
+  float ag[2][8], ab[2][8];
+  int cur = -1;
+  auto flush = [&]() {
+    if (cur < 0) return;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          slot[cur * d + ch * 8 + i] += ag[c][i];
+          slot[4 * d + cur * d + ch * 8 + i] += ab[c][i];
+        }
+    }
+  };
+  const float inv_d = 1.0f / (float)d;
+  for (int64_t row = r0; row < r1; ++row) {
+    const int grp = g[row] & gmask;
+    if (grp != cur) {
+      flush();
+      cur = grp;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { ag[c][i] = 0.f; ab[c][i] = 0.f; }
+    }
+    float v[2][8], dv[2][8];
+    float s1 = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          v[c][i] = to_f32(x[row * d + ch * 8 + i]);
+          dv[c][i] = to_f32(dz[row * d + ch * 8 + i]);
+          s1 += v[c][i];
+        }
+      }
+    }
+    const float mean = wave_sum(s1) * inv_d;
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      if (lane + 64 * c < nch)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { const float e = v[c][i] - mean; q += e * e; }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+    float sa = 0.f, sb = 0.f;       // sum dxh, sum dxh * xh
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float xh = (v[c][i] - mean) * rstd;
+          const float dxh = dv[c][i] * to_f32(gamma[grp * d + ch * 8 + i]);
+          ag[c][i] += dv[c][i] * xh;
+          ab[c][i] += dv[c][i];
+          sa += dxh;
+          sb += dxh * xh;
+          v[c][i] = xh;
+          dv[c][i] = dxh;
+        }
+      }
+    }
+    const float ma = wave_sum(sa) * inv_d, mb = wave_sum(sb) * inv_d;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int64_t idx = row * d + ch * 8 + i;
+          float o = (dv[c][i] - ma - v[c][i] * mb) * rstd;
+          if (resid) o += resid[idx];
+          dx[idx] = cvt<Tout>(o);
+        }
+      }
+    }
+  }
+  flush();
+}
+
+// ---- masked SiLU attention backward (reference-style, one thread per row and head) ------------
+// Query side: dQ_i = sum_j M_ij silu'(s_ij)/n (dv~_i . v_j) k_j, and dU_i = dy_i (.) v~_i.
+// Key side:   dK_j = sum_i M_ij silu'(s_ij)/n (dv~_i . v_j) q_i, dV_j = sum_i M_ij silu(s_ij)/n dv~_i,
+// with dv~_i = dy_i (.) u_i.  Work items: (user, q_tile-row tile) x head, one thread per row
+// (blockDim.x = q_tile, the tiling of the prep's tile_off).
+template <typename T, int DH>
+__global__ __launch_bounds__(128) void k_attn_bwd_q(
+    int32_t B, int d, int mode, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ tile_off, const float* __restrict__ ts,
+    const T* __restrict__ qkvu, const T* __restrict__ vt, const T* __restrict__ dy, T* __restrict__ dqkvu) {
+  const int item = blockIdx.x, h = blockIdx.y;
+  int lo = 0, hi = B;
+  while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (tile_off[mid] <= item) lo = mid; else hi = mid; }
+  const int b = order[lo];
+  const int i = (item - tile_off[lo]) * (int)blockDim.x + threadIdx.x;
+  const int64_t base = offsets[b];
+  const int n = (int)(offsets[b + 1] - base);
+  if (i >= n) return;
+  const UserSeg sg = seg[b];
+  const int ns = sg.n_u + sg.n_s, rc_end = ns + sg.n_r;
+  const int64_t ld = 4 * (int64_t)d;
+  const T* Qp = qkvu + base * ld + (int64_t)h * DH;
+  const T* Kp = Qp + d;
+  const T* Vp = Qp + 2 * d;
+  const T* Up = Qp + 3 * d;
+  const T* dYp = dy + base * (int64_t)d + (int64_t)h * DH;
+  float q[DH], dvt[DH], acc[DH];
+#pragma unroll
+  for (int f = 0; f < DH; ++f) {
+    q[f] = to_f32(Qp[i * ld + f]);
+    dvt[f] = to_f32(dYp[i * (int64_t)d + f]) * to_f32(Up[i * ld + f]);
+    acc[f] = 0.f;
+  }
+  const float inv_n = 1.0f / (float)n;
+  const float ti = ts[base + i];
+  for (int j = 0; j < n; ++j) {
+    if (!mtgr_visible_mode(mode, i, j, ns, rc_end, ti, ts[base + j])) continue;
+    float s = 0.f, da = 0.f;
+#pragma unroll
+    for (int f = 0; f < DH; ++f) {
+      s = fmaf(q[f], to_f32(Kp[j * ld + f]), s);
+      da = fmaf(dvt[f], to_f32(Vp[j * ld + f]), da);
+    }
+    const float sgm = 1.0f / (1.0f + __expf(-s));
+    const float ds = da * sgm * (1.0f + s * (1.0f - sgm)) * inv_n;
+#pragma unroll
+    for (int f = 0; f < DH; ++f) acc[f] = fmaf(ds, to_f32(Kp[j * ld + f]), acc[f]);
+  }
+  T* dQ = dqkvu + (base + i) * ld + (int64_t)h * DH;
+  T* dU = dQ + 3 * d;
+  const T* Vt = vt + (base + i) * (int64_t)d + (int64_t)h * DH;
+#pragma unroll
+  for (int f = 0; f < DH; ++f) {
+    dQ[f] = cvt<T>(acc[f]);
+    dU[f] = cvt<T>(to_f32(dYp[i * (int64_t)d + f]) * to_f32(Vt[f]));
+  }
+}
+
+template <typename T, int DH>
+__global__ __launch_bounds__(128) void k_attn_bwd_kv(
+    int32_t B, int d, int mode, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ tile_off, const float* __restrict__ ts,
+    const T* __restrict__ qkvu, const T* __restrict__ dy, T* __restrict__ dqkvu) {
+  const int item = blockIdx.x, h = blockIdx.y;
+  int lo = 0, hi = B;
+  while (hi - lo > 1) { const int mid = (lo + hi) >> 1; if (tile_off[mid] <= item) lo = mid; else hi = mid; }
+  const int b = order[lo];
+  const int j = (item - tile_off[lo]) * (int)blockDim.x + threadIdx.x;
+  const int64_t base = offsets[b];
+  const int n = (int)(offsets[b + 1] - base);
+  if (j >= n) return;
+  const UserSeg sg = seg[b];
+  const int ns = sg.n_u + sg.n_s, rc_end = ns + sg.n_r;
+  const int64_t ld = 4 * (int64_t)d;
+  const T* Qp = qkvu + base * ld + (int64_t)h * DH;
+  const T* Kp = Qp + d;
+  const T* Vp = Qp + 2 * d;
+  const T* Up = Qp + 3 * d;
+  const T* dYp = dy + base * (int64_t)d + (int64_t)h * DH;
+  float k[DH], v[DH], dk[DH], dv[DH];
+#pragma unroll
+  for (int f = 0; f < DH; ++f) {
+    k[f] = to_f32(Kp[j * ld + f]);
+    v[f] = to_f32(Vp[j * ld + f]);
+    dk[f] = 0.f;
+    dv[f] = 0.f;
+  }
+  const float inv_n = 1.0f / (float)n;
+  const float tj = ts[base + j];
+  for (int i = 0; i < n; ++i) {
+    if (!mtgr_visible_mode(mode, i, j, ns, rc_end, ts[base + i], tj)) continue;
+    float s = 0.f, da = 0.f;
+#pragma unroll
+    for (int f = 0; f < DH; ++f) {
+      s = fmaf(to_f32(Qp[i * ld + f]), k[f], s);
+      da = fmaf(to_f32(dYp[i * (int64_t)d + f]) * to_f32(Up[i * ld + f]), v[f], da);
+    }
+    const float sgm = 1.0f / (1.0f + __expf(-s));
+    const float p = s * sgm * inv_n;
+    const float ds = da * sgm * (1.0f + s * (1.0f - sgm)) * inv_n;
+#pragma unroll
+    for (int f = 0; f < DH; ++f) {
+      dk[f] = fmaf(ds, to_f32(Qp[i * ld + f]), dk[f]);
+      dv[f] = fmaf(p, to_f32(dYp[i * (int64_t)d + f]) * to_f32(Up[i * ld + f]), dv[f]);
+    }
+  }
+  T* dK = dqkvu + (base + j) * ld + d + (int64_t)h * DH;
+  T* dV = dK + d;
+#pragma unroll
+  for (int f = 0; f < DH; ++f) {
+    dK[f] = cvt<T>(dk[f]);
+    dV[f] = cvt<T>(dv[f]);
+  }
+}
+
+inline unsigned ew_grid(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 16384); }
+
+}  // namespace
+
+hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int kind, const void* src,
+                            void* dst, hipStream_t s) {
+  if (R == 0 && Rp == 0) return hipSuccess;
+  const int crows = C + (ones_row ? 8 : 0);
+  dim3 grid((unsigned)((crows + 63) / 64), (unsigned)((Rp + 63) / 64));
+  if (kind == 1)
+    k_transpose<bf16><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, static_cast<const bf16*>(src), static_cast<bf16*>(dst));
+  else
+    k_transpose<float><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, static_cast<const float*>(src), static_cast<float*>(dst));
+  return hipGetLastError();
+}
+
+hipError_t launch_silu(int64_t n, int kind, const void* a, void* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (kind == 1) k_silu<bf16><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const bf16*>(a), static_cast<bf16*>(out));
+  else k_silu<float><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const float*>(a), static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_silu_bwd(int64_t n, int kind, const void* a, void* dh, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (kind == 1) k_silu_bwd<bf16><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const bf16*>(a), static_cast<bf16*>(dh));
+  else k_silu_bwd<float><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const float*>(a), static_cast<float*>(dh));
+  return hipGetLastError();
+}
+
+hipError_t launch_convert(int64_t n, int kind, const float* x, void* y, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (kind == 1) k_convert<bf16><<<ew_grid(n), 256, 0, s>>>(n, x, static_cast<bf16*>(y));
+  else k_convert<float><<<ew_grid(n), 256, 0, s>>>(n, x, static_cast<float*>(y));
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce(int64_t n, int nsplit, int64_t stride, const float* part, float* out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_reduce<<<ew_grid(n), 256, 0, s>>>(n, nsplit, stride, part, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_wb(int M, int K, int Kx, int nsplit, const float* part, float* dw, float* db,
+                            hipStream_t s) {
+  const int64_t n = (int64_t)M * (K + 1);
+  if (M == 0) return hipSuccess;
+  k_reduce_wb<<<ew_grid(n), 256, 0, s>>>(M, K, Kx, nsplit, part, dw, db);
+  return hipGetLastError();
+}
+
+// wavefronts of the GroupLN backward: one slot [2][4][d] of partial parameter gradients each
+int groupln_bwd_waves(int64_t T) { return 4 * (int)std::max<int64_t>(1, std::min<int64_t>(256, (T + 255) / 256)); }
+
+hipError_t launch_groupln_bwd(int64_t T, int d, int x_kind, int act_kind, int shared, const void* x,
+                              const uint8_t* g, const void* gamma, float eps, const void* dz,
+                              const float* resid, void* dx, int out_kind, float* part, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int waves = groupln_bwd_waves(T);
+  const int64_t rpw = (T + waves - 1) / waves;
+  const unsigned grid = (unsigned)(waves / 4);
+  const int gm = shared ? 0 : 3;
+  // (x, dz, gamma, dx) types: GLN2 uses (act, act, act, act); GLN1 uses (float, act, act, float)
+  if (x_kind == 0 && act_kind == 0 && out_kind == 0)
+    k_groupln_bwd<float, float, float, float><<<grid, 256, 0, s>>>(
+        T, d, rpw, static_cast<const float*>(x), g, static_cast<const float*>(gamma), eps, gm,
+        static_cast<const float*>(dz), resid, static_cast<float*>(dx), part);
+  else if (x_kind == 1 && act_kind == 1 && out_kind == 1)
+    k_groupln_bwd<bf16, bf16, bf16, bf16><<<grid, 256, 0, s>>>(
+        T, d, rpw, static_cast<const bf16*>(x), g, static_cast<const bf16*>(gamma), eps, gm,
+        static_cast<const bf16*>(dz), resid, static_cast<bf16*>(dx), part);
+  else if (x_kind == 0 && act_kind == 1 && out_kind == 0)
+    k_groupln_bwd<float, bf16, bf16, float><<<grid, 256, 0, s>>>(
+        T, d, rpw, static_cast<const float*>(x), g, static_cast<const bf16*>(gamma), eps, gm,
+        static_cast<const bf16*>(dz), resid, static_cast<float*>(dx), part);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_bwd_ref(int32_t B, int64_t total_tiles, int q_tile, int d, int H, int mask_mode, int kind,
+                                    const int64_t* offsets, const UserSeg* seg, const int32_t* order,
+                                    const int32_t* tile_off, const float* timestamps, const void* qkvu,
+                                    const void* vt, const void* dy, void* dqkvu, hipStream_t s) {
+  if (total_tiles == 0) return hipSuccess;
+  if (q_tile != 64 && q_tile != 128) return hipErrorInvalidValue;
+  const int dh = d / H;
+  dim3 grid((unsigned)total_tiles, (unsigned)H);
+#define MTGR_BWD(TT, DHV)                                                                          \
+  do {                                                                                             \
+    k_attn_bwd_q<TT, DHV><<<grid, q_tile, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off,      \
+                                              timestamps, static_cast<const TT*>(qkvu),            \
+                                              static_cast<const TT*>(vt), static_cast<const TT*>(dy), \
+                                              static_cast<TT*>(dqkvu));                            \
+    k_attn_bwd_kv<TT, DHV><<<grid, q_tile, 0, s>>>(B, d, mask_mode, offsets, seg, order, tile_off,     \
+                                               timestamps, static_cast<const TT*>(qkvu),           \
+                                               static_cast<const TT*>(dy), static_cast<TT*>(dqkvu)); \
+  } while (0)
+  if (kind == 1) {
+    if (dh == 128) MTGR_BWD(bf16, 128);
+    else if (dh == 64) MTGR_BWD(bf16, 64);
+    else if (dh == 32) MTGR_BWD(bf16, 32);
+    else return hipErrorInvalidValue;
+  } else {
+    if (dh == 128) MTGR_BWD(float, 128);
+    else if (dh == 64) MTGR_BWD(float, 64);
+    else if (dh == 32) MTGR_BWD(float, 32);
+    else return hipErrorInvalidValue;
+  }
+#undef MTGR_BWD
+  return hipGetLastError();
+}
+
+}  // namespace mtgr

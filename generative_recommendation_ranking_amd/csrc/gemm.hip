@@ -54,7 +54,8 @@ __device__ __forceinline__ void store_out(TOut* out, const float* resid, int64_t
 template <int WM, int WN, int EPI, typename TOut>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     int64_t M, int N, int K, const bf16* __restrict__ A, const bf16* __restrict__ W,
-    const bf16* __restrict__ bias, const float* resid, TOut* out, int nN, int64_t nM, int nb) {
+    const bf16* __restrict__ bias, const float* resid, TOut* out, int nN, int64_t nM, int nb,
+    int ksplit, int64_t nMr) {
   constexpr int BM = 256, BN = 256, BK = 64, NT = 64 * WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int LP = BK + 8, CPR = BK / 8;
@@ -107,7 +108,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   if (!valid_slot(first)) first = next_slot(first);
   if (first >= nslots) return;
 
-  const int nk = K / BK;                 // >= 2 (checked by the host)
+  // Split K: M-tile index mt in [0, nM) stands for row tile mt % nMr over the K range
+  // [(mt / nMr) * nk * BK, + nk * BK), written to out + (mt / nMr) * M * N (no bias then).
+  const int nk = K / BK / ksplit;        // >= 2 (checked by the host)
   const uint32_t vo = (uint32_t)((tid / CPR) * K * 2 + (tid % CPR) * 16);  // byte offset in slab
 
   struct TileRsrc {
@@ -115,13 +118,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   };
   auto make_rsrc = [&](int64_t s) {
     int64_t mt; int ntile; decode(s, mt, ntile);
+    const int ks_off = (int)(mt / nMr) * nk * BK;
+    mt %= nMr;
     const int64_t m0 = mt * BM;
     const int n0 = ntile * BN;
     const int64_t mrows = min((int64_t)BM, M - m0);
     const int nrows = min(BN, N - n0);
+    // the resources start at column ks_off of the first row; they end where row mrows (nrows)
+    // would begin, so rows past the edge still read as zero
     TileRsrc r;
-    r.a = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * K), (short)0, (int)(mrows * K * 2), 0x00020000);
-    r.w = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * K), (short)0, nrows * K * 2, 0x00020000);
+    r.a = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * K + ks_off), (short)0,
+                                            (int)((mrows * K - ks_off) * 2), 0x00020000);
+    r.w = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * K + ks_off), (short)0,
+                                            (int)(((int64_t)nrows * K - ks_off) * 2), 0x00020000);
     return r;
   };
   bf16x8 ra[CA], rb[CB];
@@ -273,12 +282,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
       ((uint32_t)(wm * TM + (lane >> 4)) * (uint32_t)N + (uint32_t)(wn * TN + (lane & 15) * CW)) * (uint32_t)sizeof(TOut);
   auto epilogue = [&] {
     int64_t mt_e; int nt_e; decode(slot, mt_e, nt_e);
+    TOut* outp = out + (mt_e / nMr) * M * N;
+    mt_e %= nMr;
     const int64_t m0 = mt_e * BM;
     const int n0 = nt_e * BN;
     const uint32_t rows = (uint32_t)min((int64_t)BM, M - m0);
     const int nbytes = (int)(rows * (uint32_t)N * sizeof(TOut));
     const __amdgpu_buffer_rsrc_t o_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(out + m0 * N), (short)0, nbytes, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(outp + m0 * N), (short)0, nbytes, 0x00020000);
     __amdgpu_buffer_rsrc_t r_rsrc = o_rsrc;
     if constexpr (EPI == MTGR_EPI_RESIDUAL_F32)
       r_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(resid + m0 * N), (short)0, nbytes, 0x00020000);
@@ -384,6 +395,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   }
 }
 
+// grid.z > 1 splits K: block z sums over k in [z*K/gz, (z+1)*K/gz) (K a multiple of gz) and
+// writes its partial (EPI_STORE only) to out + z*M*N.
 template <int EPI>
 __global__ __launch_bounds__(256) void k_gemm_f32(int64_t M, int N, int K,
                                                   const float* __restrict__ A,
@@ -397,8 +410,11 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int64_t M, int N, int K,
   const int n0 = blockIdx.y * BN;
   const int tid = threadIdx.x;
   const int ty = tid / 16, tx = tid % 16;
+  const int kc = K / (int)gridDim.z;
+  const int kbeg = (int)blockIdx.z * kc, kfin = kbeg + kc;
+  out += (int64_t)blockIdx.z * M * N;
   float acc[4][4] = {};
-  for (int k0 = 0; k0 < K; k0 += BK) {
+  for (int k0 = kbeg; k0 < kfin; k0 += BK) {
     {
       const int r = tid / 4, c4 = (tid % 4) * 4;
 #pragma unroll
@@ -406,8 +422,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int64_t M, int N, int K,
         const int k = k0 + c4 + e;
         const int64_t m = m0 + r;
         const int n = n0 + r;
-        As[c4 + e][r] = (m < M && k < K) ? A[m * K + k] : 0.f;
-        Ws[c4 + e][r] = (n < N && k < K) ? W[(int64_t)n * K + k] : 0.f;
+        As[c4 + e][r] = (m < M && k < kfin) ? A[m * K + k] : 0.f;
+        Ws[c4 + e][r] = (n < N && k < kfin) ? W[(int64_t)n * K + k] : 0.f;
       }
     }
     __syncthreads();
@@ -439,7 +455,8 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int64_t M, int N, int K,
 
 template <int WM, int WN, int EPI, typename TOut>
 hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf16* w,
-                               const bf16* bias, const float* resid, void* out, hipStream_t s) {
+                               const bf16* bias, const float* resid, void* out, hipStream_t s,
+                               int ksplit = 1) {
   constexpr size_t lds = 2 * (size_t)(256 + 256) * (64 + 8) * sizeof(bf16) + kBiasLds * sizeof(bf16);
   auto kern = k_gemm_bf16_persistent<WM, WN, EPI, TOut>;
   static bool attr_set = false;
@@ -454,12 +471,13 @@ hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf1
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   const int nN = (N + 255) / 256;
-  const int64_t nM = (M + 255) / 256;
+  const int64_t nMr = (M + 255) / 256;
+  const int64_t nM = nMr * ksplit;
   const int64_t tiles_pad = (nM + kXcd - 1) / kXcd * kXcd * nN;
   const int64_t grid = std::min<int64_t>(tiles_pad, (int64_t)cus / kXcd * kXcd);
   // N-chunk width: estimated bytes missing a 4 MB XCD L2, activations re-read once per chunk
   // versus weights re-read once per round of concurrently running M-tiles when they do not fit.
-  const double a_bytes = (double)M * K * 2, slice = 256.0 * K * 2, l2 = 4.0 * 1024 * 1024;
+  const double a_bytes = (double)M * K * 2, slice = 256.0 * (K / ksplit) * 2, l2 = 4.0 * 1024 * 1024;
   const double wg_per_xcd = (double)grid / kXcd;
   int nb = nN;
   double best = 1e300;
@@ -471,7 +489,8 @@ hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf1
     const double t = a_bytes * chunks + w_traffic;
     if (t < best * 0.98) { best = t; nb = c; }
   }
-  kern<<<(unsigned)grid, 64 * WM * WN, lds, s>>>(M, N, K, a, w, bias, resid, static_cast<TOut*>(out), nN, nM, nb);
+  kern<<<(unsigned)grid, 64 * WM * WN, lds, s>>>(M, N, K, a, w, bias, resid, static_cast<TOut*>(out), nN, nM, nb,
+                                                  ksplit, nMr);
   return hipGetLastError();
 }
 
@@ -487,6 +506,22 @@ hipError_t launch_gemm_bf16(int64_t M, int N, int K, int epi, const bf16* a, con
       return run_bf16_persistent<4, 2, MTGR_EPI_RESIDUAL_F32, float>(M, N, K, a, w, bias, resid, out, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_bf16_splitk(int64_t M, int N, int K, int ksplit, const bf16* a, const bf16* w,
+                                   float* part, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (ksplit < 1 || K % (64 * ksplit) != 0 || K / 64 / ksplit < 2) return hipErrorInvalidValue;
+  return run_bf16_persistent<4, 2, MTGR_EPI_STORE, float>(M, N, K, a, w, nullptr, nullptr, part, s, ksplit);
+}
+
+hipError_t launch_gemm_f32_splitk(int64_t M, int N, int K, int ksplit, const float* a, const float* w,
+                                  float* part, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (ksplit < 1 || K % ksplit != 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((M + 63) / 64), (unsigned)((N + 63) / 64), (unsigned)ksplit);
+  k_gemm_f32<MTGR_EPI_STORE><<<grid, 256, 0, s>>>(M, N, K, a, w, nullptr, nullptr, part);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_f32(int64_t M, int N, int K, int epi, const float* a, const float* w,

@@ -47,16 +47,51 @@ hipError_t launch_gemm_f32(int64_t M, int N, int K, int epi, const float* a, con
 // ---- attention (attention.hip) -------------------------------------------------------------
 constexpr int kAttnQTileBf16 = 128;
 constexpr int kAttnQTileF32 = 64;
-// grid_slots = max over XCDs of that XCD's q-tile count (the host replica of k_prep_xcd)
+// grid_slots = max over XCDs of that XCD's q-tile count (the host replica of k_prep_xcd).
+// vt (may be NULL) receives the ungated V~ for the backward pass.
 // mask_mode: kMaskDynamic / kMaskCausal / kMaskFull
 hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H, int mask_mode,
                                  const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                  const int32_t* xcd_off, const float* timestamps,
-                                 const bf16* qkvu, bf16* y, hipStream_t s);
+                                 const bf16* qkvu, bf16* y, bf16* vt, hipStream_t s);
 hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H, int mask_mode,
                                 const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                 const int32_t* tile_off, const float* timestamps,
-                                const float* qkvu, float* y, hipStream_t s);
+                                const float* qkvu, float* y, float* vt, hipStream_t s);
+
+// ---- backward pieces (backward.hip) -------------------------------------------------------------
+// kind / *_kind: 0 = float, 1 = bf16
+// dst[c][r] = src[r][c] (r < R, c < C), zero for R <= r < Rp; ones_row adds row C = (r < R) and
+// rows C+1..C+7 = 0.  dst row pitch Rp.
+hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int kind, const void* src,
+                            void* dst, hipStream_t s);
+hipError_t launch_silu(int64_t n, int kind, const void* a, void* out, hipStream_t s);
+hipError_t launch_silu_bwd(int64_t n, int kind, const void* a, void* dh, hipStream_t s);
+hipError_t launch_convert(int64_t n, int kind, const float* x, void* y, hipStream_t s);
+// out[i] = sum over s < nsplit of part[s*stride + i]
+hipError_t launch_reduce(int64_t n, int nsplit, int64_t stride, const float* part, float* out, hipStream_t s);
+// sum of nsplit partials [nsplit][M][Kx] -> dw [M][K] and db [M] = column K (db may be NULL)
+hipError_t launch_reduce_wb(int M, int K, int Kx, int nsplit, const float* part, float* dw, float* db,
+                            hipStream_t s);
+// GroupLN backward: dx = GLN'(x)^T dz (+ resid); per-wavefront partials of (dgamma, dbeta)
+// [groupln_bwd_waves(T)][2][4][d]
+int groupln_bwd_waves(int64_t T);
+hipError_t launch_groupln_bwd(int64_t T, int d, int x_kind, int act_kind, int shared, const void* x,
+                              const uint8_t* g, const void* gamma, float eps, const void* dz,
+                              const float* resid, void* dx, int out_kind, float* part, hipStream_t s);
+// masked SiLU attention backward, one thread per (row, head): dqkvu [T][4d] from qkvu, the ungated
+// V~ and dy (gradient w.r.t. the gated output); work items (user, q_tile rows) in prep order
+// (tile_off built with the same q_tile, 64 or 128)
+hipError_t launch_attention_bwd_ref(int32_t B, int64_t total_tiles, int q_tile, int d, int H, int mask_mode, int kind,
+                                    const int64_t* offsets, const UserSeg* seg, const int32_t* order,
+                                    const int32_t* tile_off, const float* timestamps, const void* qkvu,
+                                    const void* vt, const void* dy, void* dqkvu, hipStream_t s);
+// split-K GEMM for weight gradients: part[s][M][N] = a[M][Ks] w[N][Ks]^T over K-range s of ksplit
+// (K a multiple of 64 * ksplit for bf16); no bias
+hipError_t launch_gemm_bf16_splitk(int64_t M, int N, int K, int ksplit, const bf16* a, const bf16* w,
+                                   float* part, hipStream_t s);
+hipError_t launch_gemm_f32_splitk(int64_t M, int N, int K, int ksplit, const float* a, const float* w,
+                                  float* part, hipStream_t s);
 
 // ---- head (head.hip) -----------------------------------------------------------------------
 // rows[c] = (out_kind) x[cand_idx[c]]  (fp32 hidden state -> head input dtype)

@@ -34,8 +34,12 @@ EXPORTED = [
     "mtgr_abi_version", "mtgr_status_str", "mtgr_encoder_workspace_size",
     "mtgr_block_workspace_size", "mtgr_attention_workspace_size", "mtgr_encoder_fwd",
     "mtgr_block_fwd", "mtgr_groupln_fwd", "mtgr_linear_fwd", "mtgr_attention_fwd",
-    "mtgr_validate_batch", "mtgr_debug_mask",
+    "mtgr_validate_batch", "mtgr_debug_mask", "mtgr_block_bwd_workspace_size", "mtgr_block_bwd",
 ]
+
+# parameter names of one block, in the field order of mtgr_block_params / mtgr_block_grads
+BLOCK_PARAM_NAMES = ("gln1_gamma", "gln1_beta", "w_qkvu", "b_qkvu", "gln2_gamma", "gln2_beta",
+                     "w_mlp1", "b_mlp1", "w_mlp2", "b_mlp2")
 
 c_i32, c_i64, c_f32, c_vp, c_sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -52,6 +56,10 @@ class MtgrBlockParams(ctypes.Structure):
                 ("b_qkvu", c_vp), ("gln2_gamma", c_vp), ("gln2_beta", c_vp), ("w_mlp1", c_vp),
                 ("b_mlp1", c_vp), ("w_mlp2", c_vp), ("b_mlp2", c_vp), ("mask_mode", c_i32),
                 ("norm_mode", c_i32)]
+
+
+class MtgrBlockGrads(ctypes.Structure):
+    _fields_ = [(name, c_vp) for name in BLOCK_PARAM_NAMES]
 
 
 class MtgrEncoderParams(ctypes.Structure):
@@ -93,6 +101,9 @@ def lib():
                                          c_vp]
         L.mtgr_validate_batch.argtypes = [P(MtgrBatch), c_vp, c_sz, c_vp, P(c_i32)]
         L.mtgr_debug_mask.argtypes = [P(MtgrBatch), c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
+        L.mtgr_block_bwd_workspace_size.argtypes = [P(MtgrBlockParams), P(MtgrBatch), P(c_sz)]
+        L.mtgr_block_bwd.argtypes = [P(MtgrBlockParams), P(MtgrBatch), c_vp, c_vp, c_vp,
+                                     P(MtgrBlockGrads), c_vp, c_sz, c_vp]
         for name in EXPORTED[2:]:
             getattr(L, name).restype = c_i32
         _lib = L
@@ -203,6 +214,13 @@ def mtgr_attention_workspace_size(batch: DeviceBatch, d: int, num_heads: int) ->
     return int(n.value)
 
 
+def mtgr_block_bwd_workspace_size(block: MtgrBlockParams, batch: DeviceBatch) -> int:
+    n = c_sz(0)
+    _check("mtgr_block_bwd_workspace_size",
+           lib().mtgr_block_bwd_workspace_size(ctypes.byref(block), ctypes.byref(batch.c), ctypes.byref(n)))
+    return int(n.value)
+
+
 def workspace(nbytes: int, device="cuda"):
     import torch
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
@@ -219,6 +237,19 @@ def mtgr_block_fwd(block: MtgrBlockParams, batch: DeviceBatch, x_in, x_out, ws, 
     _check("mtgr_block_fwd", lib().mtgr_block_fwd(
         ctypes.byref(block), ctypes.byref(batch.c), _ptr(x_in), _ptr(x_out), _ptr(ws), ws.numel(),
         _stream(stream)))
+
+
+def block_grads(grads: dict) -> MtgrBlockGrads:
+    """The C description of fp32 gradient tensors keyed by BLOCK_PARAM_NAMES (missing = NULL)."""
+    return MtgrBlockGrads(*[_ptr(grads.get(name)) for name in BLOCK_PARAM_NAMES])
+
+
+def mtgr_block_bwd(block: MtgrBlockParams, batch: DeviceBatch, x_in, dx_out, dx_in, grads: dict, ws,
+                   stream=None):
+    g = block_grads(grads)
+    _check("mtgr_block_bwd", lib().mtgr_block_bwd(
+        ctypes.byref(block), ctypes.byref(batch.c), _ptr(x_in), _ptr(dx_out), _ptr(dx_in),
+        ctypes.byref(g), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def mtgr_groupln_fwd(batch: DeviceBatch, d: int, in_dtype: int, out_dtype: int, param_dtype: int,

@@ -1,5 +1,6 @@
 /*
- * mtgr.h -- C ABI of libmtgr.so: forward pass of the MTGR HSTU encoder on one MI355X (gfx950).
+ * mtgr.h -- C ABI of libmtgr.so: forward pass of the MTGR HSTU encoder on one MI355X (gfx950),
+ * and the backward pass of one block.
  *
  * Page keys used in the citations below:
  *   [P1]/[P2] chenhuiyu blog post "MTGR" (Chinese / English)
@@ -51,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MTGR_ABI_VERSION 2
+#define MTGR_ABI_VERSION 3
 
 typedef enum {
   MTGR_OK = 0,
@@ -118,6 +119,23 @@ typedef struct mtgr_block_params {
   int32_t norm_mode;              /* MTGR_NORM_*; 0 = GroupLN */
 } mtgr_block_params;
 
+/* Parameter gradients of one block (mtgr_block_bwd): device float pointers shaped like the
+ * parameters of mtgr_block_params (gamma/beta gradients always [4][d]; with MTGR_NORM_SHARED rows
+ * 1..3 come out zero).  They are overwritten, not accumulated.  A NULL bias-gradient pointer skips
+ * that gradient; every other pointer is required. */
+typedef struct mtgr_block_grads {
+  float* gln1_gamma;              /* [4][d] */
+  float* gln1_beta;               /* [4][d] */
+  float* w_qkvu;                  /* [4d][d] */
+  float* b_qkvu;                  /* [4d] or NULL */
+  float* gln2_gamma;              /* [4][d] */
+  float* gln2_beta;               /* [4][d] */
+  float* w_mlp1;                  /* [h][d] */
+  float* b_mlp1;                  /* [h] or NULL */
+  float* w_mlp2;                  /* [d][h] */
+  float* b_mlp2;                  /* [d] or NULL */
+} mtgr_block_grads;
+
 /* L blocks plus the candidate head.  `layers` is a host array of L block descriptions that
  * must all share d, H, dtype. */
 typedef struct mtgr_encoder_params {
@@ -141,6 +159,8 @@ mtgr_status mtgr_block_workspace_size(const mtgr_block_params* p, const mtgr_bat
                                       size_t* bytes);
 mtgr_status mtgr_attention_workspace_size(const mtgr_batch* b, int32_t d, int32_t num_heads,
                                           size_t* bytes);
+mtgr_status mtgr_block_bwd_workspace_size(const mtgr_block_params* p, const mtgr_batch* b,
+                                          size_t* bytes);
 
 /* ---- the hot path ----------------------------------------------------------------------- */
 /* Full encoder: L blocks over x_in (device float [T][d]) then the head at candidate tokens.
@@ -154,6 +174,18 @@ mtgr_status mtgr_encoder_fwd(const mtgr_encoder_params* p, const mtgr_batch* b, 
 /* One block: x_out = block(x_in), both device float [T][d]; x_out may alias x_in. */
 mtgr_status mtgr_block_fwd(const mtgr_block_params* p, const mtgr_batch* b, const float* x_in,
                            float* x_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Backward pass of one block ([P3] 方法, the two update equations, differentiated by the chain
+ * rule; the pages train the model end to end, [P1]/[P2] training-system section).  Given x_in
+ * (device float [T][d], the block's input) and dx_out = dLoss/dx_out (device float [T][d]), writes
+ * dx_in = dLoss/dx_in (device float [T][d]; may alias dx_out) and the parameter gradients summed
+ * over every token of the batch into *g.  The forward activations are recomputed into the
+ * workspace (mtgr_block_bwd_workspace_size); in MTGR_BF16 they and the activation gradients are
+ * stored in bf16 with fp32 accumulation, the parameter gradients are fp32 sums of fp32 split
+ * partials.  Every reduction has a fixed order: repeated calls give identical bits. */
+mtgr_status mtgr_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const float* x_in,
+                           const float* dx_out, float* dx_in, const mtgr_block_grads* g, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* ---- kernel-level entries (the same kernels the block uses) ------------------------------ */
 /* GroupLN over T rows of width d: y = (x - mean) / sqrt(var + eps) * gamma[g] + beta[g].

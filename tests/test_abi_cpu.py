@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert M.mtgr_abi_version() == 2
+    assert M.mtgr_abi_version() == 3
     assert M.mtgr_status_str(0) == "ok"
     assert "workspace" in M.mtgr_status_str(5)
 
@@ -142,3 +142,43 @@ def test_library_has_no_undefined_internal_symbols():
     out = subprocess.run(["nm", "-D", "--undefined-only", M.LIB_PATH], capture_output=True, text=True).stdout
     bad = [line for line in out.splitlines() if "mtgr" in line]
     assert not bad, bad
+
+
+def _bwd_ws_size(block, batch):
+    n = ctypes.c_size_t(0)
+    st = M.lib().mtgr_block_bwd_workspace_size(ctypes.byref(block), ctypes.byref(batch), ctypes.byref(n))
+    return st, n.value
+
+
+def _grads(**missing):
+    g = M.MtgrBlockGrads(*[FAKE] * len(M.BLOCK_PARAM_NAMES))
+    for name in missing:
+        setattr(g, name, None)
+    return g
+
+
+def test_block_bwd_argument_checks():
+    L = M.lib()
+    b, _keep = _batch([0, 300, 1000])
+    blk = _block()
+    st, n_bwd = _bwd_ws_size(blk, b)
+    assert st == 0
+    assert n_bwd > _ws_size(blk, b)[1]          # activations and gradients are kept
+    b2, _keep2 = _batch([0, 3000, 10000])
+    assert _bwd_ws_size(blk, b2)[1] > n_bwd      # grows with T
+    assert _bwd_ws_size(_block(d=256, H=3), b)[0] == 2
+    assert _bwd_ws_size(_block(mask_mode=5), b)[0] == 4
+    big, _keep3 = _batch([0, 4_000_001])
+    assert _bwd_ws_size(blk, big)[0] == 2        # past the token limit of the weight-gradient GEMMs
+    g = _grads()
+    assert L.mtgr_block_bwd(ctypes.byref(blk), ctypes.byref(b), FAKE, FAKE, FAKE, None, FAKE, 1 << 40, None) == 1
+    for name in ("gln1_gamma", "gln1_beta", "w_qkvu", "gln2_gamma", "gln2_beta", "w_mlp1", "w_mlp2"):
+        gm = _grads(**{name: 1})
+        assert L.mtgr_block_bwd(ctypes.byref(blk), ctypes.byref(b), FAKE, FAKE, FAKE, ctypes.byref(gm),
+                                FAKE, 1 << 40, None) == 1, name
+    assert L.mtgr_block_bwd(ctypes.byref(blk), ctypes.byref(b), None, FAKE, FAKE, ctypes.byref(g),
+                            FAKE, 1 << 40, None) == 1
+    assert L.mtgr_block_bwd(ctypes.byref(blk), ctypes.byref(b), FAKE, FAKE, FAKE, ctypes.byref(g),
+                            FAKE, n_bwd - 1, None) == 5
+    assert L.mtgr_block_bwd(ctypes.byref(blk), ctypes.byref(b), FAKE, FAKE, FAKE, ctypes.byref(g),
+                            None, n_bwd, None) == 5
