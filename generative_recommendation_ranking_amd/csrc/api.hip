@@ -220,6 +220,22 @@ hipError_t attention(const mtgr_batch* b, int d, int H, int dtype, int mask_mode
                               static_cast<float*>(y), static_cast<float*>(vt), s);
 }
 
+// Attention backward: dqkvu [T][4d] from qkvu, the ungated V~ and dy = dL/d(V~ (.) U).  bf16
+// runs the MFMA kernels (g: [T][d] bf16 scratch for dy (.) U); fp32 the one-thread-per-row kernels.
+hipError_t attention_bwd(const mtgr_batch* b, int d, int H, int dtype, int mask_mode, const PrepBufs& pb,
+                         const void* qkvu, const void* vt, const void* dy, void* g, void* dqkvu,
+                         hipStream_t s) {
+  if (dtype == MTGR_BF16)
+    return launch_attention_bwd_bf16(b->num_users, b->num_tokens, xcd_grid_slots(b, H, kAttnQTileBf16), d, H,
+                                     mask_mode, b->offsets, pb.seg, pb.order, pb.xcd_off, b->timestamps,
+                                     static_cast<const bf16*>(qkvu), static_cast<const bf16*>(vt),
+                                     static_cast<const bf16*>(dy), static_cast<bf16*>(g),
+                                     static_cast<bf16*>(dqkvu), s);
+  return launch_attention_bwd_ref(b->num_users, total_tiles(b, kAttnQTileF32), kAttnQTileF32, d, H, mask_mode, 0,
+                                  b->offsets, pb.seg, pb.order, pb.tile_off, b->timestamps, qkvu, vt, dy,
+                                  dqkvu, s);
+}
+
 // One block: x_out = x_in + MLP(GLN2(attn(GLN1(x_in)) (.) U)); x_out may alias x_in.
 hipError_t run_block(const mtgr_block_params* p, const mtgr_batch* b, const PrepBufs& pb,
                      const Plan& pl, void* ws, const float* x_in, float* x_out, hipStream_t s) {
@@ -390,10 +406,8 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   MTGR_BWD_TRY(launch_groupln_bwd(T, d, act, act, shared, y, b->group_ids, p->gln2_gamma, p->ln_eps,
                                   dz, nullptr, dz, act, gpart, s));
   MTGR_BWD_TRY(gln_param_grads(T, d, gpart, g->gln2_gamma, g->gln2_beta, s));
-  // gate and attention: dqkvu from qkvu, V~ and dy
-  MTGR_BWD_TRY(launch_attention_bwd_ref(b->num_users, total_tiles(b, q_tile), q_tile, d, H,
-                                        p->mask_mode, act, b->offsets, pb.seg, pb.order, pb.tile_off,
-                                        b->timestamps, qkvu, vt, dz, dqkvu, s));
+  // gate and attention: dqkvu from qkvu, V~ and dy (G = dy (.) U goes to the free dout buffer)
+  MTGR_BWD_TRY(attention_bwd(b, d, H, dt, p->mask_mode, pb, qkvu, vt, dz, at<void>(ws, pl.dout), dqkvu, s));
   // QKVU: dxt = dqkvu W_qkvu (over dz), dW_qkvu = dqkvu^T xt, db_qkvu = sum dqkvu
   MTGR_BWD_TRY(launch_transpose(4 * (int64_t)d, d, 4 * (int64_t)d, 0, act, p->w_qkvu, wt, s));
   MTGR_BWD_TRY(linear(T, d, 4 * d, dt, MTGR_EPI_STORE, dqkvu, wt, nullptr, nullptr, dz, s));
@@ -503,6 +517,39 @@ mtgr_status mtgr_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, cons
   Sizes z = sizes_for(b, d, h, 0, p->dtype, p->num_heads);
   const BwdPlan pl = make_bwd_plan(z);
   MTGR_TRY(run_block_bwd(p, b, pl, ws, x_in, dx_out, dx_in, g, s));
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_attention_bwd_workspace_size(const mtgr_batch* b, int32_t d, int32_t num_heads,
+                                              int32_t dtype, size_t* bytes) {
+  if (!bytes) return MTGR_ERR_NULL_ARG;
+  mtgr_status st = check_batch(b);
+  if (st != MTGR_OK) return st;
+  if ((st = check_attn_shape(d, num_heads, dtype)) != MTGR_OK) return st;
+  Sizes z = sizes_for(b, d, 0, 0, dtype, num_heads);
+  *bytes = make_plan(z).total + align_up((size_t)b->num_tokens * d * esize(dtype));
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_attention_bwd(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
+                               int32_t mask_mode, const void* qkvu, const void* v_tilde,
+                               const void* dy_gated, void* dqkvu, void* ws, size_t ws_bytes,
+                               void* stream) {
+  size_t need = 0;
+  mtgr_status st = mtgr_attention_bwd_workspace_size(b, d, num_heads, dtype, &need);
+  if (st != MTGR_OK) return st;
+  if (!mask_mode_ok(mask_mode)) return MTGR_ERR_UNSUPPORTED;
+  if (b->num_tokens > 0 && (!qkvu || !v_tilde || !dy_gated || !dqkvu)) return MTGR_ERR_NULL_ARG;
+  if (!ws || ws_bytes < need) return MTGR_ERR_WORKSPACE;
+  if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Sizes z = sizes_for(b, d, 0, 0, dtype, num_heads);
+  const Plan pl = make_plan(z);
+  const PrepBufs pb = prep_bufs(ws, pl);
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), num_heads, pb,
+                       false, s));
+  MTGR_TRY(attention_bwd(b, d, num_heads, dtype, mask_mode, pb, qkvu, v_tilde, dy_gated, at<void>(ws, pl.total),
+                         dqkvu, s));
   return MTGR_OK;
 }
 

@@ -86,6 +86,13 @@ hipError_t launch_attention_bwd_ref(int32_t B, int64_t total_tiles, int q_tile, 
                                     const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                     const int32_t* tile_off, const float* timestamps, const void* qkvu,
                                     const void* vt, const void* dy, void* dqkvu, hipStream_t s);
+// bf16 attention backward on MFMA (attention_bwd.hip): G = dy (.) U into g [T][d] (workspace),
+// dU = dy (.) vt, then dK/dV (key tiles) and dQ (query tiles); work items from the forward's
+// per-XCD queues (xcd_off built with q_tile 128), grid_slots as for launch_attention_bf16
+hipError_t launch_attention_bwd_bf16(int32_t B, int64_t T, int64_t grid_slots, int d, int H, int mask_mode,
+                                     const int64_t* offsets, const UserSeg* seg, const int32_t* order,
+                                     const int32_t* xcd_off, const float* timestamps, const bf16* qkvu,
+                                     const bf16* vt, const bf16* dy, bf16* g, bf16* dqkvu, hipStream_t s);
 // split-K GEMM for weight gradients: part[s][M][N] = a[M][Ks] w[N][Ks]^T over K-range s of ksplit
 // (K a multiple of 64 * ksplit for bf16); no bias
 hipError_t launch_gemm_bf16_splitk(int64_t M, int N, int K, int ksplit, const bf16* a, const bf16* w,

@@ -35,6 +35,7 @@ EXPORTED = [
     "mtgr_block_workspace_size", "mtgr_attention_workspace_size", "mtgr_encoder_fwd",
     "mtgr_block_fwd", "mtgr_groupln_fwd", "mtgr_linear_fwd", "mtgr_attention_fwd",
     "mtgr_validate_batch", "mtgr_debug_mask", "mtgr_block_bwd_workspace_size", "mtgr_block_bwd",
+    "mtgr_attention_bwd_workspace_size", "mtgr_attention_bwd",
 ]
 
 # parameter names of one block, in the field order of mtgr_block_params / mtgr_block_grads
@@ -101,6 +102,9 @@ def lib():
                                          c_vp]
         L.mtgr_validate_batch.argtypes = [P(MtgrBatch), c_vp, c_sz, c_vp, P(c_i32)]
         L.mtgr_debug_mask.argtypes = [P(MtgrBatch), c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
+        L.mtgr_attention_bwd_workspace_size.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, P(c_sz)]
+        L.mtgr_attention_bwd.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
+                                         c_vp, c_sz, c_vp]
         L.mtgr_block_bwd_workspace_size.argtypes = [P(MtgrBlockParams), P(MtgrBatch), P(c_sz)]
         L.mtgr_block_bwd.argtypes = [P(MtgrBlockParams), P(MtgrBatch), c_vp, c_vp, c_vp,
                                      P(MtgrBlockGrads), c_vp, c_sz, c_vp]
@@ -221,6 +225,13 @@ def mtgr_block_bwd_workspace_size(block: MtgrBlockParams, batch: DeviceBatch) ->
     return int(n.value)
 
 
+def mtgr_attention_bwd_workspace_size(batch: DeviceBatch, d: int, num_heads: int, dtype: int) -> int:
+    n = c_sz(0)
+    _check("mtgr_attention_bwd_workspace_size",
+           lib().mtgr_attention_bwd_workspace_size(ctypes.byref(batch.c), d, num_heads, dtype, ctypes.byref(n)))
+    return int(n.value)
+
+
 def workspace(nbytes: int, device="cuda"):
     import torch
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
@@ -271,6 +282,13 @@ def mtgr_attention_fwd(batch: DeviceBatch, d: int, num_heads: int, dtype: int, m
     _check("mtgr_attention_fwd", lib().mtgr_attention_fwd(
         ctypes.byref(batch.c), d, num_heads, dtype, mask_mode, _ptr(qkvu), _ptr(y_gated), _ptr(ws),
         ws.numel(), _stream(stream)))
+
+
+def mtgr_attention_bwd(batch: DeviceBatch, d: int, num_heads: int, dtype: int, mask_mode: int, qkvu,
+                       v_tilde, dy_gated, dqkvu, ws, stream=None):
+    _check("mtgr_attention_bwd", lib().mtgr_attention_bwd(
+        ctypes.byref(batch.c), d, num_heads, dtype, mask_mode, _ptr(qkvu), _ptr(v_tilde), _ptr(dy_gated),
+        _ptr(dqkvu), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def mtgr_validate_batch(batch: DeviceBatch, ws, stream=None) -> int:

@@ -161,6 +161,8 @@ mtgr_status mtgr_attention_workspace_size(const mtgr_batch* b, int32_t d, int32_
                                           size_t* bytes);
 mtgr_status mtgr_block_bwd_workspace_size(const mtgr_block_params* p, const mtgr_batch* b,
                                           size_t* bytes);
+mtgr_status mtgr_attention_bwd_workspace_size(const mtgr_batch* b, int32_t d, int32_t num_heads,
+                                              int32_t dtype, size_t* bytes);
 
 /* ---- the hot path ----------------------------------------------------------------------- */
 /* Full encoder: L blocks over x_in (device float [T][d]) then the head at candidate tokens.
@@ -208,6 +210,17 @@ mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int3
 mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
                                int32_t mask_mode, const void* qkvu, void* y_gated, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* Backward of mtgr_attention_fwd: qkvu device [T][4d], v_tilde device [T][d] (the ungated
+ * V~ = (silu(Q K^T) / N (.) M) V of the forward), dy_gated device [T][d] (dLoss/d(V~ (.) U)), all
+ * in `dtype` -> dqkvu device [T][4d] in `dtype` (dQ, dK, dV, dU).  Every element of dqkvu is
+ * written.  bf16 runs MFMA kernels (P and dS rounded to bf16 as MFMA operands, fp32 accumulation,
+ * no atomics); fp32 runs one thread per (row, head).  The chain rule of the V~ update equation
+ * ([P3] 方法) under the same mask rules as the forward. */
+mtgr_status mtgr_attention_bwd(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
+                               int32_t mask_mode, const void* qkvu, const void* v_tilde,
+                               const void* dy_gated, void* dqkvu, void* ws, size_t ws_bytes,
+                               void* stream);
 
 /* ---- test / debug ------------------------------------------------------------------------ */
 /* Device-side checks of a batch (group ids in 0..3 and non-decreasing within each user, no NaN

@@ -165,3 +165,66 @@ def test_block_bwd_empty_batch_zeroes_gradients():
     assert dx.shape == (0, 64)
     for k, v in got.items():
         assert np.all(v == 0.0), k
+
+
+# ---------------------------------------------------------------------------------------------
+# attention backward alone (mtgr_attention_bwd): inputs exact in the storage dtype, one rounding
+# of each output, P and dS rounded to bf16 as MFMA operands -- the kernel tolerances of the
+# forward (1e-2 bf16, 1e-4 fp32) per block of dqkvu
+# ---------------------------------------------------------------------------------------------
+def custom_batch(lengths, d, seed, dtype, unsorted_r=False, ties=False):
+    rng = np.random.default_rng(seed)
+    n_u, n_s, n_r, k = zip(*lengths)
+    b = synth.batch_from_lengths(n_u, n_s, n_r, k, d, rng, dtype)
+    for u in range(b.num_users):
+        lo = b.offsets[u] + b.n_u[u] + b.n_s[u]
+        hi = lo + b.n_r[u]
+        if unsorted_r:
+            b.timestamps[lo:hi] = rng.permutation(b.timestamps[lo:hi])
+        if ties and hi > lo:
+            kc = b.k[u]
+            b.timestamps[lo:hi + kc] = np.round(b.timestamps[lo:hi + kc] / 600.0) * 600.0
+    return b
+
+
+@pytest.mark.parametrize("dtype,d,H,unsorted_r,mode", [
+    ("bf16", 256, 2, False, "dynamic"), ("bf16", 256, 4, True, "dynamic"), ("bf16", 768, 6, True, "dynamic"),
+    ("bf16", 256, 2, True, "causal"), ("bf16", 256, 4, False, "full"), ("bf16", 128, 1, False, "causal"),
+    ("f32", 64, 2, True, "dynamic"), ("f32", 128, 2, False, "full")])
+def test_attention_bwd_parity(dtype, d, H, unsorted_r, mode):
+    b = custom_batch(EDGE_LENGTHS + [(8, 600, 120, 77), (0, 130, 0, 130)], d, 81, dtype, unsorted_r,
+                     ties=not unsorted_r)
+    db = M.DeviceBatch(b)
+    rng = np.random.default_rng(82)
+    T = b.num_tokens
+    enc = synth.round_to_bf16 if dtype == "bf16" else (lambda a: a)
+    qkvu = rng.standard_normal((T, 4 * d)).astype(np.float32)
+    qkvu[:, :2 * d] *= 2.0 / np.sqrt(np.sqrt(d // H))  # scores with std ~4: the curved part of silu
+    qkvu = enc(qkvu)
+    dy = enc(rng.standard_normal((T, d)).astype(np.float32))
+    # the ungated V~ of the forward, from the oracle (U = 1 turns the gated output into V~)
+    ones_u = qkvu.astype(np.float64)
+    ones_u[:, 3 * d:] = 1.0
+    vt = np.zeros((T, d), np.float32)
+    for u in range(b.num_users):
+        lo, hi = int(b.offsets[u]), int(b.offsets[u + 1])
+        if hi > lo:
+            vt[lo:hi] = O.hstu_attention(ones_u[lo:hi], b.group_ids[lo:hi], b.timestamps[lo:hi], H, mode)
+    vt = enc(vt)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kd = M.MTGR_BF16 if dtype == "bf16" else M.MTGR_F32
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(DEV).to(tdt)
+    dq = torch.full((T, 4 * d), float("nan"), dtype=tdt, device=DEV)
+    ws = M.workspace(M.mtgr_attention_bwd_workspace_size(db, d, H, kd))
+    M.mtgr_attention_bwd(db, d, H, kd, M.MASK_MODES[mode], dev(qkvu), dev(vt), dev(dy), dq, ws)
+    got = to_np(dq)
+    tol = TOL_F32 if dtype == "f32" else 1e-2
+    for u in range(b.num_users):
+        lo, hi = int(b.offsets[u]), int(b.offsets[u + 1])
+        if hi == lo:
+            continue
+        ref = O.hstu_attention_backward(qkvu[lo:hi], b.group_ids[lo:hi], b.timestamps[lo:hi], H, dy[lo:hi], mode)
+        ref[:, 3 * d:] = dy[lo:hi].astype(np.float64) * vt[lo:hi]   # dU from the V~ that was passed in
+        for blk, name in enumerate("QKVU"):
+            sl = slice(blk * d, (blk + 1) * d)
+            assert rel_err(got[lo:hi, sl], ref[:, sl]) < tol, f"user {u} d{name}"
