@@ -2,7 +2,7 @@
 """Benchmark: MTGR HSTU encoder forward (bf16, fp32 accumulation) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload large-bf16] [--no-cpu-baseline]
-                    [--mask dynamic|causal|full] [--norm group|shared]
+                    [--mask dynamic|causal|full] [--norm group|shared] [--block-bwd]
 
 --mask / --norm select the ablation variants (plain causal or full mask in place of the dynamic
 mask, one shared LayerNorm in place of GroupLN); the defaults are the method itself.
@@ -17,6 +17,11 @@ Besides the headline tokens/s the line carries
   * "mfma_util": algorithmic FLOPs of the GEMM + attention launches over their summed durations
     and the bf16 dense MFMA peak;
   * "cpu_baseline": the fp64 CPU oracle timed on this host on a bounded sample of users.
+
+--block-bwd measures the backward pass of one block instead (layer 0 of the workload): one step =
+one mtgr_block_bwd over the whole batch (forward recompute, then dX and every parameter gradient)
+from a synthetic upstream gradient; its roofline entry is the attention backward (the dK/dV and dQ
+launches, 14 * d_model FLOPs per visible pair).
 """
 from __future__ import annotations
 
@@ -94,6 +99,36 @@ def flops_per_layer(b, d, h, mask="dynamic"):
             "attention": 4.0 * d * pairs, "pairs": pairs}
 
 
+def cpu_baseline_block_bwd(b, p, dout, mask="dynamic", norm="group", budget_s=12.0, max_s=30.0):
+    """The oracle's block backward (fp64 numpy) on whole users of the same batch, in index order,
+    until at least `budget_s` seconds of work; tokens of the sample per second."""
+    from oracle import mtgr_oracle as O
+    lay = O.params_layers(p)[0]
+    done, users, t0 = 0, [], time.perf_counter()
+    for u in range(b.num_users):
+        lo, hi = int(b.offsets[u]), int(b.offsets[u + 1])
+        O.block_backward(b.x[lo:hi], b.group_ids[lo:hi], b.timestamps[lo:hi], lay, p.H, dout[lo:hi],
+                         p.ln_eps, mask_mode=mask, shared_norm=(norm == "shared"))
+        done += hi - lo
+        users.append(u)
+        el = time.perf_counter() - t0
+        if el >= budget_s or el >= max_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
+            "sample": f"users {users[0]}..{users[-1]} ({len(users)} users, {done} tokens) of the "
+                      f"same batch, backward of block 0 (forward recompute included), fp64 numpy",
+            "seconds": round(el, 2)}
+
+
+def _oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:
+        return int(os.cpu_count())
+
+
 def cpu_baseline(b, p, mask="dynamic", norm="group", budget_s=12.0, max_s=30.0):
     """The oracle (fp64 numpy, as it stands) on whole users of the same batch, in index order,
     until at least `budget_s` seconds of work; tokens of the sample per second."""
@@ -111,13 +146,7 @@ def cpu_baseline(b, p, mask="dynamic", norm="group", budget_s=12.0, max_s=30.0):
         if el >= budget_s or el >= max_s:
             break
     el = time.perf_counter() - t0
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = os.cpu_count()
-    return {"value": done / el, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": done / el, "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
             "sample": f"users {users[0]}..{users[-1]} ({len(users)} users, {done} tokens) of the "
                       f"same batch, all {p.num_layers} blocks + head, fp64 numpy",
             "seconds": round(el, 2)}
@@ -133,6 +162,8 @@ def main():
     ap.add_argument("--mask", choices=["dynamic", "causal", "full"], default="dynamic")
     ap.add_argument("--norm", choices=["group", "shared"], default="group")
     ap.add_argument("--replay-steps", type=int, default=5)
+    ap.add_argument("--block-bwd", action="store_true",
+                    help="time the backward pass of one block (mtgr_block_bwd) instead of the encoder")
     ap.add_argument("--profile-kernel", choices=["attention", "copy"], default=None,
                     help="run only this kernel --steps times (for rocprofv3 counter runs)")
     args = ap.parse_args()
@@ -169,6 +200,10 @@ def main():
 
     def step():
         M.mtgr_encoder_fwd(dm, db, db.x, hidden, logits, ws)
+
+    if args.block_bwd:
+        bench_block_bwd(args, b, p, db, dm, M, torch)
+        return
 
     if args.profile_kernel == "attention":
         # layer 0's QKVU from one real block pass, then the attention launch alone
@@ -274,6 +309,93 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample of users", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(b, p, args.mask, args.norm)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def bench_block_bwd(args, b, p, db, dm, M, torch):
+    T, d, H, h = b.num_tokens, p.d, p.H, p.h
+    blk = dm.blocks[0]
+    ws = M.workspace(M.mtgr_block_bwd_workspace_size(blk, db))
+    rng = np.random.default_rng(7)
+    dout = rng.standard_normal((T, d)).astype(np.float32)
+    dxo = torch.from_numpy(dout).cuda()
+    dxi = torch.empty_like(dxo)
+    shapes = {"gln1_gamma": (4, d), "gln1_beta": (4, d), "w_qkvu": (4 * d, d), "b_qkvu": (4 * d,),
+              "gln2_gamma": (4, d), "gln2_beta": (4, d), "w_mlp1": (h, d), "b_mlp1": (h,),
+              "w_mlp2": (d, h), "b_mlp2": (d,)}
+    grads = {k: torch.empty(s_, dtype=torch.float32, device="cuda") for k, s_ in shapes.items()}
+
+    def step():
+        M.mtgr_block_bwd(blk, db, db.x, dxo, dxi, grads, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = T * args.steps / elapsed
+    print(f"[bench] block backward {ms_per_step:.2f} ms/step, {tokens_per_s / 1e6:.3f} M tokens/s",
+          file=sys.stderr, flush=True)
+
+    # attention backward alone (prep, gate, dK/dV, dQ) on layer 0's activations, HIP events on the
+    # library's stream
+    stream = torch.cuda.current_stream()
+    bf = torch.bfloat16
+    lay = dm.layers[0]
+    xt = torch.empty(T, d, dtype=bf, device="cuda")
+    qkvu = torch.empty(T, 4 * d, dtype=bf, device="cuda")
+    mask_c, norm_c = M.MASK_MODES[args.mask], M.NORM_MODES[args.norm]
+    M.mtgr_groupln_fwd(db, d, 0, 1, 1, norm_c, lay["gln1_gamma"], lay["gln1_beta"], p.ln_eps, db.x, xt)
+    M.mtgr_linear_fwd(T, 4 * d, d, M.MTGR_BF16, M.MTGR_EPI_STORE, xt, lay["w_qkvu"], lay["b_qkvu"], None, qkvu)
+    vt = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).cuda().to(bf)
+    dy = torch.from_numpy(rng.standard_normal((T, d)).astype(np.float32)).cuda().to(bf)
+    dq = torch.empty(T, 4 * d, dtype=bf, device="cuda")
+    aws = M.workspace(M.mtgr_attention_bwd_workspace_size(db, d, H, M.MTGR_BF16))
+    M.mtgr_attention_bwd(db, d, H, M.MTGR_BF16, mask_c, qkvu, vt, dy, dq, aws)
+    torch.cuda.synchronize()
+    att = 0.0
+    for _ in range(args.replay_steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        M.mtgr_attention_bwd(db, d, H, M.MTGR_BF16, mask_c, qkvu, vt, dy, dq, aws)
+        e1.record(stream)
+        e1.synchronize()
+        att += e0.elapsed_time(e1)
+    att_ms = att / args.replay_steps
+    pairs = int(visible_pairs_per_user(b, args.mask).sum())
+    att_fl = 14.0 * d * pairs
+    att_tflops = att_fl / (att_ms * 1e-3) / 1e12
+    out = {
+        "metric": "block backward tokens/sec (bf16; forward recompute + dX + parameter gradients of "
+                  "one HSTU block) on one MI355X",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "block": 0, "users": b.num_users, "tokens": T,
+                   "d_model": d, "heads": H, "mlp_hidden": h, "mask": args.mask, "norm": args.norm,
+                   "visible_pairs": pairs},
+        "roofline": {"bound": "mfma", "kernel": "attention backward (gate + dK/dV + dQ launches)",
+                     "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": att_fl, "launch_ms": round(att_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle's block backward on a sample of users", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_block_bwd(b, p, dout, args.mask, args.norm)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -269,7 +269,7 @@ hipError_t run_block(const mtgr_block_params* p, const mtgr_batch* b, const Prep
 // and fp32 partial sums (split-K slices of the weight gradients, per-wavefront GroupLN slots).
 struct BwdPlan {
   Plan prep;
-  size_t xt = 0, qkvu = 0, y = 0, vt = 0, z = 0, a = 0, hid = 0, dout = 0, dhid = 0, dz = 0;
+  size_t xt = 0, qkvu = 0, y = 0, vt = 0, z = 0, a = 0, dout = 0, dhid = 0, dz = 0;
   size_t dqkvu = 0, ta = 0, tb = 0, wt = 0, part = 0, gpart = 0, total = 0;
   int ks = 1;
   int64_t Tp = 0;
@@ -303,7 +303,6 @@ BwdPlan make_bwd_plan(const Sizes& z) {
   p.vt = take(T * d * es);
   p.z = take(T * d * es);
   p.a = take(T * h * es);
-  p.hid = take(T * h * es);
   p.dout = take(z.dtype == MTGR_BF16 ? T * d * es : 0);
   p.dhid = take(T * h * es);
   p.dz = take(T * d * es);
@@ -357,7 +356,6 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   void* vt = at<void>(ws, pl.vt);
   void* z = at<void>(ws, pl.z);
   void* a = at<void>(ws, pl.a);
-  void* hid = at<void>(ws, pl.hid);
   void* dhid = at<void>(ws, pl.dhid);
   void* dz = at<void>(ws, pl.dz);
   void* dqkvu = at<void>(ws, pl.dqkvu);
@@ -374,7 +372,7 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   } while (0)
   MTGR_BWD_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile, H, pb, false, s));
   // forward, keeping what the backward needs: GLN1 output, QKVU, V~, the gated output, GLN2
-  // output, the MLP pre-activation and its SiLU
+  // output and the MLP pre-activation (its SiLU is applied where it is read, in a transpose)
   MTGR_BWD_TRY(launch_groupln(T, d, 0, act, act, shared, x_in, b->group_ids, p->gln1_gamma,
                               p->gln1_beta, p->ln_eps, xt, s));
   MTGR_BWD_TRY(linear(T, 4 * d, d, dt, MTGR_EPI_STORE, xt, p->w_qkvu, p->b_qkvu, nullptr, qkvu, s));
@@ -382,7 +380,6 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   MTGR_BWD_TRY(launch_groupln(T, d, act, act, act, shared, y, b->group_ids, p->gln2_gamma,
                               p->gln2_beta, p->ln_eps, z, s));
   MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, z, p->w_mlp1, p->b_mlp1, nullptr, a, s));
-  MTGR_BWD_TRY(launch_silu(T * h, act, a, hid, s));
 
   // MLP2: dhid = dout W2, dW2 = dout^T hid, db2 = sum dout
   const void* dout = dx_out;
@@ -390,17 +387,17 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
     MTGR_BWD_TRY(launch_convert(T * d, act, dx_out, at<void>(ws, pl.dout), s));
     dout = at<void>(ws, pl.dout);
   }
-  MTGR_BWD_TRY(launch_transpose(d, h, d, 0, act, p->w_mlp2, wt, s));
+  MTGR_BWD_TRY(launch_transpose(d, h, d, 0, 0, act, p->w_mlp2, wt, s));
   MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, dout, wt, nullptr, nullptr, dhid, s));
-  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 0, act, dout, ta, s));
-  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp, 1, act, hid, tb, s));
+  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 0, 0, act, dout, ta, s));
+  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp, 1, 1, act, a, tb, s));     // silu(a)^T = hid^T
   MTGR_BWD_TRY(weight_grad(pl, ws, dt, d, h, ta, tb, g->w_mlp2, g->b_mlp2, s));
   // MLP1: da = dhid (.) silu'(a) (in place), dz = da W1, dW1 = da^T z, db1 = sum da
   MTGR_BWD_TRY(launch_silu_bwd(T * h, act, a, dhid, s));
-  MTGR_BWD_TRY(launch_transpose(h, d, h, 0, act, p->w_mlp1, wt, s));
+  MTGR_BWD_TRY(launch_transpose(h, d, h, 0, 0, act, p->w_mlp1, wt, s));
   MTGR_BWD_TRY(linear(T, d, h, dt, MTGR_EPI_STORE, dhid, wt, nullptr, nullptr, dz, s));
-  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp, 0, act, dhid, ta, s));
-  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 1, act, z, tb, s));
+  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp, 0, 0, act, dhid, ta, s));
+  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 1, 0, act, z, tb, s));
   MTGR_BWD_TRY(weight_grad(pl, ws, dt, h, d, ta, tb, g->w_mlp1, g->b_mlp1, s));
   // GLN2: dy (in place over dz) and the GLN2 parameter gradients
   MTGR_BWD_TRY(launch_groupln_bwd(T, d, act, act, shared, y, b->group_ids, p->gln2_gamma, p->ln_eps,
@@ -409,10 +406,10 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   // gate and attention: dqkvu from qkvu, V~ and dy (G = dy (.) U goes to the free dout buffer)
   MTGR_BWD_TRY(attention_bwd(b, d, H, dt, p->mask_mode, pb, qkvu, vt, dz, at<void>(ws, pl.dout), dqkvu, s));
   // QKVU: dxt = dqkvu W_qkvu (over dz), dW_qkvu = dqkvu^T xt, db_qkvu = sum dqkvu
-  MTGR_BWD_TRY(launch_transpose(4 * (int64_t)d, d, 4 * (int64_t)d, 0, act, p->w_qkvu, wt, s));
+  MTGR_BWD_TRY(launch_transpose(4 * (int64_t)d, d, 4 * (int64_t)d, 0, 0, act, p->w_qkvu, wt, s));
   MTGR_BWD_TRY(linear(T, d, 4 * d, dt, MTGR_EPI_STORE, dqkvu, wt, nullptr, nullptr, dz, s));
-  MTGR_BWD_TRY(launch_transpose(T, 4 * d, pl.Tp, 0, act, dqkvu, ta, s));
-  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 1, act, xt, tb, s));
+  MTGR_BWD_TRY(launch_transpose(T, 4 * d, pl.Tp, 0, 0, act, dqkvu, ta, s));
+  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 1, 0, act, xt, tb, s));
   MTGR_BWD_TRY(weight_grad(pl, ws, dt, 4 * d, d, ta, tb, g->w_qkvu, g->b_qkvu, s));
   // GLN1 plus the residual path: dx_in = dx_out + GLN1'(x_in)^T dxt
   MTGR_BWD_TRY(launch_groupln_bwd(T, d, 0, act, shared, x_in, b->group_ids, p->gln1_gamma, p->ln_eps,

@@ -19,10 +19,13 @@ template <typename T>
 __device__ __forceinline__ T cvt(float v) { return from_f32<T>(v); }
 
 // ---- transposes -----------------------------------------------------------------------------
-// dst[c][r] = src[r][c] for r < R, c < C; dst[c][r] = 0 for R <= r < Rp; with ones_row, an extra
-// row dst[C][r] = (r < R) and rows C+1 .. C+7 zero.  dst row pitch Rp.  64 x 64 tiles via LDS.
+// dst[c][r] = f(src[r][c]) for r < R, c < C (f = silu when `act`, else the identity); dst[c][r] = 0
+// for R <= r < Rp; with ones_row, an extra row dst[C][r] = (r < R) and rows C+1 .. C+7 zero.  dst
+// row pitch Rp.  64 x 64 tiles through LDS.  The bf16 variant moves 16-byte row pieces (C and Rp
+// multiples of 8): each thread reads 8 consecutive columns of one source row and writes 8
+// consecutive rows of one destination row.
 template <typename T>
-__global__ __launch_bounds__(256) void k_transpose(int64_t R, int C, int64_t Rp, int ones_row,
+__global__ __launch_bounds__(256) void k_transpose(int64_t R, int C, int64_t Rp, int ones_row, int act,
                                                    const T* __restrict__ src, T* __restrict__ dst) {
   __shared__ float tile[64][65];
   const int64_t r0 = (int64_t)blockIdx.y * 64;
@@ -34,7 +37,7 @@ __global__ __launch_bounds__(256) void k_transpose(int64_t R, int C, int64_t Rp,
     const int c = c0 + tx;
     float v = 0.f;
     if (r < R) {
-      if (c < C) v = to_f32(src[r * C + c]);
+      if (c < C) { v = to_f32(src[r * C + c]); if (act) v = silu_f32(v); }
       else if (ones_row && c == C) v = 1.f;
     }
     tile[i][tx] = v;
@@ -47,14 +50,63 @@ __global__ __launch_bounds__(256) void k_transpose(int64_t R, int C, int64_t Rp,
   }
 }
 
-// ---- elementwise ----------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void k_silu(int64_t n, const T* __restrict__ a, T* __restrict__ out) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    out[i] = cvt<T>(silu_f32(to_f32(a[i])));
+__global__ __launch_bounds__(256) void k_transpose_bf16x8(int64_t R, int C, int64_t Rp, int ones_row, int act,
+                                                          const bf16* __restrict__ src, bf16* __restrict__ dst) {
+  __shared__ float tile[64][65];
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  const int c0 = blockIdx.x * 64;
+  const int crows = C + (ones_row ? 8 : 0);
+  // load: 64 rows x 8 chunks of 8 columns; thread -> (row lr, chunk lc), two rows per thread
+  const int lc = threadIdx.x & 7, lr = threadIdx.x >> 3;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = lr + 32 * k;
+    const int64_t r = r0 + i;
+    const int c = c0 + lc * 8;
+    float v[8];
+    if (r < R && c < C) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + r * C + c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = act ? silu_f32((float)x[e]) : (float)x[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = (r < R && ones_row && c + e == C) ? 1.f : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[i][lc * 8 + e] = v[e];
+  }
+  __syncthreads();
+  // store: 64 destination rows (source columns) x 8 chunks of 8 source rows
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int i = lr + 32 * k;      // destination row c0 + i
+    const int c = c0 + i;
+    const int64_t r = r0 + lc * 8;
+    if (c < crows && r < Rp) {
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = (bf16)tile[lc * 8 + e][i];
+      *reinterpret_cast<bf16x8*>(dst + (int64_t)c * Rp + r) = o;
+    }
+  }
 }
 
-// dh <- dh (.) silu'(a), silu'(z) = sigma(z) (1 + z (1 - sigma(z)))
+// ---- elementwise ----------------------------------------------------------------------------
+// dh <- dh (.) silu'(a), silu'(z) = sigma(z) (1 + z (1 - sigma(z))); bf16: 8 elements per step
+__device__ __forceinline__ float silu_grad_f32(float z) {
+  const float sg = 1.0f / (1.0f + __expf(-z));
+  return sg * (1.0f + z * (1.0f - sg));
+}
+__global__ __launch_bounds__(256) void k_silu_bwd_bf16x8(int64_t n8, const bf16* __restrict__ a, bf16* __restrict__ dh) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    const bf16x8 z = *reinterpret_cast<const bf16x8*>(a + i * 8);
+    bf16x8 g = *reinterpret_cast<const bf16x8*>(dh + i * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) g[e] = (bf16)((float)g[e] * silu_grad_f32((float)z[e]));
+    *reinterpret_cast<bf16x8*>(dh + i * 8) = g;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_silu_bwd(int64_t n, const T* __restrict__ a, T* __restrict__ dh) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
@@ -71,13 +123,27 @@ __global__ __launch_bounds__(256) void k_convert(int64_t n, const float* __restr
 }
 
 // ---- partial-sum reduction ------------------------------------------------------------------
-// out[i] = sum_s part[s * stride + i] (i < n), s in fixed order.
-__global__ __launch_bounds__(256) void k_reduce(int64_t n, int nsplit, int64_t stride,
-                                                const float* __restrict__ part, float* __restrict__ out) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
-    float acc = 0.f;
-    for (int s = 0; s < nsplit; ++s) acc += part[s * stride + i];
-    out[i] = acc;
+// out[i] = sum_s part[s * stride + i] (i < n).  A block takes 64 columns; its 16 wavefronts sum the
+// slots s = w, w + 16, ... in increasing order, and the 16 partial sums are added in wavefront
+// order: a fixed summation order, so the result does not depend on scheduling.
+constexpr int kReduceWaves = 16;
+__global__ __launch_bounds__(64 * kReduceWaves) void k_reduce(int64_t n, int nsplit, int64_t stride,
+                                                             const float* __restrict__ part, float* __restrict__ out) {
+  __shared__ float accw[kReduceWaves][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t i = (int64_t)blockIdx.x * 64 + lane;
+  float acc = 0.f;
+  if (i < n) {
+#pragma unroll 8
+    for (int s = w; s < nsplit; s += kReduceWaves) acc += part[s * stride + i];
+  }
+  accw[w][lane] = acc;
+  __syncthreads();
+  if (w == 0 && i < n) {
+    float t = accw[0][lane];
+#pragma unroll
+    for (int k = 1; k < kReduceWaves; ++k) t += accw[k][lane];
+    out[i] = t;
   }
 }
 
@@ -329,28 +395,26 @@ inline unsigned ew_grid(int64_t n) { return (unsigned)std::min<int64_t>((n + 255
 
 }  // namespace
 
-hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int kind, const void* src,
+hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int act, int kind, const void* src,
                             void* dst, hipStream_t s) {
   if (R == 0 && Rp == 0) return hipSuccess;
   const int crows = C + (ones_row ? 8 : 0);
   dim3 grid((unsigned)((crows + 63) / 64), (unsigned)((Rp + 63) / 64));
-  if (kind == 1)
-    k_transpose<bf16><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, static_cast<const bf16*>(src), static_cast<bf16*>(dst));
+  if (kind == 1 && C % 8 == 0 && Rp % 8 == 0)
+    k_transpose_bf16x8<<<grid, 256, 0, s>>>(R, C, Rp, ones_row, act, static_cast<const bf16*>(src),
+                                             static_cast<bf16*>(dst));
+  else if (kind == 1)
+    k_transpose<bf16><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, act, static_cast<const bf16*>(src), static_cast<bf16*>(dst));
   else
-    k_transpose<float><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, static_cast<const float*>(src), static_cast<float*>(dst));
-  return hipGetLastError();
-}
-
-hipError_t launch_silu(int64_t n, int kind, const void* a, void* out, hipStream_t s) {
-  if (n == 0) return hipSuccess;
-  if (kind == 1) k_silu<bf16><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const bf16*>(a), static_cast<bf16*>(out));
-  else k_silu<float><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const float*>(a), static_cast<float*>(out));
+    k_transpose<float><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, act, static_cast<const float*>(src), static_cast<float*>(dst));
   return hipGetLastError();
 }
 
 hipError_t launch_silu_bwd(int64_t n, int kind, const void* a, void* dh, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (kind == 1) k_silu_bwd<bf16><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const bf16*>(a), static_cast<bf16*>(dh));
+  if (kind == 1 && n % 8 == 0)
+    k_silu_bwd_bf16x8<<<ew_grid(n / 8), 256, 0, s>>>(n / 8, static_cast<const bf16*>(a), static_cast<bf16*>(dh));
+  else if (kind == 1) k_silu_bwd<bf16><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const bf16*>(a), static_cast<bf16*>(dh));
   else k_silu_bwd<float><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const float*>(a), static_cast<float*>(dh));
   return hipGetLastError();
 }
@@ -364,7 +428,7 @@ hipError_t launch_convert(int64_t n, int kind, const float* x, void* y, hipStrea
 
 hipError_t launch_reduce(int64_t n, int nsplit, int64_t stride, const float* part, float* out, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  k_reduce<<<ew_grid(n), 256, 0, s>>>(n, nsplit, stride, part, out);
+  k_reduce<<<(unsigned)((n + 63) / 64), 64 * kReduceWaves, 0, s>>>(n, nsplit, stride, part, out);
   return hipGetLastError();
 }
 
@@ -377,7 +441,7 @@ hipError_t launch_reduce_wb(int M, int K, int Kx, int nsplit, const float* part,
 }
 
 // wavefronts of the GroupLN backward: one slot [2][4][d] of partial parameter gradients each
-int groupln_bwd_waves(int64_t T) { return 4 * (int)std::max<int64_t>(1, std::min<int64_t>(256, (T + 255) / 256)); }
+int groupln_bwd_waves(int64_t T) { return 4 * (int)std::max<int64_t>(1, std::min<int64_t>(1024, (T + 255) / 256)); }
 
 hipError_t launch_groupln_bwd(int64_t T, int d, int x_kind, int act_kind, int shared, const void* x,
                               const uint8_t* g, const void* gamma, float eps, const void* dz,

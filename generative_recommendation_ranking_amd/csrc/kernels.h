@@ -61,11 +61,10 @@ hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H, in
 
 // ---- backward pieces (backward.hip) -------------------------------------------------------------
 // kind / *_kind: 0 = float, 1 = bf16
-// dst[c][r] = src[r][c] (r < R, c < C), zero for R <= r < Rp; ones_row adds row C = (r < R) and
-// rows C+1..C+7 = 0.  dst row pitch Rp.
-hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int kind, const void* src,
+// dst[c][r] = f(src[r][c]) (r < R, c < C; f = silu if act, else identity), zero for R <= r < Rp;
+// ones_row adds row C = (r < R) and rows C+1..C+7 = 0.  dst row pitch Rp.
+hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int act, int kind, const void* src,
                             void* dst, hipStream_t s);
-hipError_t launch_silu(int64_t n, int kind, const void* a, void* out, hipStream_t s);
 hipError_t launch_silu_bwd(int64_t n, int kind, const void* a, void* dh, hipStream_t s);
 hipError_t launch_convert(int64_t n, int kind, const float* x, void* y, hipStream_t s);
 // out[i] = sum over s < nsplit of part[s*stride + i]
