@@ -527,3 +527,183 @@ def test_block_backward_batch_sums_users_and_isolates_them():
     np.testing.assert_array_equal(dx[n:], dxb)
     for k in grads:
         np.testing.assert_allclose(grads[k], ga[k] + gb[k], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# embedding front end oracle (oracle/embedding_oracle.py)
+# ---------------------------------------------------------------------------------------------
+from oracle import embedding_oracle as EO
+
+
+class _PairListStore:
+    """Brute force: a plain list of [key, value, last_seen] entries and a count of free rows."""
+
+    def __init__(self, rows, dim):
+        self.entries, self.rows, self.dim, self.failed = [], rows, dim, 0
+
+    def _find(self, k):
+        for e in self.entries:
+            if e[0] == k:
+                return e
+        return None
+
+    def insert(self, keys, init, step):
+        for i, k in enumerate(keys):
+            e = self._find(int(k))
+            if e is None:
+                if int(k) < 0 or len(self.entries) >= self.rows:
+                    self.failed += 1
+                    continue
+                e = [int(k), np.zeros(self.dim) if init is None else np.asarray(init[i], float), step]
+                self.entries.append(e)
+            e[2] = step
+
+    def lookup(self, keys, step=-1):
+        out, found = np.zeros((len(keys), self.dim)), np.zeros(len(keys), bool)
+        for i, k in enumerate(keys):
+            e = self._find(int(k))
+            if e is not None:
+                out[i], found[i] = e[1], True
+                if step >= 0:
+                    e[2] = step
+        return out, found
+
+    def evict(self, keys):
+        ks = {int(k) for k in keys}
+        self.entries = [e for e in self.entries if e[0] not in ks]
+
+    def evict_older(self, threshold):
+        self.entries = [e for e in self.entries if e[2] >= threshold]
+
+
+def test_store_model_matches_brute_force_on_random_operations():
+    rng = np.random.default_rng(5)
+    rows, dim = 40, 3
+    a, b = EO.EmbeddingStore(rows, dim), _PairListStore(rows, dim)
+    for step in range(300):
+        op = rng.integers(0, 4)
+        keys = rng.integers(-1, 70, rng.integers(1, 9))
+        if op == 0:
+            init = rng.standard_normal((len(keys), dim))
+            a.insert(keys, init, step)
+            b.insert(keys, init, step)
+        elif op == 1:
+            st = step if rng.random() < 0.5 else -1
+            va, fa = a.lookup(keys, st)
+            vb, fb = b.lookup(keys, st)
+            np.testing.assert_array_equal(fa, fb)
+            np.testing.assert_array_equal(va, vb)
+        elif op == 2:
+            a.evict(keys)
+            b.evict(keys)
+        else:
+            th = step - int(rng.integers(0, 40))
+            a.evict_older(th)
+            b.evict_older(th)
+        assert sorted(a.index) == sorted(e[0] for e in b.entries)
+        assert a.failed == b.failed
+        # invariants: live + free = rows, live rows distinct
+        assert len(a.index) + len(a.free) == rows
+        assert len(set(a.index.values())) == len(a.index)
+
+
+def test_store_model_insert_keeps_existing_value_and_fails_when_full():
+    s = EO.EmbeddingStore(2, 2)
+    r = s.insert([7, 7, 9], np.array([[1., 1.], [2., 2.], [3., 3.]]), step=0)
+    assert r[0] == r[1] != r[2]
+    v, f = s.lookup([7, 9, 11])
+    np.testing.assert_array_equal(v, [[1, 1], [3, 3], [0, 0]])
+    np.testing.assert_array_equal(f, [True, True, False])
+    assert s.insert([12], None, step=1) == [-1] and s.stats()["failed_inserts"] == 1
+    s.evict([7])
+    assert s.insert([12], None, step=2)[0] >= 0              # the freed row is reused
+    v, f = s.lookup([7, 12])
+    np.testing.assert_array_equal(f, [False, True])
+    np.testing.assert_array_equal(v[1], [0, 0])               # no init -> zeros
+
+
+def test_store_model_evict_older_uses_last_use():
+    s = EO.EmbeddingStore(8, 1)
+    s.insert([1, 2, 3], None, step=0)
+    s.lookup([2], step=5)
+    s.insert([3], None, step=7)
+    s.evict_older(5)
+    assert sorted(s.index) == [2, 3]
+
+
+def test_unique_with_inverse_against_sets():
+    rng = np.random.default_rng(6)
+    keys = rng.integers(0, 1 << 45, 500) // 1000 * 1000 + rng.integers(0, 3, 500)
+    uniq, inv = EO.unique_with_inverse(keys)
+    assert set(uniq.tolist()) == set(keys.tolist()) and len(uniq) == len(set(keys.tolist()))
+    np.testing.assert_array_equal(uniq[inv], keys)
+    assert np.all(np.diff(uniq) > 0)
+
+
+def test_merged_key_separates_tables():
+    assert EO.merged_key(0, 5) != EO.merged_key(1, 5)
+    assert EO.merged_key(3, 0) == 3 << 40
+    with pytest.raises(ValueError):
+        EO.merged_key(1, 1 << 40)
+
+
+def _tok_case(seed, e=4, d=6):
+    rng = np.random.default_rng(seed)
+    field_tables = [[0, 1], [2, 3, 4], [2, 3, 5], [2, 3, 6, 7]]      # item tables 2, 3 shared
+    T = 40
+    groups = np.sort(rng.integers(0, 4, T)).astype(np.int64)
+    fmax = max(len(f) for f in field_tables)
+    ids = rng.integers(0, 12, (T, fmax)).astype(np.int64)
+    store = EO.EmbeddingStore(200, e)
+    keys, vals = [], []
+    for tab in range(8):
+        for i in range(12):
+            if (tab + i) % 5 != 0:                                   # some keys absent: zeros
+                keys.append(EO.merged_key(tab, i))
+                vals.append(rng.standard_normal(e))
+    store.insert(keys, np.array(vals), step=0)
+    mlps = [{"w1": rng.standard_normal((d, len(f) * e)), "b1": rng.standard_normal(d),
+             "w2": rng.standard_normal((d, d)), "b2": rng.standard_normal(d)} for f in field_tables]
+    return ids, groups, field_tables, store, mlps
+
+
+def test_tokenizer_matches_torch_modules():
+    ids, groups, field_tables, store, mlps = _tok_case(7)
+    x = EO.tokenize(ids, groups, field_tables, store, mlps)
+    # independent formulation: one nn.Embedding per table (absent keys -> zero rows), cat, two
+    # nn.Linear layers with SiLU, per group
+    e = store.dim
+    embs = []
+    for tab in range(8):
+        w = torch.zeros(12, e, dtype=torch.float64)
+        for i in range(12):
+            k = EO.merged_key(tab, i)
+            if k in store.index:
+                w[i] = torch.from_numpy(store.values[store.index[k]])
+        embs.append(torch.nn.Embedding.from_pretrained(w))
+    for t in range(ids.shape[0]):
+        g = int(groups[t])
+        feat = torch.cat([embs[tab](torch.tensor(int(ids[t, f]))) for f, tab in enumerate(field_tables[g])])
+        l1 = torch.nn.Linear(feat.numel(), mlps[g]["w1"].shape[0], dtype=torch.float64)
+        l2 = torch.nn.Linear(mlps[g]["w2"].shape[1], mlps[g]["w2"].shape[0], dtype=torch.float64)
+        with torch.no_grad():
+            l1.weight.copy_(torch.from_numpy(mlps[g]["w1"])); l1.bias.copy_(torch.from_numpy(mlps[g]["b1"]))
+            l2.weight.copy_(torch.from_numpy(mlps[g]["w2"])); l2.bias.copy_(torch.from_numpy(mlps[g]["b2"]))
+            ref = l2(torch.nn.functional.silu(l1(feat)))
+        np.testing.assert_allclose(x[t], ref.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_tokenizer_is_per_token_and_ignores_unused_columns():
+    ids, groups, field_tables, store, mlps = _tok_case(8)
+    x = EO.tokenize(ids, groups, field_tables, store, mlps)
+    perm = np.random.default_rng(9).permutation(len(groups))
+    xp = EO.tokenize(ids[perm], groups[perm], field_tables, store, mlps)
+    np.testing.assert_allclose(xp, x[perm], rtol=0, atol=0)
+    ids2 = ids.copy()
+    for t in range(len(groups)):
+        ids2[t, len(field_tables[int(groups[t])]):] = 999999   # columns past the group's fields
+    np.testing.assert_array_equal(EO.tokenize(ids2, groups, field_tables, store, mlps), x)
+    for m in mlps:
+        m["w2"] = np.zeros_like(m["w2"])
+    x0 = EO.tokenize(ids, groups, field_tables, store, mlps)   # W2 = 0 -> x = b2 of the group
+    np.testing.assert_array_equal(x0, np.stack([mlps[int(g)]["b2"] for g in groups]))
