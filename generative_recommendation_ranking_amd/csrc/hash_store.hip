@@ -1,0 +1,394 @@
+// Hash embedding store and batch key dedup on gfx950.
+//
+// The store follows the pages' decoupled design (marovi.ai MTGR page, 方法, training-framework
+// paragraph; chenhuiyu blog "MTGR", training-system section): a compact index from key to row
+// pointer plus a separate value arena, so keys can be inserted and evicted in real time and the
+// index can be rebuilt larger without touching the values.
+//
+// Index: open addressing over lines of 8 slots {int64 key, int32 row, int32 pad} (128 bytes, one
+// cache line).  A key's home line comes from a 64-bit mix of the key; lines are probed in order.
+// One team of 8 lanes handles one key and reads a whole line with one 16-byte load per lane.  A
+// new key goes to the first empty slot of the first line (in probe order) that is not full, so a
+// lookup may stop at the first line holding an empty slot.  Slots move only from empty to a key
+// (claim, compare-and-swap on the key) and from a key to a tombstone (evict); a tombstone is never
+// reused until the index is rebuilt.  So two teams inserting the same key always contend for the
+// same slot, and the loser finds the winner's key.
+//
+// Arena: a stack of free rows, the step each row was last used, and the values [rows][dim].
+//
+// Insert runs in three launches so that no thread ever waits for another thread's write inside
+// one launch: claim (find or claim a slot per key), assign (each claimed slot pops a free row and
+// initialises it; with no row left the slot becomes a tombstone), resolve (every occurrence reads
+// its key's row).  The dedup of a batch uses the same claim step on a scratch index and numbers
+// the distinct keys in claim order.
+#include <algorithm>
+
+#include "kernels.h"
+
+namespace mtgr {
+
+namespace {
+
+constexpr int64_t kEmpty = -1;
+constexpr int64_t kTomb = -2;
+constexpr int kTeam = 8;            // lanes per key = slots per line
+
+struct Slot {
+  int64_t key;
+  int32_t row;
+  int32_t pad;
+};
+static_assert(sizeof(Slot) == 16, "slot layout");
+
+struct IndexHeader {                // at the start of the index memory (256 bytes reserved)
+  unsigned long long live;
+  unsigned long long tombstones;
+  unsigned long long dropped;       // entries a rebuild could not place
+};
+struct ArenaHeader {                // at the start of the arena memory (256 bytes reserved)
+  int32_t free_top;                 // number of rows on the free stack
+  int32_t failed;                   // insert occurrences that got no row (since init)
+};
+
+// MurmurHash3's 64-bit finaliser (Appleby, public domain): a bijective mix of all key bits.
+__device__ __forceinline__ uint64_t mix64(uint64_t k) {
+  k ^= k >> 33;
+  k *= 0xff51afd7ed558ccdULL;
+  k ^= k >> 33;
+  k *= 0xc4ceb9fe1a85ec53ULL;
+  k ^= k >> 33;
+  return k;
+}
+
+__device__ __forceinline__ uint32_t team_ballot(bool p, int lane) {
+  return (uint32_t)((__ballot(p) >> (lane & ~(kTeam - 1))) & 0xFFu);
+}
+
+// agent-coherent load of a slot key (the claim step reads lines other teams are writing)
+__device__ __forceinline__ int64_t load_key_coherent(const Slot* s) {
+  return __hip_atomic_load(&s->key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+struct View {
+  IndexHeader* ih;
+  Slot* slots;
+  int64_t lmask;                    // lines - 1
+  ArenaHeader* ah;
+  int32_t* free_stack;
+  int32_t* last_seen;
+  char* values;
+  int32_t rows;
+  int32_t row_bytes;
+};
+
+// Find or claim the slot of `key` (team-uniform).  Returns the slot index, with bit 62 set when
+// this team claimed it, or -1 when the index has no room.  Keys must be >= 0.
+__device__ int64_t claim(const View& v, int64_t key, int lane) {
+  const int sub = lane & (kTeam - 1);
+  int64_t line = (int64_t)(mix64((uint64_t)key) >> 3) & v.lmask;
+  for (int64_t probe = 0; probe <= v.lmask; ++probe) {
+    Slot* ls = v.slots + line * kTeam;
+    for (;;) {
+      const int64_t k = load_key_coherent(ls + sub);
+      const uint32_t m = team_ballot(k == key, lane);
+      if (m) return line * kTeam + (__ffs(m) - 1);
+      const uint32_t e = team_ballot(k == kEmpty, lane);
+      if (!e) break;                                   // full line: next one
+      const int first = __ffs(e) - 1;
+      int64_t old = 0;
+      if (sub == first) {
+        unsigned long long* p = reinterpret_cast<unsigned long long*>(&ls[first].key);
+        old = (int64_t)atomicCAS(p, (unsigned long long)kEmpty, (unsigned long long)key);
+      }
+      old = __shfl(old, (lane & ~(kTeam - 1)) + first, kWave);
+      if (old == kEmpty) return (line * kTeam + first) | (1LL << 62);
+      if (old == key) return line * kTeam + first;
+      // another key took the slot: read the line again
+    }
+    line = (line + 1) & v.lmask;
+  }
+  return -1;
+}
+
+// Slot index of `key`, or -1 (no concurrent writers: plain loads).
+__device__ int64_t find(const View& v, int64_t key, int lane) {
+  const int sub = lane & (kTeam - 1);
+  int64_t line = (int64_t)(mix64((uint64_t)key) >> 3) & v.lmask;
+  for (int64_t probe = 0; probe <= v.lmask; ++probe) {
+    const int64_t k = v.slots[line * kTeam + sub].key;
+    const uint32_t m = team_ballot(k == key, lane);
+    if (m) return line * kTeam + (__ffs(m) - 1);
+    if (team_ballot(k == kEmpty, lane)) return -1;
+    line = (line + 1) & v.lmask;
+  }
+  return -1;
+}
+
+// copy one value row (row_bytes, a multiple of 16) by the 8 lanes of a team; src NULL -> zeros
+__device__ __forceinline__ void team_copy(char* dst, const char* src, int row_bytes, int sub) {
+  for (int c = sub * 16; c < row_bytes; c += kTeam * 16) {
+    uint4 v = src ? *reinterpret_cast<const uint4*>(src + c) : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(dst + c) = v;
+  }
+}
+
+inline unsigned team_grid(int64_t n) {
+  const int64_t blocks = (n * kTeam + 255) / 256;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(blocks, 65536));
+}
+
+// ---- kernels ------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_index_init(Slot* slots, int64_t nslots, IndexHeader* ih) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < nslots; i += stride) {
+    slots[i].key = kEmpty;
+    slots[i].row = -1;
+    slots[i].pad = 0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) { ih->live = 0; ih->tombstones = 0; ih->dropped = 0; }
+}
+
+__global__ __launch_bounds__(256) void k_arena_init(ArenaHeader* ah, int32_t* free_stack, int32_t* last_seen,
+                                                    int32_t rows) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < rows; i += stride) {
+    free_stack[i] = rows - 1 - (int32_t)i;     // popped from the top: rows 0, 1, 2, ...
+    last_seen[i] = 0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) { ah->free_top = rows; ah->failed = 0; }
+}
+
+__global__ __launch_bounds__(256) void k_claim(View v, int64_t n, const int64_t* __restrict__ keys,
+                                               int64_t* __restrict__ res) {
+  const int lane = threadIdx.x & 63;
+  const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
+  const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
+  for (int64_t i = team; i < n; i += teams) {
+    const int64_t key = keys[i];
+    const int64_t r = key >= 0 ? claim(v, key, lane) : -1;
+    if ((lane & (kTeam - 1)) == 0) res[i] = r;
+  }
+}
+
+// claimed slots take a free row and initialise it; with none left the slot becomes a tombstone
+__global__ __launch_bounds__(256) void k_assign(View v, int64_t n, int64_t* __restrict__ res,
+                                                const char* __restrict__ init, int32_t step) {
+  const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
+  const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
+  const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
+  for (int64_t i = team; i < n; i += teams) {
+    const int64_t r = res[i];
+    if (r < 0 || !(r & (1LL << 62))) continue;
+    const int64_t slot = r & ((1LL << 62) - 1);
+    int32_t row = -1;
+    if (sub == 0) {
+      const int32_t t = atomicSub(&v.ah->free_top, 1);
+      if (t >= 1) {
+        row = v.free_stack[t - 1];
+        v.slots[slot].row = row;
+        v.last_seen[row] = step;
+        atomicAdd(&v.ih->live, 1ULL);
+      } else {
+        v.slots[slot].key = kTomb;
+        atomicAdd(&v.ih->tombstones, 1ULL);
+      }
+    }
+    row = __shfl(row, lane & ~(kTeam - 1), kWave);
+    if (row >= 0)
+      team_copy(v.values + (int64_t)row * v.row_bytes, init ? init + i * v.row_bytes : nullptr, v.row_bytes, sub);
+  }
+}
+
+// every occurrence reads its key's row; failures are counted per occurrence
+__global__ __launch_bounds__(256) void k_resolve(View v, int64_t n, const int64_t* __restrict__ res,
+                                                 int32_t* __restrict__ rows_out, int32_t step) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if (blockIdx.x == 0 && threadIdx.x == 0 && v.ah->free_top < 0) v.ah->free_top = 0;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t r = res[i];
+    int32_t row = -1;
+    if (r >= 0) {
+      const int64_t slot = r & ((1LL << 62) - 1);
+      if (v.slots[slot].key != kTomb) row = v.slots[slot].row;
+    }
+    if (row >= 0) v.last_seen[row] = step;
+    else atomicAdd(&v.ah->failed, 1);
+    if (rows_out) rows_out[i] = row;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_lookup(View v, int64_t n, const int64_t* __restrict__ keys, int32_t step,
+                                                char* __restrict__ out, int32_t* __restrict__ rows_out) {
+  const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
+  const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
+  const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
+  for (int64_t i = team; i < n; i += teams) {
+    const int64_t key = keys[i];
+    const int64_t slot = key >= 0 ? find(v, key, lane) : -1;
+    const int32_t row = slot >= 0 ? v.slots[slot].row : -1;
+    if (out) team_copy(out + i * v.row_bytes, row >= 0 ? v.values + (int64_t)row * v.row_bytes : nullptr, v.row_bytes, sub);
+    if (sub == 0) {
+      if (rows_out) rows_out[i] = row;
+      if (row >= 0 && step >= 0) v.last_seen[row] = step;
+    }
+  }
+}
+
+__device__ __forceinline__ void free_slot(View& v, int64_t slot, int64_t key) {
+  unsigned long long* p = reinterpret_cast<unsigned long long*>(&v.slots[slot].key);
+  if ((int64_t)atomicCAS(p, (unsigned long long)key, (unsigned long long)kTomb) == key) {
+    const int32_t row = v.slots[slot].row;
+    const int32_t t = atomicAdd(&v.ah->free_top, 1);
+    v.free_stack[t] = row;
+    atomicSub(&v.ih->live, 1ULL);
+    atomicAdd(&v.ih->tombstones, 1ULL);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_evict(View v, int64_t n, const int64_t* __restrict__ keys) {
+  const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
+  const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
+  const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
+  for (int64_t i = team; i < n; i += teams) {
+    const int64_t key = keys[i];
+    const int64_t slot = key >= 0 ? find(v, key, lane) : -1;
+    if (slot >= 0 && sub == 0) free_slot(v, slot, key);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_evict_older(View v, int64_t nslots, int32_t threshold) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < nslots; s += stride) {
+    const int64_t key = v.slots[s].key;
+    if (key < 0) continue;
+    const int32_t row = v.slots[s].row;
+    if (row >= 0 && v.last_seen[row] < threshold) free_slot(v, s, key);
+  }
+}
+
+// live entries of src re-indexed into dst (dst initialised; src keys are distinct)
+__global__ __launch_bounds__(256) void k_rebuild(View src, int64_t nslots, View dst) {
+  const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
+  const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
+  const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
+  for (int64_t s = team; s < nslots; s += teams) {
+    const int64_t key = src.slots[s].key;
+    if (key < 0) continue;                                   // team-uniform
+    const int64_t r = claim(dst, key, lane);
+    if (sub == 0 && r >= 0) {
+      dst.slots[r & ((1LL << 62) - 1)].row = src.slots[s].row;
+      atomicAdd(&dst.ih->live, 1ULL);
+    } else if (sub == 0) {
+      atomicAdd(&dst.ih->dropped, 1ULL);
+    }
+  }
+}
+
+// ---- dedup ---------------------------------------------------------------------------------
+// claim on a scratch index; the claiming team numbers its key (claim order) and records it
+__global__ __launch_bounds__(256) void k_dedup_claim(View v, int64_t n, const int64_t* __restrict__ keys,
+                                                     int64_t* __restrict__ res, int64_t* __restrict__ uniq,
+                                                     unsigned long long* __restrict__ count) {
+  const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
+  const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
+  const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
+  for (int64_t i = team; i < n; i += teams) {
+    const int64_t key = keys[i];
+    const int64_t r = key >= 0 ? claim(v, key, lane) : -1;   // negative keys are not keys
+    if (sub == 0) {
+      res[i] = r;
+      if (r >= 0 && (r & (1LL << 62))) {
+        const int64_t id = (int64_t)atomicAdd(count, 1ULL);
+        v.slots[r & ((1LL << 62) - 1)].row = (int32_t)id;
+        uniq[id] = key;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_dedup_inverse(View v, int64_t n, const int64_t* __restrict__ res,
+                                                       int64_t* __restrict__ inverse) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int64_t r = res[i];
+    inverse[i] = r >= 0 ? (int64_t)v.slots[r & ((1LL << 62) - 1)].row : -1;
+  }
+}
+
+__global__ void k_count_reset(unsigned long long* count) { *count = 0; }
+
+inline unsigned ew(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 65536)); }
+
+View make_view(const HashDesc& h) {
+  View v{};
+  v.ih = reinterpret_cast<IndexHeader*>(h.index_mem);
+  v.slots = reinterpret_cast<Slot*>(static_cast<char*>(h.index_mem) + kHashHeaderBytes);
+  v.lmask = h.index_cap / kTeam - 1;
+  if (h.arena_mem) {
+    char* a = static_cast<char*>(h.arena_mem);
+    v.ah = reinterpret_cast<ArenaHeader*>(a);
+    v.free_stack = reinterpret_cast<int32_t*>(a + kHashHeaderBytes);
+    v.last_seen = reinterpret_cast<int32_t*>(a + kHashHeaderBytes + hash_align((size_t)h.rows * 4));
+    v.values = a + kHashHeaderBytes + 2 * hash_align((size_t)h.rows * 4);
+  }
+  v.rows = h.rows;
+  v.row_bytes = h.row_bytes;
+  return v;
+}
+
+}  // namespace
+
+hipError_t launch_hash_init(const HashDesc& h, bool index, bool arena, hipStream_t s) {
+  View v = make_view(h);
+  if (index) k_index_init<<<ew(h.index_cap), 256, 0, s>>>(v.slots, h.index_cap, v.ih);
+  if (arena) k_arena_init<<<ew(h.rows), 256, 0, s>>>(v.ah, v.free_stack, v.last_seen, h.rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_hash_insert(const HashDesc& h, int64_t n, const int64_t* keys, const void* init, int32_t step,
+                              int32_t* rows_out, int64_t* res, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  View v = make_view(h);
+  k_claim<<<team_grid(n), 256, 0, s>>>(v, n, keys, res);
+  k_assign<<<team_grid(n), 256, 0, s>>>(v, n, res, static_cast<const char*>(init), step);
+  k_resolve<<<ew(n), 256, 0, s>>>(v, n, res, rows_out, step);
+  return hipGetLastError();
+}
+
+hipError_t launch_hash_lookup(const HashDesc& h, int64_t n, const int64_t* keys, int32_t step, void* out,
+                              int32_t* rows_out, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_lookup<<<team_grid(n), 256, 0, s>>>(make_view(h), n, keys, step, static_cast<char*>(out), rows_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_hash_evict(const HashDesc& h, int64_t n, const int64_t* keys, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  k_evict<<<team_grid(n), 256, 0, s>>>(make_view(h), n, keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_hash_evict_older(const HashDesc& h, int32_t threshold, hipStream_t s) {
+  k_evict_older<<<ew(h.index_cap), 256, 0, s>>>(make_view(h), h.index_cap, threshold);
+  return hipGetLastError();
+}
+
+hipError_t launch_hash_rebuild(const HashDesc& src, const HashDesc& dst, hipStream_t s) {
+  View d = make_view(dst);
+  k_index_init<<<ew(dst.index_cap), 256, 0, s>>>(d.slots, dst.index_cap, d.ih);
+  k_rebuild<<<team_grid(src.index_cap), 256, 0, s>>>(make_view(src), src.index_cap, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_dedup(int64_t n, const int64_t* keys, const HashDesc& scratch, int64_t* res, int64_t* uniq,
+                        int64_t* inverse, unsigned long long* count, hipStream_t s) {
+  View v = make_view(scratch);
+  k_index_init<<<ew(scratch.index_cap), 256, 0, s>>>(v.slots, scratch.index_cap, v.ih);
+  k_count_reset<<<1, 1, 0, s>>>(count);
+  if (n == 0) return hipGetLastError();
+  k_dedup_claim<<<team_grid(n), 256, 0, s>>>(v, n, keys, res, uniq, count);
+  k_dedup_inverse<<<ew(n), 256, 0, s>>>(v, n, res, inverse);
+  return hipGetLastError();
+}
+
+}  // namespace mtgr

@@ -99,6 +99,32 @@ hipError_t launch_gemm_bf16_splitk(int64_t M, int N, int K, int ksplit, const bf
 hipError_t launch_gemm_f32_splitk(int64_t M, int N, int K, int ksplit, const float* a, const float* w,
                                   float* part, hipStream_t s);
 
+// ---- hash embedding store and dedup (hash_store.hip) ------------------------------------------
+constexpr size_t kHashHeaderBytes = 256;
+inline size_t hash_align(size_t v) { return (v + 255) / 256 * 256; }
+// index_mem: header + index_cap slots of 16 bytes (index_cap a power of two >= 8); arena_mem:
+// header, free stack [rows] int32, last use [rows] int32, values [rows][row_bytes] (may be NULL
+// for a key-only index, as the dedup scratch)
+struct HashDesc {
+  void* index_mem;
+  int64_t index_cap;
+  void* arena_mem;
+  int32_t rows;
+  int32_t row_bytes;
+};
+hipError_t launch_hash_init(const HashDesc& h, bool index, bool arena, hipStream_t s);
+// res: [n] int64 scratch
+hipError_t launch_hash_insert(const HashDesc& h, int64_t n, const int64_t* keys, const void* init, int32_t step,
+                              int32_t* rows_out, int64_t* res, hipStream_t s);
+hipError_t launch_hash_lookup(const HashDesc& h, int64_t n, const int64_t* keys, int32_t step, void* out,
+                              int32_t* rows_out, hipStream_t s);
+hipError_t launch_hash_evict(const HashDesc& h, int64_t n, const int64_t* keys, hipStream_t s);
+hipError_t launch_hash_evict_older(const HashDesc& h, int32_t threshold, hipStream_t s);
+hipError_t launch_hash_rebuild(const HashDesc& src, const HashDesc& dst, hipStream_t s);
+// distinct keys in claim order into uniq, per-occurrence index into inverse, count into *count
+hipError_t launch_dedup(int64_t n, const int64_t* keys, const HashDesc& scratch, int64_t* res, int64_t* uniq,
+                        int64_t* inverse, unsigned long long* count, hipStream_t s);
+
 // ---- head (head.hip) -----------------------------------------------------------------------
 // rows[c] = (out_kind) x[cand_idx[c]]  (fp32 hidden state -> head input dtype)
 hipError_t launch_gather_rows(int64_t C, int64_t T, int d, const float* x,

@@ -36,6 +36,9 @@ EXPORTED = [
     "mtgr_block_fwd", "mtgr_groupln_fwd", "mtgr_linear_fwd", "mtgr_attention_fwd",
     "mtgr_validate_batch", "mtgr_debug_mask", "mtgr_block_bwd_workspace_size", "mtgr_block_bwd",
     "mtgr_attention_bwd_workspace_size", "mtgr_attention_bwd",
+    "mtgr_hash_index_bytes", "mtgr_hash_arena_bytes", "mtgr_hash_init", "mtgr_hash_insert_workspace_size",
+    "mtgr_hash_insert", "mtgr_hash_lookup", "mtgr_hash_evict", "mtgr_hash_evict_older", "mtgr_hash_rebuild",
+    "mtgr_hash_get_stats", "mtgr_dedup_workspace_size", "mtgr_dedup",
 ]
 
 # parameter names of one block, in the field order of mtgr_block_params / mtgr_block_grads
@@ -61,6 +64,16 @@ class MtgrBlockParams(ctypes.Structure):
 
 class MtgrBlockGrads(ctypes.Structure):
     _fields_ = [(name, c_vp) for name in BLOCK_PARAM_NAMES]
+
+
+class MtgrHashTable(ctypes.Structure):
+    _fields_ = [("index_mem", c_vp), ("index_cap", c_i64), ("arena_mem", c_vp), ("rows", c_i32),
+                ("dim", c_i32), ("dtype", c_i32)]
+
+
+class MtgrHashStats(ctypes.Structure):
+    _fields_ = [("live", c_i64), ("tombstones", c_i64), ("dropped", c_i64), ("free_rows", c_i32),
+                ("failed_inserts", c_i32)]
 
 
 class MtgrEncoderParams(ctypes.Structure):
@@ -105,6 +118,19 @@ def lib():
         L.mtgr_attention_bwd_workspace_size.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, P(c_sz)]
         L.mtgr_attention_bwd.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp,
                                          c_vp, c_sz, c_vp]
+        HT = P(MtgrHashTable)
+        L.mtgr_hash_index_bytes.argtypes = [c_i64, P(c_sz)]
+        L.mtgr_hash_arena_bytes.argtypes = [c_i32, c_i32, c_i32, P(c_sz)]
+        L.mtgr_hash_init.argtypes = [HT, c_vp]
+        L.mtgr_hash_insert_workspace_size.argtypes = [c_i64, P(c_sz)]
+        L.mtgr_hash_insert.argtypes = [HT, c_i64, c_vp, c_vp, c_i32, c_vp, c_vp, c_sz, c_vp]
+        L.mtgr_hash_lookup.argtypes = [HT, c_i64, c_vp, c_i32, c_vp, c_vp, c_vp]
+        L.mtgr_hash_evict.argtypes = [HT, c_i64, c_vp, c_vp]
+        L.mtgr_hash_evict_older.argtypes = [HT, c_i32, c_vp]
+        L.mtgr_hash_rebuild.argtypes = [HT, c_vp, c_i64, c_vp]
+        L.mtgr_hash_get_stats.argtypes = [HT, P(MtgrHashStats), c_vp]
+        L.mtgr_dedup_workspace_size.argtypes = [c_i64, P(c_sz)]
+        L.mtgr_dedup.argtypes = [c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
         L.mtgr_block_bwd_workspace_size.argtypes = [P(MtgrBlockParams), P(MtgrBatch), P(c_sz)]
         L.mtgr_block_bwd.argtypes = [P(MtgrBlockParams), P(MtgrBatch), c_vp, c_vp, c_vp,
                                      P(MtgrBlockGrads), c_vp, c_sz, c_vp]
@@ -289,6 +315,90 @@ def mtgr_attention_bwd(batch: DeviceBatch, d: int, num_heads: int, dtype: int, m
     _check("mtgr_attention_bwd", lib().mtgr_attention_bwd(
         ctypes.byref(batch.c), d, num_heads, dtype, mask_mode, _ptr(qkvu), _ptr(v_tilde), _ptr(dy_gated),
         _ptr(dqkvu), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+class DeviceHashTable:
+    """Device memory (from torch) for one hash embedding store plus its C description."""
+
+    def __init__(self, rows: int, dim: int, dtype: int = MTGR_F32, index_cap: Optional[int] = None,
+                 device="cuda"):
+        import torch
+        if index_cap is None:
+            index_cap = 8
+            while index_cap < 2 * rows:
+                index_cap *= 2
+        self.rows, self.dim, self.dtype = rows, dim, dtype
+        self.index = torch.empty(mtgr_hash_index_bytes(index_cap), dtype=torch.uint8, device=device)
+        self.arena = torch.empty(mtgr_hash_arena_bytes(rows, dim, dtype), dtype=torch.uint8, device=device)
+        self.c = MtgrHashTable(self.index.data_ptr(), index_cap, self.arena.data_ptr(), rows, dim, dtype)
+
+    def use_index(self, index_tensor, index_cap: int):
+        """Switch to a rebuilt index (same arena)."""
+        self.index = index_tensor
+        self.c.index_mem, self.c.index_cap = index_tensor.data_ptr(), index_cap
+
+
+def mtgr_hash_index_bytes(index_cap: int) -> int:
+    n = c_sz(0)
+    _check("mtgr_hash_index_bytes", lib().mtgr_hash_index_bytes(index_cap, ctypes.byref(n)))
+    return int(n.value)
+
+
+def mtgr_hash_arena_bytes(rows: int, dim: int, dtype: int) -> int:
+    n = c_sz(0)
+    _check("mtgr_hash_arena_bytes", lib().mtgr_hash_arena_bytes(rows, dim, dtype, ctypes.byref(n)))
+    return int(n.value)
+
+
+def mtgr_hash_init(t: DeviceHashTable, stream=None):
+    _check("mtgr_hash_init", lib().mtgr_hash_init(ctypes.byref(t.c), _stream(stream)))
+
+
+def mtgr_hash_insert_workspace_size(n: int) -> int:
+    b = c_sz(0)
+    _check("mtgr_hash_insert_workspace_size", lib().mtgr_hash_insert_workspace_size(n, ctypes.byref(b)))
+    return int(b.value)
+
+
+def mtgr_hash_insert(t: DeviceHashTable, keys, init_values, step: int, rows_out, ws, stream=None):
+    _check("mtgr_hash_insert", lib().mtgr_hash_insert(
+        ctypes.byref(t.c), keys.numel(), _ptr(keys), _ptr(init_values), step, _ptr(rows_out), _ptr(ws),
+        ws.numel(), _stream(stream)))
+
+
+def mtgr_hash_lookup(t: DeviceHashTable, keys, step: int, values_out, rows_out, stream=None):
+    _check("mtgr_hash_lookup", lib().mtgr_hash_lookup(
+        ctypes.byref(t.c), keys.numel(), _ptr(keys), step, _ptr(values_out), _ptr(rows_out), _stream(stream)))
+
+
+def mtgr_hash_evict(t: DeviceHashTable, keys, stream=None):
+    _check("mtgr_hash_evict", lib().mtgr_hash_evict(ctypes.byref(t.c), keys.numel(), _ptr(keys), _stream(stream)))
+
+
+def mtgr_hash_evict_older(t: DeviceHashTable, step_threshold: int, stream=None):
+    _check("mtgr_hash_evict_older", lib().mtgr_hash_evict_older(ctypes.byref(t.c), step_threshold, _stream(stream)))
+
+
+def mtgr_hash_rebuild(t: DeviceHashTable, dst_index, dst_index_cap: int, stream=None):
+    _check("mtgr_hash_rebuild", lib().mtgr_hash_rebuild(ctypes.byref(t.c), _ptr(dst_index), dst_index_cap,
+                                                        _stream(stream)))
+
+
+def mtgr_hash_get_stats(t: DeviceHashTable, stream=None) -> dict:
+    st = MtgrHashStats()
+    _check("mtgr_hash_get_stats", lib().mtgr_hash_get_stats(ctypes.byref(t.c), ctypes.byref(st), _stream(stream)))
+    return {k: int(getattr(st, k)) for k, _ in MtgrHashStats._fields_}
+
+
+def mtgr_dedup_workspace_size(n: int) -> int:
+    b = c_sz(0)
+    _check("mtgr_dedup_workspace_size", lib().mtgr_dedup_workspace_size(n, ctypes.byref(b)))
+    return int(b.value)
+
+
+def mtgr_dedup(keys, unique_out, inverse_out, num_unique_out, ws, stream=None):
+    _check("mtgr_dedup", lib().mtgr_dedup(keys.numel(), _ptr(keys), _ptr(unique_out), _ptr(inverse_out),
+                                          _ptr(num_unique_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def mtgr_validate_batch(batch: DeviceBatch, ws, stream=None) -> int:

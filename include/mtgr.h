@@ -1,6 +1,6 @@
 /*
  * mtgr.h -- C ABI of libmtgr.so: forward pass of the MTGR HSTU encoder on one MI355X (gfx950),
- * and the backward pass of one block.
+ * the backward pass of one block, and the embedding front end (hash embedding store, key dedup).
  *
  * Page keys used in the citations below:
  *   [P1]/[P2] chenhuiyu blog post "MTGR" (Chinese / English)
@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MTGR_ABI_VERSION 3
+#define MTGR_ABI_VERSION 4
 
 typedef enum {
   MTGR_OK = 0,
@@ -221,6 +221,72 @@ mtgr_status mtgr_attention_bwd(const mtgr_batch* b, int32_t d, int32_t num_heads
                                int32_t mask_mode, const void* qkvu, const void* v_tilde,
                                const void* dy_gated, void* dqkvu, void* ws, size_t ws_bytes,
                                void* stream);
+
+/* ---- hash embedding store ----------------------------------------------------------------- */
+/* The pages' decoupled embedding table ([P3] 方法, training-framework paragraph; [P1]/[P2]
+ * training-system section): a compact index from int64 key to a row of a separate value arena, so
+ * keys are inserted and evicted in real time and the index can be rebuilt larger while the values
+ * stay in place.  The caller owns both device buffers; the library keeps no state.  Keys are
+ * >= 0 (negative keys are never stored; inserting one fails, looking one up misses).
+ *   index_mem: mtgr_hash_index_bytes(index_cap) bytes, index_cap a power of two in [8, 2^40]
+ *              (slots; keep the live count below ~3/4 of it for short probes)
+ *   arena_mem: mtgr_hash_arena_bytes(rows, dim, dtype) bytes: free-row stack, last-use steps and
+ *              the values [rows][dim] in dtype (dim * element size a multiple of 16 bytes)
+ * Calls that modify the store must not overlap on the device (one stream, or ordered streams).
+ * Within one call, a key occurring several times is handled once. */
+typedef struct mtgr_hash_table {
+  void* index_mem;
+  int64_t index_cap;
+  void* arena_mem;
+  int32_t rows;
+  int32_t dim;
+  int32_t dtype;                  /* MTGR_F32 or MTGR_BF16 */
+} mtgr_hash_table;
+
+typedef struct mtgr_hash_stats {
+  int64_t live;                   /* keys in the index */
+  int64_t tombstones;             /* evicted slots not yet reclaimed by a rebuild */
+  int64_t dropped;                /* entries the rebuild that produced this index could not place */
+  int32_t free_rows;              /* arena rows on the free stack */
+  int32_t failed_inserts;         /* insert occurrences since mtgr_hash_init that got no row */
+} mtgr_hash_stats;
+
+mtgr_status mtgr_hash_index_bytes(int64_t index_cap, size_t* bytes);
+mtgr_status mtgr_hash_arena_bytes(int32_t rows, int32_t dim, int32_t dtype, size_t* bytes);
+/* Empty index, every arena row free, counters zero. */
+mtgr_status mtgr_hash_init(const mtgr_hash_table* t, void* stream);
+mtgr_status mtgr_hash_insert_workspace_size(int64_t n, size_t* bytes);
+/* Insert keys[n] (device int64).  A key already present keeps its row and value; a new key takes
+ * a free row, initialised from init_values (device [n][dim] in dtype, row i for keys[i]; for a key
+ * repeated in the call, one of its rows) or zeros when init_values is NULL.  Every occurrence's
+ * row (or -1: arena full, index full, negative key) goes to rows_out (device int32 [n], may be
+ * NULL); failures are counted per occurrence.  Rows of the keys touched record `step`. */
+mtgr_status mtgr_hash_insert(const mtgr_hash_table* t, int64_t n, const int64_t* keys,
+                             const void* init_values, int32_t step, int32_t* rows_out, void* ws,
+                             size_t ws_bytes, void* stream);
+/* Values of keys[n] into values_out (device [n][dim] in dtype, zeros for a missing key; may be
+ * NULL) and their rows into rows_out (-1 missing; may be NULL).  step >= 0 records the use. */
+mtgr_status mtgr_hash_lookup(const mtgr_hash_table* t, int64_t n, const int64_t* keys, int32_t step,
+                             void* values_out, int32_t* rows_out, void* stream);
+/* Remove keys[n] (missing keys are ignored); their rows return to the free stack. */
+mtgr_status mtgr_hash_evict(const mtgr_hash_table* t, int64_t n, const int64_t* keys, void* stream);
+/* Remove every key whose row was last used before step_threshold. */
+mtgr_status mtgr_hash_evict_older(const mtgr_hash_table* t, int32_t step_threshold, void* stream);
+/* Re-index the live keys of src into a fresh index at dst_index_mem (dst_index_cap slots, a
+ * different buffer): no tombstones, same arena rows.  Use {dst_index_mem, dst_index_cap, same
+ * arena} afterwards.  Keys that do not fit are dropped and counted (stats.dropped of dst). */
+mtgr_status mtgr_hash_rebuild(const mtgr_hash_table* src, void* dst_index_mem, int64_t dst_index_cap,
+                              void* stream);
+/* Counters of the store.  Synchronises `stream`. */
+mtgr_status mtgr_hash_get_stats(const mtgr_hash_table* t, mtgr_hash_stats* out, void* stream);
+
+/* Batch key dedup ([P3] 方法: IDs are deduplicated before the embedding lookup): the distinct
+ * values of keys[n] (device int64, >= 0) into unique_out[0 .. u-1] in an unspecified order, u into
+ * *num_unique_out (device int64), and for every i the position of keys[i] in unique_out into
+ * inverse_out[i] (device int64; -1 for a negative key).  The workspace holds a scratch index. */
+mtgr_status mtgr_dedup_workspace_size(int64_t n, size_t* bytes);
+mtgr_status mtgr_dedup(int64_t n, const int64_t* keys, int64_t* unique_out, int64_t* inverse_out,
+                       int64_t* num_unique_out, void* ws, size_t ws_bytes, void* stream);
 
 /* ---- test / debug ------------------------------------------------------------------------ */
 /* Device-side checks of a batch (group ids in 0..3 and non-decreasing within each user, no NaN

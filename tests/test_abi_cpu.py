@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert M.mtgr_abi_version() == 3
+    assert M.mtgr_abi_version() == 4
     assert M.mtgr_status_str(0) == "ok"
     assert "workspace" in M.mtgr_status_str(5)
 
@@ -182,3 +182,35 @@ def test_block_bwd_argument_checks():
                             FAKE, n_bwd - 1, None) == 5
     assert L.mtgr_block_bwd(ctypes.byref(blk), ctypes.byref(b), FAKE, FAKE, FAKE, ctypes.byref(g),
                             None, n_bwd, None) == 5
+
+
+def test_hash_store_argument_checks():
+    L = M.lib()
+    n = ctypes.c_size_t(0)
+    assert L.mtgr_hash_index_bytes(1000, ctypes.byref(n)) == 2               # not a power of two
+    assert L.mtgr_hash_index_bytes(4, ctypes.byref(n)) == 2                  # below one line
+    assert L.mtgr_hash_index_bytes(1024, ctypes.byref(n)) == 0 and n.value == 256 + 1024 * 16
+    assert L.mtgr_hash_arena_bytes(10, 6, M.MTGR_F32, ctypes.byref(n)) == 2  # 24-byte rows
+    assert L.mtgr_hash_arena_bytes(10, 8, 7, ctypes.byref(n)) == 4
+    assert L.mtgr_hash_arena_bytes(0, 8, M.MTGR_F32, ctypes.byref(n)) == 2
+    assert L.mtgr_hash_arena_bytes(10, 8, M.MTGR_BF16, ctypes.byref(n)) == 0
+    t = M.MtgrHashTable(FAKE, 1024, FAKE, 10, 8, M.MTGR_F32)
+    bad = M.MtgrHashTable(FAKE, 1000, FAKE, 10, 8, M.MTGR_F32)
+    nomem = M.MtgrHashTable(None, 1024, FAKE, 10, 8, M.MTGR_F32)
+    assert L.mtgr_hash_init(ctypes.byref(bad), None) == 2
+    assert L.mtgr_hash_init(ctypes.byref(nomem), None) == 1
+    assert L.mtgr_hash_insert(ctypes.byref(t), -1, FAKE, None, 0, None, FAKE, 8, None) == 2
+    assert L.mtgr_hash_insert(ctypes.byref(t), 0, None, None, 0, None, None, 0, None) == 0   # nothing to do
+    assert L.mtgr_hash_insert(ctypes.byref(t), 4, FAKE, None, 0, None, FAKE, 31, None) == 5
+    assert L.mtgr_hash_insert(ctypes.byref(t), 4, None, None, 0, None, FAKE, 32, None) == 1
+    assert L.mtgr_hash_lookup(ctypes.byref(t), 4, None, 0, None, None, None) == 1
+    assert L.mtgr_hash_evict(ctypes.byref(t), -2, FAKE, None) == 2
+    assert L.mtgr_hash_rebuild(ctypes.byref(t), FAKE, 1024, None) == 2       # dst must differ from src
+    assert L.mtgr_hash_rebuild(ctypes.byref(t), None, 1024, None) == 1
+    assert L.mtgr_hash_rebuild(ctypes.byref(t), FAKE + 4096, 100, None) == 2
+    assert L.mtgr_hash_get_stats(ctypes.byref(t), None, None) == 1
+    assert L.mtgr_dedup_workspace_size(100, ctypes.byref(n)) == 0
+    need = n.value
+    assert L.mtgr_dedup(100, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 5
+    assert L.mtgr_dedup(100, FAKE, FAKE, FAKE, None, FAKE, need, None) == 1
+    assert L.mtgr_dedup(100, None, FAKE, FAKE, FAKE, FAKE, need, None) == 1
