@@ -515,6 +515,13 @@ hipError_t launch_gemm_bf16_splitk(int64_t M, int N, int K, int ksplit, const bf
   return run_bf16_persistent<4, 2, MTGR_EPI_STORE, float>(M, N, K, a, w, nullptr, nullptr, part, s, ksplit);
 }
 
+hipError_t launch_gemm_bf16_f32out(int64_t M, int N, int K, const bf16* a, const bf16* w, const bf16* bias,
+                                   float* out, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K % 64 != 0 || K < 128 || N % 8 != 0) return hipErrorInvalidValue;
+  return run_bf16_persistent<4, 2, MTGR_EPI_STORE, float>(M, N, K, a, w, bias, nullptr, out, s);
+}
+
 hipError_t launch_gemm_f32_splitk(int64_t M, int N, int K, int ksplit, const float* a, const float* w,
                                   float* part, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;

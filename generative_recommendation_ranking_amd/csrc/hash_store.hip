@@ -218,8 +218,10 @@ __global__ __launch_bounds__(256) void k_resolve(View v, int64_t n, const int64_
 }
 
 __global__ __launch_bounds__(256) void k_lookup(View v, int64_t n, const int64_t* __restrict__ keys, int32_t step,
-                                                char* __restrict__ out, int32_t* __restrict__ rows_out) {
+                                                char* __restrict__ out, int32_t* __restrict__ rows_out,
+                                                const int64_t* __restrict__ n_dev) {
   const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
+  if (n_dev) n = min(n, *n_dev);
   const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
   const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
   for (int64_t i = team; i < n; i += teams) {
@@ -356,9 +358,9 @@ hipError_t launch_hash_insert(const HashDesc& h, int64_t n, const int64_t* keys,
 }
 
 hipError_t launch_hash_lookup(const HashDesc& h, int64_t n, const int64_t* keys, int32_t step, void* out,
-                              int32_t* rows_out, hipStream_t s) {
+                              int32_t* rows_out, hipStream_t s, const int64_t* n_dev) {
   if (n == 0) return hipSuccess;
-  k_lookup<<<team_grid(n), 256, 0, s>>>(make_view(h), n, keys, step, static_cast<char*>(out), rows_out);
+  k_lookup<<<team_grid(n), 256, 0, s>>>(make_view(h), n, keys, step, static_cast<char*>(out), rows_out, n_dev);
   return hipGetLastError();
 }
 

@@ -116,14 +116,40 @@ hipError_t launch_hash_init(const HashDesc& h, bool index, bool arena, hipStream
 // res: [n] int64 scratch
 hipError_t launch_hash_insert(const HashDesc& h, int64_t n, const int64_t* keys, const void* init, int32_t step,
                               int32_t* rows_out, int64_t* res, hipStream_t s);
+// n_dev (may be NULL): a device count; keys past min(n, *n_dev) are skipped
 hipError_t launch_hash_lookup(const HashDesc& h, int64_t n, const int64_t* keys, int32_t step, void* out,
-                              int32_t* rows_out, hipStream_t s);
+                              int32_t* rows_out, hipStream_t s, const int64_t* n_dev = nullptr);
 hipError_t launch_hash_evict(const HashDesc& h, int64_t n, const int64_t* keys, hipStream_t s);
 hipError_t launch_hash_evict_older(const HashDesc& h, int32_t threshold, hipStream_t s);
 hipError_t launch_hash_rebuild(const HashDesc& src, const HashDesc& dst, hipStream_t s);
 // distinct keys in claim order into uniq, per-occurrence index into inverse, count into *count
 hipError_t launch_dedup(int64_t n, const int64_t* keys, const HashDesc& scratch, int64_t* res, int64_t* uniq,
                         int64_t* inverse, unsigned long long* count, hipStream_t s);
+
+// ---- tokenizer front end (tokenizer.hip) --------------------------------------------------------
+constexpr int kTokMaxFields = 8;
+struct TokFields {                 // fields of each group and the table each one reads
+  int nfields[4];
+  int table[4][kTokMaxFields];
+};
+struct TokGroups {                 // group-sorted feature buffers
+  int nfields[4];
+  int64_t rows[4];                 // tokens of each group (as the host was told)
+  int64_t row0[4];                 // first row of each group in the [T][d] group-sorted outputs
+  bf16* feat[4];                   // [rows][nfields * e]
+};
+// per-user group counts cnt [B][4], their per-group exclusive prefix goff [4][B+1], merged keys
+// [T][fmax] (-1 for unused fields), flags reset
+hipError_t launch_tok_prepare(int32_t B, int64_t T, int fmax, const int64_t* offsets, const uint8_t* group_ids,
+                              const int64_t* ids, const TokFields& tf, int64_t* cnt, int64_t* goff, int64_t* keys,
+                              int32_t* flags, hipStream_t s);
+hipError_t launch_tok_build(int64_t T, int32_t B, int fmax, int e, const int64_t* offsets, const uint8_t* group_ids,
+                            const int64_t* cnt, const int64_t* goff, const TokGroups& tg, const int64_t* inverse,
+                            const bf16* uvals, int64_t* pos, int32_t* flags, hipStream_t s);
+hipError_t launch_tok_scatter(int64_t T, int d, const int64_t* pos, const float* y, float* x, hipStream_t s);
+// out (float [M][N]) = a[M][K] w[N][K]^T + bias (bf16 operands)
+hipError_t launch_gemm_bf16_f32out(int64_t M, int N, int K, const bf16* a, const bf16* w, const bf16* bias,
+                                   float* out, hipStream_t s);
 
 // ---- head (head.hip) -----------------------------------------------------------------------
 // rows[c] = (out_kind) x[cand_idx[c]]  (fp32 hidden state -> head input dtype)

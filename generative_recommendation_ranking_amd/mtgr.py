@@ -39,7 +39,15 @@ EXPORTED = [
     "mtgr_hash_index_bytes", "mtgr_hash_arena_bytes", "mtgr_hash_init", "mtgr_hash_insert_workspace_size",
     "mtgr_hash_insert", "mtgr_hash_lookup", "mtgr_hash_evict", "mtgr_hash_evict_older", "mtgr_hash_rebuild",
     "mtgr_hash_get_stats", "mtgr_dedup_workspace_size", "mtgr_dedup",
+    "mtgr_tokenize_workspace_size", "mtgr_tokenize",
 ]
+TOK_MAX_FIELDS = 8
+TOK_KEY_SHIFT = 40   # store key of (table, id) for the tokenizer: (table << 40) | id (include/mtgr.h)
+
+
+def tok_key(tables, ids):
+    """the tokenizer's store keys of (table, id) pairs, as the header defines them"""
+    return (np.asarray(tables, dtype=np.int64) << TOK_KEY_SHIFT) | np.asarray(ids, dtype=np.int64)
 
 # parameter names of one block, in the field order of mtgr_block_params / mtgr_block_grads
 BLOCK_PARAM_NAMES = ("gln1_gamma", "gln1_beta", "w_qkvu", "b_qkvu", "gln2_gamma", "gln2_beta",
@@ -74,6 +82,12 @@ class MtgrHashTable(ctypes.Structure):
 class MtgrHashStats(ctypes.Structure):
     _fields_ = [("live", c_i64), ("tombstones", c_i64), ("dropped", c_i64), ("free_rows", c_i32),
                 ("failed_inserts", c_i32)]
+
+
+class MtgrTokenizerParams(ctypes.Structure):
+    _fields_ = [("d_model", c_i32), ("max_fields", c_i32), ("num_fields", c_i32 * 4),
+                ("field_table", (c_i32 * 8) * 4), ("w1", c_vp * 4), ("b1", c_vp * 4), ("w2", c_vp * 4),
+                ("b2", c_vp * 4)]
 
 
 class MtgrEncoderParams(ctypes.Structure):
@@ -131,6 +145,9 @@ def lib():
         L.mtgr_hash_get_stats.argtypes = [HT, P(MtgrHashStats), c_vp]
         L.mtgr_dedup_workspace_size.argtypes = [c_i64, P(c_sz)]
         L.mtgr_dedup.argtypes = [c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]
+        L.mtgr_tokenize_workspace_size.argtypes = [P(MtgrTokenizerParams), P(MtgrBatch), HT, c_vp, P(c_sz)]
+        L.mtgr_tokenize.argtypes = [P(MtgrTokenizerParams), P(MtgrBatch), c_vp, c_vp, HT, c_i32, c_vp, c_vp, c_vp,
+                                    c_sz, c_vp]
         L.mtgr_block_bwd_workspace_size.argtypes = [P(MtgrBlockParams), P(MtgrBatch), P(c_sz)]
         L.mtgr_block_bwd.argtypes = [P(MtgrBlockParams), P(MtgrBatch), c_vp, c_vp, c_vp,
                                      P(MtgrBlockGrads), c_vp, c_sz, c_vp]
@@ -399,6 +416,55 @@ def mtgr_dedup_workspace_size(n: int) -> int:
 def mtgr_dedup(keys, unique_out, inverse_out, num_unique_out, ws, stream=None):
     _check("mtgr_dedup", lib().mtgr_dedup(keys.numel(), _ptr(keys), _ptr(unique_out), _ptr(inverse_out),
                                           _ptr(num_unique_out), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+class DeviceTokenizer:
+    """Tokenizer MLP weights on the GPU (bf16) plus the C description.  `spec` is a
+    synth.TokenizerSpec (fields per group, their tables, the per-group MLP weights)."""
+
+    def __init__(self, spec, device="cuda"):
+        import torch
+        self._keep = []
+
+        def dev(a):
+            if a is None:
+                return None
+            t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device).to(torch.bfloat16)
+            self._keep.append(t)
+            return t
+
+        c = MtgrTokenizerParams()
+        c.d_model = spec.d
+        c.max_fields = spec.max_fields
+        for g in range(4):
+            c.num_fields[g] = len(spec.field_tables[g])
+            for f, tab in enumerate(spec.field_tables[g]):
+                c.field_table[g][f] = tab
+            m = spec.mlps[g]
+            c.w1[g], c.b1[g] = _ptr(dev(m["w1"])), _ptr(dev(m.get("b1")))
+            c.w2[g], c.b2[g] = _ptr(dev(m["w2"])), _ptr(dev(m.get("b2")))
+        self.c = c
+
+
+def _i64x4(vals):
+    return (ctypes.c_int64 * 4)(*[int(v) for v in vals])
+
+
+def mtgr_tokenize_workspace_size(tok: DeviceTokenizer, batch: DeviceBatch, store: DeviceHashTable,
+                                 group_counts) -> int:
+    n = c_sz(0)
+    gc = _i64x4(group_counts)
+    _check("mtgr_tokenize_workspace_size", lib().mtgr_tokenize_workspace_size(
+        ctypes.byref(tok.c), ctypes.byref(batch.c), ctypes.byref(store.c), ctypes.cast(gc, c_vp), ctypes.byref(n)))
+    return int(n.value)
+
+
+def mtgr_tokenize(tok: DeviceTokenizer, batch: DeviceBatch, group_counts, field_ids, store: DeviceHashTable,
+                  step: int, x_out, flags_out, ws, stream=None):
+    gc = _i64x4(group_counts)
+    _check("mtgr_tokenize", lib().mtgr_tokenize(
+        ctypes.byref(tok.c), ctypes.byref(batch.c), ctypes.cast(gc, c_vp), _ptr(field_ids), ctypes.byref(store.c),
+        step, _ptr(x_out), _ptr(flags_out), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def mtgr_validate_batch(batch: DeviceBatch, ws, stream=None) -> int:

@@ -255,3 +255,78 @@ def candidate_rows(batch: Batch, users: Sequence[int]) -> np.ndarray:
     if len(users) == 0:
         return np.zeros(0, dtype=np.int64)
     return np.concatenate([np.arange(cand_off[u], cand_off[u + 1]) for u in users])
+
+
+# ---------------------------------------------------------------------------------------------
+# Tokenizer inputs: field IDs per token, the per-group MLP weights, and the contents of the
+# embedding store, as (table, id) pairs with their rows.  The field lists are this generator's
+# choice (the pages name the kinds of fields, not their number): U tokens carry (feature slot,
+# feature value); S and R items (item, category, brand, action) and (item, category, action,
+# time bucket); candidates (item, category, brand, user x category cross bucket, hour-preference
+# bucket, list position).  Item ids follow a Zipf law, so the batch repeats them across users.
+# ---------------------------------------------------------------------------------------------
+TOK_FIELD_TABLES = ([0, 1], [2, 3, 4, 5], [2, 3, 5, 6], [2, 3, 4, 7, 8, 9])
+TOK_VOCAB = (32, 1000, 1_000_000, 1000, 10_000, 8, 64, 100, 24, 512)
+
+
+@dataclasses.dataclass
+class TokenizerSpec:
+    d: int
+    e: int
+    field_tables: Sequence[Sequence[int]]
+    mlps: List[Dict[str, np.ndarray]]      # per group: w1 [d][F_g e], b1 [d], w2 [d][d], b2 [d]
+
+    @property
+    def max_fields(self) -> int:
+        return max(len(f) for f in self.field_tables)
+
+
+def make_tokenizer_inputs(batch: Batch, rng: np.random.Generator, d: int, e: int = 64,
+                          missing_frac: float = 0.05):
+    """(spec, field_ids [T][F_max] int64, group_counts [4], store_tables, store_ids, store_values):
+    the store holds every (table, id) pair the batch uses except about `missing_frac` of them,
+    each with a N(0, 1) row rounded to bf16."""
+    T = batch.num_tokens
+    g = batch.group_ids.astype(np.int64)
+    fmax = max(len(f) for f in TOK_FIELD_TABLES)
+    ids = np.full((T, fmax), -1, dtype=np.int64)
+    item = (rng.zipf(1.2, T) - 1) % TOK_VOCAB[2]
+    for grp, tables in enumerate(TOK_FIELD_TABLES):
+        rows = np.nonzero(g == grp)[0]
+        for f, tab in enumerate(tables):
+            if tab == 2:
+                col = item[rows]
+            elif tab == 3:
+                col = item[rows] % TOK_VOCAB[3]
+            elif tab == 4:
+                col = (item[rows] * 7) % TOK_VOCAB[4]
+            elif tab == 0 or tab == 9:       # slot of a U feature / list position of a candidate
+                starts = np.concatenate([[0], np.nonzero(np.diff(rows) != 1)[0] + 1])
+                run = np.zeros(len(rows), dtype=np.int64)
+                for s0, s1 in zip(starts, np.concatenate([starts[1:], [len(rows)]])):
+                    run[s0:s1] = np.arange(s1 - s0)
+                col = run % TOK_VOCAB[tab]
+            else:
+                col = rng.integers(0, TOK_VOCAB[tab], len(rows))
+            ids[rows, f] = col
+    counts = np.bincount(g, minlength=4)[:4].astype(np.int64)
+    mlps = []
+    for tables in TOK_FIELD_TABLES:
+        k = len(tables) * e
+        mlps.append({"w1": round_to_bf16(_xavier(rng, d, k)),
+                     "b1": round_to_bf16(rng.uniform(-0.1, 0.1, d).astype(np.float32)),
+                     "w2": round_to_bf16(_xavier(rng, d, d)),
+                     "b2": round_to_bf16(rng.uniform(-0.1, 0.1, d).astype(np.float32))})
+    spec = TokenizerSpec(d=d, e=e, field_tables=TOK_FIELD_TABLES, mlps=mlps)
+    pairs = set()
+    for grp, tables in enumerate(TOK_FIELD_TABLES):
+        rows = g == grp
+        for f, tab in enumerate(tables):
+            for i in np.unique(ids[rows, f]).tolist():
+                pairs.add((tab, int(i)))
+    pairs = sorted(pairs)
+    keep = rng.random(len(pairs)) >= missing_frac
+    tabs = np.array([p[0] for p in pairs], dtype=np.int64)[keep]
+    pids = np.array([p[1] for p in pairs], dtype=np.int64)[keep]
+    vals = round_to_bf16(rng.standard_normal((len(tabs), e)).astype(np.float32))
+    return spec, ids, counts, tabs, pids, vals

@@ -288,6 +288,43 @@ mtgr_status mtgr_dedup_workspace_size(int64_t n, size_t* bytes);
 mtgr_status mtgr_dedup(int64_t n, const int64_t* keys, int64_t* unique_out, int64_t* inverse_out,
                        int64_t* num_unique_out, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- tokenizer front end ----------------------------------------------------------------- */
+/* Field IDs -> encoder input.  A token of group g (U, S, R, C = 0..3) has num_fields[g] fields;
+ * field f reads table field_table[g][f] of the bf16 store at key (table << 40) | id (tables of one
+ * width merged into one store, [P3] 方法, training-framework paragraph).  The token's input is
+ *   x = W2_g silu(W1_g concat_f(emb_f) + b1_g) + b2_g
+ * (a domain-specific MLP over the concatenated field embeddings, [P1]/[P2] "Converting
+ * heterogeneous features into tokens"; the candidate token MLP(Concat(Emb(Item), Emb(Cross))),
+ * [P5] 7.3.2).  The batch's keys are deduplicated and each distinct key is read from the store
+ * once.  An id outside [0, 2^40) or a key absent from the store embeds to zeros.
+ * W1_g: device bf16 [d][num_fields[g] * dim] (num_fields[g] * dim a multiple of 64, >= 128);
+ * W2_g: device bf16 [d][d]; biases device bf16 [d] or NULL; d a multiple of 64 in [128, 4096]. */
+#define MTGR_TOK_MAX_FIELDS 8
+typedef struct mtgr_tokenizer_params {
+  int32_t d_model;
+  int32_t max_fields;                                  /* columns of field_ids, 1..8 */
+  int32_t num_fields[4];                               /* 1..max_fields */
+  int32_t field_table[4][MTGR_TOK_MAX_FIELDS];         /* 0 .. 2^23 - 1 */
+  const void* w1[4];
+  const void* b1[4];
+  const void* w2[4];
+  const void* b2[4];
+} mtgr_tokenizer_params;
+
+/* group_counts (host [4]): tokens of each group in the batch; must sum to num_tokens, with
+ * group_counts[3] == num_candidates.  field_ids: device int64 [T][max_fields] (columns past a
+ * token's num_fields are ignored).  store: dim = the embedding width, dtype MTGR_BF16.  step >= 0
+ * records the use of every key read.  x_out: device float [T][d].  flags_out (device int32, may be
+ * NULL) gets bit 0 set when the device's own group counts disagree with group_counts (such tokens
+ * get x = 0; nothing is accessed out of range). */
+mtgr_status mtgr_tokenize_workspace_size(const mtgr_tokenizer_params* p, const mtgr_batch* b,
+                                         const mtgr_hash_table* store, const int64_t group_counts[4],
+                                         size_t* bytes);
+mtgr_status mtgr_tokenize(const mtgr_tokenizer_params* p, const mtgr_batch* b,
+                          const int64_t group_counts[4], const int64_t* field_ids,
+                          const mtgr_hash_table* store, int32_t step, float* x_out, int32_t* flags_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
 /* ---- test / debug ------------------------------------------------------------------------ */
 /* Device-side checks of a batch (group ids in 0..3 and non-decreasing within each user, no NaN
  * R/C timestamp, candidate count == num_candidates).  Synchronises `stream`.  *flags_out gets

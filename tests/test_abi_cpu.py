@@ -214,3 +214,43 @@ def test_hash_store_argument_checks():
     assert L.mtgr_dedup(100, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == 5
     assert L.mtgr_dedup(100, FAKE, FAKE, FAKE, None, FAKE, need, None) == 1
     assert L.mtgr_dedup(100, None, FAKE, FAKE, FAKE, FAKE, need, None) == 1
+
+
+def test_tokenize_argument_checks():
+    L = M.lib()
+    off = np.array([0, 10, 30], dtype=np.int64)
+    b = M.MtgrBatch(2, 30, 5, off.ctypes.data, FAKE, FAKE, FAKE)
+    store = M.MtgrHashTable(FAKE, 1024, FAKE, 100, 64, M.MTGR_BF16)
+    p = M.MtgrTokenizerParams()
+    p.d_model, p.max_fields = 256, 6
+    for g, nf in enumerate((2, 4, 4, 6)):
+        p.num_fields[g] = nf
+        for f in range(nf):
+            p.field_table[g][f] = f
+        p.w1[g], p.w2[g] = FAKE, FAKE
+    n = ctypes.c_size_t(0)
+
+    def ws(gc, params=p, st=store, batch=b):
+        arr = (ctypes.c_int64 * 4)(*gc)
+        return L.mtgr_tokenize_workspace_size(ctypes.byref(params), ctypes.byref(batch), ctypes.byref(st),
+                                              ctypes.cast(arr, ctypes.c_void_p), ctypes.byref(n))
+    assert ws([2, 20, 3, 5]) == 0 and n.value > 0
+    assert ws([2, 20, 4, 5]) == 3                          # counts must sum to T
+    assert ws([2, 21, 3, 4]) == 3                          # candidates must match
+    f32 = M.MtgrHashTable(FAKE, 1024, FAKE, 100, 64, M.MTGR_F32)
+    assert ws([2, 20, 3, 5], st=f32) == 4                  # the tokenizer reads a bf16 store
+    small = M.MtgrHashTable(FAKE, 1024, FAKE, 100, 16, M.MTGR_BF16)
+    assert ws([2, 20, 3, 5], st=small) == 2                # 2 fields x 16 < 128: GEMM K too small
+    p.num_fields[0] = 7
+    assert ws([2, 20, 3, 5]) == 2                          # more fields than columns
+    p.num_fields[0] = 2
+    p.field_table[1][0] = 1 << 23
+    assert ws([2, 20, 3, 5]) == 2                          # table index past the key layout
+    p.field_table[1][0] = 0
+    p.w1[2] = None
+    assert ws([2, 20, 3, 5]) == 1
+    assert ws([2, 20, 0, 8]) == 3                          # (no R tokens: W1 of R unused; C count wrong)
+    p.w1[2] = FAKE
+    bad_off = np.array([0, 20, 10], dtype=np.int64)
+    bb = M.MtgrBatch(2, 10, 5, bad_off.ctypes.data, FAKE, FAKE, FAKE)
+    assert ws([2, 2, 1, 5], batch=bb) == 3                 # offsets not monotone

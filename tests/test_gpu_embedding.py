@@ -206,3 +206,92 @@ def test_dedup_matches_unique(n, universe):
     inv_np = inv.cpu().numpy()[:n]
     np.testing.assert_array_equal(inv_np[keys < 0], -1)
     np.testing.assert_array_equal(got_u[inv_np[keys >= 0]], valid)
+
+
+# ---------------------------------------------------------------------------------------------
+# tokenizer front end (mtgr_tokenize): x against the oracle's per-token definition; one bf16
+# rounding (the MLP hidden layer) between exact bf16 inputs and the fp32 output -> 1e-2
+# ---------------------------------------------------------------------------------------------
+TOL_TOK = 1e-2
+
+
+def rel_err(g, r):
+    g, r = np.asarray(g, np.float64), np.asarray(r, np.float64)
+    return 0.0 if r.size == 0 else float(np.abs(g - r).max() / max(np.abs(r).max(), 1e-30))
+
+
+def tok_setup(b, d, e, seed, missing_frac=0.05):
+    rng = np.random.default_rng(seed)
+    spec, ids, counts, tabs, pids, vals = synth.make_tokenizer_inputs(b, rng, d, e, missing_frac)
+    store = M.DeviceHashTable(max(len(tabs), 1), e, M.MTGR_BF16)
+    M.mtgr_hash_init(store)
+    if len(tabs):
+        keys = torch.from_numpy(M.tok_key(tabs, pids)).to(DEV)
+        M.mtgr_hash_insert(store, keys, torch.from_numpy(vals).to(DEV).to(torch.bfloat16), 0, None,
+                           M.workspace(M.mtgr_hash_insert_workspace_size(len(tabs))))
+    model = EO.EmbeddingStore(max(len(tabs), 1), e)
+    model.insert([EO.merged_key(t, i) for t, i in zip(tabs.tolist(), pids.tolist())], vals, 0)
+    return spec, ids, counts, store, model
+
+
+def run_tok(b, spec, ids, counts, store, step=-1):
+    db = M.DeviceBatch(b)
+    tok = M.DeviceTokenizer(spec)
+    ws = M.workspace(M.mtgr_tokenize_workspace_size(tok, db, store, counts))
+    x = torch.full((b.num_tokens, spec.d), float("nan"), device=DEV)
+    flags = torch.full((1,), 7, dtype=torch.int32, device=DEV)
+    M.mtgr_tokenize(tok, db, counts, torch.from_numpy(ids).to(DEV), store, step, x, flags, ws)
+    torch.cuda.synchronize()
+    return x.cpu().numpy(), int(flags.item())
+
+
+TOK_LENGTHS = [(3, 40, 17, 5), (0, 0, 0, 7), (5, 200, 0, 3), (2, 130, 90, 0), (0, 0, 0, 0), (1, 7, 150, 40),
+               (16, 300, 64, 64), (0, 0, 1, 0), (8, 600, 120, 77)]
+
+
+@pytest.mark.parametrize("d,e", [(256, 64), (128, 64), (768, 128)])
+def test_tokenize_matches_oracle(d, e):
+    rng = np.random.default_rng(41)
+    n_u, n_s, n_r, k = zip(*TOK_LENGTHS)
+    b = synth.batch_from_lengths(n_u, n_s, n_r, k, 8, rng, "bf16")
+    spec, ids, counts, store, model = tok_setup(b, d, e, 42 + d)
+    x, flags = run_tok(b, spec, ids, counts, store)
+    assert flags == 0
+    ref = EO.tokenize(ids, b.group_ids, spec.field_tables, model, spec.mlps)
+    for grp in range(4):
+        rows = b.group_ids == grp
+        assert rel_err(x[rows], ref[rows]) < TOL_TOK, f"group {grp}"
+
+
+def test_tokenize_workload_sampled_tokens_and_step():
+    b, _ = synth.make_workload("small-bf16", with_params=False)
+    spec, ids, counts, store, model = tok_setup(b, 256, 64, 43)
+    x, flags = run_tok(b, spec, ids, counts, store, step=5)
+    assert flags == 0
+    sample = np.random.default_rng(44).choice(b.num_tokens, 1500, replace=False)
+    ref = EO.tokenize(ids[sample], b.group_ids[sample], spec.field_tables, model, spec.mlps)
+    assert rel_err(x[sample], ref) < TOL_TOK
+    # every key the batch read was marked used at step 5: nothing older than 5 remains in use
+    live = M.mtgr_hash_get_stats(store)["live"]
+    M.mtgr_hash_evict_older(store, 5)
+    assert M.mtgr_hash_get_stats(store)["live"] == live
+
+
+def test_tokenize_inconsistent_counts_are_flagged_not_faulted():
+    rng = np.random.default_rng(45)
+    n_u, n_s, n_r, k = zip(*TOK_LENGTHS)
+    b = synth.batch_from_lengths(n_u, n_s, n_r, k, 8, rng, "bf16")
+    spec, ids, counts, store, model = tok_setup(b, 128, 64, 46)
+    wrong = counts.copy()
+    wrong[1] -= 10
+    wrong[2] += 10                                   # same total, same candidate count
+    x, flags = run_tok(b, spec, ids, wrong, store)
+    assert flags & 1
+    assert np.isfinite(x).all()
+
+
+def test_tokenize_empty_batch():
+    b = synth.batch_from_lengths([0, 0], [0, 0], [0, 0], [0, 0], 8, np.random.default_rng(0), "bf16")
+    spec, ids, counts, store, model = tok_setup(b, 128, 64, 47)
+    x, flags = run_tok(b, spec, ids, counts, store)
+    assert x.shape == (0, 128) and flags == 0
