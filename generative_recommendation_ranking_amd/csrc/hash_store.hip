@@ -88,6 +88,10 @@ __device__ int64_t claim(const View& v, int64_t key, int lane) {
   int64_t line = (int64_t)(mix64((uint64_t)key) >> 3) & v.lmask;
   for (int64_t probe = 0; probe <= v.lmask; ++probe) {
     Slot* ls = v.slots + line * kTeam;
+    // A plain (cached) read that shows the key is conclusive -- slots only ever gain keys during
+    // a claim -- and keeps repeated keys of a batch off the coherent path.
+    const uint32_t hit = team_ballot(ls[sub].key == key, lane);
+    if (hit) return line * kTeam + (__ffs(hit) - 1);
     for (;;) {
       const int64_t k = load_key_coherent(ls + sub);
       const uint32_t m = team_ballot(k == key, lane);
@@ -170,27 +174,46 @@ __global__ __launch_bounds__(256) void k_claim(View v, int64_t n, const int64_t*
   }
 }
 
-// claimed slots take a free row and initialise it; with none left the slot becomes a tombstone
+// Claimed slots take a free row and initialise it; with none left the slot becomes a tombstone.
+// The pops of a wavefront's teams are one atomic on the stack top (each claimant takes the
+// next row below the returned top by its rank among the wavefront's claimants).
 __global__ __launch_bounds__(256) void k_assign(View v, int64_t n, int64_t* __restrict__ res,
                                                 const char* __restrict__ init, int32_t step) {
   const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
   const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
   const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
-  for (int64_t i = team; i < n; i += teams) {
-    const int64_t r = res[i];
-    if (r < 0 || !(r & (1LL << 62))) continue;
-    const int64_t slot = r & ((1LL << 62) - 1);
+  const int64_t first_of_wave = team - (lane >> 3);
+  for (int64_t base = first_of_wave; base < n; base += teams) {   // wave-uniform trip count
+    const int64_t i = base + (lane >> 3);
+    const int64_t r = i < n ? res[i] : -1;
+    const bool want = sub == 0 && r >= 0 && (r & (1LL << 62));
+    const unsigned long long mask = __ballot(want);
     int32_t row = -1;
-    if (sub == 0) {
-      const int32_t t = atomicSub(&v.ah->free_top, 1);
-      if (t >= 1) {
-        row = v.free_stack[t - 1];
-        v.slots[slot].row = row;
-        v.last_seen[row] = step;
-        atomicAdd(&v.ih->live, 1ULL);
-      } else {
-        v.slots[slot].key = kTomb;
-        atomicAdd(&v.ih->tombstones, 1ULL);
+    if (mask) {
+      const int leader = __ffsll((long long)mask) - 1;
+      const int cnt = __popcll(mask);
+      int32_t top = 0;
+      if (lane == leader) top = atomicSub(&v.ah->free_top, cnt);
+      top = __shfl(top, leader, kWave);
+      const int rank = __popcll(mask & ((1ULL << lane) - 1));
+      int ok = 0, bad = 0;
+      if (want) {
+        const int64_t slot = r & ((1LL << 62) - 1);
+        const int32_t t = top - rank;                // this claimant's stack height
+        if (t >= 1) {
+          row = v.free_stack[t - 1];
+          v.slots[slot].row = row;
+          v.last_seen[row] = step;
+          ok = 1;
+        } else {
+          v.slots[slot].key = kTomb;
+          bad = 1;
+        }
+      }
+      const unsigned long long okm = __ballot(ok), badm = __ballot(bad);
+      if (lane == leader) {
+        if (okm) atomicAdd(&v.ih->live, (unsigned long long)__popcll(okm));
+        if (badm) atomicAdd(&v.ih->tombstones, (unsigned long long)__popcll(badm));
       }
     }
     row = __shfl(row, lane & ~(kTeam - 1), kWave);
@@ -236,35 +259,58 @@ __global__ __launch_bounds__(256) void k_lookup(View v, int64_t n, const int64_t
   }
 }
 
-__device__ __forceinline__ void free_slot(View& v, int64_t slot, int64_t key) {
-  unsigned long long* p = reinterpret_cast<unsigned long long*>(&v.slots[slot].key);
-  if ((int64_t)atomicCAS(p, (unsigned long long)key, (unsigned long long)kTomb) == key) {
-    const int32_t row = v.slots[slot].row;
-    const int32_t t = atomicAdd(&v.ah->free_top, 1);
-    v.free_stack[t] = row;
-    atomicSub(&v.ih->live, 1ULL);
-    atomicAdd(&v.ih->tombstones, 1ULL);
+// Evict the key at `slot` (compare-and-swap to a tombstone; one winner among duplicates) and push
+// the winners' rows on the free stack: one atomic on the stack top per wavefront.  Called by every
+// lane of the wavefront (want = false where there is nothing to evict).
+__device__ __forceinline__ void evict_slots(View& v, bool want, int64_t slot, int64_t key, int lane) {
+  bool won = false;
+  int32_t row = -1;
+  if (want) {
+    unsigned long long* p = reinterpret_cast<unsigned long long*>(&v.slots[slot].key);
+    won = (int64_t)atomicCAS(p, (unsigned long long)key, (unsigned long long)kTomb) == key;
+    if (won) row = v.slots[slot].row;
   }
+  const unsigned long long mask = __ballot(won);
+  if (!mask) return;
+  const int leader = __ffsll((long long)mask) - 1;
+  const int cnt = __popcll(mask);
+  int32_t top = 0;
+  if (lane == leader) {
+    top = atomicAdd(&v.ah->free_top, cnt);
+    atomicSub(&v.ih->live, (unsigned long long)cnt);
+    atomicAdd(&v.ih->tombstones, (unsigned long long)cnt);
+  }
+  top = __shfl(top, leader, kWave);
+  if (won) v.free_stack[top + __popcll(mask & ((1ULL << lane) - 1))] = row;
 }
 
 __global__ __launch_bounds__(256) void k_evict(View v, int64_t n, const int64_t* __restrict__ keys) {
   const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
   const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
   const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
-  for (int64_t i = team; i < n; i += teams) {
-    const int64_t key = keys[i];
+  for (int64_t base = team - (lane >> 3); base < n; base += teams) {   // wave-uniform trip count
+    const int64_t i = base + (lane >> 3);
+    const int64_t key = i < n ? keys[i] : -1;
     const int64_t slot = key >= 0 ? find(v, key, lane) : -1;
-    if (slot >= 0 && sub == 0) free_slot(v, slot, key);
+    evict_slots(v, sub == 0 && slot >= 0, slot, key, lane);
   }
 }
 
 __global__ __launch_bounds__(256) void k_evict_older(View v, int64_t nslots, int32_t threshold) {
+  const int lane = threadIdx.x & 63;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t s = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; s < nslots; s += stride) {
-    const int64_t key = v.slots[s].key;
-    if (key < 0) continue;
-    const int32_t row = v.slots[s].row;
-    if (row >= 0 && v.last_seen[row] < threshold) free_slot(v, s, key);
+  for (int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x - lane; base < nslots; base += stride) {
+    const int64_t s = base + lane;
+    bool want = false;
+    int64_t key = -1;
+    if (s < nslots) {
+      key = v.slots[s].key;
+      if (key >= 0) {
+        const int32_t row = v.slots[s].row;
+        want = row >= 0 && v.last_seen[row] < threshold;
+      }
+    }
+    evict_slots(v, want, s, key, lane);
   }
 }
 
@@ -287,24 +333,33 @@ __global__ __launch_bounds__(256) void k_rebuild(View src, int64_t nslots, View 
 }
 
 // ---- dedup ---------------------------------------------------------------------------------
-// claim on a scratch index; the claiming team numbers its key (claim order) and records it
+// Claim on a scratch index; each claiming team numbers its key (one atomic per wavefront for the
+// wavefront's new keys) and records it.
 __global__ __launch_bounds__(256) void k_dedup_claim(View v, int64_t n, const int64_t* __restrict__ keys,
                                                      int64_t* __restrict__ res, int64_t* __restrict__ uniq,
                                                      unsigned long long* __restrict__ count) {
   const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
   const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
   const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
-  for (int64_t i = team; i < n; i += teams) {
-    const int64_t key = keys[i];
+  const int64_t first_of_wave = team - (lane >> 3);
+  for (int64_t base = first_of_wave; base < n; base += teams) {   // wave-uniform trip count
+    const int64_t i = base + (lane >> 3);
+    const int64_t key = i < n ? keys[i] : -1;
     const int64_t r = key >= 0 ? claim(v, key, lane) : -1;   // negative keys are not keys
-    if (sub == 0) {
-      res[i] = r;
-      if (r >= 0 && (r & (1LL << 62))) {
-        const int64_t id = (int64_t)atomicAdd(count, 1ULL);
+    const bool fresh = sub == 0 && r >= 0 && (r & (1LL << 62));
+    const unsigned long long mask = __ballot(fresh);
+    if (mask) {
+      const int leader = __ffsll((long long)mask) - 1;
+      unsigned long long b0 = 0;
+      if (lane == leader) b0 = atomicAdd(count, (unsigned long long)__popcll(mask));
+      b0 = __shfl(b0, leader, kWave);
+      if (fresh) {
+        const int64_t id = (int64_t)b0 + __popcll(mask & ((1ULL << lane) - 1));
         v.slots[r & ((1LL << 62) - 1)].row = (int32_t)id;
         uniq[id] = key;
       }
     }
+    if (sub == 0 && i < n) res[i] = r;
   }
 }
 
