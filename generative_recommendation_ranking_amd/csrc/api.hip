@@ -311,7 +311,7 @@ BwdPlan make_bwd_plan(const Sizes& z) {
   p.tb = take((std::max(d, h) + 8) * (size_t)p.Tp * es);
   p.wt = take(std::max(h * d, 4 * d * d) * es);
   p.part = take((size_t)p.ks * std::max({d * (h + 8), h * (d + 8), 4 * d * (d + 8)}) * sizeof(float));
-  p.gpart = take((size_t)groupln_bwd_waves(z.T) * 8 * d * sizeof(float));
+  p.gpart = take((size_t)std::max(groupln_bwd_waves(z.T, 0), groupln_bwd_waves(z.T, 1)) * 8 * d * sizeof(float));
   p.total = off;
   return p;
 }
@@ -334,9 +334,9 @@ hipError_t weight_grad(const BwdPlan& pl, void* ws, int dtype, int M, int K, con
 }
 
 // GroupLN parameter gradients from the per-wavefront slots [waves][2][4][d].
-hipError_t gln_param_grads(int64_t T, int d, const float* gpart, float* dgamma, float* dbeta,
+hipError_t gln_param_grads(int64_t T, int d, int x_kind, const float* gpart, float* dgamma, float* dbeta,
                            hipStream_t s) {
-  const int waves = T > 0 ? groupln_bwd_waves(T) : 0;
+  const int waves = T > 0 ? groupln_bwd_waves(T, x_kind) : 0;
   hipError_t e = launch_reduce(4 * (int64_t)d, waves, 8 * (int64_t)d, gpart, dgamma, s);
   if (e != hipSuccess) return e;
   return launch_reduce(4 * (int64_t)d, waves, 8 * (int64_t)d, gpart ? gpart + 4 * d : nullptr, dbeta, s);
@@ -402,7 +402,7 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   // GLN2: dy (in place over dz) and the GLN2 parameter gradients
   MTGR_BWD_TRY(launch_groupln_bwd(T, d, act, act, shared, y, b->group_ids, p->gln2_gamma, p->ln_eps,
                                   dz, nullptr, dz, act, gpart, s));
-  MTGR_BWD_TRY(gln_param_grads(T, d, gpart, g->gln2_gamma, g->gln2_beta, s));
+  MTGR_BWD_TRY(gln_param_grads(T, d, act, gpart, g->gln2_gamma, g->gln2_beta, s));
   // gate and attention: dqkvu from qkvu, V~ and dy (G = dy (.) U goes to the free dout buffer)
   MTGR_BWD_TRY(attention_bwd(b, d, H, dt, p->mask_mode, pb, qkvu, vt, dz, at<void>(ws, pl.dout), dqkvu, s));
   // QKVU: dxt = dqkvu W_qkvu (over dz), dW_qkvu = dqkvu^T xt, db_qkvu = sum dqkvu
@@ -414,7 +414,7 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   // GLN1 plus the residual path: dx_in = dx_out + GLN1'(x_in)^T dxt
   MTGR_BWD_TRY(launch_groupln_bwd(T, d, 0, act, shared, x_in, b->group_ids, p->gln1_gamma, p->ln_eps,
                                   dz, dx_out, dx_in, 0, gpart, s));
-  MTGR_BWD_TRY(gln_param_grads(T, d, gpart, g->gln1_gamma, g->gln1_beta, s));
+  MTGR_BWD_TRY(gln_param_grads(T, d, 0, gpart, g->gln1_gamma, g->gln1_beta, s));
 #undef MTGR_BWD_TRY
   return hipSuccess;
 }
@@ -507,8 +507,8 @@ mtgr_status mtgr_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, cons
     MTGR_TRY(launch_reduce_wb(d, h, h + 8, 0, nullptr, g->w_mlp2, g->b_mlp2, s));
     MTGR_TRY(launch_reduce_wb(h, d, d + 8, 0, nullptr, g->w_mlp1, g->b_mlp1, s));
     MTGR_TRY(launch_reduce_wb(4 * d, d, d + 8, 0, nullptr, g->w_qkvu, g->b_qkvu, s));
-    MTGR_TRY(gln_param_grads(0, d, nullptr, g->gln1_gamma, g->gln1_beta, s));
-    MTGR_TRY(gln_param_grads(0, d, nullptr, g->gln2_gamma, g->gln2_beta, s));
+    MTGR_TRY(gln_param_grads(0, d, 0, nullptr, g->gln1_gamma, g->gln1_beta, s));
+    MTGR_TRY(gln_param_grads(0, d, 0, nullptr, g->gln2_gamma, g->gln2_beta, s));
     return MTGR_OK;
   }
   Sizes z = sizes_for(b, d, h, 0, p->dtype, p->num_heads);

@@ -171,11 +171,11 @@ __global__ __launch_bounds__(256) void k_reduce_wb(int M, int K, int Kx, int nsp
 // current group in registers and adds them into its own slot [2][4][d] of `part` whenever the group
 // changes (tokens come in group runs); only that wavefront touches the slot, in program order, and
 // k_reduce sums the slots in a fixed order, so the result is deterministic.
-template <typename Tx, typename Tdz, typename Tp, typename Tout>
+template <typename Tx, typename Tdz, typename Tp, typename Tout, bool PF>
 __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t rows_per_wave,
                                                      const Tx* __restrict__ x, const uint8_t* __restrict__ g,
                                                      const Tp* __restrict__ gamma, float eps, int gmask,
-                                                     const Tdz* __restrict__ dz, const float* resid, Tout* dx,
+                                                     const Tdz* dz, const float* resid, Tout* dx,
                                                      float* __restrict__ part) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -208,67 +208,156 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
     }
   };
   const float inv_d = 1.0f / (float)d;
-  for (int64_t row = r0; row < r1; ++row) {
-    const int grp = g[row] & gmask;
-    if (grp != cur) {
-      flush();
-      cur = grp;
+  if constexpr (!PF) {
+    for (int64_t row = r0; row < r1; ++row) {
+      const int grp = g[row] & gmask;
+      if (grp != cur) {
+        flush();
+        cur = grp;
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) { ag[c][i] = 0.f; ab[c][i] = 0.f; }
+      }
+      float v[2][8], dv[2][8];
+      float s1 = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            v[c][i] = to_f32(x[row * d + ch * 8 + i]);
+            dv[c][i] = to_f32(dz[row * d + ch * 8 + i]);
+            s1 += v[c][i];
+          }
+        }
+      }
+      const float mean = wave_sum(s1) * inv_d;
+      float q = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
+        if (lane + 64 * c < nch)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { ag[c][i] = 0.f; ab[c][i] = 0.f; }
-    }
-    float v[2][8], dv[2][8];
-    float s1 = 0.f;
+          for (int i = 0; i < 8; ++i) { const float e = v[c][i] - mean; q += e * e; }
+      const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+      float sa = 0.f, sb = 0.f;       // sum dxh, sum dxh * xh
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int ch = lane + 64 * c;
-      if (ch < nch) {
+      for (int c = 0; c < 2; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          v[c][i] = to_f32(x[row * d + ch * 8 + i]);
-          dv[c][i] = to_f32(dz[row * d + ch * 8 + i]);
-          s1 += v[c][i];
+          for (int i = 0; i < 8; ++i) {
+            const float xh = (v[c][i] - mean) * rstd;
+            const float dxh = dv[c][i] * to_f32(gamma[grp * d + ch * 8 + i]);
+            ag[c][i] += dv[c][i] * xh;
+            ab[c][i] += dv[c][i];
+            sa += dxh;
+            sb += dxh * xh;
+            v[c][i] = xh;
+            dv[c][i] = dxh;
+          }
+        }
+      }
+      const float ma = wave_sum(sa) * inv_d, mb = wave_sum(sb) * inv_d;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int64_t idx = row * d + ch * 8 + i;
+            float o = (dv[c][i] - ma - v[c][i] * mb) * rstd;
+            if (resid) o += resid[idx];
+            dx[idx] = cvt<Tout>(o);
+          }
         }
       }
     }
-    const float mean = wave_sum(s1) * inv_d;
-    float q = 0.f;
+  } else {
+    // Every load of a row (x, dz and the residual) is issued together; with PF the next row's loads
+    // are issued before this row is reduced, so a wavefront always has a row in flight (more
+    // registers: fewer wavefronts per SIMD, which pays off for the wide fp32 rows only).
+    float v[2][8], dv[2][8], rs[2][8];
+    float nv[2][8], ndv[2][8], nrs[2][8];
+    auto load_row = [&](int64_t row, float (&a)[2][8], float (&b)[2][8], float (&c)[2][8]) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
-      if (lane + 64 * c < nch)
+      for (int cc = 0; cc < 2; ++cc) {
+        const int ch = lane + 64 * cc;
+        if (ch < nch && row < r1) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { const float e = v[c][i] - mean; q += e * e; }
-    const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
-    float sa = 0.f, sb = 0.f;       // sum dxh, sum dxh * xh
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int ch = lane + 64 * c;
-      if (ch < nch) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float xh = (v[c][i] - mean) * rstd;
-          const float dxh = dv[c][i] * to_f32(gamma[grp * d + ch * 8 + i]);
-          ag[c][i] += dv[c][i] * xh;
-          ab[c][i] += dv[c][i];
-          sa += dxh;
-          sb += dxh * xh;
-          v[c][i] = xh;
-          dv[c][i] = dxh;
+          for (int i = 0; i < 8; ++i) {
+            const int64_t idx = row * d + ch * 8 + i;
+            a[cc][i] = to_f32(x[idx]);
+            b[cc][i] = to_f32(dz[idx]);
+            if (PF) c[cc][i] = resid ? resid[idx] : 0.f;
+          }
         }
       }
-    }
-    const float ma = wave_sum(sa) * inv_d, mb = wave_sum(sb) * inv_d;
+    };
+    if (PF) load_row(r0, nv, ndv, nrs);
+    for (int64_t row = r0; row < r1; ++row) {
+      if (PF) {
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int ch = lane + 64 * c;
-      if (ch < nch) {
+        for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int64_t idx = row * d + ch * 8 + i;
-          float o = (dv[c][i] - ma - v[c][i] * mb) * rstd;
-          if (resid) o += resid[idx];
-          dx[idx] = cvt<Tout>(o);
+          for (int i = 0; i < 8; ++i) { v[cc][i] = nv[cc][i]; dv[cc][i] = ndv[cc][i]; rs[cc][i] = nrs[cc][i]; }
+        load_row(row + 1, nv, ndv, nrs);
+      } else {
+        load_row(row, v, dv, rs);
+      }
+      const int grp = g[row] & gmask;
+      if (grp != cur) {
+        flush();
+        cur = grp;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) { ag[cc][i] = 0.f; ab[cc][i] = 0.f; }
+      }
+      float s1 = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        if (lane + 64 * cc < nch)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s1 += v[cc][i];
+      const float mean = wave_sum(s1) * inv_d;
+      float q = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
+        if (lane + 64 * cc < nch)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) { const float e = v[cc][i] - mean; q += e * e; }
+      const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+      float sa = 0.f, sb = 0.f;       // sum dxh, sum dxh * xh
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int ch = lane + 64 * cc;
+        if (ch < nch) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float xh = (v[cc][i] - mean) * rstd;
+            const float dxh = dv[cc][i] * to_f32(gamma[grp * d + ch * 8 + i]);
+            ag[cc][i] += dv[cc][i] * xh;
+            ab[cc][i] += dv[cc][i];
+            sa += dxh;
+            sb += dxh * xh;
+            v[cc][i] = xh;
+            dv[cc][i] = dxh;
+          }
+        }
+      }
+      const float ma = wave_sum(sa) * inv_d, mb = wave_sum(sb) * inv_d;
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc) {
+        const int ch = lane + 64 * cc;
+        if (ch < nch) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int64_t idx = row * d + ch * 8 + i;
+            const float r = PF ? rs[cc][i] : (resid ? resid[idx] : 0.f);
+            dx[idx] = cvt<Tout>((dv[cc][i] - ma - v[cc][i] * mb) * rstd + r);
+          }
         }
       }
     }
@@ -441,27 +530,33 @@ hipError_t launch_reduce_wb(int M, int K, int Kx, int nsplit, const float* part,
 }
 
 // wavefronts of the GroupLN backward: one slot [2][4][d] of partial parameter gradients each
-int groupln_bwd_waves(int64_t T) { return 4 * (int)std::max<int64_t>(1, std::min<int64_t>(1024, (T + 255) / 256)); }
+// wavefronts of the GroupLN backward (one slot of partial parameter gradients each): one round of
+// resident wavefronts on 256 CUs -- the fp32-input variant (prefetching, ~185 VGPRs) holds 2 per
+// SIMD, the bf16 one (~120 VGPRs) 4
+int groupln_bwd_waves(int64_t T, int x_kind) {
+  const int64_t cap = x_kind == 0 ? 512 : 1024;
+  return 4 * (int)std::max<int64_t>(1, std::min<int64_t>(cap, (T + 255) / 256));
+}
 
 hipError_t launch_groupln_bwd(int64_t T, int d, int x_kind, int act_kind, int shared, const void* x,
                               const uint8_t* g, const void* gamma, float eps, const void* dz,
                               const float* resid, void* dx, int out_kind, float* part, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int waves = groupln_bwd_waves(T);
+  const int waves = groupln_bwd_waves(T, x_kind);
   const int64_t rpw = (T + waves - 1) / waves;
   const unsigned grid = (unsigned)(waves / 4);
   const int gm = shared ? 0 : 3;
   // (x, dz, gamma, dx) types: GLN2 uses (act, act, act, act); GLN1 uses (float, act, act, float)
   if (x_kind == 0 && act_kind == 0 && out_kind == 0)
-    k_groupln_bwd<float, float, float, float><<<grid, 256, 0, s>>>(
+    k_groupln_bwd<float, float, float, float, true><<<grid, 256, 0, s>>>(
         T, d, rpw, static_cast<const float*>(x), g, static_cast<const float*>(gamma), eps, gm,
         static_cast<const float*>(dz), resid, static_cast<float*>(dx), part);
   else if (x_kind == 1 && act_kind == 1 && out_kind == 1)
-    k_groupln_bwd<bf16, bf16, bf16, bf16><<<grid, 256, 0, s>>>(
+    k_groupln_bwd<bf16, bf16, bf16, bf16, false><<<grid, 256, 0, s>>>(
         T, d, rpw, static_cast<const bf16*>(x), g, static_cast<const bf16*>(gamma), eps, gm,
         static_cast<const bf16*>(dz), resid, static_cast<bf16*>(dx), part);
   else if (x_kind == 0 && act_kind == 1 && out_kind == 0)
-    k_groupln_bwd<float, bf16, bf16, float><<<grid, 256, 0, s>>>(
+    k_groupln_bwd<float, bf16, bf16, float, true><<<grid, 256, 0, s>>>(
         T, d, rpw, static_cast<const float*>(x), g, static_cast<const bf16*>(gamma), eps, gm,
         static_cast<const bf16*>(dz), resid, static_cast<float*>(dx), part);
   else

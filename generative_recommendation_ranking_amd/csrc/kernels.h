@@ -74,7 +74,7 @@ hipError_t launch_reduce_wb(int M, int K, int Kx, int nsplit, const float* part,
                             hipStream_t s);
 // GroupLN backward: dx = GLN'(x)^T dz (+ resid); per-wavefront partials of (dgamma, dbeta)
 // [groupln_bwd_waves(T)][2][4][d]
-int groupln_bwd_waves(int64_t T);
+int groupln_bwd_waves(int64_t T, int x_kind);
 hipError_t launch_groupln_bwd(int64_t T, int d, int x_kind, int act_kind, int shared, const void* x,
                               const uint8_t* g, const void* gamma, float eps, const void* dz,
                               const float* resid, void* dx, int out_kind, float* part, hipStream_t s);
