@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(
 
 // ---- dQ -------------------------------------------------------------------------------------------
 template <int DH, int MODE>
-__global__ __launch_bounds__(256, 1) void k_attn_bwd_dq(
+__global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
     int32_t B, int H, int d, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
     const int32_t* __restrict__ order, const int32_t* __restrict__ xcd_off, const float* __restrict__ ts,
     const bf16* __restrict__ qkvu, const bf16* __restrict__ gq, bf16* __restrict__ dqkvu) {
@@ -486,29 +486,27 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dq(
     return need;
   };
 
+  // S^T and dP^T one 32-key half at a time (only half the score accumulators live), then the
+  // next tile's loads, then dQ += dS K: the loads stay in flight across the dQ MFMAs, and the
+  // kernel fits two wavefronts per SIMD.
   bf16x8 da[4];
-  auto compute = [&](int buf, int k0) {
-    f32x16 sc[2], dp[2];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { sc[mt][r] = 0.f; dp[mt][r] = 0.f; }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][sw_off<DH>(mt * 32 + l32, ks * 16 + hh * 8)]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[buf][mt * 32 + l32][ks * 16 + hh * 8]);
-        sc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sc[mt], 0, 0, 0);
-        dp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], dp[mt], 0, 0, 0);
-      }
-    }
-    // sc[mt][r], dp[mt][r]: key k0 + mt*32 + 8*(r/4) + 4*hh + r%4, query qi
+  auto scores = [&](int buf, int k0) {
     const bool unmasked = MODE == kMaskFull || (MODE == kMaskCausal ? k0 + BKV <= wq0 + 1 : k0 + BKV <= ns);
     const int jb = k0 + 4 * hh;
     const int lim_static = ns - jb, lim_rc = rc_end - jb, self = qi - jb;
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
+      f32x16 sc, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][sw_off<DH>(mt * 32 + l32, ks * 16 + hh * 8)]);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[buf][mt * 32 + l32][ks * 16 + hh * 8]);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], dp, 0, 0, 0);
+      }
+      // sc[r], dp[r]: key k0 + mt*32 + 8*(r/4) + 4*hh + r%4, query qi
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         f32x4 t4 = {};
@@ -517,9 +515,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dq(
         for (int c = 0; c < 4; ++c) {
           const int r = g4 * 4 + c;
           const int dk = mt * 32 + 8 * g4 + c;
-          const float s = sc[mt][r];
+          const float s = sc[r];
           const float sgm = sigmoid_rcp(s);
-          float ds = dp[mt][r] * sgm * (1.0f + s * (1.0f - sgm));
+          float ds = dp[r] * sgm * (1.0f + s * (1.0f - sgm));
           if (!unmasked) {
             const bool vis = MODE == kMaskCausal
                                  ? dk <= self
@@ -530,6 +528,8 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dq(
         }
       }
     }
+  };
+  auto accumulate = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -547,8 +547,9 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dq(
     const int cur = kt & 1;
     const int k0 = kt * BKV;
     const bool need = tile_needed(cur, k0);
+    if (need) scores(cur, k0);
     if (kt + 1 < nkt) stage_load(k0 + BKV);
-    if (need) compute(cur, k0);
+    if (need) accumulate(cur);
     if (kt + 1 < nkt) stage_store(cur ^ 1);
     __syncthreads();
   }
