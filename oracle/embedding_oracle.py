@@ -31,6 +31,10 @@ Readings (the same numbering as the design notes):
       is free; lookup returns the value or reports the key missing; evict frees the key's row;
       evict_older evicts every key whose last use is older than a given step.
 
+R15-R17 fill in what the pages leave open (how many fields, their widths, the MLP's depth) and are
+parity unpinned with respect to the pages: the functions below are pinned to these readings, not
+to anything the pages fix.
+
 parity pins: tests/test_oracle_pins.py checks the store model against a brute-force list-of-pairs
 model over random operation sequences and against its invariants, dedup against Python sets, and
 the tokenizer against an independent torch formulation (nn.Embedding, cat, nn.Linear).
