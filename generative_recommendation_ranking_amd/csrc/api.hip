@@ -271,11 +271,13 @@ struct BwdPlan {
   Plan prep;
   size_t xt = 0, qkvu = 0, y = 0, vt = 0, z = 0, a = 0, dout = 0, dhid = 0, dz = 0;
   size_t dqkvu = 0, ta = 0, tb = 0, wt = 0, part = 0, gpart = 0, total = 0;
-  int ks = 1;
-  int64_t Tp = 0;
+  // per weight-gradient GEMM (0: W2, 1: W1, 2: W_qkvu): split count and padded token axis
+  int ks[3] = {1, 1, 1};
+  int64_t Tp[3] = {0, 0, 0};
 };
 
 constexpr int64_t kMaxBwdTokens = 4000000;
+constexpr int64_t kGemmWorkgroups = 256;   // persistent GEMM grid: one workgroup per CU of an MI355X
 
 inline int64_t tiles256(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
 
@@ -290,13 +292,25 @@ BwdPlan make_bwd_plan(const Sizes& z) {
   };
   const size_t es = esize(z.dtype);
   const size_t T = (size_t)z.T, d = (size_t)z.d, h = (size_t)z.h;
-  // split count of the weight-gradient GEMMs: enough output tiles to cover the CUs, each split at
-  // least 2048 tokens long
-  const int64_t tmin = std::min({tiles256(d, h + 8), tiles256(h, d + 8), tiles256(4 * d, d + 8)});
-  p.ks = 1;
-  while (p.ks < 32 && tmin * p.ks * 2 <= 512 && z.T >= (int64_t)p.ks * 2 * 2048) p.ks *= 2;
-  const int64_t unit = 64 * (int64_t)p.ks;
-  p.Tp = std::max((z.T + unit - 1) / unit * unit, 2 * unit);
+  // Split count of each weight-gradient GEMM: the persistent GEMM runs one workgroup per CU, so
+  // the split count is chosen for whole rounds of tiles (tiles * splits close to a multiple of
+  // kGemmWorkgroups from below), each split at least 2048 tokens long; ties go to fewer splits.
+  const int64_t tiles[3] = {tiles256(d, h + 8), tiles256(h, d + 8), tiles256(4 * d, d + 8)};
+  int64_t tp_max = 0;
+  for (int gi = 0; gi < 3; ++gi) {
+    int best = 1;
+    double best_eff = 0.0;
+    for (int ks = 1; ks <= 32 && z.T >= (int64_t)ks * 2048; ++ks) {
+      const int64_t work = tiles[gi] * ks;
+      const int64_t rounds = (work + kGemmWorkgroups - 1) / kGemmWorkgroups;
+      const double eff = (double)work / (double)(rounds * kGemmWorkgroups);
+      if (eff > best_eff + 1e-9) { best_eff = eff; best = ks; }
+    }
+    p.ks[gi] = best;
+    const int64_t unit = 64 * (int64_t)best;
+    p.Tp[gi] = std::max((z.T + unit - 1) / unit * unit, 2 * unit);
+    tp_max = std::max(tp_max, p.Tp[gi]);
+  }
   p.xt = take(T * d * es);
   p.qkvu = take(T * 4 * d * es);
   p.y = take(T * d * es);
@@ -307,10 +321,11 @@ BwdPlan make_bwd_plan(const Sizes& z) {
   p.dhid = take(T * h * es);
   p.dz = take(T * d * es);
   p.dqkvu = take(T * 4 * d * es);
-  p.ta = take(std::max({d, h, 4 * d}) * (size_t)p.Tp * es);
-  p.tb = take((std::max(d, h) + 8) * (size_t)p.Tp * es);
+  p.ta = take(std::max({d, h, 4 * d}) * (size_t)tp_max * es);
+  p.tb = take((std::max(d, h) + 8) * (size_t)tp_max * es);
   p.wt = take(std::max(h * d, 4 * d * d) * es);
-  p.part = take((size_t)p.ks * std::max({d * (h + 8), h * (d + 8), 4 * d * (d + 8)}) * sizeof(float));
+  p.part = take(std::max({(size_t)p.ks[0] * d * (h + 8), (size_t)p.ks[1] * h * (d + 8),
+                          (size_t)p.ks[2] * 4 * d * (d + 8)}) * sizeof(float));
   p.gpart = take((size_t)std::max(groupln_bwd_waves(z.T, 0), groupln_bwd_waves(z.T, 1)) * 8 * d * sizeof(float));
   p.total = off;
   return p;
@@ -318,19 +333,19 @@ BwdPlan make_bwd_plan(const Sizes& z) {
 
 // dW [M][K] (+ db [M]) = sum over tokens of dy^T x, from the transposed operands at and bt
 // ([M][Tp] and [K+8][Tp], the row K of bt all ones) by split-K GEMMs and a fixed-order reduction.
-hipError_t weight_grad(const BwdPlan& pl, void* ws, int dtype, int M, int K, const void* at_,
+hipError_t weight_grad(const BwdPlan& pl, int gi, void* ws, int dtype, int M, int K, const void* at_,
                        const void* bt_, float* dw, float* db, hipStream_t s) {
   float* part = at<float>(ws, pl.part);
   const int Kx = K + 8;
   hipError_t e;
   if (dtype == MTGR_BF16)
-    e = launch_gemm_bf16_splitk(M, Kx, (int)pl.Tp, pl.ks, static_cast<const bf16*>(at_),
+    e = launch_gemm_bf16_splitk(M, Kx, (int)pl.Tp[gi], pl.ks[gi], static_cast<const bf16*>(at_),
                                 static_cast<const bf16*>(bt_), part, s);
   else
-    e = launch_gemm_f32_splitk(M, Kx, (int)pl.Tp, pl.ks, static_cast<const float*>(at_),
+    e = launch_gemm_f32_splitk(M, Kx, (int)pl.Tp[gi], pl.ks[gi], static_cast<const float*>(at_),
                                static_cast<const float*>(bt_), part, s);
   if (e != hipSuccess) return e;
-  return launch_reduce_wb(M, K, Kx, pl.ks, part, dw, db, s);
+  return launch_reduce_wb(M, K, Kx, pl.ks[gi], part, dw, db, s);
 }
 
 // GroupLN parameter gradients from the per-wavefront slots [waves][2][4][d].
@@ -389,16 +404,16 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   }
   MTGR_BWD_TRY(launch_transpose(d, h, d, 0, 0, act, p->w_mlp2, wt, s));
   MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, dout, wt, nullptr, nullptr, dhid, s));
-  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 0, 0, act, dout, ta, s));
-  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp, 1, 1, act, a, tb, s));     // silu(a)^T = hid^T
-  MTGR_BWD_TRY(weight_grad(pl, ws, dt, d, h, ta, tb, g->w_mlp2, g->b_mlp2, s));
+  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp[0], 0, 0, act, dout, ta, s));
+  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp[0], 1, 1, act, a, tb, s));  // silu(a)^T = hid^T
+  MTGR_BWD_TRY(weight_grad(pl, 0, ws, dt, d, h, ta, tb, g->w_mlp2, g->b_mlp2, s));
   // MLP1: da = dhid (.) silu'(a) (in place), dz = da W1, dW1 = da^T z, db1 = sum da
   MTGR_BWD_TRY(launch_silu_bwd(T * h, act, a, dhid, s));
   MTGR_BWD_TRY(launch_transpose(h, d, h, 0, 0, act, p->w_mlp1, wt, s));
   MTGR_BWD_TRY(linear(T, d, h, dt, MTGR_EPI_STORE, dhid, wt, nullptr, nullptr, dz, s));
-  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp, 0, 0, act, dhid, ta, s));
-  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 1, 0, act, z, tb, s));
-  MTGR_BWD_TRY(weight_grad(pl, ws, dt, h, d, ta, tb, g->w_mlp1, g->b_mlp1, s));
+  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp[1], 0, 0, act, dhid, ta, s));
+  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp[1], 1, 0, act, z, tb, s));
+  MTGR_BWD_TRY(weight_grad(pl, 1, ws, dt, h, d, ta, tb, g->w_mlp1, g->b_mlp1, s));
   // GLN2: dy (in place over dz) and the GLN2 parameter gradients
   MTGR_BWD_TRY(launch_groupln_bwd(T, d, act, act, shared, y, b->group_ids, p->gln2_gamma, p->ln_eps,
                                   dz, nullptr, dz, act, gpart, s));
@@ -408,9 +423,9 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   // QKVU: dxt = dqkvu W_qkvu (over dz), dW_qkvu = dqkvu^T xt, db_qkvu = sum dqkvu
   MTGR_BWD_TRY(launch_transpose(4 * (int64_t)d, d, 4 * (int64_t)d, 0, 0, act, p->w_qkvu, wt, s));
   MTGR_BWD_TRY(linear(T, d, 4 * d, dt, MTGR_EPI_STORE, dqkvu, wt, nullptr, nullptr, dz, s));
-  MTGR_BWD_TRY(launch_transpose(T, 4 * d, pl.Tp, 0, 0, act, dqkvu, ta, s));
-  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp, 1, 0, act, xt, tb, s));
-  MTGR_BWD_TRY(weight_grad(pl, ws, dt, 4 * d, d, ta, tb, g->w_qkvu, g->b_qkvu, s));
+  MTGR_BWD_TRY(launch_transpose(T, 4 * d, pl.Tp[2], 0, 0, act, dqkvu, ta, s));
+  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp[2], 1, 0, act, xt, tb, s));
+  MTGR_BWD_TRY(weight_grad(pl, 2, ws, dt, 4 * d, d, ta, tb, g->w_qkvu, g->b_qkvu, s));
   // GLN1 plus the residual path: dx_in = dx_out + GLN1'(x_in)^T dxt
   MTGR_BWD_TRY(launch_groupln_bwd(T, d, 0, act, shared, x_in, b->group_ids, p->gln1_gamma, p->ln_eps,
                                   dz, dx_out, dx_in, 0, gpart, s));
