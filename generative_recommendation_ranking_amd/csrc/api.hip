@@ -264,13 +264,13 @@ hipError_t run_block(const mtgr_block_params* p, const mtgr_batch* b, const Prep
 
 // ---- backward ----------------------------------------------------------------------------------
 // Workspace of mtgr_block_bwd after the prep buffers: the recomputed forward activations, the
-// activation gradients, transposed copies for the weight-gradient GEMMs (token axis last, padded
-// to Tp with zeros, plus a ones row whose product gives the bias gradient), one transposed weight,
-// and fp32 partial sums (split-K slices of the weight gradients, per-wavefront GroupLN slots).
+// activation gradients, in fp32 transposed copies for the weight-gradient GEMMs (token axis last,
+// padded to Tp with zeros, plus a ones row whose product gives the bias gradient), one transposed
+// weight, and fp32 partial sums (split-K slices of the weight gradients, per-wavefront GroupLN slots).
 struct BwdPlan {
   Plan prep;
   size_t xt = 0, qkvu = 0, y = 0, vt = 0, z = 0, a = 0, dout = 0, dhid = 0, dz = 0;
-  size_t dqkvu = 0, ta = 0, tb = 0, wt = 0, part = 0, gpart = 0, total = 0;
+  size_t dqkvu = 0, ta = 0, tb = 0, wt = 0, part = 0, cs = 0, gpart = 0, total = 0;
   // per weight-gradient GEMM (0: W2, 1: W1, 2: W_qkvu): split count and padded token axis
   int ks[3] = {1, 1, 1};
   int64_t Tp[3] = {0, 0, 0};
@@ -292,24 +292,40 @@ BwdPlan make_bwd_plan(const Sizes& z) {
   };
   const size_t es = esize(z.dtype);
   const size_t T = (size_t)z.T, d = (size_t)z.d, h = (size_t)z.h;
-  // Split count of each weight-gradient GEMM: the persistent GEMM runs one workgroup per CU, so
-  // the split count is chosen for whole rounds of tiles (tiles * splits close to a multiple of
-  // kGemmWorkgroups from below), each split at least 2048 tokens long; ties go to fewer splits.
-  const int64_t tiles[3] = {tiles256(d, h + 8), tiles256(h, d + 8), tiles256(4 * d, d + 8)};
+  // Split count of each weight-gradient GEMM.  The persistent GEMM runs one workgroup per CU.  bf16
+  // (k-major GEMM, no bias column): with at least 8 x 2048 tokens the split count is a multiple of
+  // the XCD count (each split's tiles share one XCD's L2), chosen for whole rounds of each XCD's
+  // workgroups, at most 64; below that 1..7 splits for whole rounds of the grid.  fp32 (transposed
+  // operands with a ones row): 1..32 splits for whole rounds of the grid.  Each split is at least
+  // 2048 tokens long, one split's rows stay within a 32-bit buffer range, ties go to fewer splits.
+  const bool bf = z.dtype == MTGR_BF16;
+  const int64_t Mg[3] = {(int64_t)d, (int64_t)h, 4 * (int64_t)d};
+  const int64_t Kg[3] = {(int64_t)h, (int64_t)d, (int64_t)d};
+  const int64_t per_xcd = kGemmWorkgroups / 8;
   int64_t tp_max = 0;
+  size_t part_max = 0, cs_max = 0;
   for (int gi = 0; gi < 3; ++gi) {
-    int best = 1;
+    const int64_t tiles = tiles256(Mg[gi], Kg[gi] + (bf ? 0 : 8));
+    const bool xcd_major = bf && z.T >= 8 * 2048;
+    int best = 0;
     double best_eff = 0.0;
-    for (int ks = 1; ks <= 32 && z.T >= (int64_t)ks * 2048; ++ks) {
-      const int64_t work = tiles[gi] * ks;
-      const int64_t rounds = (work + kGemmWorkgroups - 1) / kGemmWorkgroups;
-      const double eff = (double)work / (double)(rounds * kGemmWorkgroups);
+    for (int ks = xcd_major ? 8 : 1; ks <= (xcd_major ? 64 : bf ? 7 : 32) && (ks == 1 || z.T >= (int64_t)ks * 2048);
+         ks += xcd_major ? 8 : 1) {
+      const int64_t unit_k = 64 * (int64_t)ks;
+      const int64_t tp_k = std::max((z.T + unit_k - 1) / unit_k * unit_k, 2 * unit_k);
+      if (bf && (tp_k / ks) * std::max(Mg[gi], Kg[gi]) * 2 >= (int64_t(1) << 31)) continue;
+      const int64_t work = xcd_major ? tiles * ks / 8 : tiles * ks;
+      const int64_t slots = xcd_major ? per_xcd : kGemmWorkgroups;
+      const int64_t rounds = (work + slots - 1) / slots;
+      const double eff = (double)work / (double)(rounds * slots);
       if (eff > best_eff + 1e-9) { best_eff = eff; best = ks; }
     }
-    p.ks[gi] = best;
-    const int64_t unit = 64 * (int64_t)best;
+    p.ks[gi] = std::max(best, 1);      // the token limit keeps some split count feasible
+    const int64_t unit = 64 * (int64_t)p.ks[gi];
     p.Tp[gi] = std::max((z.T + unit - 1) / unit * unit, 2 * unit);
     tp_max = std::max(tp_max, p.Tp[gi]);
+    part_max = std::max(part_max, (size_t)p.ks[gi] * Mg[gi] * (Kg[gi] + (bf ? 0 : 8)));
+    if (bf) cs_max = std::max(cs_max, (size_t)colsum_blocks(z.T, (int)Mg[gi]) * Mg[gi]);
   }
   p.xt = take(T * d * es);
   p.qkvu = take(T * 4 * d * es);
@@ -321,29 +337,40 @@ BwdPlan make_bwd_plan(const Sizes& z) {
   p.dhid = take(T * h * es);
   p.dz = take(T * d * es);
   p.dqkvu = take(T * 4 * d * es);
-  p.ta = take(std::max({d, h, 4 * d}) * (size_t)tp_max * es);
-  p.tb = take((std::max(d, h) + 8) * (size_t)tp_max * es);
+  // transposed copies for the fp32 weight-gradient GEMMs (the bf16 ones read activations in place)
+  p.ta = take(bf ? 0 : std::max({d, h, 4 * d}) * (size_t)tp_max * es);
+  p.tb = take(bf ? 0 : (std::max(d, h) + 8) * (size_t)tp_max * es);
   p.wt = take(std::max(h * d, 4 * d * d) * es);
-  p.part = take(std::max({(size_t)p.ks[0] * d * (h + 8), (size_t)p.ks[1] * h * (d + 8),
-                          (size_t)p.ks[2] * 4 * d * (d + 8)}) * sizeof(float));
+  p.part = take(part_max * sizeof(float));
+  p.cs = take(cs_max * sizeof(float));
   p.gpart = take((size_t)std::max(groupln_bwd_waves(z.T, 0), groupln_bwd_waves(z.T, 1)) * 8 * d * sizeof(float));
   p.total = off;
   return p;
 }
 
-// dW [M][K] (+ db [M]) = sum over tokens of dy^T x, from the transposed operands at and bt
-// ([M][Tp] and [K+8][Tp], the row K of bt all ones) by split-K GEMMs and a fixed-order reduction.
-hipError_t weight_grad(const BwdPlan& pl, int gi, void* ws, int dtype, int M, int K, const void* at_,
-                       const void* bt_, float* dw, float* db, hipStream_t s) {
+// dW [M][K] (+ db [M]) = sum over tokens of dy^T x by split-K GEMMs and fixed-order reductions;
+// dy [T][M] and x [T][K] token-major.  bf16: the k-major GEMM reads them in place and db is the
+// column sum of dy.  fp32: transposed copies [M][Tp] and [K+8][Tp] (row K all ones, so that
+// column K of the product is db) and the fp32 GEMM.
+hipError_t weight_grad(const BwdPlan& pl, int gi, void* ws, int dtype, int64_t T, int M, int K, const void* dy,
+                       const void* x, float* dw, float* db, hipStream_t s) {
   float* part = at<float>(ws, pl.part);
-  const int Kx = K + 8;
   hipError_t e;
-  if (dtype == MTGR_BF16)
-    e = launch_gemm_bf16_splitk(M, Kx, (int)pl.Tp[gi], pl.ks[gi], static_cast<const bf16*>(at_),
-                                static_cast<const bf16*>(bt_), part, s);
-  else
-    e = launch_gemm_f32_splitk(M, Kx, (int)pl.Tp[gi], pl.ks[gi], static_cast<const float*>(at_),
-                               static_cast<const float*>(bt_), part, s);
+  if (dtype == MTGR_BF16) {
+    e = launch_gemm_bf16_kmajor_splitk(M, K, pl.Tp[gi], pl.ks[gi], T, static_cast<const bf16*>(dy), M,
+                                       static_cast<const bf16*>(x), K, part, s);
+    if (e == hipSuccess) e = launch_reduce_wb(M, K, K, pl.ks[gi], part, dw, nullptr, s);
+    if (e == hipSuccess && db) e = launch_colsum_bf16(T, M, static_cast<const bf16*>(dy), at<float>(ws, pl.cs), db, s);
+    return e;
+  }
+  const int Kx = K + 8;
+  void* ta = at<void>(ws, pl.ta);
+  void* tb = at<void>(ws, pl.tb);
+  e = launch_transpose(T, M, pl.Tp[gi], 0, 0, 0, dy, ta, s);
+  if (e == hipSuccess) e = launch_transpose(T, K, pl.Tp[gi], 1, 0, 0, x, tb, s);
+  if (e == hipSuccess)
+    e = launch_gemm_f32_splitk(M, Kx, (int)pl.Tp[gi], pl.ks[gi], static_cast<const float*>(ta),
+                               static_cast<const float*>(tb), part, s);
   if (e != hipSuccess) return e;
   return launch_reduce_wb(M, K, Kx, pl.ks[gi], part, dw, db, s);
 }
@@ -374,8 +401,6 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   void* dhid = at<void>(ws, pl.dhid);
   void* dz = at<void>(ws, pl.dz);
   void* dqkvu = at<void>(ws, pl.dqkvu);
-  void* ta = at<void>(ws, pl.ta);
-  void* tb = at<void>(ws, pl.tb);
   void* wt = at<void>(ws, pl.wt);
   float* gpart = at<float>(ws, pl.gpart);
   const int q_tile = q_tile_for(dt);
@@ -387,7 +412,7 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   } while (0)
   MTGR_BWD_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile, H, pb, false, s));
   // forward, keeping what the backward needs: GLN1 output, QKVU, V~, the gated output, GLN2
-  // output and the MLP pre-activation (its SiLU is applied where it is read, in a transpose)
+  // output and the MLP pre-activation a (its SiLU replaces it in the SiLU backward)
   MTGR_BWD_TRY(launch_groupln(T, d, 0, act, act, shared, x_in, b->group_ids, p->gln1_gamma,
                               p->gln1_beta, p->ln_eps, xt, s));
   MTGR_BWD_TRY(linear(T, 4 * d, d, dt, MTGR_EPI_STORE, xt, p->w_qkvu, p->b_qkvu, nullptr, qkvu, s));
@@ -396,7 +421,8 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
                               p->gln2_beta, p->ln_eps, z, s));
   MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, z, p->w_mlp1, p->b_mlp1, nullptr, a, s));
 
-  // MLP2: dhid = dout W2, dW2 = dout^T hid, db2 = sum dout
+  // MLP2 and the SiLU: dhid = dout W2, then da = dhid (.) silu'(a) in place with hid = silu(a)
+  // replacing a, then dW2 = dout^T hid, db2 = sum dout
   const void* dout = dx_out;
   if (act) {
     MTGR_BWD_TRY(launch_convert(T * d, act, dx_out, at<void>(ws, pl.dout), s));
@@ -404,16 +430,12 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   }
   MTGR_BWD_TRY(launch_transpose(d, h, d, 0, 0, act, p->w_mlp2, wt, s));
   MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, dout, wt, nullptr, nullptr, dhid, s));
-  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp[0], 0, 0, act, dout, ta, s));
-  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp[0], 1, 1, act, a, tb, s));  // silu(a)^T = hid^T
-  MTGR_BWD_TRY(weight_grad(pl, 0, ws, dt, d, h, ta, tb, g->w_mlp2, g->b_mlp2, s));
-  // MLP1: da = dhid (.) silu'(a) (in place), dz = da W1, dW1 = da^T z, db1 = sum da
   MTGR_BWD_TRY(launch_silu_bwd(T * h, act, a, dhid, s));
+  MTGR_BWD_TRY(weight_grad(pl, 0, ws, dt, T, d, h, dout, a, g->w_mlp2, g->b_mlp2, s));
+  // MLP1: dz = da W1, dW1 = da^T z, db1 = sum da
   MTGR_BWD_TRY(launch_transpose(h, d, h, 0, 0, act, p->w_mlp1, wt, s));
   MTGR_BWD_TRY(linear(T, d, h, dt, MTGR_EPI_STORE, dhid, wt, nullptr, nullptr, dz, s));
-  MTGR_BWD_TRY(launch_transpose(T, h, pl.Tp[1], 0, 0, act, dhid, ta, s));
-  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp[1], 1, 0, act, z, tb, s));
-  MTGR_BWD_TRY(weight_grad(pl, 1, ws, dt, h, d, ta, tb, g->w_mlp1, g->b_mlp1, s));
+  MTGR_BWD_TRY(weight_grad(pl, 1, ws, dt, T, h, d, dhid, z, g->w_mlp1, g->b_mlp1, s));
   // GLN2: dy (in place over dz) and the GLN2 parameter gradients
   MTGR_BWD_TRY(launch_groupln_bwd(T, d, act, act, shared, y, b->group_ids, p->gln2_gamma, p->ln_eps,
                                   dz, nullptr, dz, act, gpart, s));
@@ -423,9 +445,7 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   // QKVU: dxt = dqkvu W_qkvu (over dz), dW_qkvu = dqkvu^T xt, db_qkvu = sum dqkvu
   MTGR_BWD_TRY(launch_transpose(4 * (int64_t)d, d, 4 * (int64_t)d, 0, 0, act, p->w_qkvu, wt, s));
   MTGR_BWD_TRY(linear(T, d, 4 * d, dt, MTGR_EPI_STORE, dqkvu, wt, nullptr, nullptr, dz, s));
-  MTGR_BWD_TRY(launch_transpose(T, 4 * d, pl.Tp[2], 0, 0, act, dqkvu, ta, s));
-  MTGR_BWD_TRY(launch_transpose(T, d, pl.Tp[2], 1, 0, act, xt, tb, s));
-  MTGR_BWD_TRY(weight_grad(pl, 2, ws, dt, 4 * d, d, ta, tb, g->w_qkvu, g->b_qkvu, s));
+  MTGR_BWD_TRY(weight_grad(pl, 2, ws, dt, T, 4 * d, d, dqkvu, xt, g->w_qkvu, g->b_qkvu, s));
   // GLN1 plus the residual path: dx_in = dx_out + GLN1'(x_in)^T dxt
   MTGR_BWD_TRY(launch_groupln_bwd(T, d, 0, act, shared, x_in, b->group_ids, p->gln1_gamma, p->ln_eps,
                                   dz, dx_out, dx_in, 0, gpart, s));

@@ -92,27 +92,70 @@ __global__ __launch_bounds__(256) void k_transpose_bf16x8(int64_t R, int C, int6
 }
 
 // ---- elementwise ----------------------------------------------------------------------------
-// dh <- dh (.) silu'(a), silu'(z) = sigma(z) (1 + z (1 - sigma(z))); bf16: 8 elements per step
-__device__ __forceinline__ float silu_grad_f32(float z) {
-  const float sg = 1.0f / (1.0f + __expf(-z));
-  return sg * (1.0f + z * (1.0f - sg));
-}
-__global__ __launch_bounds__(256) void k_silu_bwd_bf16x8(int64_t n8, const bf16* __restrict__ a, bf16* __restrict__ dh) {
+// dh <- dh (.) silu'(a), silu'(z) = sigma(z) (1 + z (1 - sigma(z))), and a <- silu(a) = z sigma(z),
+// the hidden activation that the weight gradient of the MLP's second layer reads; bf16: 8 elements
+// per step
+__global__ __launch_bounds__(256) void k_silu_bwd_bf16x8(int64_t n8, bf16* __restrict__ a, bf16* __restrict__ dh) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
-    const bf16x8 z = *reinterpret_cast<const bf16x8*>(a + i * 8);
+    bf16x8 z = *reinterpret_cast<const bf16x8*>(a + i * 8);
     bf16x8 g = *reinterpret_cast<const bf16x8*>(dh + i * 8);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) g[e] = (bf16)((float)g[e] * silu_grad_f32((float)z[e]));
+    for (int e = 0; e < 8; ++e) {
+      const float zf = (float)z[e];
+      const float sg = 1.0f / (1.0f + __expf(-zf));
+      g[e] = (bf16)((float)g[e] * (sg * (1.0f + zf * (1.0f - sg))));
+      z[e] = (bf16)(zf * sg);
+    }
     *reinterpret_cast<bf16x8*>(dh + i * 8) = g;
+    *reinterpret_cast<bf16x8*>(a + i * 8) = z;
   }
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void k_silu_bwd(int64_t n, const T* __restrict__ a, T* __restrict__ dh) {
+__global__ __launch_bounds__(256) void k_silu_bwd(int64_t n, T* __restrict__ a, T* __restrict__ dh) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const float z = to_f32(a[i]);
     const float sg = 1.0f / (1.0f + __expf(-z));
     dh[i] = cvt<T>(to_f32(dh[i]) * sg * (1.0f + z * (1.0f - sg)));
+    a[i] = cvt<T>(z * sg);
+  }
+}
+
+// ---- column sums (bias gradients) ---------------------------------------------------------------
+// Block (rb, cg) sums rows [rb * rpb, +rpb) of the 512 columns cg*512 .. +511: its 4 wavefronts take
+// every 4th row each (one 16-byte chunk of 8 columns per lane, so a wavefront reads 1 KB of a row at
+// once), then the 4 wavefront sums are added in wavefront order and written to part[rb][cols].
+constexpr int kColsumRowBlocks = 2048;
+__global__ __launch_bounds__(256) void k_colsum_bf16(int64_t T, int M, int64_t rpb, const bf16* __restrict__ src,
+                                                     float* __restrict__ part) {
+  __shared__ float accw[4][512];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c0 = blockIdx.y * 512 + lane * 8;
+  const int64_t r0 = (int64_t)blockIdx.x * rpb, r1 = min(T, r0 + rpb);
+  float acc[8] = {};
+  if (c0 < M) {
+    int64_t r = r0 + w;
+    for (; r + 12 < r1; r += 16) {
+      bf16x8 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const bf16x8*>(src + (r + 4 * u) * M + c0);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += (float)v[u][e];
+    }
+    for (; r < r1; r += 4) {
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(src + r * M + c0);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += (float)v[e];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) accw[w][lane * 8 + e] = acc[e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < 512; c += 256) {
+    const int col = blockIdx.y * 512 + c;
+    if (col < M) part[(int64_t)blockIdx.x * M + col] = ((accw[0][c] + accw[1][c]) + accw[2][c]) + accw[3][c];
   }
 }
 
@@ -499,13 +542,29 @@ hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int act,
   return hipGetLastError();
 }
 
-hipError_t launch_silu_bwd(int64_t n, int kind, const void* a, void* dh, hipStream_t s) {
+hipError_t launch_silu_bwd(int64_t n, int kind, void* a, void* dh, hipStream_t s) {
   if (n == 0) return hipSuccess;
   if (kind == 1 && n % 8 == 0)
-    k_silu_bwd_bf16x8<<<ew_grid(n / 8), 256, 0, s>>>(n / 8, static_cast<const bf16*>(a), static_cast<bf16*>(dh));
-  else if (kind == 1) k_silu_bwd<bf16><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const bf16*>(a), static_cast<bf16*>(dh));
-  else k_silu_bwd<float><<<ew_grid(n), 256, 0, s>>>(n, static_cast<const float*>(a), static_cast<float*>(dh));
+    k_silu_bwd_bf16x8<<<ew_grid(n / 8), 256, 0, s>>>(n / 8, static_cast<bf16*>(a), static_cast<bf16*>(dh));
+  else if (kind == 1) k_silu_bwd<bf16><<<ew_grid(n), 256, 0, s>>>(n, static_cast<bf16*>(a), static_cast<bf16*>(dh));
+  else k_silu_bwd<float><<<ew_grid(n), 256, 0, s>>>(n, static_cast<float*>(a), static_cast<float*>(dh));
   return hipGetLastError();
+}
+
+int colsum_blocks(int64_t T, int M) {
+  const int cg = (M + 511) / 512;
+  return (int)std::max<int64_t>(1, std::min<int64_t>(kColsumRowBlocks / cg, (T + 63) / 64));
+}
+
+hipError_t launch_colsum_bf16(int64_t T, int M, const bf16* src, float* part, float* out, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (M % 8 != 0) return hipErrorInvalidValue;
+  const int nrb = colsum_blocks(T, M);
+  const int64_t rpb = (T + nrb - 1) / nrb;
+  k_colsum_bf16<<<dim3((unsigned)nrb, (unsigned)((M + 511) / 512)), 256, 0, s>>>(T, M, rpb, src, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_reduce(M, nrb, M, part, out, s);
 }
 
 hipError_t launch_convert(int64_t n, int kind, const float* x, void* y, hipStream_t s) {

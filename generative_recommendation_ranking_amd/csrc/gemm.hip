@@ -26,6 +26,9 @@ namespace mtgr {
 
 namespace {
 
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
 constexpr int kXcd = 8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -51,11 +54,17 @@ __device__ __forceinline__ void store_out(TOut* out, const float* resid, int64_t
 //   * Per slab: the fragments of k-step ks+1 are read before the MFMAs of k-step ks; the next
 //     slab is written to LDS and the one after it fetched after k-step 1; one barrier after
 //     k-step 2 (LDS traffic only) covers both buffers.
-template <int WM, int WN, int EPI, typename TOut>
+// KMAJOR: both operands token-major (k-major) for weight gradients, out[m][n] = sum_t A[t][m] W[t][n] over the
+// token axis K (t_rows real rows, the rest read as zero), A and W with row pitches lda and ldb;
+// the slab is staged as [k][m] / [k][n] and the MFMA fragments come from transposing LDS reads.
+// Split K with a split count that is a multiple of the XCD count: every tile of a split runs on
+// one XCD, so the split's A and W slabs are fetched into that XCD's L2 once and shared by all of
+// its row and column tiles.
+template <int WM, int WN, int EPI, typename TOut, bool KMAJOR = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     int64_t M, int N, int K, const bf16* __restrict__ A, const bf16* __restrict__ W,
     const bf16* __restrict__ bias, const float* resid, TOut* out, int nN, int64_t nM, int nb,
-    int ksplit, int64_t nMr) {
+    int ksplit, int64_t nMr, int64_t t_rows, int lda, int ldb) {
   constexpr int BM = 256, BN = 256, BK = 64, NT = 64 * WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int LP = BK + 8, CPR = BK / 8;
@@ -68,6 +77,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   // Bias table in LDS: the whole vector when N <= kBiasLds (staged once), else the current
   // tile's slice (staged at the start of each tile).  It seeds the accumulators.
   bf16* Bias = reinterpret_cast<bf16*>(smem + 2 * (BM + BN) * LP * sizeof(bf16));
+  constexpr int TP = BM + 32;   // k-major slabs [BK][BM + 32]: the same bytes as [BM][LP]; a pitch of 16
+                                // (mod 64) dwords keeps the transposing reads conflict-free
+  static_assert(BK * TP == BM * LP && BN == BM, "k-major slab layout");
+  bf16 (*At)[BK][TP] = reinterpret_cast<bf16 (*)[BK][TP]>(smem);
+  bf16 (*Bt)[BK][TP] = reinterpret_cast<bf16 (*)[BK][TP]>(smem + 2 * BM * LP * sizeof(bf16));
   const bool bias_whole = bias != nullptr && N <= kBiasLds;
   const bool bias_slice = bias != nullptr && N > kBiasLds;
 
@@ -108,48 +122,96 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   if (!valid_slot(first)) first = next_slot(first);
   if (first >= nslots) return;
 
-  // Split K: M-tile index mt in [0, nM) stands for row tile mt % nMr over the K range
-  // [(mt / nMr) * nk * BK, + nk * BK), written to out + (mt / nMr) * M * N (no bias then).
+  // Split K: M-tile index mt in [0, nM) stands for a row tile r over the K range of split sp,
+  // [sp * nk * BK, + nk * BK), written to out + sp * M * N (no bias then).  Split-major order (split
+  // count a multiple of the XCD count): XCD x = mt % kXcd holds splits x, x + kXcd, ..., each with
+  // all its row tiles; otherwise sp = mt / nMr, r = mt % nMr.
   const int nk = K / BK / ksplit;        // >= 2 (checked by the host)
-  const uint32_t vo = (uint32_t)((tid / CPR) * K * 2 + (tid % CPR) * 16);  // byte offset in slab
+  const bool split_major = ksplit > 1 && ksplit % kXcd == 0;
+  auto split_row = [&](int64_t mt, int& sp, int64_t& r) {
+    if (split_major) {
+      const int64_t j = mt / kXcd;
+      sp = (int)((j / nMr) * kXcd + mt % kXcd);
+      r = j % nMr;
+    } else {
+      sp = (int)(mt / nMr);
+      r = mt % nMr;
+    }
+  };
+  const uint32_t vo = KMAJOR ? 0u : (uint32_t)((tid / CPR) * K * 2 + (tid % CPR) * 16);  // byte offset in slab
+  // k-major: thread -> (token row tid/32 of 16, 16-byte chunk tid%32 of a 512-byte row segment)
+  const uint32_t vo_a = KMAJOR ? (uint32_t)((tid >> 5) * lda * 2 + (tid & 31) * 16) : 0u;
+  const uint32_t vo_b = KMAJOR ? (uint32_t)((tid >> 5) * ldb * 2 + (tid & 31) * 16) : 0u;
 
   struct TileRsrc {
     __amdgpu_buffer_rsrc_t a, w;
   };
   auto make_rsrc = [&](int64_t s) {
     int64_t mt; int ntile; decode(s, mt, ntile);
-    const int ks_off = (int)(mt / nMr) * nk * BK;
-    mt %= nMr;
-    const int64_t m0 = mt * BM;
+    int sp; int64_t rt;
+    split_row(mt, sp, rt);
+    const int ks_off = sp * nk * BK;
+    const int64_t m0 = rt * BM;
     const int n0 = ntile * BN;
     const int64_t mrows = min((int64_t)BM, M - m0);
     const int nrows = min(BN, N - n0);
-    // the resources start at column ks_off of the first row; they end where row mrows (nrows)
-    // would begin, so rows past the edge still read as zero
     TileRsrc r;
-    r.a = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * K + ks_off), (short)0,
-                                            (int)((mrows * K - ks_off) * 2), 0x00020000);
-    r.w = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * K + ks_off), (short)0,
-                                            (int)(((int64_t)nrows * K - ks_off) * 2), 0x00020000);
+    if constexpr (KMAJOR) {
+      // the split's token rows [ks_off, ks_off + nk*BK), clipped at t_rows; the resources start at
+      // the tile's first column and end where the split's last real row ends, so padding rows read
+      // as zero (columns past M or N read neighbouring data that only reaches dropped outputs)
+      const int64_t rows = max((int64_t)0, min(t_rows, (int64_t)ks_off + (int64_t)nk * BK) - ks_off);
+      const int64_t abytes = max((int64_t)0, (rows * lda - m0) * 2);
+      const int64_t wbytes = max((int64_t)0, (rows * ldb - n0) * 2);
+      r.a = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)ks_off * lda + m0), (short)0, (int)abytes, 0x00020000);
+      r.w = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)ks_off * ldb + n0), (short)0, (int)wbytes, 0x00020000);
+    } else {
+      // the resources start at column ks_off of the first row; they end where row mrows (nrows)
+      // would begin, so rows past the edge still read as zero
+      r.a = __builtin_amdgcn_make_buffer_rsrc((void*)(A + m0 * K + ks_off), (short)0,
+                                              (int)((mrows * K - ks_off) * 2), 0x00020000);
+      r.w = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * K + ks_off), (short)0,
+                                              (int)(((int64_t)nrows * K - ks_off) * 2), 0x00020000);
+    }
     return r;
   };
   bf16x8 ra[CA], rb[CB];
   auto issue_loads = [&](const TileRsrc& r, int kt) {
-    const int kb = kt * BK * 2;
+    if constexpr (KMAJOR) {
+      static_assert(CA == BK / 16 && CB == BK / 16, "k-major staging: 16 token rows per pass");
 #pragma unroll
-    for (int i = 0; i < CA; ++i)
-      ra[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.a, vo, i * RSTEP * K * 2 + kb, 0));
+      for (int i = 0; i < CA; ++i)
+        ra[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               r.a, vo_a, (uint32_t)(kt * BK + i * 16) * (uint32_t)lda * 2u, 0));
 #pragma unroll
-    for (int i = 0; i < CB; ++i)
-      rb[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.w, vo, i * RSTEP * K * 2 + kb, 0));
+      for (int i = 0; i < CB; ++i)
+        rb[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                               r.w, vo_b, (uint32_t)(kt * BK + i * 16) * (uint32_t)ldb * 2u, 0));
+    } else {
+      const int kb = kt * BK * 2;
+#pragma unroll
+      for (int i = 0; i < CA; ++i)
+        ra[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.a, vo, i * RSTEP * K * 2 + kb, 0));
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+        rb[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r.w, vo, i * RSTEP * K * 2 + kb, 0));
+    }
   };
   auto store_slab = [&](int buf) {
+    if constexpr (KMAJOR) {
+      const int row = tid >> 5, c8 = (tid & 31) * 8;
 #pragma unroll
-    for (int i = 0; i < CA; ++i)
-      *reinterpret_cast<bf16x8*>(&As[buf][tid / CPR + i * RSTEP][(tid % CPR) * 8]) = ra[i];
+      for (int i = 0; i < CA; ++i) *reinterpret_cast<bf16x8*>(&At[buf][row + 16 * i][c8]) = ra[i];
 #pragma unroll
-    for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<bf16x8*>(&Bs[buf][tid / CPR + i * RSTEP][(tid % CPR) * 8]) = rb[i];
+      for (int i = 0; i < CB; ++i) *reinterpret_cast<bf16x8*>(&Bt[buf][row + 16 * i][c8]) = rb[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < CA; ++i)
+        *reinterpret_cast<bf16x8*>(&As[buf][tid / CPR + i * RSTEP][(tid % CPR) * 8]) = ra[i];
+#pragma unroll
+      for (int i = 0; i < CB; ++i)
+        *reinterpret_cast<bf16x8*>(&Bs[buf][tid / CPR + i * RSTEP][(tid % CPR) * 8]) = rb[i];
+    }
   };
   // Software pipeline over the K slabs of this workgroup's tiles, one after another: slab g is
   // in LDS buffer g%2 and the fragments of k-step ks+1 are read before the MFMAs of k-step ks.
@@ -164,13 +226,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   constexpr int KS = BK / 16;
   static_assert(KS == 4, "the schedule below assumes four k-steps per slab");
   bf16x8 fa[2][FM], fb[2][FN];
+  // k-major fragments: the 16 k of k-step ks come from two transposing reads of 4 rows each,
+  // rows kb + 4*hh + e%4 (+8 for e >= 4); A and B take the same k order, so the contraction holds
+  auto tr_frag = [&](const bf16 (*tile)[TP], int ks, int col0) {
+    const int kb = (ks >> 1) * 32 + (ks & 1) * 16 + 4 * hh + (lane & 15) / 4;
+    const int fc = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tile[kb][fc]));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&tile[kb + 8][fc]));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
   auto read_frags = [&](int buf, int ks, int fslot) {
+    if constexpr (KMAJOR) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-      fa[fslot][i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * TM + i * 32 + l32][ks * 16 + hh * 8]);
+      for (int i = 0; i < FM; ++i) fa[fslot][i] = tr_frag(At[buf], ks, wm * TM + i * 32);
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      fb[fslot][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * TN + j * 32 + l32][ks * 16 + hh * 8]);
+      for (int j = 0; j < FN; ++j) fb[fslot][j] = tr_frag(Bt[buf], ks, wn * TN + j * 32);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[fslot][i] = *reinterpret_cast<const bf16x8*>(&As[buf][wm * TM + i * 32 + l32][ks * 16 + hh * 8]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[fslot][j] = *reinterpret_cast<const bf16x8*>(&Bs[buf][wn * TN + j * 32 + l32][ks * 16 + hh * 8]);
+    }
     // keep the reads ahead of the MFMAs that follow (the scheduler would otherwise sink them)
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -282,9 +360,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
       ((uint32_t)(wm * TM + (lane >> 4)) * (uint32_t)N + (uint32_t)(wn * TN + (lane & 15) * CW)) * (uint32_t)sizeof(TOut);
   auto epilogue = [&] {
     int64_t mt_e; int nt_e; decode(slot, mt_e, nt_e);
-    TOut* outp = out + (mt_e / nMr) * M * N;
-    mt_e %= nMr;
-    const int64_t m0 = mt_e * BM;
+    int sp_e; int64_t rt_e;
+    split_row(mt_e, sp_e, rt_e);
+    TOut* outp = out + sp_e * M * N;
+    const int64_t m0 = rt_e * BM;
     const int n0 = nt_e * BN;
     const uint32_t rows = (uint32_t)min((int64_t)BM, M - m0);
     const int nbytes = (int)(rows * (uint32_t)N * sizeof(TOut));
@@ -453,12 +532,17 @@ __global__ __launch_bounds__(256) void k_gemm_f32(int64_t M, int N, int K,
   }
 }
 
-template <int WM, int WN, int EPI, typename TOut>
+struct KMajorArgs {
+  int64_t t_rows = 0;
+  int lda = 0, ldb = 0;
+};
+
+template <int WM, int WN, int EPI, typename TOut, bool KMAJOR = false>
 hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf16* w,
                                const bf16* bias, const float* resid, void* out, hipStream_t s,
-                               int ksplit = 1) {
+                               int ksplit = 1, KMajorArgs km = KMajorArgs()) {
   constexpr size_t lds = 2 * (size_t)(256 + 256) * (64 + 8) * sizeof(bf16) + kBiasLds * sizeof(bf16);
-  auto kern = k_gemm_bf16_persistent<WM, WN, EPI, TOut>;
+  auto kern = k_gemm_bf16_persistent<WM, WN, EPI, TOut, KMAJOR>;
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -479,9 +563,10 @@ hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf1
   // versus weights re-read once per round of concurrently running M-tiles when they do not fit.
   const double a_bytes = (double)M * K * 2, slice = 256.0 * (K / ksplit) * 2, l2 = 4.0 * 1024 * 1024;
   const double wg_per_xcd = (double)grid / kXcd;
+  // (split-major split K: all of a split's column tiles at once, they share its slabs)
   int nb = nN;
   double best = 1e300;
-  for (int c = 1; c <= nN; ++c) {
+  for (int c = 1; c <= nN && !(ksplit > 1 && ksplit % kXcd == 0); ++c) {
     const double chunks = (double)((nN + c - 1) / c);
     const bool fits = c * slice <= 0.6 * l2;
     const double rounds = (double)((nM + kXcd - 1) / kXcd) * c / std::max(1.0, wg_per_xcd);
@@ -490,7 +575,7 @@ hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf1
     if (t < best * 0.98) { best = t; nb = c; }
   }
   kern<<<(unsigned)grid, 64 * WM * WN, lds, s>>>(M, N, K, a, w, bias, resid, static_cast<TOut*>(out), nN, nM, nb,
-                                                  ksplit, nMr);
+                                                  ksplit, nMr, km.t_rows, km.lda, km.ldb);
   return hipGetLastError();
 }
 
@@ -513,6 +598,21 @@ hipError_t launch_gemm_bf16_splitk(int64_t M, int N, int K, int ksplit, const bf
   if (M == 0 || N == 0) return hipSuccess;
   if (ksplit < 1 || K % (64 * ksplit) != 0 || K / 64 / ksplit < 2) return hipErrorInvalidValue;
   return run_bf16_persistent<4, 2, MTGR_EPI_STORE, float>(M, N, K, a, w, nullptr, nullptr, part, s, ksplit);
+}
+
+hipError_t launch_gemm_bf16_kmajor_splitk(int M, int N, int64_t Kp, int ksplit, int64_t T, const bf16* a, int lda,
+                                          const bf16* w, int ldb, float* part, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (ksplit < 1 || Kp % (64 * ksplit) != 0 || Kp / 64 / ksplit < 2 || T > Kp || lda < M || ldb < N ||
+      ldb % 8 != 0 || lda % 8 != 0)
+    return hipErrorInvalidValue;
+  // a split's rows must stay within a 32-bit buffer range
+  if ((Kp / ksplit) * (int64_t)std::max(lda, ldb) * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  KMajorArgs km;
+  km.t_rows = T;
+  km.lda = lda;
+  km.ldb = ldb;
+  return run_bf16_persistent<4, 2, MTGR_EPI_STORE, float, true>(M, N, (int)Kp, a, w, nullptr, nullptr, part, s, ksplit, km);
 }
 
 hipError_t launch_gemm_bf16_f32out(int64_t M, int N, int K, const bf16* a, const bf16* w, const bf16* bias,

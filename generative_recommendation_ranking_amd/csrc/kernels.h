@@ -65,7 +65,8 @@ hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H, in
 // ones_row adds row C = (r < R) and rows C+1..C+7 = 0.  dst row pitch Rp.
 hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int act, int kind, const void* src,
                             void* dst, hipStream_t s);
-hipError_t launch_silu_bwd(int64_t n, int kind, const void* a, void* dh, hipStream_t s);
+// dh <- dh (.) silu'(a); then a <- silu(a) (the MLP's hidden activation, for its weight gradient)
+hipError_t launch_silu_bwd(int64_t n, int kind, void* a, void* dh, hipStream_t s);
 hipError_t launch_convert(int64_t n, int kind, const float* x, void* y, hipStream_t s);
 // out[i] = sum over s < nsplit of part[s*stride + i]
 hipError_t launch_reduce(int64_t n, int nsplit, int64_t stride, const float* part, float* out, hipStream_t s);
@@ -96,6 +97,16 @@ hipError_t launch_attention_bwd_bf16(int32_t B, int64_t T, int64_t grid_slots, i
 // (K a multiple of 64 * ksplit for bf16); no bias
 hipError_t launch_gemm_bf16_splitk(int64_t M, int N, int K, int ksplit, const bf16* a, const bf16* w,
                                    float* part, hipStream_t s);
+// k-major split-K GEMM for weight gradients without transposed copies: part[s][m][n] =
+// sum over token rows t of split s of a[t][m] w[t][n] (a: [T][lda], w: [T][ldb], token axis padded
+// to Kp with zero rows; Kp a multiple of 64 * ksplit, at least two 64-row slabs per split); a split
+// count that is a multiple of 8 keeps each split on one XCD
+hipError_t launch_gemm_bf16_kmajor_splitk(int M, int N, int64_t Kp, int ksplit, int64_t T, const bf16* a, int lda,
+                                          const bf16* w, int ldb, float* part, hipStream_t s);
+// column sums of a bf16 [T][M] matrix (M % 8 == 0): per-block partials part[colsum_blocks(T, M)][M],
+// then out[m] = their sum in block order (deterministic); part holds colsum_blocks(T, M) * M floats
+int colsum_blocks(int64_t T, int M);
+hipError_t launch_colsum_bf16(int64_t T, int M, const bf16* src, float* part, float* out, hipStream_t s);
 hipError_t launch_gemm_f32_splitk(int64_t M, int N, int K, int ksplit, const float* a, const float* w,
                                   float* part, hipStream_t s);
 
