@@ -366,8 +366,8 @@ hipError_t weight_grad(const BwdPlan& pl, int gi, void* ws, int dtype, int64_t T
   const int Kx = K + 8;
   void* ta = at<void>(ws, pl.ta);
   void* tb = at<void>(ws, pl.tb);
-  e = launch_transpose(T, M, pl.Tp[gi], 0, 0, 0, dy, ta, s);
-  if (e == hipSuccess) e = launch_transpose(T, K, pl.Tp[gi], 1, 0, 0, x, tb, s);
+  e = launch_transpose(T, M, pl.Tp[gi], 0, 0, dy, ta, s);
+  if (e == hipSuccess) e = launch_transpose(T, K, pl.Tp[gi], 1, 0, x, tb, s);
   if (e == hipSuccess)
     e = launch_gemm_f32_splitk(M, Kx, (int)pl.Tp[gi], pl.ks[gi], static_cast<const float*>(ta),
                                static_cast<const float*>(tb), part, s);
@@ -428,12 +428,12 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
     MTGR_BWD_TRY(launch_convert(T * d, act, dx_out, at<void>(ws, pl.dout), s));
     dout = at<void>(ws, pl.dout);
   }
-  MTGR_BWD_TRY(launch_transpose(d, h, d, 0, 0, act, p->w_mlp2, wt, s));
+  MTGR_BWD_TRY(launch_transpose(d, h, d, 0, act, p->w_mlp2, wt, s));
   MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, dout, wt, nullptr, nullptr, dhid, s));
   MTGR_BWD_TRY(launch_silu_bwd(T * h, act, a, dhid, s));
   MTGR_BWD_TRY(weight_grad(pl, 0, ws, dt, T, d, h, dout, a, g->w_mlp2, g->b_mlp2, s));
   // MLP1: dz = da W1, dW1 = da^T z, db1 = sum da
-  MTGR_BWD_TRY(launch_transpose(h, d, h, 0, 0, act, p->w_mlp1, wt, s));
+  MTGR_BWD_TRY(launch_transpose(h, d, h, 0, act, p->w_mlp1, wt, s));
   MTGR_BWD_TRY(linear(T, d, h, dt, MTGR_EPI_STORE, dhid, wt, nullptr, nullptr, dz, s));
   MTGR_BWD_TRY(weight_grad(pl, 1, ws, dt, T, h, d, dhid, z, g->w_mlp1, g->b_mlp1, s));
   // GLN2: dy (in place over dz) and the GLN2 parameter gradients
@@ -443,7 +443,7 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   // gate and attention: dqkvu from qkvu, V~ and dy (G = dy (.) U goes to the free dout buffer)
   MTGR_BWD_TRY(attention_bwd(b, d, H, dt, p->mask_mode, pb, qkvu, vt, dz, at<void>(ws, pl.dout), dqkvu, s));
   // QKVU: dxt = dqkvu W_qkvu (over dz), dW_qkvu = dqkvu^T xt, db_qkvu = sum dqkvu
-  MTGR_BWD_TRY(launch_transpose(4 * (int64_t)d, d, 4 * (int64_t)d, 0, 0, act, p->w_qkvu, wt, s));
+  MTGR_BWD_TRY(launch_transpose(4 * (int64_t)d, d, 4 * (int64_t)d, 0, act, p->w_qkvu, wt, s));
   MTGR_BWD_TRY(linear(T, d, 4 * d, dt, MTGR_EPI_STORE, dqkvu, wt, nullptr, nullptr, dz, s));
   MTGR_BWD_TRY(weight_grad(pl, 2, ws, dt, T, 4 * d, d, dqkvu, xt, g->w_qkvu, g->b_qkvu, s));
   // GLN1 plus the residual path: dx_in = dx_out + GLN1'(x_in)^T dxt

@@ -19,13 +19,12 @@ template <typename T>
 __device__ __forceinline__ T cvt(float v) { return from_f32<T>(v); }
 
 // ---- transposes -----------------------------------------------------------------------------
-// dst[c][r] = f(src[r][c]) for r < R, c < C (f = silu when `act`, else the identity); dst[c][r] = 0
-// for R <= r < Rp; with ones_row, an extra row dst[C][r] = (r < R) and rows C+1 .. C+7 zero.  dst
+// dst[c][r] = src[r][c] for r < R, c < C; dst[c][r] = 0 for R <= r < Rp; with ones_row, an extra row dst[C][r] = (r < R) and rows C+1 .. C+7 zero.  dst
 // row pitch Rp.  64 x 64 tiles through LDS.  The bf16 variant moves 16-byte row pieces (C and Rp
 // multiples of 8): each thread reads 8 consecutive columns of one source row and writes 8
 // consecutive rows of one destination row.
 template <typename T>
-__global__ __launch_bounds__(256) void k_transpose(int64_t R, int C, int64_t Rp, int ones_row, int act,
+__global__ __launch_bounds__(256) void k_transpose(int64_t R, int C, int64_t Rp, int ones_row,
                                                    const T* __restrict__ src, T* __restrict__ dst) {
   __shared__ float tile[64][65];
   const int64_t r0 = (int64_t)blockIdx.y * 64;
@@ -37,7 +36,7 @@ __global__ __launch_bounds__(256) void k_transpose(int64_t R, int C, int64_t Rp,
     const int c = c0 + tx;
     float v = 0.f;
     if (r < R) {
-      if (c < C) { v = to_f32(src[r * C + c]); if (act) v = silu_f32(v); }
+      if (c < C) v = to_f32(src[r * C + c]);
       else if (ones_row && c == C) v = 1.f;
     }
     tile[i][tx] = v;
@@ -50,7 +49,7 @@ __global__ __launch_bounds__(256) void k_transpose(int64_t R, int C, int64_t Rp,
   }
 }
 
-__global__ __launch_bounds__(256) void k_transpose_bf16x8(int64_t R, int C, int64_t Rp, int ones_row, int act,
+__global__ __launch_bounds__(256) void k_transpose_bf16x8(int64_t R, int C, int64_t Rp, int ones_row,
                                                           const bf16* __restrict__ src, bf16* __restrict__ dst) {
   __shared__ float tile[64][65];
   const int64_t r0 = (int64_t)blockIdx.y * 64;
@@ -67,7 +66,7 @@ __global__ __launch_bounds__(256) void k_transpose_bf16x8(int64_t R, int C, int6
     if (r < R && c < C) {
       const bf16x8 x = *reinterpret_cast<const bf16x8*>(src + r * C + c);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[e] = act ? silu_f32((float)x[e]) : (float)x[e];
+      for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[e] = (r < R && ones_row && c + e == C) ? 1.f : 0.f;
@@ -190,9 +189,9 @@ __global__ __launch_bounds__(64 * kReduceWaves) void k_reduce(int64_t n, int nsp
   }
 }
 
-// Sum the nsplit split-K partials of an extended weight gradient [M][Kx] (column K = the bias
-// gradient, from the ones row appended to the transposed activations) into dW [M][K] and db [M]
-// (db may be NULL), partials added in split order.
+// Sum the nsplit split-K partials of a weight gradient [M][Kx] into dW [M][K] and, when db is not
+// NULL, db [M] = column K (Kx > K: the bias gradient, from the ones row appended to the transposed
+// activations of the fp32 path), partials added in split order.
 __global__ __launch_bounds__(256) void k_reduce_wb(int M, int K, int Kx, int nsplit, const float* __restrict__ part,
                                                    float* __restrict__ dw, float* __restrict__ db) {
   const int64_t n = (int64_t)M * (K + 1);
@@ -527,18 +526,18 @@ inline unsigned ew_grid(int64_t n) { return (unsigned)std::min<int64_t>((n + 255
 
 }  // namespace
 
-hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int act, int kind, const void* src,
+hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int kind, const void* src,
                             void* dst, hipStream_t s) {
   if (R == 0 && Rp == 0) return hipSuccess;
   const int crows = C + (ones_row ? 8 : 0);
   dim3 grid((unsigned)((crows + 63) / 64), (unsigned)((Rp + 63) / 64));
   if (kind == 1 && C % 8 == 0 && Rp % 8 == 0)
-    k_transpose_bf16x8<<<grid, 256, 0, s>>>(R, C, Rp, ones_row, act, static_cast<const bf16*>(src),
+    k_transpose_bf16x8<<<grid, 256, 0, s>>>(R, C, Rp, ones_row, static_cast<const bf16*>(src),
                                              static_cast<bf16*>(dst));
   else if (kind == 1)
-    k_transpose<bf16><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, act, static_cast<const bf16*>(src), static_cast<bf16*>(dst));
+    k_transpose<bf16><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, static_cast<const bf16*>(src), static_cast<bf16*>(dst));
   else
-    k_transpose<float><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, act, static_cast<const float*>(src), static_cast<float*>(dst));
+    k_transpose<float><<<grid, 256, 0, s>>>(R, C, Rp, ones_row, static_cast<const float*>(src), static_cast<float*>(dst));
   return hipGetLastError();
 }
 

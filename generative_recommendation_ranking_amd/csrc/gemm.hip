@@ -593,13 +593,6 @@ hipError_t launch_gemm_bf16(int64_t M, int N, int K, int epi, const bf16* a, con
   }
 }
 
-hipError_t launch_gemm_bf16_splitk(int64_t M, int N, int K, int ksplit, const bf16* a, const bf16* w,
-                                   float* part, hipStream_t s) {
-  if (M == 0 || N == 0) return hipSuccess;
-  if (ksplit < 1 || K % (64 * ksplit) != 0 || K / 64 / ksplit < 2) return hipErrorInvalidValue;
-  return run_bf16_persistent<4, 2, MTGR_EPI_STORE, float>(M, N, K, a, w, nullptr, nullptr, part, s, ksplit);
-}
-
 hipError_t launch_gemm_bf16_kmajor_splitk(int M, int N, int64_t Kp, int ksplit, int64_t T, const bf16* a, int lda,
                                           const bf16* w, int ldb, float* part, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;

@@ -61,9 +61,9 @@ hipError_t launch_attention_f32(int32_t B, int64_t total_tiles, int d, int H, in
 
 // ---- backward pieces (backward.hip) -------------------------------------------------------------
 // kind / *_kind: 0 = float, 1 = bf16
-// dst[c][r] = f(src[r][c]) (r < R, c < C; f = silu if act, else identity), zero for R <= r < Rp;
-// ones_row adds row C = (r < R) and rows C+1..C+7 = 0.  dst row pitch Rp.
-hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int act, int kind, const void* src,
+// dst[c][r] = src[r][c] (r < R, c < C), zero for R <= r < Rp; ones_row adds row C = (r < R) and
+// rows C+1..C+7 = 0.  dst row pitch Rp.
+hipError_t launch_transpose(int64_t R, int C, int64_t Rp, int ones_row, int kind, const void* src,
                             void* dst, hipStream_t s);
 // dh <- dh (.) silu'(a); then a <- silu(a) (the MLP's hidden activation, for its weight gradient)
 hipError_t launch_silu_bwd(int64_t n, int kind, void* a, void* dh, hipStream_t s);
@@ -93,10 +93,6 @@ hipError_t launch_attention_bwd_bf16(int32_t B, int64_t T, int64_t grid_slots, i
                                      const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                      const int32_t* xcd_off, const float* timestamps, const bf16* qkvu,
                                      const bf16* vt, const bf16* dy, bf16* g, bf16* dqkvu, hipStream_t s);
-// split-K GEMM for weight gradients: part[s][M][N] = a[M][Ks] w[N][Ks]^T over K-range s of ksplit
-// (K a multiple of 64 * ksplit for bf16); no bias
-hipError_t launch_gemm_bf16_splitk(int64_t M, int N, int K, int ksplit, const bf16* a, const bf16* w,
-                                   float* part, hipStream_t s);
 // k-major split-K GEMM for weight gradients without transposed copies: part[s][m][n] =
 // sum over token rows t of split s of a[t][m] w[t][n] (a: [T][lda], w: [T][ldb], token axis padded
 // to Kp with zero rows; Kp a multiple of 64 * ksplit, at least two 64-row slabs per split); a split

@@ -127,12 +127,25 @@ def test_block_bwd_bf16(d, H, h, mask, norm):
 
 
 def test_block_bwd_bf16_split_k():
-    """About 10k tokens: the weight-gradient GEMMs split the token axis four ways."""
+    """About 10k tokens: the weight-gradient GEMMs split the token axis into a few splits."""
     rng = np.random.default_rng(74)
     lengths = [(16, int(rng.integers(200, 700)), int(rng.integers(0, 100)), int(rng.integers(1, 64)))
                for _ in range(18)]
     b, p, dout = make_case(lengths, 256, 4, 512, "bf16", 75)
     assert b.num_tokens >= 8192
+    dx, g = run_bwd(b, p, dout)
+    rdx, rg = oracle_bwd(b, p, dout)
+    check(dx, g, rdx, rg, TOL_BF16)
+
+
+def test_block_bwd_bf16_xcd_split():
+    """About 20k tokens: the weight-gradient GEMMs split the token axis a multiple of 8 ways, each
+    split's tiles on one XCD, and the bias gradients come from the column-sum kernel."""
+    rng = np.random.default_rng(77)
+    lengths = [(8, int(rng.integers(300, 600)), int(rng.integers(0, 80)), int(rng.integers(1, 40)))
+               for _ in range(40)]
+    b, p, dout = make_case(lengths, 128, 2, 256, "bf16", 78)
+    assert b.num_tokens >= 16384
     dx, g = run_bwd(b, p, dout)
     rdx, rg = oracle_bwd(b, p, dout)
     check(dx, g, rdx, rg, TOL_BF16)
