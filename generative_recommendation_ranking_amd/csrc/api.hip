@@ -274,6 +274,7 @@ struct BwdPlan {
   // per weight-gradient GEMM (0: W2, 1: W1, 2: W_qkvu): split count and padded token axis
   int ks[3] = {1, 1, 1};
   int64_t Tp[3] = {0, 0, 0};
+  bool ok = true;   // every bf16 split within a 32-bit buffer range
 };
 
 constexpr int64_t kMaxBwdTokens = 4000000;
@@ -320,7 +321,8 @@ BwdPlan make_bwd_plan(const Sizes& z) {
       const double eff = (double)work / (double)(rounds * slots);
       if (eff > best_eff + 1e-9) { best_eff = eff; best = ks; }
     }
-    p.ks[gi] = std::max(best, 1);      // the token limit keeps some split count feasible
+    p.ks[gi] = std::max(best, 1);
+    if (best == 0) p.ok = false;
     const int64_t unit = 64 * (int64_t)p.ks[gi];
     p.Tp[gi] = std::max((z.T + unit - 1) / unit * unit, 2 * unit);
     tp_max = std::max(tp_max, p.Tp[gi]);
@@ -516,11 +518,13 @@ mtgr_status mtgr_block_bwd_workspace_size(const mtgr_block_params* p, const mtgr
   mtgr_status st = check_block(p);
   if (st != MTGR_OK) return st;
   if ((st = check_batch(b)) != MTGR_OK) return st;
-  // the weight-gradient GEMMs run over the padded token axis; one 256-row slab of it must stay
-  // within a 32-bit buffer range
+  // a bound on the workspace; the bf16 weight-gradient GEMMs also need split counts that keep each
+  // split's activation rows within a 32-bit buffer range
   if (b->num_tokens > kMaxBwdTokens) return MTGR_ERR_BAD_SHAPE;
   Sizes z = sizes_for(b, p->d_model, p->mlp_hidden, 0, p->dtype, p->num_heads);
-  *bytes = make_bwd_plan(z).total;
+  const BwdPlan pl = make_bwd_plan(z);
+  if (!pl.ok) return MTGR_ERR_BAD_SHAPE;
+  *bytes = pl.total;
   return MTGR_OK;
 }
 
