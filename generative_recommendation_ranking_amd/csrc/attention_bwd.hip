@@ -10,7 +10,7 @@
 //   k_gate_bwd      G (bf16 [T][d], workspace) and dU, elementwise.
 //   k_attn_bwd_dkv  work item = (user, head, 128 keys), 4 wavefronts x 32 keys.  The K and V rows
 //                   of a wavefront's keys stay in registers while 64-query tiles of Q and G stream
-//                   through LDS.  S and dP = G V^T are computed with the key as the MFMA column,
+//                   through LDS (LDS-direct buffer loads, no staging registers).  S and dP = G V^T are computed with the key as the MFMA column,
 //                   so that each lane holds one key and 16 queries; P and dS, rounded to bf16, are
 //                   then directly the A operands of dV += P^T G and dK += dS^T Q.
 //   k_attn_bwd_dq   work item = (user, head, 128 queries), the forward kernel's tiling: Q and G
@@ -77,6 +77,11 @@ __device__ __forceinline__ bool decode_item(int32_t B, int H, const int32_t* __r
   return true;
 }
 
+// 16 bytes per lane from a buffer resource straight into LDS: lane l writes lds + 16 l
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ float sigmoid_rcp(float s) { return __builtin_amdgcn_rcpf(1.0f + __expf(-s)); }
 
 // B operand of a k-step over 16 tokens from a swizzled tile: slot e of lane-half hh is token
@@ -127,8 +132,6 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(
   constexpr int CPR = DH / 8;            // 16-byte chunks per row
   constexpr int NT = DH / 32;            // 32-feature output tiles
   constexpr int KS = DH / 16;            // feature k-steps
-  constexpr int CH = BQ * CPR / 256;     // chunks per thread per operand and tile
-  constexpr int RSTEP = 256 / CPR;       // rows between a thread's chunks
   constexpr int OP = DH + 4;             // fp32 pitch of staged output rows
   constexpr size_t kLoopBytes = 4 * BQ * DH * sizeof(bf16) + 2 * BQ * sizeof(float);
   constexpr size_t kEpiBytes = 4 * 32 * OP * sizeof(float) + 2 * 4 * 32 * sizeof(float);
@@ -182,42 +185,50 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(
   const int qt0 = qlo / BQ;
   const int nqt = qhi > qlo ? (qhi + BQ - 1) / BQ - qt0 : 0;
 
+  // The accumulators start as the result of an MFMA on zeros rather than as zeros written by
+  // VALU moves: both inputs of their loop-carried value then come from MFMAs, so the register
+  // allocator keeps them in accumulation registers for the whole key loop instead of moving all
+  // 128 through the general registers on every query tile.
   f32x16 dk[NT], dv[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { dk[t][r] = 0.f; dv[t][r] = 0.f; }
+  for (int t = 0; t < NT; ++t) {
+    dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zero8, zero8, f32x16{}, 0, 0, 0);
+    dv[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(zero8, zero8, f32x16{}, 0, 0, 0);
+  }
 
-  // Staging: every thread copies CH 16-byte chunks of the Q tile and CH of the G tile through
-  // buffer loads over this user's rows (rows past n read as zero).
+  // Staging: LDS-direct buffer loads.  One wavefront instruction fills 1 KB of a tile, lane l the
+  // 16 bytes at l*16: the chunk at swizzled position pos of row r, i.e. source chunk pos ^ swz(r).
+  // Rows past n read as zero (the resources end at row n).  Timestamps go through a register.
   const uint32_t q_row = (uint32_t)(ld * 2), g_row = (uint32_t)d * 2;
   const __amdgpu_buffer_rsrc_t q_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)Qp, (short)0, (int)((uint32_t)n * q_row), 0x00020000);
   const __amdgpu_buffer_rsrc_t g_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)Gp, (short)0, (int)((uint32_t)n * g_row), 0x00020000);
-  const int st_r = tid / CPR, st_c = tid % CPR;
-  const uint32_t q_vo = (uint32_t)st_r * q_row + st_c * 16, g_vo = (uint32_t)st_r * g_row + st_c * 16;
-  bf16x8 stg[2 * CH];
-  float rt = -INFINITY;
-  auto stage_load = [&](int q0) {
+  constexpr int NI = BQ * CPR / 64 / 4;  // 1 KB loads per wavefront per operand and tile
+  static_assert(NI * 4 * 64 == BQ * CPR, "LDS-direct staging covers the tile");
+  uint32_t q_vo[NI], g_vo[NI];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const uint32_t r = (uint32_t)(q0 + i * RSTEP);
-      stg[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, q_vo, r * q_row, 0));
-      stg[CH + i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(g_rsrc, g_vo, r * g_row, 0));
+  for (int i = 0; i < NI; ++i) {
+    const int p = (w * NI + i) * 64 + lane;
+    const int r = p / CPR, c = (p % CPR) ^ swz<DH>(r);
+    q_vo[i] = (uint32_t)r * q_row + c * 16;
+    g_vo[i] = (uint32_t)r * g_row + c * 16;
+  }
+  float rt = -INFINITY;
+  auto stage_load = [&](int q0, int buf) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      lds_dma16(q_rsrc, &Qs[buf][(w * NI + i) * 512], q_vo[i], (uint32_t)q0 * q_row);
+      lds_dma16(g_rsrc, &Gs[buf][(w * NI + i) * 512], g_vo[i], (uint32_t)q0 * g_row);
     }
     if (MODE == kMaskDynamic && tid < BQ) {
       const int i = q0 + tid;   // R/C queries carry their timestamp, the rest -inf
       rt = (i >= ns && i < n) ? ts[base + i] : -INFINITY;
     }
   };
+  // waits for this thread's loads (the tile and its timestamp) before the barrier that publishes it
   auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const int off = sw_off<DH>(st_r + i * RSTEP, st_c * 8);
-      *reinterpret_cast<bf16x8*>(&Qs[buf][off]) = stg[i];
-      *reinterpret_cast<bf16x8*>(&Gs[buf][off]) = stg[CH + i];
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (MODE == kMaskDynamic && tid < BQ) Tq[buf][tid] = rt;
   };
 
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(
   };
 
   if (nqt > 0) {
-    stage_load(qt0 * BQ);
+    stage_load(qt0 * BQ, 0);
     stage_store(0);
   }
   __syncthreads();
@@ -297,7 +308,7 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(
     const int cur = it & 1;
     const int q0 = (qt0 + it) * BQ;
     const bool need = tile_needed(cur, q0);
-    if (it + 1 < nqt) stage_load(q0 + BQ);
+    if (it + 1 < nqt) stage_load(q0 + BQ, cur ^ 1);
     if (need) compute(cur, q0);
     if (it + 1 < nqt) stage_store(cur ^ 1);
     __syncthreads();
