@@ -14,8 +14,8 @@
 //                   so that each lane holds one key and 16 queries; P and dS, rounded to bf16, are
 //                   then directly the A operands of dV += P^T G and dK += dS^T Q.
 //   k_attn_bwd_dq   work item = (user, head, 128 queries), the forward kernel's tiling: Q and G
-//                   rows in registers, 64-key tiles of K and V through LDS; S^T and dP^T with the
-//                   query as the column, then dQ += dS K.
+//                   rows in registers, 64-key tiles of K and V through LDS (LDS-direct loads);
+//                   S^T and dP^T with the query as the column, then dQ += dS K.
 // Both take their work items from the forward's per-XCD queues (the tile counts agree: 128 keys
 // or 128 queries per item).  Ranges and skipping follow the mask as in the forward: under the
 // dynamic mask a candidate key is visible only to itself, so candidate keys take no MFMA path at
@@ -23,10 +23,11 @@
 // epilogues.  An R-key wavefront skips a query tile that holds no later R/C query and none of
 // its own rows.
 //
-// LDS tiles read both along a row (operands contracting over features) and across rows (operands
-// contracting over tokens, ds_read_b64_tr_b16) have pitch d_h, with the 16-byte chunk c of row r
-// stored at chunk position c ^ swz(r); swz keeps the 16-lane row reads, the 32-lane transposing
-// reads and the staging stores free of bank conflicts (64 banks of 4 bytes).
+// Every LDS tile (Q and G in dK/dV, K and V in dQ) has pitch d_h, with the 16-byte chunk c of row
+// r stored at chunk position c ^ swz(r); swz keeps the 16-lane row reads and the 32-lane
+// transposing reads (ds_read_b64_tr_b16) free of bank conflicts (64 banks of 4 bytes).  Tiles are
+// filled by LDS-direct buffer loads: one wavefront instruction writes 1 KB, lane l the 16 bytes at
+// l*16, so lane l fetches the source chunk that belongs at that swizzled position.
 #include "kernels.h"
 
 namespace mtgr {
@@ -400,16 +401,13 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
   constexpr int CPR = DH / 8;
   constexpr int NT = DH / 32;
   constexpr int KS = DH / 16;
-  constexpr int CH = BKV * CPR / 256;
-  constexpr int RSTEP = 256 / CPR;
-  constexpr int VP = DH + 8;             // V rows are only read along the row: padded pitch
   constexpr int OP = DH + 4;
-  constexpr size_t kLoopBytes = (2 * BKV * DH + 2 * BKV * VP) * sizeof(bf16) + 2 * BKV * sizeof(float);
+  constexpr size_t kLoopBytes = 4 * BKV * DH * sizeof(bf16) + 2 * BKV * sizeof(float);
   constexpr size_t kEpiBytes = 4 * 32 * OP * sizeof(float) + 4 * 32 * sizeof(float);
   __shared__ __attribute__((aligned(16))) char arena[kLoopBytes > kEpiBytes ? kLoopBytes : kEpiBytes];
   bf16 (*Ks)[BKV * DH] = reinterpret_cast<bf16 (*)[BKV * DH]>(arena);
-  bf16 (*Vs)[BKV][VP] = reinterpret_cast<bf16 (*)[BKV][VP]>(arena + 2 * BKV * DH * sizeof(bf16));
-  float (*Ts)[BKV] = reinterpret_cast<float (*)[BKV]>(arena + (2 * BKV * DH + 2 * BKV * VP) * sizeof(bf16));
+  bf16 (*Vs)[BKV * DH] = reinterpret_cast<bf16 (*)[BKV * DH]>(arena + 2 * BKV * DH * sizeof(bf16));
+  float (*Ts)[BKV] = reinterpret_cast<float (*)[BKV]>(arena + 4 * BKV * DH * sizeof(bf16));
 
   int b, h, tile;
   if (!decode_item(B, H, order, xcd_off, b, h, tile)) return;
@@ -459,25 +457,27 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
   const int nbytes = (int)((uint32_t)kend * row_b);
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kp, (short)0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vp, (short)0, nbytes, 0x00020000);
-  const int st_r = tid / CPR, st_c = tid % CPR;
-  const uint32_t st_off = (uint32_t)st_r * row_b + st_c * 16;
-  bf16x8 stg[2 * CH];
-  float rt = INFINITY;
-  auto stage_load = [&](int k0) {
+  // K and V tiles, both swizzled, through LDS-direct buffer loads
+  constexpr int NI = BKV * CPR / 64 / 4;
+  static_assert(NI * 4 * 64 == BKV * CPR, "LDS-direct staging covers the tile");
+  uint32_t st_vo[NI];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const uint32_t so = (uint32_t)(k0 + i * RSTEP) * row_b;
-      stg[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, st_off, so, 0));
-      stg[CH + i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, st_off, so, 0));
+  for (int i = 0; i < NI; ++i) {
+    const int p = (w * NI + i) * 64 + lane;
+    const int r = p / CPR, c = (p % CPR) ^ swz<DH>(r);
+    st_vo[i] = (uint32_t)r * row_b + c * 16;
+  }
+  float rt = INFINITY;
+  auto stage_load = [&](int k0, int buf) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      lds_dma16(k_rsrc, &Ks[buf][(w * NI + i) * 512], st_vo[i], (uint32_t)k0 * row_b);
+      lds_dma16(v_rsrc, &Vs[buf][(w * NI + i) * 512], st_vo[i], (uint32_t)k0 * row_b);
     }
     if (MODE == kMaskDynamic && tid < BKV) rt = (k0 + tid < kend) ? ts[base + k0 + tid] : INFINITY;
   };
   auto stage_store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      *reinterpret_cast<bf16x8*>(&Ks[buf][sw_off<DH>(st_r + i * RSTEP, st_c * 8)]) = stg[i];
-      *reinterpret_cast<bf16x8*>(&Vs[buf][st_r + i * RSTEP][st_c * 8]) = stg[CH + i];
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if (MODE == kMaskDynamic && tid < BKV) Ts[buf][tid] = rt;
   };
 
@@ -513,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(&Ks[buf][sw_off<DH>(mt * 32 + l32, ks * 16 + hh * 8)]);
-        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[buf][mt * 32 + l32][ks * 16 + hh * 8]);
+        const bf16x8 va = *reinterpret_cast<const bf16x8*>(&Vs[buf][sw_off<DH>(mt * 32 + l32, ks * 16 + hh * 8)]);
         sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[ks], sc, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, gf[ks], dp, 0, 0, 0);
       }
@@ -551,7 +551,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
     }
   };
 
-  stage_load(0);
+  stage_load(0, 0);
   stage_store(0);
   __syncthreads();
   for (int kt = 0; kt < nkt; ++kt) {
@@ -559,7 +559,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
     const int k0 = kt * BKV;
     const bool need = tile_needed(cur, k0);
     if (need) scores(cur, k0);
-    if (kt + 1 < nkt) stage_load(k0 + BKV);
+    if (kt + 1 < nkt) stage_load(k0 + BKV, cur ^ 1);
     if (need) accumulate(cur);
     if (kt + 1 < nkt) stage_store(cur ^ 1);
     __syncthreads();
