@@ -22,8 +22,9 @@
 // S^T = K Q^T (A = 32 keys x 16 features from LDS, B = this wavefront's Q fragments, held in
 // registers for the whole work item), so that the accumulator of one lane holds one query and
 // 16 keys.  After silu and masking those values are rounded to bf16 and used directly as the A
-// operand of O = P V; V is stored transposed in LDS (feature-major, keys permuted so the 8 keys
-// a lane needs are contiguous), and the B fragment is one 16-byte LDS read.
+// operand of O = P V.  V stays row-major in LDS; each B fragment of P V is two transposing
+// reads (ds_read_b64_tr_b16) that hand every lane the 8 keys of its feature column in the order
+// the score accumulator holds them.
 //
 // LDS per workgroup: K 2 x 64 x (d_h+8) and V 2 x 64 x (d_h+32) bf16 (double-buffered,
 // register-staged global->LDS copies), ~75 KB at d_h = 128, two workgroups per CU.
