@@ -423,16 +423,21 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
                               p->gln2_beta, p->ln_eps, z, s));
   MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, z, p->w_mlp1, p->b_mlp1, nullptr, a, s));
 
-  // MLP2 and the SiLU: dhid = dout W2, then da = dhid (.) silu'(a) in place with hid = silu(a)
-  // replacing a, then dW2 = dout^T hid, db2 = sum dout
+  // MLP2 and the SiLU: dhid = dout W2, da = dhid (.) silu'(a) (in bf16 inside the GEMM's
+  // epilogue), with hid = silu(a) replacing a; then dW2 = dout^T hid, db2 = sum dout
   const void* dout = dx_out;
   if (act) {
     MTGR_BWD_TRY(launch_convert(T * d, act, dx_out, at<void>(ws, pl.dout), s));
     dout = at<void>(ws, pl.dout);
   }
   MTGR_BWD_TRY(launch_transpose(d, h, d, 0, act, p->w_mlp2, wt, s));
-  MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, dout, wt, nullptr, nullptr, dhid, s));
-  MTGR_BWD_TRY(launch_silu_bwd(T * h, act, a, dhid, s));
+  if (act) {   // bf16: the SiLU backward runs in the GEMM's epilogue
+    MTGR_BWD_TRY(launch_gemm_bf16_silu_bwd(T, h, d, static_cast<const bf16*>(dout), static_cast<const bf16*>(wt),
+                                           static_cast<bf16*>(a), static_cast<bf16*>(dhid), s));
+  } else {
+    MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, dout, wt, nullptr, nullptr, dhid, s));
+    MTGR_BWD_TRY(launch_silu_bwd(T * h, act, a, dhid, s));
+  }
   MTGR_BWD_TRY(weight_grad(pl, 0, ws, dt, T, d, h, dout, a, g->w_mlp2, g->b_mlp2, s));
   // MLP1: dz = da W1, dW1 = da^T z, db1 = sum da
   MTGR_BWD_TRY(launch_transpose(h, d, h, 0, act, p->w_mlp1, wt, s));

@@ -18,6 +18,7 @@
 //
 // fp32 path: a plain 64x64 register-tiled VALU kernel (used by the fp32 storage mode).
 #include <algorithm>
+#include <type_traits>
 
 #include "../../include/mtgr.h"
 #include "kernels.h"
@@ -64,7 +65,7 @@ template <int WM, int WN, int EPI, typename TOut, bool KMAJOR = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     int64_t M, int N, int K, const bf16* __restrict__ A, const bf16* __restrict__ W,
     const bf16* __restrict__ bias, const float* resid, TOut* out, int nN, int64_t nM, int nb,
-    int ksplit, int64_t nMr, int64_t t_rows, int lda, int ldb) {
+    int ksplit, int64_t nMr, int64_t t_rows, int lda, int ldb, bf16* aux) {
   constexpr int BM = 256, BN = 256, BK = 64, NT = 64 * WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int LP = BK + 8, CPR = BK / 8;
@@ -349,9 +350,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   // the compiler can also count past them when it waits for the next tile's prefetched slab.
   constexpr uint32_t kDrop = 0x80000000u;   // > any valid byte offset (N <= 2^20, 256 rows)
   constexpr int SP = 272;                    // staging row pitch, bytes (16-byte aligned, 4-bank skew)
-  constexpr int CPS = sizeof(TOut) == 2 ? 4 : 2;   // MFMA column tiles per pass: 256 bytes of row
+  // staged element type: the output type, except the SiLU-backward epilogue, which stages fp32
+  // and finishes the product with silu'(a) on the way out
+  using TS = std::conditional_t<EPI == kEpiSiluBwd, float, TOut>;
+  constexpr int CPS = sizeof(TS) == 2 ? 4 : 2;     // MFMA column tiles per pass: 256 bytes of row
   constexpr int NPASS = FM * FN / CPS;
-  constexpr int CW = 16 / (int)sizeof(TOut);       // columns per 16-byte chunk
+  constexpr int CW = 16 / (int)sizeof(TS);         // columns per 16-byte staged chunk
   static_assert(NT == 512 && WM * WN == 8 && 32 * SP <= BM * LP * (int)sizeof(bf16) / 4,
                 "each wavefront stages 32 rows in a quarter of one operand buffer");
   // byte offset of this lane's first chunk inside a wavefront tile (row lane/16, 16-byte chunk
@@ -372,6 +376,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     __amdgpu_buffer_rsrc_t r_rsrc = o_rsrc;
     if constexpr (EPI == MTGR_EPI_RESIDUAL_F32)
       r_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(resid + m0 * N), (short)0, nbytes, 0x00020000);
+    if constexpr (EPI == kEpiSiluBwd)   // the pre-activation a, read and overwritten with silu(a)
+      r_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(aux + m0 * N), (short)0, nbytes, 0x00020000);
     // this wavefront's staging region: a quarter of the operand buffer the last slab used
     char* stage = (wave < 4 ? reinterpret_cast<char*>(&As[cur ^ 1][0][0])
                             : reinterpret_cast<char*>(&Bs[cur ^ 1][0][0])) + (wave & 3) * (BM * LP * (int)sizeof(bf16) / 4);
@@ -401,6 +407,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
         for (int it = 0; it < 8; ++it)
           rq[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r_rsrc, vo_c, s_off(it), 0));
       }
+      u32x2 za[8];
+      if constexpr (EPI == kEpiSiluBwd) {
+#pragma unroll
+        for (int it = 0; it < 8; ++it) za[it] = __builtin_amdgcn_raw_buffer_load_b64(r_rsrc, vo_c, s_off(it), 0);
+      }
       // registers -> LDS: row l32, columns jj*32 + 8g + 4hh .. +3 of this pass
 #pragma unroll
       for (int jj = 0; jj < CPS; ++jj) {
@@ -414,8 +425,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = silu_rcp(v[e]);
           }
-          char* dst = stage + l32 * SP + cl * (int)sizeof(TOut);
-          if constexpr (sizeof(TOut) == 4) {
+          char* dst = stage + l32 * SP + cl * (int)sizeof(TS);
+          if constexpr (sizeof(TS) == 4) {
             f32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = v[e];
@@ -444,7 +455,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
           for (int e = 0; e < 4; ++e) f[e] += rq[it][e];
           c = __builtin_bit_cast(u32x4, f);
         }
-        store_chunk(c, it);
+        if constexpr (EPI == kEpiSiluBwd) {
+          // da = acc (.) silu'(a), silu'(z) = s (1 + z (1 - s)), s = sigmoid(z); a <- silu(a) = z s
+          const f32x4 f = __builtin_bit_cast(f32x4, c);
+          const bf16x4 z4 = __builtin_bit_cast(bf16x4, za[it]);
+          bf16x4 d4, h4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = (float)z4[e];
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+            d4[e] = (bf16)(f[e] * (sg * (1.0f + z * (1.0f - sg))));
+            h4[e] = (bf16)(z * sg);
+          }
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, d4), o_rsrc, vo_c, s_off(it), 0);
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), r_rsrc, vo_c, s_off(it), 0);
+        } else {
+          store_chunk(c, it);
+        }
       }
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -540,7 +567,7 @@ struct KMajorArgs {
 template <int WM, int WN, int EPI, typename TOut, bool KMAJOR = false>
 hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf16* w,
                                const bf16* bias, const float* resid, void* out, hipStream_t s,
-                               int ksplit = 1, KMajorArgs km = KMajorArgs()) {
+                               int ksplit = 1, KMajorArgs km = KMajorArgs(), bf16* aux = nullptr) {
   constexpr size_t lds = 2 * (size_t)(256 + 256) * (64 + 8) * sizeof(bf16) + kBiasLds * sizeof(bf16);
   auto kern = k_gemm_bf16_persistent<WM, WN, EPI, TOut, KMAJOR>;
   static bool attr_set = false;
@@ -575,7 +602,7 @@ hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf1
     if (t < best * 0.98) { best = t; nb = c; }
   }
   kern<<<(unsigned)grid, 64 * WM * WN, lds, s>>>(M, N, K, a, w, bias, resid, static_cast<TOut*>(out), nN, nM, nb,
-                                                  ksplit, nMr, km.t_rows, km.lda, km.ldb);
+                                                  ksplit, nMr, km.t_rows, km.lda, km.ldb, aux);
   return hipGetLastError();
 }
 
@@ -591,6 +618,13 @@ hipError_t launch_gemm_bf16(int64_t M, int N, int K, int epi, const bf16* a, con
       return run_bf16_persistent<4, 2, MTGR_EPI_RESIDUAL_F32, float>(M, N, K, a, w, bias, resid, out, s);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_bf16_silu_bwd(int64_t M, int N, int K, const bf16* a, const bf16* w, bf16* act,
+                                     bf16* out, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K % 64 != 0 || K < 128 || N % 8 != 0) return hipErrorInvalidValue;
+  return run_bf16_persistent<4, 2, kEpiSiluBwd, bf16>(M, N, K, a, w, nullptr, nullptr, out, s, 1, KMajorArgs(), act);
 }
 
 hipError_t launch_gemm_bf16_kmajor_splitk(int M, int N, int64_t Kp, int ksplit, int64_t T, const bf16* a, int lda,

@@ -93,6 +93,12 @@ hipError_t launch_attention_bwd_bf16(int32_t B, int64_t T, int64_t grid_slots, i
                                      const int64_t* offsets, const UserSeg* seg, const int32_t* order,
                                      const int32_t* xcd_off, const float* timestamps, const bf16* qkvu,
                                      const bf16* vt, const bf16* dy, bf16* g, bf16* dqkvu, hipStream_t s);
+// the backward of the MLP's SiLU fused into the GEMM that produces its input gradient: with
+// g = a[M][K] w[N][K]^T (fp32), out = bf16(g (.) silu'(act)) and act <- bf16(silu(act)) in place
+// (act: the pre-activation [M][N], bf16)
+constexpr int kEpiSiluBwd = 16;   // internal epilogue id (not one of the public MTGR_EPI_*)
+hipError_t launch_gemm_bf16_silu_bwd(int64_t M, int N, int K, const bf16* a, const bf16* w, bf16* act,
+                                     bf16* out, hipStream_t s);
 // k-major split-K GEMM for weight gradients without transposed copies: part[s][m][n] =
 // sum over token rows t of split s of a[t][m] w[t][n] (a: [T][lda], w: [T][ldb], token axis padded
 // to Kp with zero rows; Kp a multiple of 64 * ksplit, at least two 64-row slabs per split); a split
