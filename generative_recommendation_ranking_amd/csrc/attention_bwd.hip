@@ -30,6 +30,8 @@
 // l*16, so lane l fetches the source chunk that belongs at that swizzled position.
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace mtgr {
 
 namespace {
@@ -244,44 +246,42 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(
   };
 
   bf16x8 pa[4], da[4];
-  auto compute = [&](int buf, int q0) {
-    f32x16 sc[2], dp[2];
+  auto compute_t = [&](auto masked_tag, int buf, int q0) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    // sc[r], dp[r] of one 32-query half: query q0 + mt*32 + 8*(r/4) + 4*hh + r%4, key kj.  Rows
+    // and keys past the user's end were loaded as zeros: their score, silu and dP are 0 already.
+    // The halves run one after the other, so only one half's score accumulators are live and the
+    // first half's SiLU can overlap the second half's MFMAs.
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      f32x16 sc, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) { sc[mt][r] = 0.f; dp[mt][r] = 0.f; }
+      for (int r = 0; r < 16; ++r) { sc[r] = 0.f; dp[r] = 0.f; }
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
+      for (int ks = 0; ks < KS; ++ks) {
         const int off = sw_off<DH>(mt * 32 + l32, ks * 16 + hh * 8);
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(&Qs[buf][off]);
         const bf16x8 ga = *reinterpret_cast<const bf16x8*>(&Gs[buf][off]);
-        sc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sc[mt], 0, 0, 0);
-        dp[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp[mt], 0, 0, 0);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[ks], sc, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ga, vf[ks], dp, 0, 0, 0);
       }
-    }
-    // sc[mt][r], dp[mt][r]: query q0 + mt*32 + 8*(r/4) + 4*hh + r%4, key kj.  Rows and keys past
-    // the user's end were loaded as zeros: their score, silu and dP are 0 already.
-    const bool unmasked = MODE == kMaskFull || (MODE == kMaskCausal ? q0 >= wk0 + 31 : wk0 + 32 <= ns);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         f32x4 t4 = {};
-        if (MODE == kMaskDynamic && !unmasked) t4 = *reinterpret_cast<const f32x4*>(&Tq[buf][mt * 32 + 8 * g4 + 4 * hh]);
+        if (MODE == kMaskDynamic && kMasked) t4 = *reinterpret_cast<const f32x4*>(&Tq[buf][mt * 32 + 8 * g4 + 4 * hh]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = g4 * 4 + c;
           const int qi = q0 + mt * 32 + 8 * g4 + 4 * hh + c;
-          const float s = sc[mt][r];
+          const float s = sc[r];
           const float sgm = sigmoid_rcp(s);
           float p = s * sgm;
-          float ds = dp[mt][r] * sgm * (1.0f + s * (1.0f - sgm));
-          if (!unmasked) {
+          float ds = dp[r] * sgm * (1.0f + s * (1.0f - sgm));
+          if constexpr (kMasked) {
             // the rule of mtgr_visible with the key side folded into tk (finite only for R keys)
             const bool vis = MODE == kMaskCausal ? kj <= qi : (kj < ns) | (qi == kj) | (t4[c] > tk);
-            if (!vis) { p = 0.f; ds = 0.f; }
+            p = vis ? p : 0.f;
+            ds = vis ? ds : 0.f;
           }
           pa[mt * 2 + (r >> 3)][r & 7] = (bf16)p;
           da[mt * 2 + (r >> 3)][r & 7] = (bf16)ds;
@@ -298,6 +298,13 @@ __global__ __launch_bounds__(256, 1) void k_attn_bwd_dkv(
         dk[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], qb, dk[t], 0, 0, 0);
       }
     }
+  };
+
+  // tiles every pair of which is visible take the branch-free unmasked body
+  auto compute = [&](int buf, int q0) {
+    const bool unmasked = MODE == kMaskFull || (MODE == kMaskCausal ? q0 >= wk0 + 31 : wk0 + 32 <= ns);
+    if (unmasked) compute_t(std::false_type{}, buf, q0);
+    else compute_t(std::true_type{}, buf, q0);
   };
 
   if (nqt > 0) {
@@ -501,8 +508,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
   // next tile's loads, then dQ += dS K: the loads stay in flight across the dQ MFMAs, and the
   // kernel fits two wavefronts per SIMD.
   bf16x8 da[4];
-  auto scores = [&](int buf, int k0) {
-    const bool unmasked = MODE == kMaskFull || (MODE == kMaskCausal ? k0 + BKV <= wq0 + 1 : k0 + BKV <= ns);
+  auto scores_t = [&](auto masked_tag, int buf, int k0) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     const int jb = k0 + 4 * hh;
     const int lim_static = ns - jb, lim_rc = rc_end - jb, self = qi - jb;
 #pragma unroll
@@ -521,7 +528,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         f32x4 t4 = {};
-        if (MODE == kMaskDynamic && !unmasked) t4 = *reinterpret_cast<const f32x4*>(&Ts[buf][mt * 32 + 8 * g4 + 4 * hh]);
+        if (MODE == kMaskDynamic && kMasked) t4 = *reinterpret_cast<const f32x4*>(&Ts[buf][mt * 32 + 8 * g4 + 4 * hh]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int r = g4 * 4 + c;
@@ -529,16 +536,22 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
           const float s = sc[r];
           const float sgm = sigmoid_rcp(s);
           float ds = dp[r] * sgm * (1.0f + s * (1.0f - sgm));
-          if (!unmasked) {
+          if constexpr (kMasked) {
             const bool vis = MODE == kMaskCausal
                                  ? dk <= self
                                  : (dk < lim_static) | (dk == self) | (q_rc & (dk < lim_rc) & (t4[c] < tq));
-            if (!vis) ds = 0.f;
+            ds = vis ? ds : 0.f;
           }
           da[mt * 2 + (r >> 3)][r & 7] = (bf16)ds;
         }
       }
     }
+  };
+  // tiles every pair of which is visible take the branch-free unmasked body
+  auto scores = [&](int buf, int k0) {
+    const bool unmasked = MODE == kMaskFull || (MODE == kMaskCausal ? k0 + BKV <= wq0 + 1 : k0 + BKV <= ns);
+    if (unmasked) scores_t(std::false_type{}, buf, k0);
+    else scores_t(std::true_type{}, buf, k0);
   };
   auto accumulate = [&](int buf) {
 #pragma unroll
