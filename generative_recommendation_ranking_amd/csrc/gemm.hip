@@ -128,7 +128,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   // count a multiple of the XCD count): XCD x = mt % kXcd holds splits x, x + kXcd, ..., each with
   // all its row tiles; otherwise sp = mt / nMr, r = mt % nMr.
   const int nk = K / BK / ksplit;        // >= 2 (checked by the host)
-  const bool split_major = ksplit > 1 && ksplit % kXcd == 0;
+  const bool split_major = KMAJOR && ksplit > 1 && ksplit % kXcd == 0;   // (k-major GEMMs only)
   auto split_row = [&](int64_t mt, int& sp, int64_t& r) {
     if (split_major) {
       const int64_t j = mt / kXcd;
@@ -593,7 +593,7 @@ hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf1
   // (split-major split K: all of a split's column tiles at once, they share its slabs)
   int nb = nN;
   double best = 1e300;
-  for (int c = 1; c <= nN && !(ksplit > 1 && ksplit % kXcd == 0); ++c) {
+  for (int c = 1; c <= nN && !(KMAJOR && ksplit > 1 && ksplit % kXcd == 0); ++c) {
     const double chunks = (double)((nN + c - 1) / c);
     const bool fits = c * slice <= 0.6 * l2;
     const double rounds = (double)((nM + kXcd - 1) / kXcd) * c / std::max(1.0, wg_per_xcd);
