@@ -62,7 +62,8 @@ int64_t dedup_cap(int64_t n) {
 // ---- tokenizer --------------------------------------------------------------------------------
 struct TokPlan {
   size_t flags = 0, cnt = 0, goff = 0, keys = 0, dedup = 0, uniq = 0, inverse = 0, ucount = 0, uvals = 0;
-  size_t pos = 0, feat = 0, hid = 0, y = 0, total = 0;
+  size_t pos = 0, rowmap = 0, feat = 0, hid = 0, y = 0, total = 0;
+  bool direct = false;   // the second GEMM writes token rows directly (x fits one 31-bit range)
   size_t feat_off[4] = {0, 0, 0, 0};
   int64_t row0[4] = {0, 0, 0, 0};
   int64_t dedup_cap = 0;
@@ -89,6 +90,8 @@ TokPlan tok_plan(const mtgr_tokenizer_params* p, const mtgr_batch* b, int e, con
   pl.ucount = take(8);
   pl.uvals = take((size_t)n * e * 2);
   pl.pos = take((size_t)T * 8);
+  pl.direct = T * (int64_t)p->d_model * 4 < (int64_t(1) << 31);
+  pl.rowmap = take(pl.direct ? (size_t)T * 4 : 0);
   size_t feat_bytes = 0;
   int64_t r0 = 0;
   for (int g = 0; g < 4; ++g) {
@@ -99,7 +102,7 @@ TokPlan tok_plan(const mtgr_tokenizer_params* p, const mtgr_batch* b, int e, con
   }
   pl.feat = take(feat_bytes);
   pl.hid = take((size_t)T * p->d_model * 2);
-  pl.y = take((size_t)T * p->d_model * 4);
+  pl.y = take(pl.direct ? 0 : (size_t)T * p->d_model * 4);
   pl.total = off;
   return pl;
 }
@@ -182,6 +185,7 @@ mtgr_status mtgr_tokenize(const mtgr_tokenizer_params* p, const mtgr_batch* b, c
   int64_t* pos = reinterpret_cast<int64_t*>(w + pl.pos);
   bf16* hid = reinterpret_cast<bf16*>(w + pl.hid);
   float* y = reinterpret_cast<float*>(w + pl.y);
+  int32_t* rowmap = pl.direct ? reinterpret_cast<int32_t*>(w + pl.rowmap) : nullptr;
   const int64_t n = T * fmax;
 #define TOK_TRY(x)                                      \
   do {                                                  \
@@ -206,17 +210,22 @@ mtgr_status mtgr_tokenize(const mtgr_tokenizer_params* p, const mtgr_batch* b, c
     tg.feat[g] = reinterpret_cast<bf16*>(w + pl.feat + pl.feat_off[g]);
   }
   TOK_TRY(launch_tok_build(T, b->num_users, fmax, e, b->offsets, b->group_ids, cnt, goff, tg, inverse, uvals, pos,
-                           flags, s));
+                           rowmap, flags, s));
+  if (pl.direct) TOK_TRY(launch_tok_zero_unplaced(T, d, pos, x_out, s));
   for (int g = 0; g < 4; ++g) {
     const int64_t rows = group_counts[g];
     if (rows == 0) continue;
     const int K = p->num_fields[g] * e;
     TOK_TRY(launch_gemm_bf16(rows, d, K, MTGR_EPI_SILU, tg.feat[g], static_cast<const bf16*>(p->w1[g]),
                              static_cast<const bf16*>(p->b1[g]), nullptr, hid + pl.row0[g] * d, s));
-    TOK_TRY(launch_gemm_bf16_f32out(rows, d, d, hid + pl.row0[g] * d, static_cast<const bf16*>(p->w2[g]),
-                                    static_cast<const bf16*>(p->b2[g]), y + pl.row0[g] * d, s));
+    if (pl.direct)
+      TOK_TRY(launch_gemm_bf16_f32out_rows(rows, d, d, hid + pl.row0[g] * d, static_cast<const bf16*>(p->w2[g]),
+                                           static_cast<const bf16*>(p->b2[g]), rowmap + pl.row0[g], T, x_out, s));
+    else
+      TOK_TRY(launch_gemm_bf16_f32out(rows, d, d, hid + pl.row0[g] * d, static_cast<const bf16*>(p->w2[g]),
+                                      static_cast<const bf16*>(p->b2[g]), y + pl.row0[g] * d, s));
   }
-  TOK_TRY(launch_tok_scatter(T, d, pos, y, x_out, s));
+  if (!pl.direct) TOK_TRY(launch_tok_scatter(T, d, pos, y, x_out, s));
 #undef TOK_TRY
   return MTGR_OK;
 }

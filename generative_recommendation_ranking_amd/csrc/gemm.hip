@@ -65,7 +65,7 @@ template <int WM, int WN, int EPI, typename TOut, bool KMAJOR = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     int64_t M, int N, int K, const bf16* __restrict__ A, const bf16* __restrict__ W,
     const bf16* __restrict__ bias, const float* resid, TOut* out, int nN, int64_t nM, int nb,
-    int ksplit, int64_t nMr, int64_t t_rows, int lda, int ldb, bf16* aux) {
+    int ksplit, int64_t nMr, int64_t t_rows, int lda, int ldb, void* aux) {
   constexpr int BM = 256, BN = 256, BK = 64, NT = 64 * WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int LP = BK + 8, CPR = BK / 8;
@@ -371,13 +371,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     const int n0 = nt_e * BN;
     const uint32_t rows = (uint32_t)min((int64_t)BM, M - m0);
     const int nbytes = (int)(rows * (uint32_t)N * sizeof(TOut));
+    // row scatter: the resource spans the whole destination [t_rows][N]; rows come from the map
     const __amdgpu_buffer_rsrc_t o_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(outp + m0 * N), (short)0, nbytes, 0x00020000);
+        EPI == kEpiRowScatter
+            ? __builtin_amdgcn_make_buffer_rsrc((void*)outp, (short)0, (int)(t_rows * N * (int64_t)sizeof(TOut)), 0x00020000)
+            : __builtin_amdgcn_make_buffer_rsrc((void*)(outp + m0 * N), (short)0, nbytes, 0x00020000);
     __amdgpu_buffer_rsrc_t r_rsrc = o_rsrc;
     if constexpr (EPI == MTGR_EPI_RESIDUAL_F32)
       r_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(resid + m0 * N), (short)0, nbytes, 0x00020000);
     if constexpr (EPI == kEpiSiluBwd)   // the pre-activation a, read and overwritten with silu(a)
-      r_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(aux + m0 * N), (short)0, nbytes, 0x00020000);
+      r_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<bf16*>(aux) + m0 * N), (short)0, nbytes, 0x00020000);
     // this wavefront's staging region: a quarter of the operand buffer the last slab used
     char* stage = (wave < 4 ? reinterpret_cast<char*>(&As[cur ^ 1][0][0])
                             : reinterpret_cast<char*>(&Bs[cur ^ 1][0][0])) + (wave & 3) * (BM * LP * (int)sizeof(bf16) / 4);
@@ -411,6 +414,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
       if constexpr (EPI == kEpiSiluBwd) {
 #pragma unroll
         for (int it = 0; it < 8; ++it) za[it] = __builtin_amdgcn_raw_buffer_load_b64(r_rsrc, vo_c, s_off(it), 0);
+      }
+      // row scatter: destination row of each chunk (-1: none), read before the pass's stores
+      uint32_t vo_r[8];
+      if constexpr (EPI == kEpiRowScatter) {
+        const int32_t* rowmap = static_cast<const int32_t*>(aux);
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+          const int64_t gr = m0 + wm * TM + i * 32 + it * 4 + (lane >> 4);
+          const int32_t dst = (gr < M) ? rowmap[gr] : -1;
+          vo_r[it] = (dst >= 0 && col_ok)
+                         ? ((uint32_t)dst * (uint32_t)N + (uint32_t)(n0 + wn * TN + j0 * 32 + (lane & 15) * CW)) * (uint32_t)sizeof(TOut)
+                         : kDrop;
+        }
       }
       // registers -> LDS: row l32, columns jj*32 + 8g + 4hh .. +3 of this pass
 #pragma unroll
@@ -469,6 +485,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
           }
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, d4), o_rsrc, vo_c, s_off(it), 0);
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h4), r_rsrc, vo_c, s_off(it), 0);
+        } else if constexpr (EPI == kEpiRowScatter) {
+          __builtin_amdgcn_raw_buffer_store_b128(c, o_rsrc, vo_r[it], 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          asm volatile("s_nop 1");
+          __builtin_amdgcn_sched_barrier(0);
         } else {
           store_chunk(c, it);
         }
@@ -567,7 +588,7 @@ struct KMajorArgs {
 template <int WM, int WN, int EPI, typename TOut, bool KMAJOR = false>
 hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf16* w,
                                const bf16* bias, const float* resid, void* out, hipStream_t s,
-                               int ksplit = 1, KMajorArgs km = KMajorArgs(), bf16* aux = nullptr) {
+                               int ksplit = 1, KMajorArgs km = KMajorArgs(), void* aux = nullptr) {
   constexpr size_t lds = 2 * (size_t)(256 + 256) * (64 + 8) * sizeof(bf16) + kBiasLds * sizeof(bf16);
   auto kern = k_gemm_bf16_persistent<WM, WN, EPI, TOut, KMAJOR>;
   static bool attr_set = false;
@@ -625,6 +646,17 @@ hipError_t launch_gemm_bf16_silu_bwd(int64_t M, int N, int K, const bf16* a, con
   if (M == 0 || N == 0) return hipSuccess;
   if (K % 64 != 0 || K < 128 || N % 8 != 0) return hipErrorInvalidValue;
   return run_bf16_persistent<4, 2, kEpiSiluBwd, bf16>(M, N, K, a, w, nullptr, nullptr, out, s, 1, KMajorArgs(), act);
+}
+
+hipError_t launch_gemm_bf16_f32out_rows(int64_t M, int N, int K, const bf16* a, const bf16* w, const bf16* bias,
+                                        const int32_t* rowmap, int64_t out_rows, float* out, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K % 64 != 0 || K < 128 || N % 8 != 0) return hipErrorInvalidValue;
+  if (out_rows * N * 4 >= (int64_t(1) << 31)) return hipErrorInvalidValue;   // one 31-bit buffer range
+  KMajorArgs km;
+  km.t_rows = out_rows;
+  return run_bf16_persistent<4, 2, kEpiRowScatter, float>(M, N, K, a, w, bias, nullptr, out, s, 1, km,
+                                                          const_cast<int32_t*>(rowmap));
 }
 
 hipError_t launch_gemm_bf16_kmajor_splitk(int M, int N, int64_t Kp, int ksplit, int64_t T, const bf16* a, int lda,

@@ -97,6 +97,11 @@ hipError_t launch_attention_bwd_bf16(int32_t B, int64_t T, int64_t grid_slots, i
 // g = a[M][K] w[N][K]^T (fp32), out = bf16(g (.) silu'(act)) and act <- bf16(silu(act)) in place
 // (act: the pre-activation [M][N], bf16)
 constexpr int kEpiSiluBwd = 16;   // internal epilogue id (not one of the public MTGR_EPI_*)
+// out[rowmap[m]][n] = a[m][K] w[n][K]^T + bias (fp32), row m dropped where rowmap[m] < 0; out has
+// out_rows rows (out_rows * N * 4 < 2^31)
+constexpr int kEpiRowScatter = 17;
+hipError_t launch_gemm_bf16_f32out_rows(int64_t M, int N, int K, const bf16* a, const bf16* w, const bf16* bias,
+                                        const int32_t* rowmap, int64_t out_rows, float* out, hipStream_t s);
 hipError_t launch_gemm_bf16_silu_bwd(int64_t M, int N, int K, const bf16* a, const bf16* w, bf16* act,
                                      bf16* out, hipStream_t s);
 // k-major split-K GEMM for weight gradients without transposed copies: part[s][m][n] =
@@ -158,8 +163,9 @@ hipError_t launch_tok_prepare(int32_t B, int64_t T, int fmax, const int64_t* off
                               int32_t* flags, hipStream_t s);
 hipError_t launch_tok_build(int64_t T, int32_t B, int fmax, int e, const int64_t* offsets, const uint8_t* group_ids,
                             const int64_t* cnt, const int64_t* goff, const TokGroups& tg, const int64_t* inverse,
-                            const bf16* uvals, int64_t* pos, int32_t* flags, hipStream_t s);
+                            const bf16* uvals, int64_t* pos, int32_t* rowmap, int32_t* flags, hipStream_t s);
 hipError_t launch_tok_scatter(int64_t T, int d, const int64_t* pos, const float* y, float* x, hipStream_t s);
+hipError_t launch_tok_zero_unplaced(int64_t T, int d, const int64_t* pos, float* x, hipStream_t s);
 // out (float [M][N]) = a[M][K] w[N][K]^T + bias (bf16 operands)
 hipError_t launch_gemm_bf16_f32out(int64_t M, int N, int K, const bf16* a, const bf16* w, const bf16* bias,
                                    float* out, hipStream_t s);

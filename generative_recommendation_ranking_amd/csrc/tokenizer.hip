@@ -18,7 +18,9 @@
 //   k_tok_build   each token's concatenated field embeddings, written to its row of the
 //                 group-sorted feature buffer (group g rows are contiguous, width F_g * e)
 //   GEMMs         per group: hid = silu(feat W1_g^T + b1_g), y = hid W2_g^T + b2_g (fp32)
-//   k_tok_scatter x[t] = y[pos(t)]
+//   k_tok_scatter x[t] = y[pos(t)]; when x fits one 31-bit buffer range the second GEMM writes each
+//                 row straight to its token instead (rowmap: sorted row -> token), and
+//                 k_tok_zero_unplaced zeroes the tokens that got no sorted row
 // Positions are computed from the device's own counts; every write is bounded by the group sizes
 // the host was given, so inconsistent sizes give wrong rows, never out-of-range accesses.
 #include <algorithm>
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(256) void k_tok_build(int64_t T, int32_t B, int fma
                                                    const int64_t* __restrict__ cnt, const int64_t* __restrict__ goff,
                                                    TokGroups tg, const int64_t* __restrict__ inverse,
                                                    const bf16* __restrict__ uvals, int64_t* __restrict__ pos,
-                                                   int32_t* __restrict__ flags) {
+                                                   int32_t* __restrict__ rowmap, int32_t* __restrict__ flags) {
   const int lane16 = threadIdx.x & 15;
   const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 4;
   const int64_t teams = ((int64_t)gridDim.x * blockDim.x) >> 4;
@@ -130,7 +132,10 @@ __global__ __launch_bounds__(256) void k_tok_build(int64_t T, int32_t B, int fma
       if (lane16 == 0) { pos[t] = -1; atomicOr(flags, 1); }
       continue;
     }
-    if (lane16 == 0) pos[t] = tg.row0[grp] + p;
+    if (lane16 == 0) {
+      pos[t] = tg.row0[grp] + p;
+      if (rowmap) rowmap[tg.row0[grp] + p] = (int32_t)t;
+    }
     const int nf = tg.nfields[grp];
     bf16* dst = tg.feat[grp] + p * (int64_t)(nf * e);
     for (int c = lane16; c < nf * cpf; c += 16) {
@@ -158,6 +163,18 @@ __global__ __launch_bounds__(256) void k_tok_scatter(int64_t T, int d, const int
 
 __global__ void k_flags_reset(int32_t* flags) { *flags = 0; }
 
+__global__ __launch_bounds__(256) void k_fill_i32(int64_t n, int32_t v, int32_t* __restrict__ p) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+// x[t] = 0 for every token that has no sorted row (pos[t] < 0)
+__global__ __launch_bounds__(256) void k_tok_zero_unplaced(int64_t T, int d, const int64_t* __restrict__ pos,
+                                                           float* __restrict__ x) {
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < T; t += (int64_t)gridDim.x * blockDim.x)
+    if (pos[t] < 0)
+      for (int c = 0; c < d; c += 4) *reinterpret_cast<float4*>(x + t * d + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
 inline unsigned ew(int64_t n) { return (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 255) / 256, 65536)); }
 
 }  // namespace
@@ -176,11 +193,22 @@ hipError_t launch_tok_prepare(int32_t B, int64_t T, int fmax, const int64_t* off
 
 hipError_t launch_tok_build(int64_t T, int32_t B, int fmax, int e, const int64_t* offsets, const uint8_t* group_ids,
                             const int64_t* cnt, const int64_t* goff, const TokGroups& tg, const int64_t* inverse,
-                            const bf16* uvals, int64_t* pos, int32_t* flags, hipStream_t s) {
+                            const bf16* uvals, int64_t* pos, int32_t* rowmap, int32_t* flags, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int64_t blocks = std::min<int64_t>((T * 16 + 255) / 256, 65536);
+  if (rowmap) {
+    k_fill_i32<<<ew(T), 256, 0, s>>>(T, -1, rowmap);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
   k_tok_build<<<(unsigned)blocks, 256, 0, s>>>(T, B, fmax, e, offsets, group_ids, cnt, goff, tg, inverse, uvals,
-                                               pos, flags);
+                                               pos, rowmap, flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_tok_zero_unplaced(int64_t T, int d, const int64_t* pos, float* x, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  k_tok_zero_unplaced<<<ew(T), 256, 0, s>>>(T, d, pos, x);
   return hipGetLastError();
 }
 

@@ -288,6 +288,14 @@ def test_tokenize_inconsistent_counts_are_flagged_not_faulted():
     x, flags = run_tok(b, spec, ids, wrong, store)
     assert flags & 1
     assert np.isfinite(x).all()
+    # the S tokens past the stated S count (the last 10 in batch order) have no row: x = 0; every
+    # other token is still tokenized correctly
+    s_tokens = np.flatnonzero(b.group_ids == 1)
+    unplaced = s_tokens[-10:]
+    assert (x[unplaced] == 0).all()
+    placed = np.setdiff1d(np.arange(b.num_tokens), unplaced)
+    ref = EO.tokenize(ids[placed], b.group_ids[placed], spec.field_tables, model, spec.mlps)
+    assert rel_err(x[placed], ref) < TOL_TOK
 
 
 def test_tokenize_empty_batch():
