@@ -175,50 +175,74 @@ __global__ __launch_bounds__(256) void k_claim(View v, int64_t n, const int64_t*
 }
 
 // Claimed slots take a free row and initialise it; with none left the slot becomes a tombstone.
-// The pops of a wavefront's teams are one atomic on the stack top (each claimant takes the
-// next row below the returned top by its rank among the wavefront's claimants).
+// A workgroup takes a chunk of kAssignKeys occurrences (a wavefront a quarter of it, in order):
+// it counts the chunk's claimants, pops that many rows with one atomic on the stack top, and
+// gives each claimant the row below the returned top by its rank within the chunk.  One atomic
+// per 2048 occurrences, instead of one per wavefront step, keeps the stack top from serialising
+// a large insert.
+constexpr int kAssignSteps = 64;                       // team steps per wavefront and chunk
+constexpr int kAssignKeys = 4 * kTeam * kAssignSteps;  // occurrences per workgroup chunk (2048)
 __global__ __launch_bounds__(256) void k_assign(View v, int64_t n, int64_t* __restrict__ res,
                                                 const char* __restrict__ init, int32_t step) {
-  const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
-  const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
-  const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
-  const int64_t first_of_wave = team - (lane >> 3);
-  for (int64_t base = first_of_wave; base < n; base += teams) {   // wave-uniform trip count
-    const int64_t i = base + (lane >> 3);
-    const int64_t r = i < n ? res[i] : -1;
-    const bool want = sub == 0 && r >= 0 && (r & (1LL << 62));
-    const unsigned long long mask = __ballot(want);
-    int32_t row = -1;
-    if (mask) {
-      const int leader = __ffsll((long long)mask) - 1;
-      const int cnt = __popcll(mask);
-      int32_t top = 0;
-      if (lane == leader) top = atomicSub(&v.ah->free_top, cnt);
-      top = __shfl(top, leader, kWave);
-      const int rank = __popcll(mask & ((1ULL << lane) - 1));
-      int ok = 0, bad = 0;
+  __shared__ int s_cnt[4];
+  __shared__ int32_t s_top;
+  const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1), w = threadIdx.x >> 6;
+  const int64_t nchunks = (n + kAssignKeys - 1) / kAssignKeys;
+  for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {   // block-uniform
+    const int64_t wave0 = chunk * kAssignKeys + (int64_t)w * kTeam * kAssignSteps;
+    auto claimant = [&](int it, int64_t& i, int64_t& r) {
+      i = wave0 + (int64_t)it * kTeam + (lane >> 3);
+      r = (sub == 0 && i < n) ? res[i] : -1;
+      return r >= 0 && (r & (1LL << 62));
+    };
+    // this wavefront's claimants, then the chunk's pop
+    int cnt = 0;
+    for (int it = 0; it < kAssignSteps; ++it) {
+      int64_t i, r;
+      cnt += __popcll(__ballot(claimant(it, i, r)));
+    }
+    if (lane == 0) s_cnt[w] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int total = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+      s_top = total ? atomicSub(&v.ah->free_top, total) : 0;
+    }
+    __syncthreads();
+    int rank0 = 0;                                     // claimants of the earlier wavefronts
+    for (int k = 0; k < w; ++k) rank0 += s_cnt[k];
+    const int32_t top = s_top;
+    int ok_n = 0, bad_n = 0;
+    for (int it = 0; it < kAssignSteps; ++it) {
+      int64_t i, r;
+      const bool want = claimant(it, i, r);
+      const unsigned long long mask = __ballot(want);
+      int32_t row = -1;
+      bool ok = false, bad = false;
       if (want) {
         const int64_t slot = r & ((1LL << 62) - 1);
-        const int32_t t = top - rank;                // this claimant's stack height
+        const int32_t t = top - (rank0 + __popcll(mask & ((1ULL << lane) - 1)));   // this claimant's stack height
         if (t >= 1) {
           row = v.free_stack[t - 1];
           v.slots[slot].row = row;
           v.last_seen[row] = step;
-          ok = 1;
+          ok = true;
         } else {
           v.slots[slot].key = kTomb;
-          bad = 1;
+          bad = true;
         }
       }
-      const unsigned long long okm = __ballot(ok), badm = __ballot(bad);
-      if (lane == leader) {
-        if (okm) atomicAdd(&v.ih->live, (unsigned long long)__popcll(okm));
-        if (badm) atomicAdd(&v.ih->tombstones, (unsigned long long)__popcll(badm));
-      }
+      rank0 += __popcll(mask);
+      ok_n += __popcll(__ballot(ok));
+      bad_n += __popcll(__ballot(bad));
+      row = __shfl(row, lane & ~(kTeam - 1), kWave);
+      if (row >= 0)
+        team_copy(v.values + (int64_t)row * v.row_bytes, init ? init + i * v.row_bytes : nullptr, v.row_bytes, sub);
     }
-    row = __shfl(row, lane & ~(kTeam - 1), kWave);
-    if (row >= 0)
-      team_copy(v.values + (int64_t)row * v.row_bytes, init ? init + i * v.row_bytes : nullptr, v.row_bytes, sub);
+    if (lane == 0) {
+      if (ok_n) atomicAdd(&v.ih->live, (unsigned long long)ok_n);
+      if (bad_n) atomicAdd(&v.ih->tombstones, (unsigned long long)bad_n);
+    }
+    __syncthreads();                                   // s_cnt and s_top are reused by the next chunk
   }
 }
 
@@ -407,7 +431,8 @@ hipError_t launch_hash_insert(const HashDesc& h, int64_t n, const int64_t* keys,
   if (n == 0) return hipSuccess;
   View v = make_view(h);
   k_claim<<<team_grid(n), 256, 0, s>>>(v, n, keys, res);
-  k_assign<<<team_grid(n), 256, 0, s>>>(v, n, res, static_cast<const char*>(init), step);
+  k_assign<<<(unsigned)std::min<int64_t>((n + kAssignKeys - 1) / kAssignKeys, 65536), 256, 0, s>>>(
+      v, n, res, static_cast<const char*>(init), step);
   k_resolve<<<ew(n), 256, 0, s>>>(v, n, res, rows_out, step);
   return hipGetLastError();
 }
