@@ -357,11 +357,10 @@ __global__ __launch_bounds__(256) void k_rebuild(View src, int64_t nslots, View 
 }
 
 // ---- dedup ---------------------------------------------------------------------------------
-// Claim on a scratch index; each claiming team numbers its key (one atomic per wavefront for the
-// wavefront's new keys) and records it.
+// Claim on a scratch index: res[i] = the slot of keys[i], bit 62 set where this occurrence's team
+// claimed it (the key's first claimant).
 __global__ __launch_bounds__(256) void k_dedup_claim(View v, int64_t n, const int64_t* __restrict__ keys,
-                                                     int64_t* __restrict__ res, int64_t* __restrict__ uniq,
-                                                     unsigned long long* __restrict__ count) {
+                                                     int64_t* __restrict__ res) {
   const int lane = threadIdx.x & 63, sub = lane & (kTeam - 1);
   const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
   const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
@@ -370,20 +369,51 @@ __global__ __launch_bounds__(256) void k_dedup_claim(View v, int64_t n, const in
     const int64_t i = base + (lane >> 3);
     const int64_t key = i < n ? keys[i] : -1;
     const int64_t r = key >= 0 ? claim(v, key, lane) : -1;   // negative keys are not keys
-    const bool fresh = sub == 0 && r >= 0 && (r & (1LL << 62));
-    const unsigned long long mask = __ballot(fresh);
-    if (mask) {
-      const int leader = __ffsll((long long)mask) - 1;
-      unsigned long long b0 = 0;
-      if (lane == leader) b0 = atomicAdd(count, (unsigned long long)__popcll(mask));
-      b0 = __shfl(b0, leader, kWave);
-      if (fresh) {
-        const int64_t id = (int64_t)b0 + __popcll(mask & ((1ULL << lane) - 1));
-        v.slots[r & ((1LL << 62) - 1)].row = (int32_t)id;
-        uniq[id] = key;
-      }
-    }
     if (sub == 0 && i < n) res[i] = r;
+  }
+}
+
+// Number the claimed keys: a workgroup takes a chunk of kAssignKeys occurrences, counts its
+// claimants, takes that many ids with one atomic on the count and gives them out in chunk order;
+// the id goes to the key's slot and the key to unique[id].
+__global__ __launch_bounds__(256) void k_dedup_number(View v, int64_t n, const int64_t* __restrict__ keys,
+                                                      const int64_t* __restrict__ res, int64_t* __restrict__ uniq,
+                                                      unsigned long long* __restrict__ count) {
+  __shared__ int s_cnt[4];
+  __shared__ unsigned long long s_base;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t nchunks = (n + kAssignKeys - 1) / kAssignKeys;
+  constexpr int kPerWave = kAssignKeys / 4;
+  for (int64_t chunk = blockIdx.x; chunk < nchunks; chunk += gridDim.x) {   // block-uniform
+    const int64_t wave0 = chunk * kAssignKeys + (int64_t)w * kPerWave;
+    int cnt = 0;
+    for (int it = 0; it < kPerWave; it += 64) {
+      const int64_t i = wave0 + it + lane;
+      const int64_t r = i < n ? res[i] : -1;
+      cnt += __popcll(__ballot(r >= 0 && (r & (1LL << 62))));
+    }
+    if (lane == 0) s_cnt[w] = cnt;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const int total = s_cnt[0] + s_cnt[1] + s_cnt[2] + s_cnt[3];
+      s_base = total ? atomicAdd(count, (unsigned long long)total) : 0ULL;
+    }
+    __syncthreads();
+    int64_t id = (int64_t)s_base;
+    for (int k = 0; k < w; ++k) id += s_cnt[k];
+    for (int it = 0; it < kPerWave; it += 64) {
+      const int64_t i = wave0 + it + lane;
+      const int64_t r = i < n ? res[i] : -1;
+      const bool fresh = r >= 0 && (r & (1LL << 62));
+      const unsigned long long mask = __ballot(fresh);
+      if (fresh) {
+        const int64_t my = id + __popcll(mask & ((1ULL << lane) - 1));
+        v.slots[r & ((1LL << 62) - 1)].row = (int32_t)my;
+        uniq[my] = keys[i];
+      }
+      id += __popcll(mask);
+    }
+    __syncthreads();                                   // s_cnt and s_base are reused by the next chunk
   }
 }
 
@@ -468,7 +498,9 @@ hipError_t launch_dedup(int64_t n, const int64_t* keys, const HashDesc& scratch,
   k_index_init<<<ew(scratch.index_cap), 256, 0, s>>>(v.slots, scratch.index_cap, v.ih);
   k_count_reset<<<1, 1, 0, s>>>(count);
   if (n == 0) return hipGetLastError();
-  k_dedup_claim<<<team_grid(n), 256, 0, s>>>(v, n, keys, res, uniq, count);
+  k_dedup_claim<<<team_grid(n), 256, 0, s>>>(v, n, keys, res);
+  k_dedup_number<<<(unsigned)std::min<int64_t>((n + kAssignKeys - 1) / kAssignKeys, 65536), 256, 0, s>>>(
+      v, n, keys, res, uniq, count);
   k_dedup_inverse<<<ew(n), 256, 0, s>>>(v, n, res, inverse);
   return hipGetLastError();
 }
