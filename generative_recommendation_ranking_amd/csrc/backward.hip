@@ -213,6 +213,31 @@ __global__ __launch_bounds__(256) void k_reduce_wb(int M, int K, int Kx, int nsp
 // current group in registers and adds them into its own slot [2][4][d] of `part` whenever the group
 // changes (tokens come in group runs); only that wavefront touches the slot, in program order, and
 // k_reduce sums the slots in a fixed order, so the result is deterministic.
+// 8 consecutive values (16-byte aligned bf16, 32-byte aligned fp32) as one or two vector accesses
+__device__ __forceinline__ void ld8(const bf16* p, float (&o)[8]) {
+  const bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (float)v[i];
+}
+__device__ __forceinline__ void ld8(const float* p, float (&o)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { o[i] = a[i]; o[i + 4] = b[i]; }
+}
+__device__ __forceinline__ void st8(bf16* p, const float (&v)[8]) {
+  bf16x8 o;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x8*>(p) = o;
+}
+__device__ __forceinline__ void st8(float* p, const float (&v)[8]) {
+  f32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[i + 4]; }
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+
 template <typename Tx, typename Tdz, typename Tp, typename Tout, bool PF>
 __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t rows_per_wave,
                                                      const Tx* __restrict__ x, const uint8_t* __restrict__ g,
@@ -267,12 +292,10 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
       for (int c = 0; c < 2; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nch) {
+          ld8(x + row * d + ch * 8, v[c]);
+          ld8(dz + row * d + ch * 8, dv[c]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            v[c][i] = to_f32(x[row * d + ch * 8 + i]);
-            dv[c][i] = to_f32(dz[row * d + ch * 8 + i]);
-            s1 += v[c][i];
-          }
+          for (int i = 0; i < 8; ++i) s1 += v[c][i];
         }
       }
       const float mean = wave_sum(s1) * inv_d;
@@ -288,10 +311,12 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
       for (int c = 0; c < 2; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nch) {
+          float gm[8];
+          ld8(gamma + grp * d + ch * 8, gm);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const float xh = (v[c][i] - mean) * rstd;
-            const float dxh = dv[c][i] * to_f32(gamma[grp * d + ch * 8 + i]);
+            const float dxh = dv[c][i] * gm[i];
             ag[c][i] += dv[c][i] * xh;
             ab[c][i] += dv[c][i];
             sa += dxh;
@@ -306,13 +331,12 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
       for (int c = 0; c < 2; ++c) {
         const int ch = lane + 64 * c;
         if (ch < nch) {
+          float rr[8] = {};
+          if (resid) ld8(resid + row * d + ch * 8, rr);
+          float o[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int64_t idx = row * d + ch * 8 + i;
-            float o = (dv[c][i] - ma - v[c][i] * mb) * rstd;
-            if (resid) o += resid[idx];
-            dx[idx] = cvt<Tout>(o);
-          }
+          for (int i = 0; i < 8; ++i) o[i] = (dv[c][i] - ma - v[c][i] * mb) * rstd + rr[i];
+          st8(dx + row * d + ch * 8, o);
         }
       }
     }
@@ -327,12 +351,13 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
       for (int cc = 0; cc < 2; ++cc) {
         const int ch = lane + 64 * cc;
         if (ch < nch && row < r1) {
+          ld8(x + row * d + ch * 8, a[cc]);
+          ld8(dz + row * d + ch * 8, b[cc]);
+          if (resid) {
+            ld8(resid + row * d + ch * 8, c[cc]);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int64_t idx = row * d + ch * 8 + i;
-            a[cc][i] = to_f32(x[idx]);
-            b[cc][i] = to_f32(dz[idx]);
-            if (PF) c[cc][i] = resid ? resid[idx] : 0.f;
+            for (int i = 0; i < 8; ++i) c[cc][i] = 0.f;
           }
         }
       }
@@ -376,10 +401,12 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
       for (int cc = 0; cc < 2; ++cc) {
         const int ch = lane + 64 * cc;
         if (ch < nch) {
+          float gm[8];
+          ld8(gamma + grp * d + ch * 8, gm);
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const float xh = (v[cc][i] - mean) * rstd;
-            const float dxh = dv[cc][i] * to_f32(gamma[grp * d + ch * 8 + i]);
+            const float dxh = dv[cc][i] * gm[i];
             ag[cc][i] += dv[cc][i] * xh;
             ab[cc][i] += dv[cc][i];
             sa += dxh;
@@ -394,12 +421,10 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
       for (int cc = 0; cc < 2; ++cc) {
         const int ch = lane + 64 * cc;
         if (ch < nch) {
+          float o[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int64_t idx = row * d + ch * 8 + i;
-            const float r = PF ? rs[cc][i] : (resid ? resid[idx] : 0.f);
-            dx[idx] = cvt<Tout>((dv[cc][i] - ma - v[cc][i] * mb) * rstd + r);
-          }
+          for (int i = 0; i < 8; ++i) o[i] = (dv[cc][i] - ma - v[cc][i] * mb) * rstd + rs[cc][i];
+          st8(dx + row * d + ch * 8, o);
         }
       }
     }
