@@ -426,8 +426,8 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
   // MLP2 and the SiLU: dhid = dout W2, da = dhid (.) silu'(a) (in bf16 inside the GEMM's
   // epilogue), with hid = silu(a) replacing a; then dW2 = dout^T hid, db2 = sum dout
   const void* dout = dx_out;
-  if (act) {
-    MTGR_BWD_TRY(launch_convert(T * d, act, dx_out, at<void>(ws, pl.dout), s));
+  if (act) {   // bf16 copy of dout; db2 = its column sums, taken from the fp32 values on the way
+    MTGR_BWD_TRY(launch_convert_colsum(T, d, dx_out, at<bf16>(ws, pl.dout), at<float>(ws, pl.cs), g->b_mlp2, s));
     dout = at<void>(ws, pl.dout);
   }
   MTGR_BWD_TRY(launch_transpose(d, h, d, 0, act, p->w_mlp2, wt, s));
@@ -438,7 +438,7 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
     MTGR_BWD_TRY(linear(T, h, d, dt, MTGR_EPI_STORE, dout, wt, nullptr, nullptr, dhid, s));
     MTGR_BWD_TRY(launch_silu_bwd(T * h, act, a, dhid, s));
   }
-  MTGR_BWD_TRY(weight_grad(pl, 0, ws, dt, T, d, h, dout, a, g->w_mlp2, g->b_mlp2, s));
+  MTGR_BWD_TRY(weight_grad(pl, 0, ws, dt, T, d, h, dout, a, g->w_mlp2, act ? nullptr : g->b_mlp2, s));
   // MLP1: dz = da W1, dW1 = da^T z, db1 = sum da
   MTGR_BWD_TRY(launch_transpose(h, d, h, 0, act, p->w_mlp1, wt, s));
   MTGR_BWD_TRY(linear(T, d, h, dt, MTGR_EPI_STORE, dhid, wt, nullptr, nullptr, dz, s));

@@ -547,6 +547,40 @@ __global__ __launch_bounds__(128) void k_attn_bwd_kv(
   }
 }
 
+// fp32 -> bf16 conversion of a [T][M] matrix fused with the column sums of the fp32 values, in the
+// layout of k_colsum_bf16 (per-block partials, fixed-order reduction); part NULL: conversion only
+__global__ __launch_bounds__(256) void k_convert_colsum(int64_t T, int M, int64_t rpb, const float* __restrict__ src,
+                                                        bf16* __restrict__ dst, float* __restrict__ part) {
+  __shared__ float accw[4][512];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c0 = blockIdx.y * 512 + lane * 8;
+  const int64_t r0 = (int64_t)blockIdx.x * rpb, r1 = min(T, r0 + rpb);
+  float acc[8] = {};
+  if (c0 < M) {
+    for (int64_t r = r0 + w; r < r1; r += 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src + r * M + c0);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(src + r * M + c0 + 4);
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[e] += a[e];
+        acc[e + 4] += b[e];
+        o[e] = (bf16)a[e];
+        o[e + 4] = (bf16)b[e];
+      }
+      *reinterpret_cast<bf16x8*>(dst + r * M + c0) = o;
+    }
+  }
+  if (!part) return;                                   // block-uniform
+#pragma unroll
+  for (int e = 0; e < 8; ++e) accw[w][lane * 8 + e] = acc[e];
+  __syncthreads();
+  for (int c = threadIdx.x; c < 512; c += 256) {
+    const int col = blockIdx.y * 512 + c;
+    if (col < M) part[(int64_t)blockIdx.x * M + col] = ((accw[0][c] + accw[1][c]) + accw[2][c]) + accw[3][c];
+  }
+}
+
 inline unsigned ew_grid(int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 16384); }
 
 }  // namespace
@@ -573,6 +607,19 @@ hipError_t launch_silu_bwd(int64_t n, int kind, void* a, void* dh, hipStream_t s
   else if (kind == 1) k_silu_bwd<bf16><<<ew_grid(n), 256, 0, s>>>(n, static_cast<bf16*>(a), static_cast<bf16*>(dh));
   else k_silu_bwd<float><<<ew_grid(n), 256, 0, s>>>(n, static_cast<float*>(a), static_cast<float*>(dh));
   return hipGetLastError();
+}
+
+hipError_t launch_convert_colsum(int64_t T, int M, const float* src, bf16* dst, float* part, float* out,
+                                hipStream_t s) {
+  if (T == 0 || M == 0) return hipSuccess;
+  if (M % 8 != 0) return hipErrorInvalidValue;
+  const int nrb = colsum_blocks(T, M);
+  const int64_t rpb = (T + nrb - 1) / nrb;
+  k_convert_colsum<<<dim3((unsigned)nrb, (unsigned)((M + 511) / 512)), 256, 0, s>>>(T, M, rpb, src, dst,
+                                                                                   out ? part : nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !out) return e;
+  return launch_reduce(M, nrb, M, part, out, s);
 }
 
 int colsum_blocks(int64_t T, int M) {

@@ -114,6 +114,10 @@ hipError_t launch_gemm_bf16_kmajor_splitk(int M, int N, int64_t Kp, int ksplit, 
 // then out[m] = their sum in block order (deterministic); part holds colsum_blocks(T, M) * M floats
 int colsum_blocks(int64_t T, int M);
 hipError_t launch_colsum_bf16(int64_t T, int M, const bf16* src, float* part, float* out, hipStream_t s);
+// dst = bf16(src) for an fp32 [T][M] matrix and, when out is not NULL, out[m] = the column sums of
+// src (fp32, the same partial layout and order as launch_colsum_bf16)
+hipError_t launch_convert_colsum(int64_t T, int M, const float* src, bf16* dst, float* part, float* out,
+                                 hipStream_t s);
 hipError_t launch_gemm_f32_splitk(int64_t M, int N, int K, int ksplit, const float* a, const float* w,
                                   float* part, hipStream_t s);
 
