@@ -7,15 +7,18 @@
 // With `shared` set every token takes gamma[0], beta[0]: one plain LayerNorm, the ablation
 // without GroupLN (marovi.ai MTGR page, 方法, GLN paragraph).
 //
-// Mapping: one 64-lane wavefront per token row, four rows per 256-thread workgroup.  Each lane
-// holds up to two 8-element chunks of the row in registers (d <= 1024), so the row is read from
-// HBM once; mean and variance are two wavefront reductions over registers (two-pass, fp32).
+// Mapping: one 64-lane wavefront per two token rows (both rows' loads in flight together), four
+// wavefronts per 256-thread workgroup.  Each lane holds up to two 8-element chunks of a row in
+// registers (d <= 1024), so the row is read from HBM once; mean and variance are two wavefront
+// reductions over registers (two-pass, fp32).
 // The kernel is HBM-bound: it moves (in_bytes + out_bytes) * d per token.
 #include "kernels.h"
 
 namespace mtgr {
 
 namespace {
+
+constexpr int kRowsPerWave = 2;   // rows a wavefront normalises together (their loads overlap)
 
 __device__ __forceinline__ void load8(const float* p, float v[8]) {
   f32x4 a = *reinterpret_cast<const f32x4*>(p);
@@ -48,54 +51,83 @@ __global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __
                                                  const Tp* __restrict__ gamma,
                                                  const Tp* __restrict__ beta, float eps,
                                                  int gmask, Tout* __restrict__ y) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
   const int lane = threadIdx.x & 63;
-  if (row >= T) return;
+  if (row0 >= T) return;
   const int nch = d >> 3;
-  const Tin* xr = x + row * d;
-  float v[2][8];
-  float s = 0.f;
+  // every row's loads are issued before the first reduction, so each wavefront keeps
+  // kRowsPerWave rows in flight
+  float v[kRowsPerWave][2][8];
+  float s[kRowsPerWave];
+  int grp[kRowsPerWave];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch < nch) {
-      load8(xr + ch * 8, v[c]);
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int64_t row = row0 + r;
+    s[r] = 0.f;
+    grp[r] = 0;
+    if (row < T) {
+      const Tin* xr = x + row * d;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s += v[c][i];
+      for (int c = 0; c < 2; ++c) {
+        const int ch = lane + 64 * c;
+        if (ch < nch) load8(xr + ch * 8, v[r][c]);
+      }
+      // gmask 3: the token's group (ids outside 0..3 are rejected by validation; this stays in
+      // bounds regardless); gmask 0: row 0 for every token
+      grp[r] = g[row] & gmask;
     }
   }
   const float inv_d = 1.0f / (float)d;
-  const float mean = wave_sum(s) * inv_d;
-  float q = 0.f;
+  float mean[kRowsPerWave], rstd[kRowsPerWave];
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch < nch) {
+  for (int r = 0; r < kRowsPerWave; ++r) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float e = v[c][i] - mean;
-        q += e * e;
+    for (int c = 0; c < 2; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch && row0 + r < T) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s[r] += v[r][c][i];
       }
     }
   }
-  const float var = wave_sum(q) * inv_d;
-  const float rstd = 1.0f / sqrtf(var + eps);
-  // gmask 3: the token's group (ids outside 0..3 are rejected by validation; this stays in
-  // bounds regardless); gmask 0: row 0 for every token
-  const int grp = g[row] & gmask;
-  const Tp* gr = gamma + (int64_t)grp * d;
-  const Tp* br = beta + (int64_t)grp * d;
-  Tout* yr = y + row * d;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int ch = lane + 64 * c;
-    if (ch < nch) {
-      float ga[8], be[8], o[8];
-      load8(gr + ch * 8, ga);
-      load8(br + ch * 8, be);
+  for (int r = 0; r < kRowsPerWave; ++r) mean[r] = wave_sum(s[r]) * inv_d;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = (v[c][i] - mean) * rstd * ga[i] + be[i];
-      store8(yr + ch * 8, o);
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch && row0 + r < T) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float e = v[r][c][i] - mean[r];
+          q += e * e;
+        }
+      }
+    }
+    s[r] = q;
+  }
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) rstd[r] = 1.0f / sqrtf(wave_sum(s[r]) * inv_d + eps);
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int64_t row = row0 + r;
+    if (row >= T) break;
+    const Tp* gr = gamma + (int64_t)grp[r] * d;
+    const Tp* br = beta + (int64_t)grp[r] * d;
+    Tout* yr = y + row * d;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const int ch = lane + 64 * c;
+      if (ch < nch) {
+        float ga[8], be[8], o[8];
+        load8(gr + ch * 8, ga);
+        load8(br + ch * 8, be);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (v[r][c][i] - mean[r]) * rstd[r] * ga[i] + be[i];
+        store8(yr + ch * 8, o);
+      }
     }
   }
 }
@@ -104,7 +136,8 @@ template <typename Tin, typename Tout, typename Tp>
 hipError_t run(int64_t T, int d, const void* x, const uint8_t* g, const void* gamma,
                const void* beta, float eps, int gmask, void* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  const int64_t blocks = (T + 3) / 4;
+  const int64_t rows_per_block = 4 * kRowsPerWave;
+  const int64_t blocks = (T + rows_per_block - 1) / rows_per_block;
   k_groupln<Tin, Tout, Tp><<<(unsigned)blocks, 256, 0, s>>>(
       T, d, static_cast<const Tin*>(x), g, static_cast<const Tp*>(gamma),
       static_cast<const Tp*>(beta), eps, gmask, static_cast<Tout*>(y));

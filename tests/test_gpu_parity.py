@@ -162,6 +162,32 @@ def test_groupln_parity(kin, kout, d, shared):
     assert rel_err(to_np(y), ref) < tol
 
 
+# a token count that is not a multiple of the rows one workgroup normalises (8: two per wavefront),
+# so the last wavefront holds a single row
+@pytest.mark.parametrize("kin,kout,d", [(0, 1, 768), (1, 1, 768), (0, 0, 64)])
+def test_groupln_ragged_rows(kin, kout, d):
+    b = custom_batch(EDGE_LENGTHS + [(0, 3, 0, 0)], d, 2, "f32")
+    assert b.num_tokens % 8 == 3
+    db = M.DeviceBatch(b)
+    rng = np.random.default_rng(4)
+    gamma = synth.round_to_bf16(rng.uniform(0.5, 1.5, (4, d)).astype(np.float32))
+    beta = synth.round_to_bf16(rng.uniform(-0.1, 0.1, (4, d)).astype(np.float32))
+    x = b.x * rng.uniform(0.2, 5.0, (b.num_tokens, 1)).astype(np.float32) - 0.5
+    if kin == 1:
+        x = synth.round_to_bf16(x)
+    tin = torch.bfloat16 if kin else torch.float32
+    tout = torch.bfloat16 if kout else torch.float32
+    tp = torch.bfloat16 if kout else torch.float32
+    y = torch.full((b.num_tokens + 1, d), 7.0, dtype=tout, device=DEV)   # one guard row past the end
+    M.mtgr_groupln_fwd(db, d, kin, kout, kout, M.MTGR_NORM_GROUP, torch.from_numpy(gamma).to(DEV).to(tp),
+                       torch.from_numpy(beta).to(DEV).to(tp), 1e-5, torch.from_numpy(x).to(DEV).to(tin), y)
+    out = to_np(y)
+    ref = O.group_layer_norm(x, b.group_ids, gamma, beta, 1e-5, shared=False)
+    tol = TOL_F32 if kout == 0 else TOL_BF16_KERNEL
+    assert rel_err(out[:-1], ref) < tol
+    assert np.all(out[-1] == 7.0), "the row past the last token was written"
+
+
 # N > 4096 takes the per-tile bias slice path; N % 256 != 0 leaves a ragged last column tile
 @pytest.mark.parametrize("M_,N,K,epi,with_bias", [
     (1000, 256, 128, 0, True), (3001, 96, 256, 1, True), (777, 768, 3072, 2, True),
