@@ -123,6 +123,17 @@ mtgr_status check_attn_shape(int32_t d, int32_t H, int32_t dtype) {
   return MTGR_OK;
 }
 
+// The bf16 attention kernels reach one user's rows of a head through 32-bit buffer offsets; the
+// widest rows they address are the QKVU rows (4d bf16 values, 8d bytes), so one user's rows must
+// span less than 2^31 bytes: at d = 768, users of up to 349,525 tokens.
+mtgr_status check_user_rows(const mtgr_batch* b, int32_t d, int32_t dtype) {
+  if (dtype != MTGR_BF16) return MTGR_OK;
+  int64_t longest = 0;
+  for (int32_t i = 0; i < b->num_users; ++i)
+    longest = std::max(longest, b->offsets_host[i + 1] - b->offsets_host[i]);
+  return longest * 8 * (int64_t)d < ((int64_t)1 << 31) ? MTGR_OK : MTGR_ERR_BAD_SHAPE;
+}
+
 inline bool mask_mode_ok(int32_t m) { return m >= MTGR_MASK_DYNAMIC && m <= MTGR_MASK_FULL; }
 inline bool norm_mode_ok(int32_t m) { return m == MTGR_NORM_GROUP || m == MTGR_NORM_SHARED; }
 
@@ -486,6 +497,7 @@ mtgr_status mtgr_encoder_workspace_size(const mtgr_encoder_params* p, const mtgr
   mtgr_status st = check_encoder(p);
   if (st != MTGR_OK) return st;
   if ((st = check_batch(b)) != MTGR_OK) return st;
+  if ((st = check_user_rows(b, p->layers[0].d_model, p->layers[0].dtype)) != MTGR_OK) return st;
   Sizes z = sizes_for(b, p->layers[0].d_model, 0, p->head_hidden, p->layers[0].dtype,
                       p->layers[0].num_heads);
   for (int32_t l = 0; l < p->num_layers; ++l) z.h = std::max(z.h, (int)p->layers[l].mlp_hidden);
@@ -500,6 +512,7 @@ mtgr_status mtgr_block_workspace_size(const mtgr_block_params* p, const mtgr_bat
   mtgr_status st = check_block(p);
   if (st != MTGR_OK) return st;
   if ((st = check_batch(b)) != MTGR_OK) return st;
+  if ((st = check_user_rows(b, p->d_model, p->dtype)) != MTGR_OK) return st;
   Sizes z = sizes_for(b, p->d_model, p->mlp_hidden, 0, p->dtype, p->num_heads);
   z.need_acts = true;
   *bytes = make_plan(z).total;
@@ -523,6 +536,7 @@ mtgr_status mtgr_block_bwd_workspace_size(const mtgr_block_params* p, const mtgr
   mtgr_status st = check_block(p);
   if (st != MTGR_OK) return st;
   if ((st = check_batch(b)) != MTGR_OK) return st;
+  if ((st = check_user_rows(b, p->d_model, p->dtype)) != MTGR_OK) return st;
   // a bound on the workspace; the bf16 weight-gradient GEMMs also need split counts that keep each
   // split's activation rows within a 32-bit buffer range
   if (b->num_tokens > kMaxBwdTokens) return MTGR_ERR_BAD_SHAPE;
@@ -567,6 +581,7 @@ mtgr_status mtgr_attention_bwd_workspace_size(const mtgr_batch* b, int32_t d, in
   mtgr_status st = check_batch(b);
   if (st != MTGR_OK) return st;
   if ((st = check_attn_shape(d, num_heads, dtype)) != MTGR_OK) return st;
+  if ((st = check_user_rows(b, d, dtype)) != MTGR_OK) return st;
   Sizes z = sizes_for(b, d, 0, 0, dtype, num_heads);
   *bytes = make_plan(z).total + align_up((size_t)b->num_tokens * d * esize(dtype));
   return MTGR_OK;
@@ -689,6 +704,7 @@ mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads
   mtgr_status st = mtgr_attention_workspace_size(b, d, num_heads, &need);
   if (st != MTGR_OK) return st;
   if ((st = check_attn_shape(d, num_heads, dtype)) != MTGR_OK) return st;
+  if ((st = check_user_rows(b, d, dtype)) != MTGR_OK) return st;
   if (!mask_mode_ok(mask_mode)) return MTGR_ERR_UNSUPPORTED;
   if (!ws || ws_bytes < need) return MTGR_ERR_WORKSPACE;
   if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;

@@ -57,7 +57,8 @@ extern "C" {
 typedef enum {
   MTGR_OK = 0,
   MTGR_ERR_NULL_ARG = 1,     /* a required pointer is NULL */
-  MTGR_ERR_BAD_SHAPE = 2,    /* d, H, h, M, N, K out of the supported set */
+  MTGR_ERR_BAD_SHAPE = 2,    /* d, H, h, M, N, K out of the supported set; also, in bf16, a user
+                                whose QKVU rows span 2^31 bytes or more (8 d bytes per token) */
   MTGR_ERR_BAD_BATCH = 3,    /* offsets not monotone, T or C inconsistent, bad group order */
   MTGR_ERR_UNSUPPORTED = 4,  /* dtype / epilogue / option not implemented */
   MTGR_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the reported size */

@@ -79,6 +79,21 @@ def test_block_workspace_size_and_shape_checks():
     assert _ws_size(_block(norm_mode=2), b)[0] == 4          # unknown norm mode
 
 
+def test_user_row_span_limit():
+    # bf16 attention addresses one user's QKVU rows (8 d bytes each) through 32-bit offsets
+    d = 768
+    longest_ok = ((1 << 31) - 1) // (8 * d)            # 349,525 tokens at d = 768
+    b, _keep = _batch([0, 10, 10 + longest_ok])
+    assert _ws_size(_block(d=d, H=6, h=3072), b)[0] == 0
+    b, _keep = _batch([0, 10, 10 + longest_ok + 1])
+    assert _ws_size(_block(d=d, H=6, h=3072), b)[0] == 2
+    n = ctypes.c_size_t(0)
+    assert M.lib().mtgr_block_bwd_workspace_size(ctypes.byref(_block(d=d, H=6, h=3072)), ctypes.byref(b),
+                                                 ctypes.byref(n)) == 2
+    # fp32 storage indexes rows with 64-bit arithmetic: no such limit
+    assert _ws_size(_block(d=d, H=6, h=3072, dtype=M.MTGR_F32), b)[0] == 0
+
+
 @pytest.mark.parametrize("offsets,T,code", [
     ([0, 10, 5], None, 3),        # decreasing offsets
     ([1, 10, 30], None, 3),       # offsets[0] != 0
