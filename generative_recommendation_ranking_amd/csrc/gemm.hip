@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   constexpr int BM = 256, BN = 256, BK = 64, NT = 64 * WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int LP = BK + 8, CPR = BK / 8;
-  constexpr int CA = BM * CPR / NT, CB = BN * CPR / NT;   // 8 and 8 chunks per thread
+  constexpr int CA = BM * CPR / NT, CB = BN * CPR / NT;   // 4 and 4 chunks per thread
   constexpr int RSTEP = NT / CPR;                          // rows covered by one chunk index
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
