@@ -659,10 +659,9 @@ hipError_t launch_reduce_wb(int M, int K, int Kx, int nsplit, const float* part,
   return hipGetLastError();
 }
 
-// wavefronts of the GroupLN backward: one slot [2][4][d] of partial parameter gradients each
-// wavefronts of the GroupLN backward (one slot of partial parameter gradients each): one round of
-// resident wavefronts on 256 CUs -- the fp32-input variant (prefetching, ~185 VGPRs) holds 2 per
-// SIMD, the bf16 one (~120 VGPRs) 4
+// Wavefronts of the GroupLN backward, each with one slot [2][4][d] of partial parameter gradients:
+// one round of resident wavefronts on 256 CUs -- the fp32-input variant (prefetching, ~185 VGPRs)
+// holds 2 per SIMD, the bf16 one (~120 VGPRs) 4
 int groupln_bwd_waves(int64_t T, int x_kind) {
   const int64_t cap = x_kind == 0 ? 512 : 1024;
   return 4 * (int)std::max<int64_t>(1, std::min<int64_t>(cap, (T + 255) / 256));
