@@ -11,179 +11,13 @@
 #include "kernels.h"
 
 using namespace mtgr;
+using namespace mtgr::plan;
 
 namespace {
-
-constexpr size_t kAlign = 256;
-inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
-
-inline int esize(int dtype) { return dtype == MTGR_BF16 ? 2 : 4; }
-
-struct Plan {
-  size_t seg = 0, order = 0, tile_off = 0, cand_off = 0, cand_idx = 0, flags = 0, xcd_off = 0;
-  size_t xt = 0, big = 0, y = 0, xres = 0, hin = 0, hhid = 0;
-  size_t total = 0;
-};
-
-struct Sizes {
-  int64_t B = 0, T = 0, C = 0;
-  int d = 0, h = 0, hh = 0, dtype = MTGR_F32, H = 0;
-  bool need_xres = false, need_head = false, need_acts = false;
-};
-
-Plan make_plan(const Sizes& z) {
-  Plan p;
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    size_t at = off;
-    off += align_up(bytes);
-    return at;
-  };
-  const size_t es = esize(z.dtype);
-  p.flags = take(4 * sizeof(int32_t));
-  p.seg = take((size_t)z.B * sizeof(UserSeg));
-  p.order = take((size_t)z.B * sizeof(int32_t));
-  p.tile_off = take((size_t)(z.B + 1) * sizeof(int32_t));
-  p.cand_off = take((size_t)(z.B + 1) * sizeof(int64_t));
-  p.cand_idx = take((size_t)z.C * sizeof(int64_t));
-  const int64_t rounds = (z.B * z.H + kXcdCount - 1) / kXcdCount;
-  p.xcd_off = take((size_t)kXcdCount * (rounds + 1) * sizeof(int32_t));
-  if (z.need_acts) {
-    p.xt = take((size_t)z.T * z.d * es);
-    p.big = take((size_t)z.T * std::max(4 * z.d, z.h) * es);
-    p.y = take((size_t)z.T * z.d * es);
-  }
-  if (z.need_xres) p.xres = take((size_t)z.T * z.d * sizeof(float));
-  if (z.need_head) {
-    p.hin = take((size_t)z.C * z.d * es);
-    p.hhid = take((size_t)z.C * z.hh * es);
-  }
-  p.total = off;
-  return p;
-}
 
 template <typename T>
 inline T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
-}
-
-mtgr_status check_batch(const mtgr_batch* b) {
-  if (!b) return MTGR_ERR_NULL_ARG;
-  if (b->num_users < 0 || b->num_tokens < 0 || b->num_candidates < 0) return MTGR_ERR_BAD_BATCH;
-  if (b->num_users == 0) return (b->num_tokens == 0 && b->num_candidates == 0) ? MTGR_OK : MTGR_ERR_BAD_BATCH;
-  if (!b->offsets_host || !b->offsets) return MTGR_ERR_NULL_ARG;
-  if (b->num_tokens > 0 && (!b->group_ids || !b->timestamps)) return MTGR_ERR_NULL_ARG;
-  const int64_t* o = b->offsets_host;
-  if (o[0] != 0) return MTGR_ERR_BAD_BATCH;
-  for (int32_t i = 0; i < b->num_users; ++i) {
-    if (o[i + 1] < o[i]) return MTGR_ERR_BAD_BATCH;
-    if (o[i + 1] - o[i] > (int64_t)(1 << 30)) return MTGR_ERR_BAD_BATCH;
-  }
-  if (o[b->num_users] != b->num_tokens) return MTGR_ERR_BAD_BATCH;
-  if (b->num_candidates > b->num_tokens) return MTGR_ERR_BAD_BATCH;
-  return MTGR_OK;
-}
-
-int64_t total_tiles(const mtgr_batch* b, int q_tile) {
-  int64_t t = 0;
-  for (int32_t i = 0; i < b->num_users; ++i) {
-    const int64_t n = b->offsets_host[i + 1] - b->offsets_host[i];
-    t += (n + q_tile - 1) / q_tile;
-  }
-  return t;
-}
-
-// Host replica of the device-side placement (k_prep_users' LPT order, k_prep_xcd's snake deal):
-// the largest per-XCD q-tile count, which sizes the attention grid.
-int64_t xcd_grid_slots(const mtgr_batch* b, int H, int q_tile) {
-  const int32_t B = b->num_users;
-  std::vector<int32_t> order(B);
-  for (int32_t i = 0; i < B; ++i) order[i] = i;
-  auto len = [&](int32_t u) { return b->offsets_host[u + 1] - b->offsets_host[u]; };
-  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return len(x) > len(y); });
-  const int64_t G = (int64_t)B * H;
-  int64_t tot[kXcdCount] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t g = 0; g < G; ++g) {
-    const int64_t k = g / kXcdCount, r = g % kXcdCount;
-    const int x = (int)((k & 1) ? (kXcdCount - 1 - r) : r);
-    tot[x] += (len(order[g / H]) + q_tile - 1) / q_tile;
-  }
-  return *std::max_element(tot, tot + kXcdCount);
-}
-
-bool dh_ok(int dtype, int dh) {
-  if (dtype == MTGR_BF16) return dh == 64 || dh == 128;
-  return dh == 32 || dh == 64 || dh == 128;
-}
-
-mtgr_status check_attn_shape(int32_t d, int32_t H, int32_t dtype) {
-  if (dtype != MTGR_F32 && dtype != MTGR_BF16) return MTGR_ERR_UNSUPPORTED;
-  if (d <= 0 || H <= 0 || d % H != 0 || d > 1024) return MTGR_ERR_BAD_SHAPE;
-  if (!dh_ok(dtype, d / H)) return MTGR_ERR_BAD_SHAPE;
-  return MTGR_OK;
-}
-
-// The bf16 attention kernels reach one user's rows of a head through 32-bit buffer offsets; the
-// widest rows they address are the QKVU rows (4d bf16 values, 8d bytes), so one user's rows must
-// span less than 2^31 bytes: at d = 768, users of up to 349,525 tokens.
-mtgr_status check_user_rows(const mtgr_batch* b, int32_t d, int32_t dtype) {
-  if (dtype != MTGR_BF16) return MTGR_OK;
-  int64_t longest = 0;
-  for (int32_t i = 0; i < b->num_users; ++i)
-    longest = std::max(longest, b->offsets_host[i + 1] - b->offsets_host[i]);
-  return longest * 8 * (int64_t)d < ((int64_t)1 << 31) ? MTGR_OK : MTGR_ERR_BAD_SHAPE;
-}
-
-inline bool mask_mode_ok(int32_t m) { return m >= MTGR_MASK_DYNAMIC && m <= MTGR_MASK_FULL; }
-inline bool norm_mode_ok(int32_t m) { return m == MTGR_NORM_GROUP || m == MTGR_NORM_SHARED; }
-
-mtgr_status check_block(const mtgr_block_params* p) {
-  if (!p) return MTGR_ERR_NULL_ARG;
-  mtgr_status st = check_attn_shape(p->d_model, p->num_heads, p->dtype);
-  if (st != MTGR_OK) return st;
-  if (!mask_mode_ok(p->mask_mode) || !norm_mode_ok(p->norm_mode)) return MTGR_ERR_UNSUPPORTED;
-  const int mult = p->dtype == MTGR_BF16 ? 64 : 8;
-  if (p->d_model % mult != 0 || p->mlp_hidden <= 0 || p->mlp_hidden % mult != 0 ||
-      p->mlp_hidden > 8192)
-    return MTGR_ERR_BAD_SHAPE;
-  if (p->dtype == MTGR_BF16 && (p->d_model < 128 || p->mlp_hidden < 128))
-    return MTGR_ERR_BAD_SHAPE;   // the bf16 GEMM pipeline needs at least two 64-wide K slabs
-  if (!(p->ln_eps >= 0.f) || !std::isfinite(p->ln_eps)) return MTGR_ERR_BAD_SHAPE;
-  if (!p->gln1_gamma || !p->gln1_beta || !p->w_qkvu || !p->gln2_gamma || !p->gln2_beta ||
-      !p->w_mlp1 || !p->w_mlp2)
-    return MTGR_ERR_NULL_ARG;
-  return MTGR_OK;
-}
-
-mtgr_status check_encoder(const mtgr_encoder_params* p) {
-  if (!p || !p->layers) return MTGR_ERR_NULL_ARG;
-  if (p->num_layers < 1) return MTGR_ERR_BAD_SHAPE;
-  for (int32_t l = 0; l < p->num_layers; ++l) {
-    mtgr_status st = check_block(&p->layers[l]);
-    if (st != MTGR_OK) return st;
-    if (p->layers[l].d_model != p->layers[0].d_model ||
-        p->layers[l].num_heads != p->layers[0].num_heads ||
-        p->layers[l].dtype != p->layers[0].dtype)
-      return MTGR_ERR_BAD_SHAPE;
-  }
-  const int mult = p->layers[0].dtype == MTGR_BF16 ? 32 : 8;
-  if (p->head_hidden <= 0 || p->head_hidden % mult != 0 || p->head_hidden > 8192)
-    return MTGR_ERR_BAD_SHAPE;
-  if (!p->w_head1 || !p->w_head2) return MTGR_ERR_NULL_ARG;
-  return MTGR_OK;
-}
-
-Sizes sizes_for(const mtgr_batch* b, int d, int h, int hh, int dtype, int H) {
-  Sizes z;
-  z.H = H;
-  z.B = b->num_users;
-  z.T = b->num_tokens;
-  z.C = b->num_candidates;
-  z.d = d;
-  z.h = h;
-  z.hh = hh;
-  z.dtype = dtype;
-  return z;
 }
 
 PrepBufs prep_bufs(void* ws, const Plan& p) {
@@ -274,93 +108,6 @@ hipError_t run_block(const mtgr_block_params* p, const mtgr_batch* b, const Prep
 }
 
 // ---- backward ----------------------------------------------------------------------------------
-// Workspace of mtgr_block_bwd after the prep buffers: the recomputed forward activations, the
-// activation gradients, in fp32 transposed copies for the weight-gradient GEMMs (token axis last,
-// padded to Tp with zeros, plus a ones row whose product gives the bias gradient), one transposed
-// weight, and fp32 partial sums (split-K slices of the weight gradients, per-wavefront GroupLN slots).
-struct BwdPlan {
-  Plan prep;
-  size_t xt = 0, qkvu = 0, y = 0, vt = 0, z = 0, a = 0, dout = 0, dhid = 0, dz = 0;
-  size_t dqkvu = 0, ta = 0, tb = 0, wt = 0, part = 0, cs = 0, gpart = 0, total = 0;
-  // per weight-gradient GEMM (0: W2, 1: W1, 2: W_qkvu): split count and padded token axis
-  int ks[3] = {1, 1, 1};
-  int64_t Tp[3] = {0, 0, 0};
-  bool ok = true;   // every bf16 split within a 32-bit buffer range
-};
-
-constexpr int64_t kMaxBwdTokens = 4000000;
-constexpr int64_t kGemmWorkgroups = 256;   // persistent GEMM grid: one workgroup per CU of an MI355X
-
-inline int64_t tiles256(int64_t M, int64_t N) { return ((M + 255) / 256) * ((N + 255) / 256); }
-
-BwdPlan make_bwd_plan(const Sizes& z) {
-  BwdPlan p;
-  p.prep = make_plan(z);
-  size_t off = p.prep.total;
-  auto take = [&](size_t bytes) {
-    size_t at = off;
-    off += align_up(bytes);
-    return at;
-  };
-  const size_t es = esize(z.dtype);
-  const size_t T = (size_t)z.T, d = (size_t)z.d, h = (size_t)z.h;
-  // Split count of each weight-gradient GEMM.  The persistent GEMM runs one workgroup per CU.  bf16
-  // (k-major GEMM, no bias column): with at least 8 x 2048 tokens the split count is a multiple of
-  // the XCD count (each split's tiles share one XCD's L2), chosen for whole rounds of each XCD's
-  // workgroups, at most 64; below that 1..7 splits for whole rounds of the grid.  fp32 (transposed
-  // operands with a ones row): 1..32 splits for whole rounds of the grid.  Each split is at least
-  // 2048 tokens long, one split's rows stay within a 32-bit buffer range, ties go to fewer splits.
-  const bool bf = z.dtype == MTGR_BF16;
-  const int64_t Mg[3] = {(int64_t)d, (int64_t)h, 4 * (int64_t)d};
-  const int64_t Kg[3] = {(int64_t)h, (int64_t)d, (int64_t)d};
-  const int64_t per_xcd = kGemmWorkgroups / 8;
-  int64_t tp_max = 0;
-  size_t part_max = 0, cs_max = 0;
-  for (int gi = 0; gi < 3; ++gi) {
-    const int64_t tiles = tiles256(Mg[gi], Kg[gi] + (bf ? 0 : 8));
-    const bool xcd_major = bf && z.T >= 8 * 2048;
-    int best = 0;
-    double best_eff = 0.0;
-    for (int ks = xcd_major ? 8 : 1; ks <= (xcd_major ? 64 : bf ? 7 : 32) && (ks == 1 || z.T >= (int64_t)ks * 2048);
-         ks += xcd_major ? 8 : 1) {
-      const int64_t unit_k = 64 * (int64_t)ks;
-      const int64_t tp_k = std::max((z.T + unit_k - 1) / unit_k * unit_k, 2 * unit_k);
-      if (bf && (tp_k / ks) * std::max(Mg[gi], Kg[gi]) * 2 >= (int64_t(1) << 31)) continue;
-      const int64_t work = xcd_major ? tiles * ks / 8 : tiles * ks;
-      const int64_t slots = xcd_major ? per_xcd : kGemmWorkgroups;
-      const int64_t rounds = (work + slots - 1) / slots;
-      const double eff = (double)work / (double)(rounds * slots);
-      if (eff > best_eff + 1e-9) { best_eff = eff; best = ks; }
-    }
-    p.ks[gi] = std::max(best, 1);
-    if (best == 0) p.ok = false;
-    const int64_t unit = 64 * (int64_t)p.ks[gi];
-    p.Tp[gi] = std::max((z.T + unit - 1) / unit * unit, 2 * unit);
-    tp_max = std::max(tp_max, p.Tp[gi]);
-    part_max = std::max(part_max, (size_t)p.ks[gi] * Mg[gi] * (Kg[gi] + (bf ? 0 : 8)));
-    if (bf) cs_max = std::max(cs_max, (size_t)colsum_blocks(z.T, (int)Mg[gi]) * Mg[gi]);
-  }
-  p.xt = take(T * d * es);
-  p.qkvu = take(T * 4 * d * es);
-  p.y = take(T * d * es);
-  p.vt = take(T * d * es);
-  p.z = take(T * d * es);
-  p.a = take(T * h * es);
-  p.dout = take(z.dtype == MTGR_BF16 ? T * d * es : 0);
-  p.dhid = take(T * h * es);
-  p.dz = take(T * d * es);
-  p.dqkvu = take(T * 4 * d * es);
-  // transposed copies for the fp32 weight-gradient GEMMs (the bf16 ones read activations in place)
-  p.ta = take(bf ? 0 : std::max({d, h, 4 * d}) * (size_t)tp_max * es);
-  p.tb = take(bf ? 0 : (std::max(d, h) + 8) * (size_t)tp_max * es);
-  p.wt = take(std::max(h * d, 4 * d * d) * es);
-  p.part = take(part_max * sizeof(float));
-  p.cs = take(cs_max * sizeof(float));
-  p.gpart = take((size_t)std::max(groupln_bwd_waves(z.T, 0), groupln_bwd_waves(z.T, 1)) * 8 * d * sizeof(float));
-  p.total = off;
-  return p;
-}
-
 // dW [M][K] (+ db [M]) = sum over tokens of dy^T x by split-K GEMMs and fixed-order reductions;
 // dy [T][M] and x [T][K] token-major.  bf16: the k-major GEMM reads them in place and db is the
 // column sum of dy.  fp32: transposed copies [M][Tp] and [K+8][Tp] (row K all ones, so that

@@ -124,7 +124,6 @@ __global__ __launch_bounds__(256) void k_silu_bwd(int64_t n, T* __restrict__ a, 
 // Block (rb, cg) sums rows [rb * rpb, +rpb) of the 512 columns cg*512 .. +511: its 4 wavefronts take
 // every 4th row each (one 16-byte chunk of 8 columns per lane, so a wavefront reads 1 KB of a row at
 // once), then the 4 wavefront sums are added in wavefront order and written to part[rb][cols].
-constexpr int kColsumRowBlocks = 2048;
 __global__ __launch_bounds__(256) void k_colsum_bf16(int64_t T, int M, int64_t rpb, const bf16* __restrict__ src,
                                                      float* __restrict__ part) {
   __shared__ float accw[4][512];
@@ -622,11 +621,6 @@ hipError_t launch_convert_colsum(int64_t T, int M, const float* src, bf16* dst, 
   return launch_reduce(M, nrb, M, part, out, s);
 }
 
-int colsum_blocks(int64_t T, int M) {
-  const int cg = (M + 511) / 512;
-  return (int)std::max<int64_t>(1, std::min<int64_t>(kColsumRowBlocks / cg, (T + 63) / 64));
-}
-
 hipError_t launch_colsum_bf16(int64_t T, int M, const bf16* src, float* part, float* out, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (M % 8 != 0) return hipErrorInvalidValue;
@@ -657,14 +651,6 @@ hipError_t launch_reduce_wb(int M, int K, int Kx, int nsplit, const float* part,
   if (M == 0) return hipSuccess;
   k_reduce_wb<<<ew_grid(n), 256, 0, s>>>(M, K, Kx, nsplit, part, dw, db);
   return hipGetLastError();
-}
-
-// Wavefronts of the GroupLN backward, each with one slot [2][4][d] of partial parameter gradients:
-// one round of resident wavefronts on 256 CUs -- the fp32-input variant (prefetching, ~185 VGPRs)
-// holds 2 per SIMD, the bf16 one (~120 VGPRs) 4
-int groupln_bwd_waves(int64_t T, int x_kind) {
-  const int64_t cap = x_kind == 0 ? 512 : 1024;
-  return 4 * (int)std::max<int64_t>(1, std::min<int64_t>(cap, (T + 255) / 256));
 }
 
 hipError_t launch_groupln_bwd(int64_t T, int d, int x_kind, int act_kind, int shared, const void* x,

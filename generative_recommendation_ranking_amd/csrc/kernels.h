@@ -6,8 +6,11 @@
 #include <stdint.h>
 
 #include "common.h"
+#include "plan.h"
 
 namespace mtgr {
+
+static_assert(sizeof(UserSeg) == kUserSegBytes, "the planner sizes the segment table");
 
 // ---- batch prep (prep.hip) ----------------------------------------------------------------
 // Segment counts per user, LPT user order (longest users first), q-tile offsets in that order,
@@ -21,7 +24,6 @@ struct PrepBufs {
   int32_t* flags;      // [4]   validation flags / counters
   int32_t* xcd_off;    // [8][R+1] per-XCD q-tile prefix over (user, head) groups, R = ceil(B*H/8)
 };
-constexpr int kXcdCount = 8;  // MI355X: 8 XCDs, workgroups dispatched round-robin by id
 hipError_t launch_prep(int32_t B, int64_t C, const int64_t* offsets, const uint8_t* group_ids,
                        int q_tile, int heads, const PrepBufs& pb, bool want_cand_idx,
                        hipStream_t s);
@@ -45,8 +47,6 @@ hipError_t launch_gemm_f32(int64_t M, int N, int K, int epi, const float* a, con
                            const float* bias, const float* resid, float* out, hipStream_t s);
 
 // ---- attention (attention.hip) -------------------------------------------------------------
-constexpr int kAttnQTileBf16 = 128;
-constexpr int kAttnQTileF32 = 64;
 // grid_slots = max over XCDs of that XCD's q-tile count (the host replica of k_prep_xcd).
 // vt (may be NULL) receives the ungated V~ for the backward pass.
 // mask_mode: kMaskDynamic / kMaskCausal / kMaskFull
@@ -74,8 +74,7 @@ hipError_t launch_reduce(int64_t n, int nsplit, int64_t stride, const float* par
 hipError_t launch_reduce_wb(int M, int K, int Kx, int nsplit, const float* part, float* dw, float* db,
                             hipStream_t s);
 // GroupLN backward: dx = GLN'(x)^T dz (+ resid); per-wavefront partials of (dgamma, dbeta)
-// [groupln_bwd_waves(T)][2][4][d]
-int groupln_bwd_waves(int64_t T, int x_kind);
+// [groupln_bwd_waves(T)][2][4][d] (plan.h)
 hipError_t launch_groupln_bwd(int64_t T, int d, int x_kind, int act_kind, int shared, const void* x,
                               const uint8_t* g, const void* gamma, float eps, const void* dz,
                               const float* resid, void* dx, int out_kind, float* part, hipStream_t s);
@@ -111,8 +110,7 @@ hipError_t launch_gemm_bf16_silu_bwd(int64_t M, int N, int K, const bf16* a, con
 hipError_t launch_gemm_bf16_kmajor_splitk(int M, int N, int64_t Kp, int ksplit, int64_t T, const bf16* a, int lda,
                                           const bf16* w, int ldb, float* part, hipStream_t s);
 // column sums of a bf16 [T][M] matrix (M % 8 == 0): per-block partials part[colsum_blocks(T, M)][M],
-// then out[m] = their sum in block order (deterministic); part holds colsum_blocks(T, M) * M floats
-int colsum_blocks(int64_t T, int M);
+// then out[m] = their sum in block order (deterministic); part holds colsum_blocks(T, M) * M floats (plan.h)
 hipError_t launch_colsum_bf16(int64_t T, int M, const bf16* src, float* part, float* out, hipStream_t s);
 // dst = bf16(src) for an fp32 [T][M] matrix and, when out is not NULL, out[m] = the column sums of
 // src (fp32, the same partial layout and order as launch_colsum_bf16)

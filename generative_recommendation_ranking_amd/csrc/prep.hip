@@ -13,8 +13,6 @@ namespace mtgr {
 
 namespace {
 
-constexpr int kLptMaxUsers = 16384;  // above this, users keep their index order
-
 __device__ int64_t lower_bound_group(const uint8_t* g, int64_t lo, int64_t hi, int v) {
   while (lo < hi) {
     int64_t mid = lo + ((hi - lo) >> 1);

@@ -16,7 +16,8 @@ from typing import List, Optional
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmtgr.so")
+# MTGR_LIB may name another build of the same library (the host-sanitized copy, for the ABI checks)
+LIB_PATH = os.environ.get("MTGR_LIB") or os.path.join(_PKG, "libmtgr.so")
 
 MTGR_OK = 0
 MTGR_F32, MTGR_BF16 = 0, 1
