@@ -43,6 +43,15 @@ isolation / temporal-replay invariants).  The readings R3, R8, R9 and R10 are pa
 respect to the paper: the pages never fix them, so they are pinned only by construction.
 The block backward (the chain rule of the same equations) is pinned by central finite differences
 of block_forward and by autograd of an independent torch formulation of the block.
+
+R19 (bf16 storage, used only to set the tolerance of the bf16 block backward): the pages train in
+bf16 mixed precision ([P3] 主要贡献 and 方法, training-framework paragraph) without saying where
+values are rounded.  block_backward_bf16_storage reads "bf16 storage" as: arithmetic in float64,
+and every tensor that is kept between two steps in the storage type -- plus the two per-pair
+factors that enter a matrix product as bf16 operands (silu(S) and the masked dS) -- rounded to
+the nearest bfloat16 (ties to even) where it is kept.  It is pinned by reducing exactly to
+block_backward when the rounding is the identity, and by the rounding itself matching torch's
+float32 -> bfloat16 conversion.
 """
 from __future__ import annotations
 
@@ -353,4 +362,111 @@ def block_backward_batch(offsets: np.ndarray, groups: np.ndarray, times: np.ndar
     if total is None:
         total = {k: np.zeros_like(np.asarray(layer[k] if layer.get(k) is not None else 0.0, dtype=np.float64))
                  for k in BLOCK_PARAM_NAMES if layer.get(k) is not None}
+    return dx, total
+
+
+# ----------------------------------------------------------------------------------------------
+# The block backward under bf16 storage (reading R19): the same chain rule as block_backward,
+# with the stored tensors rounded to bfloat16.  Test infrastructure for the bf16 tolerance only.
+# ----------------------------------------------------------------------------------------------
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """Nearest bfloat16 value of each element (via float32; ties to even), returned as float64."""
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    out = u.astype(np.uint32).view(np.float32).astype(np.float64)
+    return np.where(np.isfinite(f), out, f.astype(np.float64))
+
+
+def block_backward_bf16_storage(x: np.ndarray, groups: np.ndarray, times: np.ndarray,
+                                layer: Dict[str, np.ndarray], num_heads: int, dout: np.ndarray,
+                                eps: float = 1e-5, mask_mode: str = "dynamic", shared_norm: bool = False,
+                                store=round_bf16):
+    """block_backward for one user with `store` applied wherever a bf16 tensor is kept (R19).
+
+    Forward recompute: X~, QKVU, silu(S) as a product operand, the ungated V~ and the gated Y,
+    Z, the MLP1 pre-activation a and then silu(a).  Backward: dout, da = dhid (.) silu'(a), dz,
+    dy (the GLN2 input gradient), G = dy (.) U, the masked dS as a product operand, dQ/dK/dV/dU,
+    and dX~.  The residual stream x, dx_in and every parameter gradient are sums in float64 of
+    the stored values; db2 is the sum of the unrounded dout.  The factor 1/N is applied to the
+    product's sum (silu(S) and dS are stored without it).  With store = identity this is
+    block_backward step for step.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    n, d = x.shape
+    dh = d // num_heads
+    N = float(n)
+    M = mask(groups, times, mask_mode).astype(np.float64)
+    # forward recompute
+    xt = store(group_layer_norm(x, groups, layer["gln1_gamma"], layer["gln1_beta"], eps, shared_norm))
+    qkvu = store(linear(xt, layer["w_qkvu"], layer.get("b_qkvu")))
+    Q, K, V, U = qkvu[:, :d], qkvu[:, d:2 * d], qkvu[:, 2 * d:3 * d], qkvu[:, 3 * d:]
+    acc = np.empty((n, d))
+    S_h, P_h = [], []
+    for h in range(num_heads):
+        sl = slice(h * dh, (h + 1) * dh)
+        S = Q[:, sl] @ K[:, sl].T
+        P = store(silu(S) * M)                         # a product operand
+        acc[:, sl] = P @ V[:, sl] / N
+        S_h.append(S)
+        P_h.append(P)
+    vt = store(acc)                                    # ungated V~
+    y = store(acc * U)                                 # V~ (.) U
+    z = store(group_layer_norm(y, groups, layer["gln2_gamma"], layer["gln2_beta"], eps, shared_norm))
+    a = store(linear(z, layer["w_mlp1"], layer.get("b_mlp1")))
+    hid = store(silu(a))
+    # MLP2 and the SiLU
+    grads = {}
+    dout_s = store(dout)
+    dhid = dout_s @ np.asarray(layer["w_mlp2"], dtype=np.float64)
+    grads["w_mlp2"] = dout_s.T @ hid
+    grads["b_mlp2"] = dout.sum(axis=0)
+    da = store(dhid * silu_grad(a))
+    # MLP1
+    dz = store(da @ np.asarray(layer["w_mlp1"], dtype=np.float64))
+    grads["w_mlp1"] = da.T @ z
+    grads["b_mlp1"] = da.sum(axis=0)
+    # GLN2
+    dyg, grads["gln2_gamma"], grads["gln2_beta"] = group_layer_norm_backward(
+        y, groups, layer["gln2_gamma"], dz, eps, shared_norm)
+    dyg = store(dyg)
+    # gate and attention
+    G = store(dyg * U)
+    dqkvu = np.zeros((n, 4 * d))
+    for h in range(num_heads):
+        sl = slice(h * dh, (h + 1) * dh)
+        dP = G[:, sl] @ V[:, sl].T
+        dS = store(dP * silu_grad(S_h[h]) * M)         # a product operand
+        dqkvu[:, sl] = dS @ K[:, sl] / N
+        dqkvu[:, d + h * dh:d + (h + 1) * dh] = dS.T @ Q[:, sl] / N
+        dqkvu[:, 2 * d + h * dh:2 * d + (h + 1) * dh] = P_h[h].T @ G[:, sl] / N
+    dqkvu[:, 3 * d:] = dyg * vt
+    dqkvu = store(dqkvu)
+    # QKVU and GLN1 with the residual path
+    dxt = store(dqkvu @ np.asarray(layer["w_qkvu"], dtype=np.float64))
+    grads["w_qkvu"] = dqkvu.T @ xt
+    grads["b_qkvu"] = dqkvu.sum(axis=0)
+    dx1, grads["gln1_gamma"], grads["gln1_beta"] = group_layer_norm_backward(
+        x, groups, layer["gln1_gamma"], dxt, eps, shared_norm)
+    return dout + dx1, grads
+
+
+def block_backward_batch_bf16_storage(offsets: np.ndarray, groups: np.ndarray, times: np.ndarray,
+                                      x: np.ndarray, layer: Dict[str, np.ndarray], num_heads: int,
+                                      dout: np.ndarray, eps: float = 1e-5, mask_mode: str = "dynamic",
+                                      shared_norm: bool = False, store=round_bf16):
+    """block_backward_bf16_storage over a packed batch (dx per token, gradients summed over users)."""
+    offsets = np.asarray(offsets, dtype=np.int64)
+    x = np.asarray(x, dtype=np.float64)
+    dx = np.zeros_like(x)
+    total = None
+    for b in range(offsets.shape[0] - 1):
+        lo, hi = int(offsets[b]), int(offsets[b + 1])
+        if hi == lo:
+            continue
+        dxb, g = block_backward_bf16_storage(x[lo:hi], groups[lo:hi], times[lo:hi], layer, num_heads,
+                                             dout[lo:hi], eps, mask_mode, shared_norm, store)
+        dx[lo:hi] = dxb
+        total = g if total is None else {k: total[k] + g[k] for k in g}
     return dx, total

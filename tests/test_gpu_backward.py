@@ -4,14 +4,20 @@ The oracle differentiates the block by the chain rule per user and sums paramete
 users (oracle.mtgr_oracle.block_backward_batch).  Tolerances, max |gpu - oracle| / max |oracle|
 per tensor:
   * fp32 storage: 1e-4 for dx and every parameter gradient.
-  * bf16 storage: 5e-2.  The library stores the recomputed activations and the activation
+  * bf16 storage, two bounds.  The library stores the recomputed activations and the activation
     gradients in bf16 (fp32 accumulation); a gradient passes through about a dozen such roundings
-    (2^-9 relative each) between dx_out and dW_qkvu / dgamma1.  The Q and K gradients are the
-    sensitive ones: with d_h = 128 the scores reach |s| ~ 40 and dS = dA silu'(s) M / N amplifies
-    the rounding of dy and of Q, K.  The fp64 oracle evaluated with bf16 rounding applied at the
-    same storage points (and nowhere else) already differs from the exact oracle by 2.6% on dx and
-    on the Q/K rows of dW_qkvu for the d = 256, two-head case below, so the bound is about twice
-    that.  The fp32 cases run the same kernels (templated on the storage type) at 1e-4.
+    (2^-9 relative each) between dx_out and dW_qkvu / dgamma1, and the Q and K gradients are the
+    sensitive ones (with d_h = 128 the scores reach |s| ~ 40 and dS = dA silu'(s) M / N amplifies
+    the rounding of dy and of Q, K).
+      - Against the oracle's bf16-storage evaluation (oracle.block_backward_bf16_storage: the same
+        chain rule in fp64 with the stored tensors rounded to bf16, reading R19): TOL_BF16_STORED.
+        What remains is the library's fp32 summation order and its fp32 transcendentals, plus
+        rounding decisions that flip between the two.
+      - Against the exact oracle: 5e-2, since the bf16-storage evaluation itself differs from the
+        exact one by up to ~2.6% on dx and on the Q/K rows of dW_qkvu in these cases.
+    The fp32 cases run the same kernels (templated on the storage type) at 1e-4.
+Each comparison also reports the element-wise error |g - r| / (|r| + 1e-6 max|r|) (its maximum
+and 99.9th percentile), which is not bounded: near-zero elements dominate it.
 """
 import numpy as np
 import pytest
@@ -26,6 +32,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 TOL_F32 = 1e-4
 TOL_BF16 = 5e-2
+TOL_BF16_STORED = 1e-2
 
 EDGE_LENGTHS = [(3, 40, 17, 5), (0, 0, 0, 7), (5, 200, 0, 3), (2, 130, 90, 0), (0, 0, 0, 0),
                 (1, 7, 150, 40), (16, 300, 64, 64), (0, 0, 1, 0)]
@@ -84,13 +91,40 @@ def oracle_bwd(b, p, dout, mask="dynamic", norm="group"):
                                   p.ln_eps, mask_mode=mask, shared_norm=(norm == "shared"))
 
 
-def check(dx, g, rdx, rg, tol):
+def oracle_bwd_stored(b, p, dout, mask="dynamic", norm="group"):
+    lay = O.params_layers(p)[0]
+    return O.block_backward_batch_bf16_storage(b.offsets, b.group_ids, b.timestamps, b.x, lay, p.H, dout,
+                                               p.ln_eps, mask_mode=mask, shared_norm=(norm == "shared"))
+
+
+def elem_err(g, r):
+    """element-wise |g - r| / (|r| + 1e-6 max|r|): (max, 99.9th percentile)"""
+    g = np.asarray(g, dtype=np.float64).ravel()
+    r = np.asarray(r, dtype=np.float64).ravel()
+    if r.size == 0:
+        return 0.0, 0.0
+    e = np.abs(g - r) / (np.abs(r) + 1e-6 * max(np.abs(r).max(), 1e-30))
+    return float(e.max()), float(np.percentile(e, 99.9))
+
+
+def check(dx, g, rdx, rg, tol, label=""):
     errs = {"dx": rel_err(dx, rdx)}
     for k in g:
         errs[k] = rel_err(g[k], rg[k])
+    ee = {k: elem_err(dx if k == "dx" else g[k], rdx if k == "dx" else rg[k]) for k in errs}
+    print(f"{label} max rel err {max(errs.values()):.3e} ({max(errs, key=errs.get)}); element-wise "
+          f"max {max(v[0] for v in ee.values()):.2e}, p99.9 {max(v[1] for v in ee.values()):.2e}")
     bad = {k: v for k, v in errs.items() if not v < tol}
     assert not bad, (bad, errs)
     return errs
+
+
+def check_bf16(b, p, dout, dx, g, mask="dynamic", norm="group"):
+    """the bf16 bounds: against the bf16-storage evaluation and against the exact oracle"""
+    sdx, sg = oracle_bwd_stored(b, p, dout, mask, norm)
+    check(dx, g, sdx, sg, TOL_BF16_STORED, "vs bf16-storage oracle:")
+    rdx, rg = oracle_bwd(b, p, dout, mask, norm)
+    check(dx, g, rdx, rg, TOL_BF16, "vs exact oracle:")
 
 
 @pytest.mark.parametrize("mask,norm", [("dynamic", "group"), ("causal", "group"), ("dynamic", "shared"),
@@ -122,8 +156,7 @@ def test_block_bwd_ragged_fp32(d, H, h, mask):
 def test_block_bwd_bf16(d, H, h, mask, norm):
     b, p, dout = make_case(EDGE_LENGTHS + [(8, 600, 120, 77)], d, H, h, "bf16", 73 + h)
     dx, g = run_bwd(b, p, dout, mask, norm)
-    rdx, rg = oracle_bwd(b, p, dout, mask, norm)
-    check(dx, g, rdx, rg, TOL_BF16)
+    check_bf16(b, p, dout, dx, g, mask, norm)
 
 
 def test_block_bwd_bf16_split_k():
@@ -134,8 +167,7 @@ def test_block_bwd_bf16_split_k():
     b, p, dout = make_case(lengths, 256, 4, 512, "bf16", 75)
     assert b.num_tokens >= 8192
     dx, g = run_bwd(b, p, dout)
-    rdx, rg = oracle_bwd(b, p, dout)
-    check(dx, g, rdx, rg, TOL_BF16)
+    check_bf16(b, p, dout, dx, g)
 
 
 def test_block_bwd_bf16_xcd_split():
@@ -147,8 +179,53 @@ def test_block_bwd_bf16_xcd_split():
     b, p, dout = make_case(lengths, 128, 2, 256, "bf16", 78)
     assert b.num_tokens >= 16384
     dx, g = run_bwd(b, p, dout)
-    rdx, rg = oracle_bwd(b, p, dout)
-    check(dx, g, rdx, rg, TOL_BF16)
+    check_bf16(b, p, dout, dx, g)
+
+
+def _sparse_case(b, p, users, seed):
+    """dout nonzero only on the rows of `users`: every parameter gradient is then exactly the sum
+    over those users (each user's contribution is linear in its dout), and every other row's dx is
+    exactly zero -- so the oracle needs only those users while the GPU runs the whole batch."""
+    rng = np.random.default_rng(seed)
+    dout = np.zeros((b.num_tokens, p.d), np.float32)
+    rows = synth.user_rows(b, users)
+    dout[rows] = rng.standard_normal((rows.shape[0], p.d)).astype(np.float32)
+    return dout, rows
+
+
+def _check_sparse(b, p, users, dout, rows, dx, g):
+    others = np.ones(b.num_tokens, bool)
+    others[rows] = False
+    assert np.all(dx[others] == 0.0), "a user without upstream gradient got a nonzero dx"
+    s = synth.subset(b, users)
+    check_bf16(s, p, dout[rows], dx[rows], g)
+
+
+def test_block_bwd_bf16_64_way_split():
+    """At least 64 x 2048 tokens with d = 256, h = 1024: each weight-gradient GEMM splits the token
+    axis 64 ways (eight splits per XCD), as the benchmark's full-size backward does."""
+    rng = np.random.default_rng(79)
+    lengths = [(8, int(rng.integers(300, 600)), int(rng.integers(0, 80)), int(rng.integers(1, 40)))
+               for _ in range(300)]
+    b, p, _ = make_case(lengths, 256, 2, 1024, "bf16", 80)
+    assert b.num_tokens >= 64 * 2048
+    B = b.num_users
+    users = sorted({0, 1, 37, B // 2, B - 2, B - 1})
+    dout, rows = _sparse_case(b, p, users, 81)
+    dx, g = run_bwd(b, p, dout)
+    _check_sparse(b, p, users, dout, rows, dx, g)
+
+
+def test_block_bwd_large_workload_sampled_users():
+    """Layer 0 of the large workload in the benchmark's launch configuration (630k tokens, d = 768,
+    h = 3072, 64-way split weight gradients); upstream gradient on the shortest and the last user."""
+    b, p = synth.make_workload("large-bf16")
+    p.layers = p.layers[:1]
+    n = np.diff(b.offsets)
+    users = sorted({int(np.argmin(n)), b.num_users - 1})
+    dout, rows = _sparse_case(b, p, users, 82)
+    dx, g = run_bwd(b, p, dout)
+    _check_sparse(b, p, users, dout, rows, dx, g)
 
 
 def test_block_bwd_deterministic_and_in_place():

@@ -263,9 +263,12 @@ def test_tokenize_matches_oracle(d, e):
         assert rel_err(x[rows], ref[rows]) < TOL_TOK, f"group {grp}"
 
 
-def test_tokenize_workload_sampled_tokens_and_step():
-    b, _ = synth.make_workload("small-bf16", with_params=False)
-    spec, ids, counts, store, model = tok_setup(b, 256, 64, 43)
+@pytest.mark.parametrize("name,d", [("small-bf16", 256), ("large-bf16", 768)])
+def test_tokenize_workload_sampled_tokens_and_step(name, d):
+    """The whole batch on the GPU (large-bf16 with d = 768, e = 64 is the benchmark's front-end
+    configuration); the oracle recomputes 1500 sampled tokens (tokens are independent)."""
+    b, _ = synth.make_workload(name, with_params=False)
+    spec, ids, counts, store, model = tok_setup(b, d, 64, 43)
     x, flags = run_tok(b, spec, ids, counts, store, step=5)
     assert flags == 0
     sample = np.random.default_rng(44).choice(b.num_tokens, 1500, replace=False)

@@ -330,12 +330,23 @@ def test_encoder_bf16_custom_parity_with_biases(mask, norm):
     assert rel_err(logit, rl) < TOL_BF16_ENCODER
 
 
-def _sample_users(b, k_extra):
+def elem_err(g, r):
+    """element-wise |g - r| / (|r| + 1e-6 max|r|): (max, 99.9th percentile); reported, not bounded"""
+    g = np.asarray(g, dtype=np.float64).ravel()
+    r = np.asarray(r, dtype=np.float64).ravel()
+    if r.size == 0:
+        return 0.0, 0.0
+    e = np.abs(g - r) / (np.abs(r) + 1e-6 * max(np.abs(r).max(), 1e-30))
+    return float(e.max()), float(np.percentile(e, 99.9))
+
+
+def _sample_users(b, k_extra, survey_subset=False):
+    """the longest and the shortest user plus users 0 .. k_extra-1; with survey_subset instead
+    users 0-7 and the first user whose long-term history is at the workload's cap of 3000 items"""
+    if survey_subset:
+        return sorted(set(range(8)) | {int(np.flatnonzero(b.n_s == 3000)[0])})
     n = b.offsets[1:] - b.offsets[:-1]
-    longest = int(np.argmax(n))
-    shortest = int(np.argmin(n))
-    extra = [u for u in range(k_extra) if u not in (longest, shortest)]
-    return sorted(set([longest, shortest] + extra))
+    return sorted({int(np.argmax(n)), int(np.argmin(n))} | set(range(k_extra)))
 
 
 @pytest.mark.parametrize("name,k_extra,mask,norm", [
@@ -344,15 +355,19 @@ def _sample_users(b, k_extra):
     ("large-bf16", 0, "causal", "shared")])
 def test_encoder_workload_sampled_users(name, k_extra, mask, norm):
     """Full-size batch on the GPU (the configuration the benchmark times); the oracle recomputes a
-    few users exactly (users never interact, so a subset is exact)."""
+    few users exactly (users never interact, so a subset is exact).  For the benchmark's own
+    workload (large-bf16, the method's mask) that is users 0-7 and the first user at the 3000-item
+    history cap (about 24k tokens, a minute or two of the oracle on the host)."""
     b, p = workload(name)
     hid, logit = run_encoder(b, p, mask, norm)
-    users = _sample_users(b, k_extra)
+    users = _sample_users(b, k_extra, survey_subset=(name == "large-bf16" and mask == "dynamic"))
     rh, rl = oracle_subset(b, p, users, mask, norm)
     gh = hid[synth.user_rows(b, users)]
     gl = logit[synth.candidate_rows(b, users)]
     e_h, e_l = rel_err(gh, rh), rel_err(gl, rl)
-    print(f"{name} ({mask}, {norm}): users {users} hidden rel err {e_h:.3e} logits rel err {e_l:.3e}")
+    (eh_max, eh_p), (el_max, el_p) = elem_err(gh, rh), elem_err(gl, rl)
+    print(f"{name} ({mask}, {norm}): users {users} hidden rel err {e_h:.3e} logits rel err {e_l:.3e}; "
+          f"element-wise hidden max {eh_max:.2e} p99.9 {eh_p:.2e}, logits max {el_max:.2e} p99.9 {el_p:.2e}")
     assert e_h < TOL_BF16_ENCODER
     assert e_l < TOL_BF16_ENCODER
     assert np.isfinite(hid).all() and np.isfinite(logit).all()

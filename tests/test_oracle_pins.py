@@ -504,10 +504,90 @@ def test_block_backward_matches_torch_autograd():
     y = torch.cat(heads, dim=1) * u
     z = gln(y, P["gln2_gamma"], P["gln2_beta"])
     out = torch.nn.functional.silu(z @ P["w_mlp1"].T + P["b_mlp1"]) @ P["w_mlp2"].T + P["b_mlp2"] + xt_
+    # P7(e): the block's forward itself, from this torch formulation with the dense mask
+    np.testing.assert_allclose(O.block_forward(x, g, t, lay, H), out.detach().numpy(), rtol=1e-10, atol=1e-12)
     (out * torch.from_numpy(dout)).sum().backward()
     np.testing.assert_allclose(dx, xt_.grad.numpy(), rtol=1e-10, atol=1e-12)
     for name, p in P.items():
         np.testing.assert_allclose(grads[name], p.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+
+
+def _torch_block_forward(x, g, t, lay, H, eps=1e-5):
+    """One HSTU block written independently with torch ops (marovi.ai MTGR page, 方法, the two
+    update equations): a dense [n, n] mask tensor from the three rules (fun-rec 7.3.4), GroupLN as
+    torch layer_norm plus a per-group gather of gamma/beta, F.silu, and matrix products."""
+    T = torch.float64
+    gt = torch.from_numpy(g.astype(np.int64))
+    tt = torch.from_numpy(t.astype(np.float64))
+    n, d = x.shape
+    vis = ((gt == 0) | (gt == 1))[None, :] | torch.eye(n, dtype=torch.bool) | (
+        ((gt == 2) | (gt == 3))[:, None] & (gt == 2)[None, :] & (tt[None, :] < tt[:, None]))
+    P = {k: torch.tensor(v, dtype=T) for k, v in lay.items() if v is not None}
+    zero = lambda m: torch.zeros(m, dtype=T)
+    xt_ = torch.tensor(x, dtype=T)
+
+    def gln(v, gamma, beta):
+        return torch.nn.functional.layer_norm(v, (d,), eps=eps) * gamma[gt] + beta[gt]
+
+    qkvu = gln(xt_, P["gln1_gamma"], P["gln1_beta"]) @ P["w_qkvu"].T + P.get("b_qkvu", zero(4 * d))
+    q, k, v, u = qkvu.split(d, dim=1)
+    dh = d // H
+    heads = [(torch.nn.functional.silu(q[:, sl] @ k[:, sl].T) * vis / n) @ v[:, sl]
+             for sl in (slice(i * dh, (i + 1) * dh) for i in range(H))]
+    z = gln(torch.cat(heads, dim=1) * u, P["gln2_gamma"], P["gln2_beta"])
+    hid = torch.nn.functional.silu(z @ P["w_mlp1"].T + P.get("b_mlp1", zero(P["w_mlp1"].shape[0])))
+    return (hid @ P["w_mlp2"].T + P.get("b_mlp2", zero(d)) + xt_).numpy()
+
+
+@pytest.mark.parametrize("seed,with_bias,shuffle_r", [(95, True, False), (96, False, True), (97, True, True)])
+def test_block_forward_matches_torch_formulation(seed, with_bias, shuffle_r):
+    """P7(e): the oracle's whole block equals an independent torch formulation with a dense mask,
+    on users holding every group, unsorted R events, an R/C timestamp tie and zero or nonzero biases."""
+    g, t, x, lay, _, H = _tiny_block(seed=seed, with_bias=with_bias)
+    rng = np.random.default_rng(seed)
+    if shuffle_r:
+        t[4:8] = rng.permutation(t[4:8])
+    t[9] = t[5]                                     # a candidate tied with an R event: not visible
+    np.testing.assert_allclose(O.block_forward(x, g, t, lay, H), _torch_block_forward(x, g, t, lay, H),
+                               rtol=1e-10, atol=1e-12)
+
+
+def test_round_bf16_matches_torch_conversion():
+    """R19's rounding is the nearest bfloat16, ties to even: torch's float32 -> bfloat16."""
+    rng = np.random.default_rng(98)
+    v = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.uniform(-30, 30, 4000),
+                        [0.0, -0.0, 1.0, -1.5, 3.4e38, 1e-40, np.inf, -np.inf]]).astype(np.float32)
+    # exact halfway cases: the 16 dropped bits are 0x8000, with an even and an odd kept bit
+    ties = (rng.integers(0x3F000000, 0x47000000, 2000).astype(np.uint32) & 0xFFFF0000) | 0x8000
+    v = np.concatenate([v, ties.view(np.float32)])
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_bf16(v), ref)
+
+
+@pytest.mark.parametrize("mask_mode,shared", [("dynamic", False), ("causal", True), ("full", False)])
+def test_bf16_storage_backward_reduces_to_exact(mask_mode, shared):
+    """With the identity as the storage rounding, the R19 evaluation is the exact chain rule."""
+    g, t, x, lay, dout, H = _tiny_block(seed=99)
+    dx, grads = O.block_backward(x, g, t, lay, H, dout, mask_mode=mask_mode, shared_norm=shared)
+    dx2, grads2 = O.block_backward_bf16_storage(x, g, t, lay, H, dout, mask_mode=mask_mode,
+                                                shared_norm=shared, store=lambda a: a)
+    np.testing.assert_allclose(dx2, dx, rtol=1e-12, atol=1e-13)
+    for name in grads:
+        np.testing.assert_allclose(grads2[name], grads[name], rtol=1e-12, atol=1e-13, err_msg=name)
+
+
+def test_bf16_storage_backward_stays_near_exact():
+    """With bf16 rounding (2^-9 relative per stored value) the result moves, but by a few percent
+    at most of each tensor's largest magnitude."""
+    g, t, x, lay, dout, H = _tiny_block(seed=100)
+    lay = {k: (O.round_bf16(v) if v is not None else None) for k, v in lay.items()}
+    x = O.round_bf16(x)
+    dx, grads = O.block_backward(x, g, t, lay, H, dout)
+    dx2, grads2 = O.block_backward_bf16_storage(x, g, t, lay, H, dout)
+    rel = lambda a, b: float(np.abs(a - b).max() / np.abs(b).max())
+    np.testing.assert_array_equal(grads2["b_mlp2"], grads["b_mlp2"])   # sums of the unrounded dout
+    errs = [rel(dx2, dx)] + [rel(grads2[k], grads[k]) for k in grads if k != "b_mlp2"]
+    assert 0.0 < min(errs) and max(errs) < 5e-2, errs
 
 
 def test_block_backward_batch_sums_users_and_isolates_them():
