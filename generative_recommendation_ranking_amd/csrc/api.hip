@@ -29,10 +29,12 @@ PrepBufs prep_bufs(void* ws, const Plan& p) {
   pb.cand_idx = at<int64_t>(ws, p.cand_idx);
   pb.flags = at<int32_t>(ws, p.flags);
   pb.xcd_off = at<int32_t>(ws, p.xcd_off);
+  pb.xcd_fwd = at<int32_t>(ws, p.xcd_fwd);
   return pb;
 }
 
 inline int q_tile_for(int dtype) { return dtype == MTGR_BF16 ? kAttnQTileBf16 : kAttnQTileF32; }
+inline int q_tile_fwd_for(int dtype) { return dtype == MTGR_BF16 ? kAttnFwdQTileBf16 : 0; }
 
 mtgr_status hip_status(hipError_t e) { return e == hipSuccess ? MTGR_OK : MTGR_ERR_HIP; }
 
@@ -55,8 +57,8 @@ hipError_t attention(const mtgr_batch* b, int d, int H, int dtype, int mask_mode
                      const PrepBufs& pb, const void* qkvu, void* y, hipStream_t s,
                      void* vt = nullptr) {
   if (dtype == MTGR_BF16)
-    return launch_attention_bf16(b->num_users, xcd_grid_slots(b, H, kAttnQTileBf16), d, H,
-                                 mask_mode, b->offsets, pb.seg, pb.order, pb.xcd_off, b->timestamps,
+    return launch_attention_bf16(b->num_users, xcd_grid_slots(b, H, kAttnFwdQTileBf16), d, H,
+                                 mask_mode, b->offsets, pb.seg, pb.order, pb.xcd_fwd, b->timestamps,
                                  static_cast<const bf16*>(qkvu), static_cast<bf16*>(y),
                                  static_cast<bf16*>(vt), s);
   const int64_t tiles = total_tiles(b, kAttnQTileF32);
@@ -170,7 +172,7 @@ hipError_t run_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, const 
     e = (expr);                         \
     if (e != hipSuccess) return e;      \
   } while (0)
-  MTGR_BWD_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile, H, pb, false, s));
+  MTGR_BWD_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile, q_tile_fwd_for(dt), H, pb, false, s));
   // forward, keeping what the backward needs: GLN1 output, QKVU, V~, the gated output, GLN2
   // output and the MLP pre-activation a (its SiLU replaces it in the SiLU backward)
   MTGR_BWD_TRY(launch_groupln(T, d, 0, act, act, shared, x_in, b->group_ids, p->gln1_gamma,
@@ -349,7 +351,7 @@ mtgr_status mtgr_attention_bwd(const mtgr_batch* b, int32_t d, int32_t num_heads
   Sizes z = sizes_for(b, d, 0, 0, dtype, num_heads);
   const Plan pl = make_plan(z);
   const PrepBufs pb = prep_bufs(ws, pl);
-  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), num_heads, pb,
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), q_tile_fwd_for(dtype), num_heads, pb,
                        false, s));
   MTGR_TRY(attention_bwd(b, d, num_heads, dtype, mask_mode, pb, qkvu, v_tilde, dy_gated, at<void>(ws, pl.total),
                          dqkvu, s));
@@ -373,7 +375,7 @@ mtgr_status mtgr_encoder_fwd(const mtgr_encoder_params* p, const mtgr_batch* b, 
   z.need_acts = z.need_xres = z.need_head = true;
   const Plan pl = make_plan(z);
   const PrepBufs pb = prep_bufs(ws, pl);
-  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dt), z.H, pb, true, s));
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dt), q_tile_fwd_for(dt), z.H, pb, true, s));
   float* xr = hidden_out ? hidden_out : at<float>(ws, pl.xres);
   for (int32_t l = 0; l < p->num_layers; ++l) {
     const float* src = (l == 0) ? x_in : xr;
@@ -405,7 +407,7 @@ mtgr_status mtgr_block_fwd(const mtgr_block_params* p, const mtgr_batch* b, cons
   z.need_acts = true;
   const Plan pl = make_plan(z);
   const PrepBufs pb = prep_bufs(ws, pl);
-  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(p->dtype), z.H, pb, false, s));
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(p->dtype), q_tile_fwd_for(p->dtype), z.H, pb, false, s));
   MTGR_TRY(run_block(p, b, pb, pl, ws, x_in, x_out, s));
   return MTGR_OK;
 }
@@ -460,7 +462,7 @@ mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads
   Sizes z = sizes_for(b, d, 0, 0, MTGR_F32, num_heads);
   const Plan pl = make_plan(z);
   const PrepBufs pb = prep_bufs(ws, pl);
-  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), num_heads, pb, false, s));
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), q_tile_fwd_for(dtype), num_heads, pb, false, s));
   MTGR_TRY(attention(b, d, num_heads, dtype, mask_mode, pb, qkvu, y_gated, s));
   return MTGR_OK;
 }
@@ -502,7 +504,7 @@ mtgr_status mtgr_debug_mask(const mtgr_batch* b, int32_t user, int32_t mask_mode
   if (!mask_dev) return MTGR_ERR_NULL_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const PrepBufs pb = prep_bufs(ws, pl);
-  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, kAttnQTileF32, 0, pb, false, s));
+  MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, kAttnQTileF32, 0, 0, pb, false, s));
   MTGR_TRY(launch_debug_mask(user, mask_mode, b->offsets, pb.seg, b->timestamps, n, mask_dev, s));
   return MTGR_OK;
 }

@@ -6,8 +6,11 @@
 // the user's total token count.  No softmax, no 1/sqrt(d_h), no running max.  Users never
 // attend to each other (sequence packing, chenhuiyu blog "MTGR", training-system section).
 //
-// Work item = (user, head, 128-row q-tile); one 256-thread workgroup (4 wavefronts x 32 query
-// rows).  Work items are ordered longest user first (LPT) by the prep kernels.
+// Work item = (user, head, q-tile of 32 NW rows); one workgroup of NW wavefronts x 32 query rows.
+// The forward runs NW = 4 (128 rows, two workgroups per CU); 8 wavefronts sharing each K/V tile
+// over 256 rows halve the global K/V traffic per FLOP but measured slower (6.09 vs 5.85 ms per
+// layer on the large workload).  Work items are ordered longest user first (LPT) by the prep
+// kernels.
 //
 // Key range of a work item.  Tokens are ordered U, S, R, C.  Static keys [0, n_static) are
 // visible to every row; R keys [n_static, rc_end) only to R/C rows, by timestamp; C keys only
@@ -27,14 +30,14 @@
 // the score accumulator holds them.
 //
 // LDS per workgroup: K 2 x 64 x (d_h+8) and V 2 x 64 x (d_h+32) bf16 (double-buffered,
-// register-staged global->LDS copies), ~75 KB at d_h = 128, two workgroups per CU.
+// register-staged global->LDS copies), ~75 KB at d_h = 128 and NW = 4, shared afterwards with the
+// fp32 staging of the output rows.
 #include "kernels.h"
 
 namespace mtgr {
 
 namespace {
 
-constexpr int BQ = kAttnQTileBf16;  // 128 query rows per work item
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int BKV = 64;             // keys per tile
@@ -49,26 +52,30 @@ __device__ __forceinline__ int find_slot(const int32_t* __restrict__ tile_off, i
 }
 
 // MODE: kMaskDynamic (the three rules), kMaskCausal (j <= i) or kMaskFull (all keys of the user).
-template <int DH, int MODE>
-__global__ __launch_bounds__(256, 2) void k_attn_bf16(
+// NW wavefronts of 32 query rows each.
+template <int DH, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
     int32_t B, int H, int d, const int64_t* __restrict__ offsets, const UserSeg* __restrict__ seg,
     const int32_t* __restrict__ order, const int32_t* __restrict__ xcd_off,
     const float* __restrict__ ts, const bf16* __restrict__ qkvu, bf16* __restrict__ y,
     bf16* __restrict__ vt) {
+  constexpr int BQ = 32 * NW;                     // query rows per work item
+  constexpr int NTH = 64 * NW;                    // threads per workgroup
+  static_assert(BQ == kAttnFwdQTileBf16, "work items come from queues built with the forward's q-tile");
   constexpr int KP = DH + 8;                     // K row pitch: 16-byte reads of 16 rows hit distinct banks
   // V row pitch: a transposing read by 32 lanes touches 4 rows x 2 column chunks of 32 bytes;
   // a pitch of 16 (mod 64) dwords puts those 8 chunks on disjoint banks.
   constexpr int VP = DH + 32;
   constexpr int DCH = DH / 8;                    // 16-byte chunks per key row
-  constexpr int CH = BKV * DCH / 256;            // K (and V) chunks per thread per tile
+  constexpr int CH = BKV * DCH / NTH;            // K (and V) chunks per thread per tile
   constexpr int NT = DH / 32;                    // output tiles of 32 features
-  static_assert(CH * 256 == BKV * DCH && CH <= 4, "staging layout");
+  static_assert(CH * NTH == BKV * DCH && CH <= 4, "staging layout");
 
   // One LDS arena: K and V^T tiles (double-buffered) and the tile timestamps during the key loop;
   // reused afterwards to stage each wavefront's output rows for vectorised stores.
   constexpr int OP = DH + 4;                                   // fp32 pitch of staged output rows
   constexpr size_t kLoopBytes = (2 * BKV * KP + 2 * BKV * VP) * sizeof(bf16) + 2 * BKV * sizeof(float);
-  constexpr size_t kEpiBytes = 4 * 32 * OP * sizeof(float) + 4 * 32 * sizeof(float);
+  constexpr size_t kEpiBytes = NW * 32 * OP * sizeof(float) + NW * 32 * sizeof(float);
   __shared__ __attribute__((aligned(16))) char arena[kLoopBytes > kEpiBytes ? kLoopBytes : kEpiBytes];
   bf16 (*Ks)[BKV][KP] = reinterpret_cast<bf16 (*)[BKV][KP]>(arena);
   bf16 (*Vs)[BKV][VP] = reinterpret_cast<bf16 (*)[BKV][VP]>(arena + 2 * BKV * KP * sizeof(bf16));
@@ -140,8 +147,8 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   const int nbytes = (int)((uint32_t)kend * row_bytes);
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kp, (short)0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vp, (short)0, nbytes, 0x00020000);
-  const int st_key = tid / DCH, st_c = tid % DCH;             // chunk i: key st_key + i*(256/DCH)
-  constexpr int KSTEP = 256 / DCH;
+  const int st_key = tid / DCH, st_c = tid % DCH;             // chunk i: key st_key + i*(NTH/DCH)
+  constexpr int KSTEP = NTH / DCH;
   const uint32_t st_off = (uint32_t)st_key * row_bytes + st_c * 16;
 
   auto stage_load = [&](int k0) {
@@ -281,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bf16(
   // Stage this wavefront's O rows (fp32) in LDS: element r of tile t is row 8*(r/4)+4*hh+r%4,
   // feature t*32 + l32.  The key loop ended with a barrier, so the arena is free.
   float* Os = reinterpret_cast<float*>(arena) + w * 32 * OP;
-  float* Ps = reinterpret_cast<float*>(arena) + 4 * 32 * OP + w * 32;
+  float* Ps = reinterpret_cast<float*>(arena) + NW * 32 * OP + w * 32;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -379,10 +386,11 @@ hipError_t attn_bf16_mode(unsigned grid, int32_t B, int d, int H, const int64_t*
                           const float* timestamps, const bf16* qkvu, bf16* y, bf16* vt,
                           hipStream_t s) {
   const int dh = d / H;
+  constexpr int NW = kAttnFwdQTileBf16 / 32;
   if (dh == 128)
-    k_attn_bf16<128, MODE><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y, vt);
+    k_attn_bf16<128, MODE, NW><<<grid, 64 * NW, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y, vt);
   else if (dh == 64)
-    k_attn_bf16<64, MODE><<<grid, 256, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y, vt);
+    k_attn_bf16<64, MODE, NW><<<grid, 64 * NW, 0, s>>>(B, H, d, offsets, seg, order, xcd_off, timestamps, qkvu, y, vt);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

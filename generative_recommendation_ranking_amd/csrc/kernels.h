@@ -23,9 +23,11 @@ struct PrepBufs {
   int64_t* cand_idx;   // [C]   token row of each candidate, packed order
   int32_t* flags;      // [4]   validation flags / counters
   int32_t* xcd_off;    // [8][R+1] per-XCD q-tile prefix over (user, head) groups, R = ceil(B*H/8)
+  int32_t* xcd_fwd;    // [8][R+1] the same for the forward's q-tile size (may be NULL)
 };
+// q_tile sizes tile_off and xcd_off; q_tile_fwd > 0 also builds xcd_fwd
 hipError_t launch_prep(int32_t B, int64_t C, const int64_t* offsets, const uint8_t* group_ids,
-                       int q_tile, int heads, const PrepBufs& pb, bool want_cand_idx,
+                       int q_tile, int q_tile_fwd, int heads, const PrepBufs& pb, bool want_cand_idx,
                        hipStream_t s);
 hipError_t launch_validate(int32_t B, const int64_t* offsets, const uint8_t* group_ids,
                            const float* timestamps, int32_t* flags, hipStream_t s);
@@ -47,7 +49,8 @@ hipError_t launch_gemm_f32(int64_t M, int N, int K, int epi, const float* a, con
                            const float* bias, const float* resid, float* out, hipStream_t s);
 
 // ---- attention (attention.hip) -------------------------------------------------------------
-// grid_slots = max over XCDs of that XCD's q-tile count (the host replica of k_prep_xcd).
+// grid_slots = max over XCDs of that XCD's q-tile count (the host replica of k_prep_xcd); the bf16
+// forward takes its work from queues built with kAttnFwdQTileBf16.
 // vt (may be NULL) receives the ungated V~ for the backward pass.
 // mask_mode: kMaskDynamic / kMaskCausal / kMaskFull
 hipError_t launch_attention_bf16(int32_t B, int64_t grid_slots, int d, int H, int mask_mode,

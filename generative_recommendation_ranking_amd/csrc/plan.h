@@ -3,7 +3,7 @@
 // into the library and, on its own, into a host unit test (with the address and undefined-behaviour
 // sanitizers).
 //
-// Placement of attention work.  A work item is (user, head, q-tile of 128 or 64 rows).  Users are
+// Placement of attention work.  A work item is (user, head, q-tile of 256, 128 or 64 rows).  Users are
 // taken longest first (LPT) so the heaviest items start first; (user, head) groups g = p*H + h
 // (p the user's position in that order) are dealt to the 8 XCDs in snake order, and every XCD runs
 // its groups' q-tiles back to back so a group's tiles share one L2.  The device builds the same
@@ -24,7 +24,8 @@ namespace mtgr {
 
 constexpr int kXcdCount = 8;           // MI355X: 8 XCDs, workgroups dispatched round-robin by id
 constexpr int kLptMaxUsers = 16384;    // above this many users the work order is the index order
-constexpr int kAttnQTileBf16 = 128;    // query rows per attention work item (bf16 kernels)
+constexpr int kAttnQTileBf16 = 128;    // query (key) rows per work item of the bf16 attention backward
+constexpr int kAttnFwdQTileBf16 = 128; // query rows per work item of the bf16 attention forward
 constexpr int kAttnQTileF32 = 64;      // (fp32 kernels)
 constexpr size_t kUserSegBytes = 16;   // sizeof(UserSeg): four int32 segment lengths
 
@@ -194,7 +195,7 @@ inline Sizes sizes_for(const mtgr_batch* b, int d, int h, int hh, int dtype, int
 
 // Byte offsets of the workspace regions (each 256-byte aligned), and the total.
 struct Plan {
-  size_t seg = 0, order = 0, tile_off = 0, cand_off = 0, cand_idx = 0, flags = 0, xcd_off = 0;
+  size_t seg = 0, order = 0, tile_off = 0, cand_off = 0, cand_idx = 0, flags = 0, xcd_off = 0, xcd_fwd = 0;
   size_t xt = 0, big = 0, y = 0, xres = 0, hin = 0, hhid = 0;
   size_t total = 0;
 };
@@ -216,6 +217,7 @@ inline Plan make_plan(const Sizes& z) {
   p.cand_idx = take((size_t)z.C * sizeof(int64_t));
   const int64_t rounds = (z.B * z.H + kXcdCount - 1) / kXcdCount;
   p.xcd_off = take((size_t)kXcdCount * (rounds + 1) * sizeof(int32_t));
+  p.xcd_fwd = take((size_t)kXcdCount * (rounds + 1) * sizeof(int32_t));
   if (z.need_acts) {
     p.xt = take((size_t)z.T * z.d * es);
     p.big = take((size_t)z.T * std::max(4 * z.d, z.h) * es);

@@ -169,13 +169,15 @@ __global__ void k_debug_mask(int mode, const int64_t* __restrict__ offsets, cons
 }  // namespace
 
 hipError_t launch_prep(int32_t B, int64_t C, const int64_t* offsets, const uint8_t* group_ids,
-                       int q_tile, int heads, const PrepBufs& pb, bool want_cand_idx,
+                       int q_tile, int q_tile_fwd, int heads, const PrepBufs& pb, bool want_cand_idx,
                        hipStream_t s) {
   if (B <= 0) return hipSuccess;
   k_prep_users<<<(B + 255) / 256, 256, 0, s>>>(B, offsets, group_ids, pb.seg, pb.order);
   k_prep_scan<<<1, 1024, 0, s>>>(B, q_tile, offsets, pb.seg, pb.order, pb.tile_off, pb.cand_off);
   if (want_cand_idx) k_prep_cand<<<B, 256, 0, s>>>(B, C, offsets, pb.seg, pb.cand_off, pb.cand_idx);
   if (pb.xcd_off && heads > 0) k_prep_xcd<<<1, 64, 0, s>>>(B, heads, q_tile, offsets, pb.order, pb.xcd_off);
+  if (pb.xcd_fwd && heads > 0 && q_tile_fwd > 0)
+    k_prep_xcd<<<1, 64, 0, s>>>(B, heads, q_tile_fwd, offsets, pb.order, pb.xcd_fwd);
   return hipGetLastError();
 }
 

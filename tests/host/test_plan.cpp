@@ -91,7 +91,7 @@ static void test_grid_matches_device(std::mt19937_64& rng) {
       HostBatch hb(lens);
       const std::vector<int32_t> order = device_order(hb.off);
       for (int H : {1, 4, 6}) {
-        for (int qt : {kAttnQTileBf16, kAttnQTileF32}) {
+        for (int qt : {kAttnFwdQTileBf16, kAttnQTileBf16, kAttnQTileF32}) {
           int64_t dev[kXcdCount], host[kXcdCount];
           device_queues(hb.off, order, H, qt, dev);
           plan::xcd_queue_tiles(&hb.b, H, qt, host);
@@ -129,6 +129,7 @@ static void test_plans() {
       const int64_t rounds = (z.B * z.H + kXcdCount - 1) / kXcdCount;
       check_regions({{p.flags, 16}, {p.seg, z.B * kUserSegBytes}, {p.order, z.B * 4}, {p.tile_off, (z.B + 1) * 4},
                      {p.cand_off, (z.B + 1) * 8}, {p.cand_idx, z.C * 8}, {p.xcd_off, kXcdCount * (rounds + 1) * 4},
+                     {p.xcd_fwd, kXcdCount * (rounds + 1) * 4},
                      {p.xt, T * z.d * es}, {p.big, T * 4 * z.d * es}, {p.y, T * z.d * es}, {p.xres, T * z.d * 4},
                      {p.hin, z.C * z.d * es}, {p.hhid, z.C * z.hh * es}},
                     p.total);
