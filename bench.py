@@ -20,8 +20,9 @@ Besides the headline tokens/s the line carries
 
 --block-bwd measures the backward pass of one block instead (layer 0 of the workload): one step =
 one mtgr_block_bwd over the whole batch (forward recompute, then dX and every parameter gradient)
-from a synthetic upstream gradient; its roofline entry is the attention backward (the dK/dV and dQ
-launches, 14 * d_model FLOPs per visible pair).
+from a synthetic upstream gradient; its roofline entry is the attention backward (the gate, dK/dV
+and dQ launches) at 10 * d_model algorithmic FLOPs per visible pair, with the 14 * d_model the
+kernels execute (dQ recomputes S and dP) reported beside it.
 
 --front-end measures the embedding front end instead: one step = one mtgr_tokenize over the whole
 batch (field IDs -> dedup -> hash-store lookup -> per-group MLP -> encoder input x), with 64-wide
@@ -123,7 +124,37 @@ def cpu_baseline_block_bwd(b, p, dout, mask="dynamic", norm="group", budget_s=12
     return {"value": done / el, "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
             "sample": f"users {users[0]}..{users[-1]} ({len(users)} users, {done} tokens) of the "
                       f"same batch, backward of block 0 (forward recompute included), fp64 numpy",
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2), "host": host_cpu()}
+
+
+def host_cpu():
+    """model name and logical CPU count of the host (lscpu, else /proc/cpuinfo)"""
+    model = None
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                model = line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    if model is None:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+    return {"model": model, "logical_cpus": os.cpu_count()}
+
+
+def survey_user_order(b):
+    """users in the order the baseline samples them: the first user whose long-term history sits at
+    the workload's 3000-item cap (when there is one), then users 0, 1, 2, ..."""
+    tail = np.flatnonzero(np.asarray(b.n_s) == 3000)
+    first = [int(tail[0])] if tail.size else []
+    return first + [u for u in range(b.num_users) if u not in first]
 
 
 def _oracle_threads():
@@ -134,14 +165,16 @@ def _oracle_threads():
         return int(os.cpu_count())
 
 
-def cpu_baseline(b, p, mask="dynamic", norm="group", budget_s=12.0, max_s=30.0):
-    """The oracle (fp64 numpy, as it stands) on whole users of the same batch, in index order,
-    until at least `budget_s` seconds of work; tokens of the sample per second."""
+def cpu_baseline(b, p, mask="dynamic", norm="group", budget_s=20.0, max_s=30.0):
+    """The oracle (fp64 numpy, as it stands) on whole users of the same batch -- the first user at
+    the 3000-item history cap, then users 0, 1, 2, ... (the start of the subset users 0-7 plus that
+    user, which takes about 100 s in full) -- until at least `budget_s` seconds of work; tokens of
+    the sample per second."""
     from generative_recommendation_ranking_amd import synth
     from oracle import mtgr_oracle as O
     layers, head = O.params_layers(p), O.params_head(p)
     done, users, t0 = 0, [], time.perf_counter()
-    for u in range(b.num_users):
+    for u in survey_user_order(b):
         s = synth.subset(b, [u])
         O.encoder_forward(s.offsets, s.group_ids, s.timestamps, s.x, layers, head, p.H, p.ln_eps,
                           mask_mode=mask, shared_norm=(norm == "shared"))
@@ -152,9 +185,9 @@ def cpu_baseline(b, p, mask="dynamic", norm="group", budget_s=12.0, max_s=30.0):
             break
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
-            "sample": f"users {users[0]}..{users[-1]} ({len(users)} users, {done} tokens) of the "
-                      f"same batch, all {p.num_layers} blocks + head, fp64 numpy",
-            "seconds": round(el, 2)}
+            "sample": f"users {users} ({len(users)} users, {done} tokens) of the same batch, all "
+                      f"{p.num_layers} blocks + head, fp64 numpy",
+            "seconds": round(el, 2), "host": host_cpu()}
 
 
 def main():
@@ -171,8 +204,9 @@ def main():
                     help="time the backward pass of one block (mtgr_block_bwd) instead of the encoder")
     ap.add_argument("--front-end", action="store_true",
                     help="time the tokenizer front end (mtgr_tokenize) and the hash-store lookup instead")
-    ap.add_argument("--profile-kernel", choices=["attention", "copy"], default=None,
-                    help="run only this kernel --steps times (for rocprofv3 counter runs)")
+    ap.add_argument("--profile-kernel", choices=["attention", "copy", "layer"], default=None,
+                    help="run only this kernel (attention, a plain copy) or one layer's kernel sequence "
+                         "(layer) --steps times, for rocprofv3 counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); users are independent, "
@@ -233,18 +267,19 @@ def main():
                           "attention_source_sha256_16": attention_source_hash()}), flush=True)
         return
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed / args.steps * 1e3
-    tokens_per_s = b.num_tokens * args.steps / elapsed
-    print(f"[bench] {ms_per_step:.2f} ms/step, {tokens_per_s / 1e6:.3f} M tokens/s",
-          file=sys.stderr, flush=True)
+    if args.profile_kernel != "layer":
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        ms_per_step = elapsed / args.steps * 1e3
+        tokens_per_s = b.num_tokens * args.steps / elapsed
+        print(f"[bench] {ms_per_step:.2f} ms/step, {tokens_per_s / 1e6:.3f} M tokens/s",
+              file=sys.stderr, flush=True)
 
     # ---- replay of one layer's kernel sequence through the kernel-level entries, timed with
     # HIP events on the same stream (layer 0's weights; every layer has the same shapes)
@@ -268,6 +303,14 @@ def main():
     for _, fn in seq:
         fn()
     torch.cuda.synchronize()
+    if args.profile_kernel == "layer":
+        for _ in range(args.steps):
+            for _, fn in seq:
+                fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_kernel": "layer", "launches_each": args.steps + 1,
+                          "kernels": [k for k, _ in seq]}), flush=True)
+        return
     times = {k: 0.0 for k, _ in seq}
     for _ in range(args.replay_steps):
         for k, fn in seq:
@@ -337,7 +380,7 @@ def cpu_baseline_tokenize(ids, groups, spec, tabs, pids, vals, budget_s=10.0):
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tokens/s", "cores": _oracle_threads(), "kind": "oracle",
             "sample": f"the batch's first {done} tokens, per-token dict lookups + fp64 numpy MLP",
-            "seconds": round(el, 2)}
+            "seconds": round(el, 2), "host": host_cpu()}
 
 
 def bench_front_end(args, b, p, db, M, torch, synth):
@@ -494,7 +537,10 @@ def bench_block_bwd(args, b, p, db, dm, M, torch):
         att += e0.elapsed_time(e1)
     att_ms = att / args.replay_steps
     pairs = int(visible_pairs_per_user(b, args.mask).sum())
-    att_fl = 14.0 * d * pairs
+    # algorithmic: S, dP, dV, dQ, dK, 2 d FLOPs each per visible pair; the kernels execute 14 d
+    # (the dQ pass recomputes S and dP so that dQ is written without atomics)
+    att_fl = 10.0 * d * pairs
+    att_fl_exec = 14.0 * d * pairs
     att_tflops = att_fl / (att_ms * 1e-3) / 1e12
     out = {
         "metric": "block backward tokens/sec (bf16; forward recompute + dX + parameter gradients of "
@@ -516,7 +562,9 @@ def bench_block_bwd(args, b, p, db, dm, M, torch):
         "roofline": {"bound": "mfma", "kernel": "attention backward (gate + dK/dV + dQ launches)",
                      "achieved": round(att_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "flops_per_launch": att_fl, "launch_ms": round(att_ms, 4)},
+                     "flops_per_launch": att_fl, "launch_ms": round(att_ms, 4),
+                     "executed_flops_per_launch": att_fl_exec,
+                     "executed_tflops": round(att_fl_exec / (att_ms * 1e-3) / 1e12, 1)},
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle's block backward on a sample of users", file=sys.stderr, flush=True)
