@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/mtgr.h"
@@ -12,6 +13,12 @@
 
 using namespace mtgr;
 using namespace mtgr::plan;
+
+// Fixed device scratch of mtgr_attention_fwd_noalloc: the batch-prep tables of one call.  Every GPU
+// the library runs on holds its own copy until the process ends; host code reaches it only through
+// the per-device address from hipGetSymbolAddress (the array's name is a host-side stand-in).
+static constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
 
 namespace {
 
@@ -38,6 +45,28 @@ inline int q_tile_fwd_for(int dtype) { return dtype == MTGR_BF16 ? kAttnFwdQTile
 
 mtgr_status hip_status(hipError_t e) { return e == hipSuccess ? MTGR_OK : MTGR_ERR_HIP; }
 
+// Device address of `scratch` on the current device, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+hipError_t scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
 #define MTGR_TRY(expr)                           \
   do {                                           \
     hipError_t _e = (expr);                      \
@@ -53,11 +82,16 @@ hipError_t linear(int64_t M, int N, int K, int dtype, int epi, const void* a, co
                          static_cast<const float*>(bias), resid, static_cast<float*>(out), s);
 }
 
+// order_buf (room for min(B, kLptMaxUsers) entries, or NULL to use a vector) holds the host's work
+// order while the grid is sized
 hipError_t attention(const mtgr_batch* b, int d, int H, int dtype, int mask_mode,
                      const PrepBufs& pb, const void* qkvu, void* y, hipStream_t s,
-                     void* vt = nullptr) {
+                     void* vt = nullptr, int32_t* order_buf = nullptr) {
   if (dtype == MTGR_BF16)
-    return launch_attention_bf16(b->num_users, xcd_grid_slots(b, H, kAttnFwdQTileBf16), d, H,
+    return launch_attention_bf16(b->num_users,
+                                 order_buf ? xcd_grid_slots(b, H, kAttnFwdQTileBf16, order_buf)
+                                           : xcd_grid_slots(b, H, kAttnFwdQTileBf16),
+                                 d, H,
                                  mask_mode, b->offsets, pb.seg, pb.order, pb.xcd_fwd, b->timestamps,
                                  static_cast<const bf16*>(qkvu), static_cast<bf16*>(y),
                                  static_cast<bf16*>(vt), s);
@@ -236,6 +270,7 @@ const char* mtgr_status_str(int32_t status) {
     case MTGR_ERR_UNSUPPORTED: return "unsupported dtype or option";
     case MTGR_ERR_WORKSPACE: return "workspace missing or too small";
     case MTGR_ERR_HIP: return "HIP launch or copy failed";
+    case MTGR_ERR_SCRATCH_LIMIT: return "batch needs more than the fixed scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }
@@ -464,6 +499,33 @@ mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads
   const PrepBufs pb = prep_bufs(ws, pl);
   MTGR_TRY(launch_prep(b->num_users, b->num_candidates, b->offsets, b->group_ids, q_tile_for(dtype), q_tile_fwd_for(dtype), num_heads, pb, false, s));
   MTGR_TRY(attention(b, d, num_heads, dtype, mask_mode, pb, qkvu, y_gated, s));
+  return MTGR_OK;
+}
+
+mtgr_status mtgr_attention_fwd_noalloc(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
+                                       int32_t mask_mode, const void* qkvu, void* y_gated, void* stream) {
+  mtgr_status st = check_batch(b);
+  if (st != MTGR_OK) return st;
+  if (d <= 0 || num_heads <= 0 || d % num_heads != 0) return MTGR_ERR_BAD_SHAPE;
+  if ((st = check_attn_shape(d, num_heads, dtype)) != MTGR_OK) return st;
+  if ((st = check_user_rows(b, d, dtype)) != MTGR_OK) return st;
+  if (!mask_mode_ok(mask_mode)) return MTGR_ERR_UNSUPPORTED;
+  // the prep tables of this call (no candidate index: the attention does not read it)
+  Sizes z = sizes_for(b, d, 0, 0, MTGR_F32, num_heads);
+  z.C = 0;
+  const Plan pl = make_plan(z);
+  if (pl.total > kNoAllocScratchBytes) return MTGR_ERR_SCRATCH_LIMIT;
+  if (b->num_users == 0 || b->num_tokens == 0) return MTGR_OK;
+  if (!qkvu || !y_gated) return MTGR_ERR_NULL_ARG;
+  void* ws = nullptr;
+  MTGR_TRY(scratch_for_current_device(&ws));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const PrepBufs pb = prep_bufs(ws, pl);
+  // the host's work order for the grid size, in place of a heap vector
+  int32_t order_buf[kLptMaxUsers];
+  MTGR_TRY(launch_prep(b->num_users, 0, b->offsets, b->group_ids, q_tile_for(dtype), q_tile_fwd_for(dtype), num_heads,
+                       pb, false, s));
+  MTGR_TRY(attention(b, d, num_heads, dtype, mask_mode, pb, qkvu, y_gated, s, nullptr, order_buf));
   return MTGR_OK;
 }
 

@@ -134,15 +134,16 @@ inline mtgr_status check_encoder(const mtgr_encoder_params* p) {
 inline int64_t user_len(const mtgr_batch* b, int32_t u) { return b->offsets_host[u + 1] - b->offsets_host[u]; }
 
 // The order in which users' work is dealt: longest first, ties by index (B <= kLptMaxUsers), else
-// index order.  The same rule as the device's batch prep.
-inline std::vector<int32_t> user_order(const mtgr_batch* b) {
+// index order.  The same rule as the device's batch prep.  `order` has room for B entries; the sort
+// is in place (a total order, so std::sort needs no buffer of its own).
+inline void user_order(const mtgr_batch* b, int32_t* order) {
   const int32_t B = b->num_users;
-  std::vector<int32_t> order(B);
   for (int32_t i = 0; i < B; ++i) order[i] = i;
   if (B <= kLptMaxUsers)
-    std::stable_sort(order.begin(), order.end(),
-                     [&](int32_t x, int32_t y) { return user_len(b, x) > user_len(b, y); });
-  return order;
+    std::sort(order, order + B, [&](int32_t x, int32_t y) {
+      const int64_t lx = user_len(b, x), ly = user_len(b, y);
+      return lx > ly || (lx == ly && x < y);
+    });
 }
 
 // XCD that group g = p*H + h goes to: round k = g / 8 takes groups 8k .. 8k+7, XCD x the group
@@ -152,15 +153,30 @@ inline int xcd_of_group(int64_t g) {
   return (int)((k & 1) ? (kXcdCount - 1 - r) : r);
 }
 
-// q-tiles queued on each XCD.
-inline void xcd_queue_tiles(const mtgr_batch* b, int H, int q_tile, int64_t tiles[kXcdCount]) {
-  const std::vector<int32_t> order = user_order(b);
+// q-tiles queued on each XCD.  `order_buf` (room for B entries, may be NULL above kLptMaxUsers
+// users) holds the work order.
+inline void xcd_queue_tiles(const mtgr_batch* b, int H, int q_tile, int64_t tiles[kXcdCount], int32_t* order_buf) {
+  const int32_t B = b->num_users;
+  if (B <= kLptMaxUsers) user_order(b, order_buf);
   for (int x = 0; x < kXcdCount; ++x) tiles[x] = 0;
-  const int64_t G = (int64_t)b->num_users * H;
-  for (int64_t g = 0; g < G; ++g) tiles[xcd_of_group(g)] += (user_len(b, order[g / H]) + q_tile - 1) / q_tile;
+  const int64_t G = (int64_t)B * H;
+  for (int64_t g = 0; g < G; ++g) {
+    const int32_t p = (int32_t)(g / H);
+    const int32_t u = B <= kLptMaxUsers ? order_buf[p] : p;
+    tiles[xcd_of_group(g)] += (user_len(b, u) + q_tile - 1) / q_tile;
+  }
+}
+inline void xcd_queue_tiles(const mtgr_batch* b, int H, int q_tile, int64_t tiles[kXcdCount]) {
+  std::vector<int32_t> order(b->num_users <= kLptMaxUsers ? b->num_users : 0);
+  xcd_queue_tiles(b, H, q_tile, tiles, order.data());
 }
 
 // The attention grid, in workgroups per XCD: the longest XCD queue.
+inline int64_t xcd_grid_slots(const mtgr_batch* b, int H, int q_tile, int32_t* order_buf) {
+  int64_t tiles[kXcdCount];
+  xcd_queue_tiles(b, H, q_tile, tiles, order_buf);
+  return *std::max_element(tiles, tiles + kXcdCount);
+}
 inline int64_t xcd_grid_slots(const mtgr_batch* b, int H, int q_tile) {
   int64_t tiles[kXcdCount];
   xcd_queue_tiles(b, H, q_tile, tiles);

@@ -28,7 +28,7 @@ MASK_MODES = {"dynamic": MTGR_MASK_DYNAMIC, "causal": MTGR_MASK_CAUSAL, "full": 
 NORM_MODES = {"group": MTGR_NORM_GROUP, "shared": MTGR_NORM_SHARED}
 STATUS_NAMES = {0: "MTGR_OK", 1: "MTGR_ERR_NULL_ARG", 2: "MTGR_ERR_BAD_SHAPE",
                 3: "MTGR_ERR_BAD_BATCH", 4: "MTGR_ERR_UNSUPPORTED", 5: "MTGR_ERR_WORKSPACE",
-                6: "MTGR_ERR_HIP"}
+                6: "MTGR_ERR_HIP", 7: "MTGR_ERR_SCRATCH_LIMIT"}
 
 # every symbol include/mtgr.h declares
 EXPORTED = [
@@ -40,7 +40,7 @@ EXPORTED = [
     "mtgr_hash_index_bytes", "mtgr_hash_arena_bytes", "mtgr_hash_init", "mtgr_hash_insert_workspace_size",
     "mtgr_hash_insert", "mtgr_hash_lookup", "mtgr_hash_evict", "mtgr_hash_evict_older", "mtgr_hash_rebuild",
     "mtgr_hash_get_stats", "mtgr_dedup_workspace_size", "mtgr_dedup",
-    "mtgr_tokenize_workspace_size", "mtgr_tokenize",
+    "mtgr_tokenize_workspace_size", "mtgr_tokenize", "mtgr_attention_fwd_noalloc",
 ]
 TOK_MAX_FIELDS = 8
 TOK_KEY_SHIFT = 40   # store key of (table, id) for the tokenizer: (table << 40) | id (include/mtgr.h)
@@ -128,6 +128,7 @@ def lib():
         L.mtgr_linear_fwd.argtypes = [c_i64, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]
         L.mtgr_attention_fwd.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz,
                                          c_vp]
+        L.mtgr_attention_fwd_noalloc.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]
         L.mtgr_validate_batch.argtypes = [P(MtgrBatch), c_vp, c_sz, c_vp, P(c_i32)]
         L.mtgr_debug_mask.argtypes = [P(MtgrBatch), c_i32, c_i32, c_vp, c_vp, c_sz, c_vp]
         L.mtgr_attention_bwd_workspace_size.argtypes = [P(MtgrBatch), c_i32, c_i32, c_i32, P(c_sz)]
@@ -326,6 +327,12 @@ def mtgr_attention_fwd(batch: DeviceBatch, d: int, num_heads: int, dtype: int, m
     _check("mtgr_attention_fwd", lib().mtgr_attention_fwd(
         ctypes.byref(batch.c), d, num_heads, dtype, mask_mode, _ptr(qkvu), _ptr(y_gated), _ptr(ws),
         ws.numel(), _stream(stream)))
+
+
+def mtgr_attention_fwd_noalloc(batch: DeviceBatch, d: int, num_heads: int, dtype: int, mask_mode: int, qkvu,
+                               y_gated, stream=None):
+    _check("mtgr_attention_fwd_noalloc", lib().mtgr_attention_fwd_noalloc(
+        ctypes.byref(batch.c), d, num_heads, dtype, mask_mode, _ptr(qkvu), _ptr(y_gated), _stream(stream)))
 
 
 def mtgr_attention_bwd(batch: DeviceBatch, d: int, num_heads: int, dtype: int, mask_mode: int, qkvu,

@@ -29,7 +29,8 @@
  *   - Every buffer is owned by the caller.  "device" pointers are HIP device memory of the
  *     current device; "host" pointers are ordinary host memory read during the call only.
  *   - The library never allocates device memory: scratch space is a caller-provided workspace
- *     whose size the *_workspace_size functions report.  It keeps no state between calls.
+ *     whose size the *_workspace_size functions report.  It keeps no state between calls.  The one
+ *     exception is mtgr_attention_fwd_noalloc, whose scratch is a fixed array of the library.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call returns
  *     after enqueueing.  Faults inside kernels surface at the caller's next synchronisation.
  *   - Argument and shape errors are found on the host before anything is enqueued and are
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define MTGR_ABI_VERSION 4
+#define MTGR_ABI_VERSION 5
 
 typedef enum {
   MTGR_OK = 0,
@@ -62,7 +63,9 @@ typedef enum {
   MTGR_ERR_BAD_BATCH = 3,    /* offsets not monotone, T or C inconsistent, bad group order */
   MTGR_ERR_UNSUPPORTED = 4,  /* dtype / epilogue / option not implemented */
   MTGR_ERR_WORKSPACE = 5,    /* workspace NULL or smaller than the reported size */
-  MTGR_ERR_HIP = 6           /* a HIP launch or copy failed */
+  MTGR_ERR_HIP = 6,          /* a HIP launch or copy failed */
+  MTGR_ERR_SCRATCH_LIMIT = 7 /* mtgr_attention_fwd_noalloc: the batch's prep tables exceed the
+                                library's fixed scratch (4 MiB per device) */
 } mtgr_status;
 
 typedef enum { MTGR_F32 = 0, MTGR_BF16 = 1 } mtgr_dtype;
@@ -211,6 +214,17 @@ mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int3
 mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
                                int32_t mask_mode, const void* qkvu, void* y_gated, void* ws,
                                size_t ws_bytes, void* stream);
+
+/* mtgr_attention_fwd without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).  The batch-prep tables
+ * live in a fixed scratch array of 4 MiB that the library holds on every device it runs on until the
+ * process ends: about 32 bytes per user plus 8 bytes per (user, head) group and 8 per XCD (e.g. up to
+ * 26,000 users at 16 heads, 52,000 at 6).  A batch that needs more returns MTGR_ERR_SCRATCH_LIMIT before anything is
+ * enqueued.  Every call on one device writes that device's scratch: calls that overlap on one GPU (two
+ * streams, or two host threads) race and must be serialised by the caller.  Results equal
+ * mtgr_attention_fwd's bit for bit.  No device or host heap memory is allocated. */
+mtgr_status mtgr_attention_fwd_noalloc(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
+                                       int32_t mask_mode, const void* qkvu, void* y_gated, void* stream);
 
 /* Backward of mtgr_attention_fwd: qkvu device [T][4d], v_tilde device [T][d] (the ungated
  * V~ = (silu(Q K^T) / N (.) M) V of the forward), dy_gated device [T][d] (dLoss/d(V~ (.) U)), all

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol():
     L = M.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert M.mtgr_abi_version() == 4
+    assert M.mtgr_abi_version() == 5
     assert M.mtgr_status_str(0) == "ok"
     assert "workspace" in M.mtgr_status_str(5)
 
@@ -142,6 +142,25 @@ def test_linear_and_groupln_argument_checks():
     ws = 1 << 20
     assert L.mtgr_attention_fwd(ctypes.byref(b), 256, 4, M.MTGR_BF16, 7, FAKE, FAKE, FAKE, ws, None) == 4
     assert L.mtgr_debug_mask(ctypes.byref(b), 0, -1, FAKE, FAKE, ws, None) == 4
+
+
+def test_attention_noalloc_host_checks():
+    """The no-allocation attention entry checks its arguments and the fixed scratch limit on the host,
+    before any HIP call."""
+    L = M.lib()
+    b, _keep = _batch([0, 10, 30])
+    assert L.mtgr_attention_fwd_noalloc(ctypes.byref(b), 256, 4, M.MTGR_BF16, 7, FAKE, FAKE, None) == 4
+    assert L.mtgr_attention_fwd_noalloc(ctypes.byref(b), 256, 3, M.MTGR_BF16, 0, FAKE, FAKE, None) == 2
+    assert L.mtgr_attention_fwd_noalloc(ctypes.byref(b), 256, 4, M.MTGR_BF16, 0, None, FAKE, None) == 1
+    assert L.mtgr_attention_fwd_noalloc(None, 256, 4, M.MTGR_BF16, 0, FAKE, FAKE, None) == 1
+    # 65,536 one-token users at 16 heads: prep tables of ~10 MB, beyond the 4 MiB scratch
+    big, _keep2 = _batch(np.arange(65537))
+    assert L.mtgr_attention_fwd_noalloc(ctypes.byref(big), 1024, 16, M.MTGR_BF16, 0, FAKE, FAKE, None) == 7
+    assert "scratch" in M.mtgr_status_str(7)
+    # an empty batch is a no-op
+    off = np.zeros(1, np.int64)
+    e = M.MtgrBatch(0, 0, 0, off.ctypes.data, None, None, None)
+    assert L.mtgr_attention_fwd_noalloc(ctypes.byref(e), 256, 4, M.MTGR_BF16, 0, None, None, None) == 0
 
 
 def test_empty_batch_is_a_no_op():
