@@ -7,10 +7,8 @@
 // attend to each other (sequence packing, chenhuiyu blog "MTGR", training-system section).
 //
 // Work item = (user, head, q-tile of 32 NW rows); one workgroup of NW wavefronts x 32 query rows.
-// The forward runs NW = 4 (128 rows, two workgroups per CU); 8 wavefronts sharing each K/V tile
-// over 256 rows halve the global K/V traffic per FLOP but measured slower (6.09 vs 5.85 ms per
-// layer on the large workload).  Work items are ordered longest user first (LPT) by the prep
-// kernels.
+// The forward runs NW = 4 (128 rows, two workgroups per CU, so two wavefronts per SIMD).  Work
+// items are ordered longest user first (LPT) by the prep kernels.
 //
 // Key range of a work item.  Tokens are ordered U, S, R, C.  Static keys [0, n_static) are
 // visible to every row; R keys [n_static, rc_end) only to R/C rows, by timestamp; C keys only
@@ -29,9 +27,22 @@
 // reads (ds_read_b64_tr_b16) that hand every lane the 8 keys of its feature column in the order
 // the score accumulator holds them.
 //
-// LDS per workgroup: K 2 x 64 x (d_h+8) and V 2 x 64 x (d_h+32) bf16 (double-buffered,
-// register-staged global->LDS copies), ~75 KB at d_h = 128 and NW = 4, shared afterwards with the
-// fp32 staging of the output rows.
+// Staging: K, V and timestamp tiles go global -> LDS by LDS-direct buffer loads (no registers,
+// no LDS write instructions), double-buffered: the loads of tile k+1 are issued before tile k is
+// computed and waited for at the barrier that ends it.  Rows are unpadded and XOR-swizzled in
+// 16-byte chunks.  LDS per workgroup: 4 x 64 x d_h bf16 + 512 B (65 KB at d_h = 128), reused
+// afterwards for the fp32 staging of the output rows.
+//
+// Where the time goes (large workload, d_h = 128; MFMA work is within 2% of the algorithmic
+// count).  A wavefront's 64-key tile costs 32 MFMAs (1024 cycles), ~176 vector instructions for
+// SiLU (64 of them transcendental, 8 cycles each on gfx950) and 48 LDS fragment reads (32 KB);
+// vector work and MFMAs of one wavefront barely overlap, across the two wavefronts of a SIMD
+// about a quarter of the MFMA time does.  Measured per layer: register-staged copies 5.69 ms,
+// LDS-direct 5.32 ms.  Tried and slower: SiLU interleaved between the MFMAs of one wavefront
+// (5.63 ms); s_setprio raised over the MFMA phases (no change); an 8-wavefront ping-pong, where
+// the two wavefronts of a SIMD alternate MFMA and vector phases between workgroup barriers over
+// three LDS slots (co-issue doubled but barrier waits grew: 8% slower); 8 wavefronts over 256
+// rows with plain double buffering (4% slower).
 #include "kernels.h"
 
 namespace mtgr {
@@ -41,6 +52,17 @@ namespace {
 typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 constexpr int BKV = 64;             // keys per tile
+
+// LDS-direct buffer load: lane l's `bytes` (4 or 16) land at lds + l * bytes (lds wave-uniform).
+// Kept in a device function of its own: written in a kernel's body, the builtin stops the host
+// pass from emitting that kernel's launch stub.
+__device__ __forceinline__ void lds_load(__amdgpu_buffer_rsrc_t r, void* lds, int bytes, uint32_t voff,
+                                         uint32_t soff) {
+  if (bytes == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, soff, 0, 0);
+}
 
 __device__ __forceinline__ int find_slot(const int32_t* __restrict__ tile_off, int B, int item) {
   int lo = 0, hi = B;  // largest p with tile_off[p] <= item
@@ -60,26 +82,31 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
     const float* __restrict__ ts, const bf16* __restrict__ qkvu, bf16* __restrict__ y,
     bf16* __restrict__ vt) {
   constexpr int BQ = 32 * NW;                     // query rows per work item
-  constexpr int NTH = 64 * NW;                    // threads per workgroup
   static_assert(BQ == kAttnFwdQTileBf16, "work items come from queues built with the forward's q-tile");
-  constexpr int KP = DH + 8;                     // K row pitch: 16-byte reads of 16 rows hit distinct banks
-  // V row pitch: a transposing read by 32 lanes touches 4 rows x 2 column chunks of 32 bytes;
-  // a pitch of 16 (mod 64) dwords puts those 8 chunks on disjoint banks.
-  constexpr int VP = DH + 32;
-  constexpr int DCH = DH / 8;                    // 16-byte chunks per key row
-  constexpr int CH = BKV * DCH / NTH;            // K (and V) chunks per thread per tile
+  static_assert(NW == 4, "the epilogue stages each wavefront's rows in one of the four tile buffers");
+  constexpr int CPR = DH / 8;                    // 16-byte chunks per key row
+  constexpr int RB = 1024 / (DH * 2);            // key rows per 1 KB LDS-direct block
+  constexpr int NBW = BKV / RB / NW;             // blocks per wavefront, per operand and tile
+  constexpr int TILE = BKV * DH;                 // bf16 elements of one K or V tile
   constexpr int NT = DH / 32;                    // output tiles of 32 features
-  static_assert(CH * NTH == BKV * DCH && CH <= 4, "staging layout");
+  static_assert(NBW * RB * NW == BKV && NBW >= 1, "staging layout");
+  static_assert(32 * DH * sizeof(float) <= TILE * sizeof(bf16), "a wavefront's output rows fit one tile buffer");
 
-  // One LDS arena: K and V^T tiles (double-buffered) and the tile timestamps during the key loop;
-  // reused afterwards to stage each wavefront's output rows for vectorised stores.
-  constexpr int OP = DH + 4;                                   // fp32 pitch of staged output rows
-  constexpr size_t kLoopBytes = (2 * BKV * KP + 2 * BKV * VP) * sizeof(bf16) + 2 * BKV * sizeof(float);
-  constexpr size_t kEpiBytes = NW * 32 * OP * sizeof(float) + NW * 32 * sizeof(float);
-  __shared__ __attribute__((aligned(16))) char arena[kLoopBytes > kEpiBytes ? kLoopBytes : kEpiBytes];
-  bf16 (*Ks)[BKV][KP] = reinterpret_cast<bf16 (*)[BKV][KP]>(arena);
-  bf16 (*Vs)[BKV][VP] = reinterpret_cast<bf16 (*)[BKV][VP]>(arena + 2 * BKV * KP * sizeof(bf16));
-  float (*Ts)[BKV] = reinterpret_cast<float (*)[BKV]>(arena + (2 * BKV * KP + 2 * BKV * VP) * sizeof(bf16));
+  // K and V tiles, double-buffered, as separate arrays so that reads of one buffer are not held
+  // up behind the LDS-direct loads filling the other.  Rows are unpadded; the 16-byte chunk c of
+  // row r sits at chunk position c ^ swk(r) (K) or c ^ swv(r) (V), which keeps the fragment reads
+  // below free of bank conflicts (64 banks of 4 bytes).
+  __shared__ __attribute__((aligned(1024))) bf16 Ks0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 Ks1[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs0[TILE];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs1[TILE];
+  __shared__ __attribute__((aligned(256))) float Ts0[BKV];
+  __shared__ __attribute__((aligned(256))) float Ts1[BKV];
+  __shared__ float Ps_all[NW * 32];              // candidate rows' own-term weights, epilogue only
+  // K fragment reads: 16 lanes take rows r..r+15 at one logical chunk
+  auto swk = [](int r) { return DH == 128 ? (r & 15) : ((r >> 1) & 7); };
+  // V transposing reads: 32 lanes take 4 rows x 4 chunks of one 64-byte column block
+  auto swv = [](int r) { return DH == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); };
 
   // Work decode: workgroup ids go round-robin to the XCDs, so id % 8 is the XCD and id / 8 the
   // position in that XCD's queue; the queue lists its (user, head) groups' q-tiles back to back,
@@ -107,7 +134,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
   const bf16* Up = Qp + 3 * d;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   const int wq0 = q0 + w * 32;
   const int qi = wq0 + l32;
@@ -137,39 +164,55 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[t][r] = 0.f;
 
-  // Staging: every thread copies CH 16-byte chunks of the K tile and CH of the V tile (both kept
-  // row-major in LDS), through buffer loads over this user's rows of head h sized to the first
-  // kend keys, so keys at or past kend read as zero.  Per-lane byte offset in a VGPR, the tile
-  // offset in an SGPR.
-  bf16x8 stg[2 * CH];
-  float rt = INFINITY;
+  // Staging: LDS-direct buffer loads (global -> LDS without registers).  One wavefront
+  // instruction fills a contiguous 1 KB block, lane l its 16 bytes at 16 l, i.e. row l / CPR,
+  // chunk position l % CPR of the block's RB rows; the lane fetches the global chunk that the
+  // swizzle puts there.  The buffers span this user's rows of head h up to kend, with the tile
+  // offset in the SGPR offset: the range check covers both, so keys at or past kend land in LDS
+  // as zeros.  Timestamps come the same way (one wavefront, 4 bytes a lane).
   const uint32_t row_bytes = (uint32_t)(ld * 2);
   const int nbytes = (int)((uint32_t)kend * row_bytes);
   const __amdgpu_buffer_rsrc_t k_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Kp, (short)0, nbytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t v_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Vp, (short)0, nbytes, 0x00020000);
-  const int st_key = tid / DCH, st_c = tid % DCH;             // chunk i: key st_key + i*(NTH/DCH)
-  constexpr int KSTEP = NTH / DCH;
-  const uint32_t st_off = (uint32_t)st_key * row_bytes + st_c * 16;
-
-  auto stage_load = [&](int k0) {
+  const __amdgpu_buffer_rsrc_t t_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(ts + base), (short)0, kend * (int)sizeof(float), 0x00020000);
+  uint32_t vo_k[NBW], vo_v[NBW];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const uint32_t so = (uint32_t)(k0 + i * KSTEP) * row_bytes;
-      stg[i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(k_rsrc, st_off, so, 0));
-      stg[CH + i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(v_rsrc, st_off, so, 0));
-    }
-    if (MODE == kMaskDynamic && tid < BKV) rt = (k0 + tid < kend) ? ts[base + k0 + tid] : INFINITY;
-  };
-  auto stage_store = [&](int buf) {
+  for (int i = 0; i < NBW; ++i) {
+    const int row = (w * NBW + i) * RB + lane / CPR, p = lane % CPR;
+    vo_k[i] = (uint32_t)row * row_bytes + (uint32_t)((p ^ swk(row)) * 16);
+    vo_v[i] = (uint32_t)row * row_bytes + (uint32_t)((p ^ swv(row)) * 16);
+  }
+  auto stage = [&](bf16* kd, bf16* vd, float* td, int k0) {
+    const uint32_t so = (uint32_t)k0 * row_bytes;
 #pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      *reinterpret_cast<bf16x8*>(&Ks[buf][st_key + i * KSTEP][st_c * 8]) = stg[i];
-      *reinterpret_cast<bf16x8*>(&Vs[buf][st_key + i * KSTEP][st_c * 8]) = stg[CH + i];
+    for (int i = 0; i < NBW; ++i) {
+      lds_load(k_rsrc, kd + (w * NBW + i) * 512, 16, vo_k[i], so);
+      lds_load(v_rsrc, vd + (w * NBW + i) * 512, 16, vo_v[i], so);
     }
-    if (MODE == kMaskDynamic && tid < BKV) Ts[buf][tid] = rt;
+    if (MODE == kMaskDynamic && w == 0) lds_load(t_rsrc, td, 4, (uint32_t)lane * 4u, (uint32_t)k0 * 4u);
+  };
+  // every wavefront's LDS-direct loads have landed: its own wait, then the barrier
+  auto publish = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+    __syncthreads();
   };
 
-  auto tile_needed = [&](int buf, int k0) {
+  // fragment offsets (bytes within a tile).  K, k-step ks: row mt*32 + l32, logical chunk 2 ks + hh.
+  uint32_t koff[DH / 16];
+#pragma unroll
+  for (int ks = 0; ks < DH / 16; ++ks) koff[ks] = (uint32_t)((l32 * CPR + ((2 * ks + hh) ^ swk(l32))) * 16);
+  // V, output tile t: the transposing read of lane s in a 16-lane group starts at row
+  // rl = 4 hh + (s / 4) of an 8-row group and features t*32 + 16*(group % 2) + 4*(s % 4).
+  uint32_t voff[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int rl = 4 * hh + ((lane & 15) >> 2);
+    const int c = 4 * t + 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);
+    voff[t] = (uint32_t)((rl * CPR + (c ^ swv(rl))) * 16 + 8 * (lane & 1));
+  }
+
+  auto tile_needed = [&](const float* Tb, int k0) {
     if (MODE == kMaskFull) return wave_rows;
     if (MODE == kMaskCausal) return wave_rows && k0 <= wq0 + 31;
     bool need = wave_rows && (k0 < ns || (wave_rc && k0 < rc_end));
@@ -177,7 +220,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
       // pure R tile: skip when no key is earlier than the wavefront's latest R/C row and the
       // wavefront's own R rows (the diagonal) are not in it
       const int j = k0 + lane;
-      const float tk = (j < kend) ? Ts[buf][lane] : INFINITY;
+      const float tk = (j < kend) ? Tb[lane] : INFINITY;
       const float tmin = wave_min(tk);
       const bool diag = max(wr_lo, k0) < min(wr_hi, k0 + BKV);
       if (!diag && tmin >= wave_tmax) need = false;
@@ -185,7 +228,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
     return need;
   };
   bf16x8 pa[4];
-  auto scores = [&](int buf, int k0) {
+  auto scores = [&](const bf16* Kb, const float* Tb, int k0) {
     f32x16 sc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -195,7 +238,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
     for (int ks = 0; ks < DH / 16; ++ks) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&Ks[buf][mt * 32 + l32][ks * 16 + hh * 8]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Kb) + koff[ks] +
+                                                            mt * 32 * DH * (int)sizeof(bf16));
         sc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[mt], 0, 0, 0);
       }
     }
@@ -212,14 +256,15 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
       // Mask.  With jb = k0 + 4*hh this lane's keys are jb + dk, dk = mt*32 + 8*(r/4) + r%4 a
       // compile-time constant, so the visibility rule (the same as mtgr_visible) becomes three
       // integer compares against per-lane offsets plus one timestamp compare.  Keys at or past
-      // kend were loaded as zeros: their score and silu are 0 already.
+      // kend were loaded as zeros: their score and silu are 0 already (their timestamps are 0 too,
+      // but the per-lane limits already make them invisible).
       const int jb = k0 + 4 * hh;
       const int lim_static = ns - jb, lim_rc = rc_end - jb, self = qi - jb;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const f32x4 t4 = *reinterpret_cast<const f32x4*>(&Ts[buf][mt * 32 + 8 * g4 + 4 * hh]);
+          const f32x4 t4 = *reinterpret_cast<const f32x4*>(&Tb[mt * 32 + 8 * g4 + 4 * hh]);
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             const int r = g4 * 4 + c;
@@ -234,7 +279,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
       }
     }
   };
-  auto accumulate = [&](int buf) {
+  auto accumulate = [&](const bf16* Vb) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -243,29 +288,33 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
         // kb + 4*hh + jj%4 (+8 for jj >= 4), kb = (ks/2)*32 + (ks%2)*16, feature t*32 + lane%32.
         // ds_read_b64_tr_b16 hands lane i of a 16-lane group element i%4 of the 4-element rows
         // addressed by lanes i/4 + 4e: point lane s at row kb + 4*hh + s/4, features
-        // t*32 + 16*(group%2) + 4*(s%4), and each read returns 4 keys of one feature column.
-        const int kb = (ks >> 1) * 32 + (ks & 1) * 16 + 4 * hh + (lane & 15) / 4;
-        const int fc = t * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&Vs[buf][kb][fc]));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(&Vs[buf][kb + 8][fc]));
+        // t*32 + 16*(group%2) + 4*(s%4) (voff[t], swizzled), and each read returns 4 keys of one
+        // feature column.
+        const char* vb = reinterpret_cast<const char*>(Vb) + voff[t] + ((ks >> 1) * 32 + (ks & 1) * 16) * DH * 2;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vb);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + 8 * DH * 2));
         const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], vf, o[t], 0, 0, 0);
       }
     }
   };
 
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int cur = kt & 1;
+  // Key loop, unrolled by two so that each half names its buffers at compile time: the next
+  // tile's LDS-direct loads go out first and land while this tile is computed.
+  auto step = [&](const bf16* Kb, const bf16* Vb, const float* Tb, bf16* Kn, bf16* Vn, float* Tn, int kt) {
     const int k0 = kt * BKV;
-    const bool need = tile_needed(cur, k0);
-    if (need) scores(cur, k0);
-    if (kt + 1 < nkt) stage_load(k0 + BKV);
-    if (need) accumulate(cur);
-    if (kt + 1 < nkt) stage_store(cur ^ 1);
-    __syncthreads();
+    if (kt + 1 < nkt) stage(Kn, Vn, Tn, k0 + BKV);
+    if (tile_needed(Tb, k0)) {
+      scores(Kb, Tb, k0);
+      accumulate(Vb);
+    }
+    publish();
+  };
+  stage(Ks0, Vs0, Ts0, 0);
+  publish();
+  for (int kt = 0; kt < nkt; kt += 2) {
+    step(Ks0, Vs0, Ts0, Ks1, Vs1, Ts1, kt);
+    if (kt + 1 < nkt) step(Ks1, Vs1, Ts1, Ks0, Vs0, Ts0, kt + 1);
   }
 
   if (!wave_rows) return;
@@ -285,15 +334,17 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
   const float s_self = part + __shfl_xor(part, 32, kWave);
   const float p_self = q_c ? (float)(bf16)silu_rcp(s_self) : 0.f;
 
-  // Stage this wavefront's O rows (fp32) in LDS: element r of tile t is row 8*(r/4)+4*hh+r%4,
-  // feature t*32 + l32.  The key loop ended with a barrier, so the arena is free.
-  float* Os = reinterpret_cast<float*>(arena) + w * 32 * OP;
-  float* Ps = reinterpret_cast<float*>(arena) + NW * 32 * OP + w * 32;
+  // Stage this wavefront's O rows (fp32) in LDS, one tile buffer per wavefront (the key loop
+  // ended with a barrier and no loads in flight, so they are free): element r of tile t is row
+  // 8*(r/4)+4*hh+r%4, feature t*32 + l32, stored at column feature ^ (32 * ((row / 4) % 2)) of an
+  // unpadded row so that the two lane halves write disjoint banks.
+  float* Os = reinterpret_cast<float*>(w == 0 ? Ks0 : w == 1 ? Ks1 : w == 2 ? Vs0 : Vs1);
+  float* Ps = Ps_all + w * 32;
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int r = 0; r < 16; ++r)
-      Os[(8 * (r >> 2) + 4 * hh + (r & 3)) * OP + t * 32 + l32] = o[t][r];
+      Os[(8 * (r >> 2) + 4 * hh + (r & 3)) * DH + ((t ^ hh) * 32 + l32)] = o[t][r];
   if (hh == 0) Ps[l32] = p_self;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -301,12 +352,13 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
 
   // y = (O + p_self v) / n (.) u, 8 features per lane step, 16-byte loads and stores.
   const float inv_n = 1.0f / (float)n;
-  for (int idx = lane; idx < 32 * DCH; idx += 64) {
-    const int ql = idx / DCH, c = idx % DCH;
+  for (int idx = lane; idx < 32 * CPR; idx += 64) {
+    const int ql = idx / CPR, c = idx % CPR;
     const int q = wq0 + ql;
     if (q >= n) continue;
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Os[ql * OP + c * 8]);
-    const f32x4 a1 = *reinterpret_cast<const f32x4*>(&Os[ql * OP + c * 8 + 4]);
+    const int col = (c * 8) ^ (32 * ((ql >> 2) & 1));
+    const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Os[ql * DH + col]);
+    const f32x4 a1 = *reinterpret_cast<const f32x4*>(&Os[ql * DH + col + 4]);
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 4; ++e) { acc[e] = a0[e]; acc[e + 4] = a1[e]; }
