@@ -172,12 +172,16 @@ mtgr_status mtgr_attention_bwd_workspace_size(const mtgr_batch* b, int32_t d, in
 /* Full encoder: L blocks over x_in (device float [T][d]) then the head at candidate tokens.
  * hidden_out (device float [T][d], may be NULL) receives the final hidden states and may alias
  * x_in; logits (device float [C][2]) receive (CTR, CTCVR) logits in packed candidate order
- * (user-major, then token order within the user).  No sigmoid is applied. */
+ * (user-major, then token order within the user).  No sigmoid is applied.
+ * Follows [P3] 方法 (the stack of HSTU blocks over the packed sample D) and [P1]/[P2] token
+ * section with [P5] 7.3.1 (multi-task CTR/CTCVR scores read at the candidate tokens). */
 mtgr_status mtgr_encoder_fwd(const mtgr_encoder_params* p, const mtgr_batch* b, const float* x_in,
                              float* hidden_out, float* logits, void* ws, size_t ws_bytes,
                              void* stream);
 
-/* One block: x_out = block(x_in), both device float [T][d]; x_out may alias x_in. */
+/* One block: x_out = block(x_in), both device float [T][d]; x_out may alias x_in.
+ * The HSTU block of [P3] 方法, its two update equations (attention update, then the residual
+ * MLP), with GroupLN before each ([P5] 7.3.3) and the mask of mask_mode ([P5] 7.3.4). */
 mtgr_status mtgr_block_fwd(const mtgr_block_params* p, const mtgr_batch* b, const float* x_in,
                            float* x_out, void* ws, size_t ws_bytes, void* stream);
 
@@ -197,20 +201,27 @@ mtgr_status mtgr_block_bwd(const mtgr_block_params* p, const mtgr_batch* b, cons
 /* GroupLN over T rows of width d: y = (x - mean) / sqrt(var + eps) * gamma[g] + beta[g].
  * x in `in_dtype`, y in `out_dtype`, gamma/beta [4][d] in `param_dtype` ([1][d] suffices with
  * MTGR_NORM_SHARED, which uses g = 0 for every row).
- * Supported (in, out): (F32, F32), (F32, BF16), (BF16, BF16). */
+ * Supported (in, out): (F32, F32), (F32, BF16), (BF16, BF16).
+ * The GLN equation of [P5] 7.3.3 (LayerNorm statistics per token, affine parameters per token
+ * group; [P3] 方法, GLN paragraph); the variance is the biased one (1/d). */
 mtgr_status mtgr_groupln_fwd(const mtgr_batch* b, int32_t d, int32_t in_dtype, int32_t out_dtype,
                              int32_t param_dtype, int32_t norm_mode, const void* gamma,
                              const void* beta, float eps, const void* x, void* y, void* stream);
 
 /* out = epilogue(a[M][K] W[N][K]^T + bias[N]); a, W, bias in `dtype`; see MTGR_EPI_*.
- * bf16: K a multiple of 64 and >= 128, N a multiple of 8.  fp32: K a multiple of 4. */
+ * bf16: K a multiple of 64 and >= 128, N a multiple of 8.  fp32: K a multiple of 4.
+ * The affine maps of the block ([P3] 方法: the Q/K/V/U projection of the first update
+ * equation, the two MLP layers with SiLU and the residual add of the second). */
 mtgr_status mtgr_linear_fwd(int64_t M, int32_t N, int32_t K, int32_t dtype, int32_t epilogue,
                             const void* a, const void* w, const void* bias, const float* resid,
                             void* out, void* stream);
 
 /* Masked SiLU attention with the U gate for every user and head, under mask `mask_mode`
  * (MTGR_MASK_*): qkvu device [T][4d] in `dtype` -> y_gated device [T][d] in `dtype` (V~ (.) U).
- * The normaliser is the user's token count N in every mode. */
+ * The normaliser is the user's token count N in every mode.
+ * The V~ update equation of [P3] 方法 (silu(Q K^T) / N masked by M, times V, per head) with the
+ * U gate of the second update, under the rules of [P5] 7.3.4; users never attend to each other
+ * ([P1]/[P2] training-system section, sequence packing). */
 mtgr_status mtgr_attention_fwd(const mtgr_batch* b, int32_t d, int32_t num_heads, int32_t dtype,
                                int32_t mask_mode, const void* qkvu, void* y_gated, void* ws,
                                size_t ws_bytes, void* stream);
