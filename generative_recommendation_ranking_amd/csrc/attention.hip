@@ -38,7 +38,7 @@
 // SiLU (64 of them transcendental, 8 cycles each on gfx950) and 48 LDS fragment reads (32 KB);
 // vector work and MFMAs of one wavefront barely overlap, across the two wavefronts of a SIMD
 // about a quarter of the MFMA time does.  Measured per layer: register-staged copies 5.69 ms,
-// LDS-direct 5.32 ms.  Tried and slower: SiLU interleaved between the MFMAs of one wavefront
+// LDS-direct 5.32 ms, fragments requested one (K) and two (V) steps ahead of their MFMAs 5.23 ms.  Tried and slower: SiLU interleaved between the MFMAs of one wavefront
 // (5.63 ms); s_setprio raised over the MFMA phases (no change); an 8-wavefront ping-pong, where
 // the two wavefronts of a SIMD alternate MFMA and vector phases between workgroup barriers over
 // three LDS slots (co-issue doubled but barrier waits grew: 8% slower); 8 wavefronts over 256
@@ -234,14 +234,25 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[mt][r] = 0.f;
+    // the K fragments of k-step ks + 1 are requested before the MFMAs of k-step ks (the
+    // scheduling barriers keep the compiler from sinking the reads back to their use)
+    constexpr int NKS = DH / 16;
+    bf16x8 kf[2][2];
+    auto kread = [&](int ks, bf16x8* dst) {
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks) {
+      for (int mt = 0; mt < 2; ++mt)
+        dst[mt] = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Kb) + koff[ks] +
+                                                   mt * 32 * DH * (int)sizeof(bf16));
+    };
+    kread(0, kf[0]);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(Kb) + koff[ks] +
-                                                            mt * 32 * DH * (int)sizeof(bf16));
-        sc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[mt], 0, 0, 0);
-      }
+    for (int ks = 0; ks < NKS; ++ks) {
+      if (ks + 1 < NKS) kread(ks + 1, kf[(ks + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        sc[mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks & 1][mt], qf[ks], sc[mt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // sc[mt][r]: key k0 + mt*32 + 8*(r/4) + 4*hh + r%4, query qi
     // tiles every key of which is visible to every row of the wavefront skip the mask
@@ -280,22 +291,29 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
     }
   };
   auto accumulate = [&](const bf16* Vb) {
+    // B fragment (keys x features) of P V k-step ks and output tile t: slot jj of lane-half hh is
+    // key kb + 4*hh + jj%4 (+8 for jj >= 4), kb = (ks/2)*32 + (ks%2)*16, feature t*32 + lane%32.
+    // ds_read_b64_tr_b16 hands lane i of a 16-lane group element i%4 of the 4-element rows
+    // addressed by lanes i/4 + 4e: point lane s at row kb + 4*hh + s/4, features
+    // t*32 + 16*(group%2) + 4*(s%4) (voff[t], swizzled), and each read returns 4 keys of one
+    // feature column.  Fragments are requested two (ks, t) steps ahead of their MFMA.
+    constexpr int NS = 4 * NT;
+    auto vread = [&](int i) {
+      const int ks = i / NT, t = i % NT;
+      const char* vb = reinterpret_cast<const char*>(Vb) + voff[t] + ((ks >> 1) * 32 + (ks & 1) * 16) * DH * 2;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vb);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + 8 * DH * 2));
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 vf[3];
+    vf[0] = vread(0);
+    vf[1] = vread(1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        // B fragment (keys x features) of PV k-step ks: slot jj of lane-half hh is key
-        // kb + 4*hh + jj%4 (+8 for jj >= 4), kb = (ks/2)*32 + (ks%2)*16, feature t*32 + lane%32.
-        // ds_read_b64_tr_b16 hands lane i of a 16-lane group element i%4 of the 4-element rows
-        // addressed by lanes i/4 + 4e: point lane s at row kb + 4*hh + s/4, features
-        // t*32 + 16*(group%2) + 4*(s%4) (voff[t], swizzled), and each read returns 4 keys of one
-        // feature column.
-        const char* vb = reinterpret_cast<const char*>(Vb) + voff[t] + ((ks >> 1) * 32 + (ks & 1) * 16) * DH * 2;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vb);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb + 8 * DH * 2));
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], vf, o[t], 0, 0, 0);
-      }
+    for (int i = 0; i < NS; ++i) {
+      if (i + 2 < NS) vf[(i + 2) % 3] = vread(i + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      o[i % NT] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[i / NT], vf[i % 3], o[i % NT], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
