@@ -237,12 +237,34 @@ __device__ __forceinline__ void st8(float* p, const float (&v)[8]) {
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
 
+// Sum over the 64 lanes of a wavefront, through DPP row operations instead of LDS permutes: the
+// butterfly within each quad, the two halves of each row of 16 (mirror), then rows 0+1 and
+// 2+3 (broadcast of lane 15 into row 1 and 3) and the two halves (lane 31 into rows 2 and 3);
+// lane 63 then holds the total, which is read back as a scalar.  Fixed order: deterministic.
+template <int CTRL, int ROW_MASK> __device__ __forceinline__ float dpp_add(float v) {
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
+                                                                   false));
+}
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
+  v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
+  v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
+  v = dpp_add<0x140, 0xF>(v);   // row_mirror
+  v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// PF: prefetch row+1 while row is reduced (wide fp32 rows); without it a wavefront holds one row
+// and needs fewer registers, so more wavefronts share a SIMD (the bf16 variant).
 template <typename Tx, typename Tdz, typename Tp, typename Tout, bool PF>
 __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t rows_per_wave,
                                                      const Tx* __restrict__ x, const uint8_t* __restrict__ g,
                                                      const Tp* __restrict__ gamma, float eps, int gmask,
                                                      const Tdz* dz, const float* resid, Tout* dx,
                                                      float* __restrict__ part) {
+  // the residual path exists for fp32-input rows only (GroupLN1); the bf16 variant takes none
+  constexpr bool kResid = sizeof(Tx) == 4;
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nch = d >> 3;
@@ -259,6 +281,7 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
   const int64_t r0 = wave * rows_per_wave;
   const int64_t r1 = min(T, r0 + rows_per_wave);
   float ag[2][8], ab[2][8];
+  float gm[2][8];                                   // gamma of the current group, in registers
   int cur = -1;
   auto flush = [&]() {
     if (cur < 0) return;
@@ -274,157 +297,90 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
     }
   };
   const float inv_d = 1.0f / (float)d;
-  if constexpr (!PF) {
-    for (int64_t row = r0; row < r1; ++row) {
-      const int grp = g[row] & gmask;
-      if (grp != cur) {
-        flush();
-        cur = grp;
+  // With PF the loads of row+1 (x, dz and the residual) are issued before row is reduced, so a
+  // wavefront always has a row in flight.  Nothing else is loaded per row: vector loads retire in
+  // order, and a per-row gamma load issued after the prefetch would make every row wait for the
+  // next one.  gamma is loaded when the group changes (tokens come in group runs).
+  float v[2][8], dv[2][8], rs[2][8];
+  float nv[2][8], ndv[2][8], nrs[2][8];
+  auto load_row = [&](int64_t row, float (&a)[2][8], float (&b)[2][8], float (&c)[2][8]) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c)
+    for (int cc = 0; cc < 2; ++cc) {
+      const int ch = lane + 64 * cc;
+      if (ch < nch && row < r1) {
+        ld8(x + row * d + ch * 8, a[cc]);
+        ld8(dz + row * d + ch * 8, b[cc]);
+        if (kResid && resid) {
+          ld8(resid + row * d + ch * 8, c[cc]);
+        } else {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) { ag[c][i] = 0.f; ab[c][i] = 0.f; }
-      }
-      float v[2][8], dv[2][8];
-      float s1 = 0.f;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int ch = lane + 64 * c;
-        if (ch < nch) {
-          ld8(x + row * d + ch * 8, v[c]);
-          ld8(dz + row * d + ch * 8, dv[c]);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) s1 += v[c][i];
-        }
-      }
-      const float mean = wave_sum(s1) * inv_d;
-      float q = 0.f;
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-        if (lane + 64 * c < nch)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) { const float e = v[c][i] - mean; q += e * e; }
-      const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
-      float sa = 0.f, sb = 0.f;       // sum dxh, sum dxh * xh
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int ch = lane + 64 * c;
-        if (ch < nch) {
-          float gm[8];
-          ld8(gamma + grp * d + ch * 8, gm);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float xh = (v[c][i] - mean) * rstd;
-            const float dxh = dv[c][i] * gm[i];
-            ag[c][i] += dv[c][i] * xh;
-            ab[c][i] += dv[c][i];
-            sa += dxh;
-            sb += dxh * xh;
-            v[c][i] = xh;
-            dv[c][i] = dxh;
-          }
-        }
-      }
-      const float ma = wave_sum(sa) * inv_d, mb = wave_sum(sb) * inv_d;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int ch = lane + 64 * c;
-        if (ch < nch) {
-          float rr[8] = {};
-          if (resid) ld8(resid + row * d + ch * 8, rr);
-          float o[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = (dv[c][i] - ma - v[c][i] * mb) * rstd + rr[i];
-          st8(dx + row * d + ch * 8, o);
+          for (int i = 0; i < 8; ++i) c[cc][i] = 0.f;
         }
       }
     }
-  } else {
-    // Every load of a row (x, dz and the residual) is issued together; with PF the next row's loads
-    // are issued before this row is reduced, so a wavefront always has a row in flight (more
-    // registers: fewer wavefronts per SIMD, which pays off for the wide fp32 rows only).
-    float v[2][8], dv[2][8], rs[2][8];
-    float nv[2][8], ndv[2][8], nrs[2][8];
-    auto load_row = [&](int64_t row, float (&a)[2][8], float (&b)[2][8], float (&c)[2][8]) {
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ch = lane + 64 * cc;
-        if (ch < nch && row < r1) {
-          ld8(x + row * d + ch * 8, a[cc]);
-          ld8(dz + row * d + ch * 8, b[cc]);
-          if (resid) {
-            ld8(resid + row * d + ch * 8, c[cc]);
-          } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) c[cc][i] = 0.f;
-          }
-        }
-      }
-    };
-    if (PF) load_row(r0, nv, ndv, nrs);
-    for (int64_t row = r0; row < r1; ++row) {
-      if (PF) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) { v[cc][i] = nv[cc][i]; dv[cc][i] = ndv[cc][i]; rs[cc][i] = nrs[cc][i]; }
-        load_row(row + 1, nv, ndv, nrs);
-      } else {
-        load_row(row, v, dv, rs);
-      }
-      const int grp = g[row] & gmask;
-      if (grp != cur) {
-        flush();
-        cur = grp;
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) { ag[cc][i] = 0.f; ab[cc][i] = 0.f; }
-      }
-      float s1 = 0.f;
+  };
+  if (PF && r0 < r1) load_row(r0, nv, ndv, nrs);
+  for (int64_t row = r0; row < r1; ++row) {
+    const int grp = g[row] & gmask;
+    if constexpr (PF) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc)
-        if (lane + 64 * cc < nch)
 #pragma unroll
-          for (int i = 0; i < 8; ++i) s1 += v[cc][i];
-      const float mean = wave_sum(s1) * inv_d;
-      float q = 0.f;
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-        if (lane + 64 * cc < nch)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) { const float e = v[cc][i] - mean; q += e * e; }
-      const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
-      float sa = 0.f, sb = 0.f;       // sum dxh, sum dxh * xh
+        for (int i = 0; i < 8; ++i) { v[cc][i] = nv[cc][i]; dv[cc][i] = ndv[cc][i]; rs[cc][i] = nrs[cc][i]; }
+    }
+    if (grp != cur) {
+      flush();
+      cur = grp;
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         const int ch = lane + 64 * cc;
-        if (ch < nch) {
-          float gm[8];
-          ld8(gamma + grp * d + ch * 8, gm);
+        if (ch < nch) ld8(gamma + grp * d + ch * 8, gm[cc]);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const float xh = (v[cc][i] - mean) * rstd;
-            const float dxh = dv[cc][i] * gm[i];
-            ag[cc][i] += dv[cc][i] * xh;
-            ab[cc][i] += dv[cc][i];
-            sa += dxh;
-            sb += dxh * xh;
-            v[cc][i] = xh;
-            dv[cc][i] = dxh;
-          }
+        for (int i = 0; i < 8; ++i) { ag[cc][i] = 0.f; ab[cc][i] = 0.f; }
+      }
+    }
+    if constexpr (PF) load_row(row + 1, nv, ndv, nrs);
+    else load_row(row, v, dv, rs);
+    float s1 = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+      if (lane + 64 * cc < nch)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s1 += v[cc][i];
+    const float mean = wave_sum_dpp(s1) * inv_d;
+    float q = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc)
+      if (lane + 64 * cc < nch)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { const float e = v[cc][i] - mean; q += e * e; }
+    const float rstd = 1.0f / sqrtf(wave_sum_dpp(q) * inv_d + eps);
+    float sa = 0.f, sb = 0.f;       // sum dxh, sum dxh * xh
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      if (lane + 64 * cc < nch) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float xh = (v[cc][i] - mean) * rstd;
+          const float dxh = dv[cc][i] * gm[cc][i];
+          ag[cc][i] += dv[cc][i] * xh;
+          ab[cc][i] += dv[cc][i];
+          sa += dxh;
+          sb += dxh * xh;
+          v[cc][i] = xh;
+          dv[cc][i] = dxh;
         }
       }
-      const float ma = wave_sum(sa) * inv_d, mb = wave_sum(sb) * inv_d;
+    }
+    const float ma = wave_sum_dpp(sa) * inv_d, mb = wave_sum_dpp(sb) * inv_d;
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const int ch = lane + 64 * cc;
-        if (ch < nch) {
-          float o[8];
+    for (int cc = 0; cc < 2; ++cc) {
+      const int ch = lane + 64 * cc;
+      if (ch < nch) {
+        float o[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = (dv[cc][i] - ma - v[cc][i] * mb) * rstd + rs[cc][i];
-          st8(dx + row * d + ch * 8, o);
-        }
+        for (int i = 0; i < 8; ++i) o[i] = (dv[cc][i] - ma - v[cc][i] * mb) * rstd + (kResid ? rs[cc][i] : 0.f);
+        st8(dx + row * d + ch * 8, o);
       }
     }
   }
@@ -666,7 +622,7 @@ hipError_t launch_groupln_bwd(int64_t T, int d, int x_kind, int act_kind, int sh
     k_groupln_bwd<float, float, float, float, true><<<grid, 256, 0, s>>>(
         T, d, rpw, static_cast<const float*>(x), g, static_cast<const float*>(gamma), eps, gm,
         static_cast<const float*>(dz), resid, static_cast<float*>(dx), part);
-  else if (x_kind == 1 && act_kind == 1 && out_kind == 1)
+  else if (x_kind == 1 && act_kind == 1 && out_kind == 1 && !resid)
     k_groupln_bwd<bf16, bf16, bf16, bf16, false><<<grid, 256, 0, s>>>(
         T, d, rpw, static_cast<const bf16*>(x), g, static_cast<const bf16*>(gamma), eps, gm,
         static_cast<const bf16*>(dz), resid, static_cast<bf16*>(dx), part);

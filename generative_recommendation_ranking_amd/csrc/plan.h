@@ -37,7 +37,7 @@ inline int colsum_blocks(int64_t T, int M) {
   return (int)std::max<int64_t>(1, std::min<int64_t>(kColsumRowBlocks / cg, (T + 63) / 64));
 }
 // Wavefronts of the GroupLN backward, each with one slot [2][4][d] of partial parameter gradients:
-// one round of resident wavefronts on 256 CUs -- the fp32-input variant (prefetching, ~185 VGPRs)
+// one round of resident wavefronts on 256 CUs -- the fp32-input variant (prefetching, ~190 VGPRs)
 // holds 2 per SIMD, the bf16 one (~120 VGPRs) 4
 inline int groupln_bwd_waves(int64_t T, int x_kind) {
   const int64_t cap = x_kind == 0 ? 512 : 1024;
