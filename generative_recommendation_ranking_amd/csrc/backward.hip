@@ -237,24 +237,6 @@ __device__ __forceinline__ void st8(float* p, const float (&v)[8]) {
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
 
-// Sum over the 64 lanes of a wavefront, through DPP row operations instead of LDS permutes: the
-// butterfly within each quad, the two halves of each row of 16 (mirror), then rows 0+1 and
-// 2+3 (broadcast of lane 15 into row 1 and 3) and the two halves (lane 31 into rows 2 and 3);
-// lane 63 then holds the total, which is read back as a scalar.  Fixed order: deterministic.
-template <int CTRL, int ROW_MASK> __device__ __forceinline__ float dpp_add(float v) {
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF,
-                                                                   false));
-}
-__device__ __forceinline__ float wave_sum_dpp(float v) {
-  v = dpp_add<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
-  v = dpp_add<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
-  v = dpp_add<0x141, 0xF>(v);   // row_half_mirror
-  v = dpp_add<0x140, 0xF>(v);   // row_mirror
-  v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-  v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
-  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
 // PF: prefetch row+1 while row is reduced (wide fp32 rows); without it a wavefront holds one row
 // and needs fewer registers, so more wavefronts share a SIMD (the bf16 variant).
 template <typename Tx, typename Tdz, typename Tp, typename Tout, bool PF>
@@ -347,14 +329,14 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
       if (lane + 64 * cc < nch)
 #pragma unroll
         for (int i = 0; i < 8; ++i) s1 += v[cc][i];
-    const float mean = wave_sum_dpp(s1) * inv_d;
+    const float mean = wave_sum(s1) * inv_d;
     float q = 0.f;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc)
       if (lane + 64 * cc < nch)
 #pragma unroll
         for (int i = 0; i < 8; ++i) { const float e = v[cc][i] - mean; q += e * e; }
-    const float rstd = 1.0f / sqrtf(wave_sum_dpp(q) * inv_d + eps);
+    const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
     float sa = 0.f, sb = 0.f;       // sum dxh, sum dxh * xh
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
@@ -372,7 +354,7 @@ __global__ __launch_bounds__(256) void k_groupln_bwd(int64_t T, int d, int64_t r
         }
       }
     }
-    const float ma = wave_sum_dpp(sa) * inv_d, mb = wave_sum_dpp(sb) * inv_d;
+    const float ma = wave_sum(sa) * inv_d, mb = wave_sum(sb) * inv_d;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
       const int ch = lane + 64 * cc;

@@ -20,20 +20,32 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }  // RNE
 
+// Reductions over the 64 lanes of a wavefront (called with every lane active), on DPP row
+// operations instead of LDS permutes: the butterfly within each quad, the two halves of each row
+// of 16 (mirrors), then rows 0+1 and 2+3 (lane 15 broadcast into rows 1 and 3) and the two halves
+// (lane 31 into rows 2 and 3); lane 63 then holds the result, read back as a scalar.  Lanes a
+// broadcast does not reach combine with the identity.  The order is fixed: deterministic.
+template <int CTRL, int ROW_MASK> __device__ __forceinline__ float dpp_mov(float v, float identity) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, identity), __builtin_bit_cast(int, v),
+                                                               CTRL, ROW_MASK, 0xF, false));
+}
+template <typename Op> __device__ __forceinline__ float wave_reduce(float v, float identity, Op op) {
+  v = op(v, dpp_mov<0xB1, 0xF>(v, identity));     // quad_perm [1,0,3,2]
+  v = op(v, dpp_mov<0x4E, 0xF>(v, identity));     // quad_perm [2,3,0,1]
+  v = op(v, dpp_mov<0x141, 0xF>(v, identity));    // row_half_mirror
+  v = op(v, dpp_mov<0x140, 0xF>(v, identity));    // row_mirror
+  v = op(v, dpp_mov<0x142, 0xA>(v, identity));    // row_bcast:15 into rows 1 and 3
+  v = op(v, dpp_mov<0x143, 0xC>(v, identity));    // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_reduce(v, 0.f, [](float a, float b) { return a + b; });
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
-  return v;
+  return wave_reduce(v, INFINITY, [](float a, float b) { return fminf(a, b); });
 }
 
 // silu(z) = z * sigmoid(z) = z / (1 + e^-z).  __expf maps to the hardware exp2 with a
