@@ -337,20 +337,36 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
 
   if (!wave_rows) return;
 
-  // Candidate rows under the dynamic mask: their own term silu(q_i . k_i) v_i (the diagonal of
-  // the C block, which the key loop stops short of).
+  // Every global load of the epilogue is issued before anything waits for one, so their
+  // latencies overlap: the K rows of candidate queries (their own term silu(q_i . k_i) v_i, the
+  // diagonal of the C block, which the key loop stops short of), and the U rows, plus the V rows of
+  // candidate queries, of the output chunks this lane writes.
+  // Buffer loads whose ranges cover exactly the rows wanted (U: the user's rows; K and V: its
+  // candidate rows), so a lane with nothing to load passes an offset past the range and reads
+  // zeros, with no branch (a branch per load made the compiler wait for each one).
   const bool q_c = MODE == kMaskDynamic && q_valid && qi >= rc_end;
-  float part = 0.f;
-  if (q_c) {
+  constexpr uint32_t kOut = 0x80000000u;         // past every range (rows span < 2^31 bytes)
+  const int n_c = MODE == kMaskDynamic ? n - rc_end : 0;
+  const __amdgpu_buffer_rsrc_t u_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)Up, (short)0, (int)((uint32_t)n * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t kc_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Kp + (int64_t)rc_end * ld), (short)0, (int)((uint32_t)n_c * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t vc_rsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(Vp + (int64_t)rc_end * ld), (short)0, (int)((uint32_t)n_c * row_bytes), 0x00020000);
+  bf16x8 kr[DH / 16];
+  const uint32_t k_off = q_c ? (uint32_t)(qi - rc_end) * row_bytes + hh * 16 : kOut;
 #pragma unroll
-    for (int ks = 0; ks < DH / 16; ++ks) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(Kp + qi * ld + ks * 16 + hh * 8);
+  for (int ks = 0; ks < DH / 16; ++ks)
+    kr[ks] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(kc_rsrc, k_off, ks * 32, 0));
+  constexpr int NE = 32 * CPR / 64;              // 16-byte output chunks per lane
+  bf16x8 u8[NE], v8[NE];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part += (float)qf[ks][e] * (float)kf[e];
-    }
+  for (int e = 0; e < NE; ++e) {
+    const int idx = lane + 64 * e, ql = idx / CPR, c = idx % CPR, q = wq0 + ql;
+    const uint32_t u_off = q < n ? (uint32_t)q * row_bytes + c * 16 : kOut;
+    const uint32_t v_off = (MODE == kMaskDynamic && q < n && q >= rc_end) ? (uint32_t)(q - rc_end) * row_bytes + c * 16 : kOut;
+    u8[e] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(u_rsrc, u_off, 0, 0));
+    v8[e] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(vc_rsrc, v_off, 0, 0));
   }
-  const float s_self = part + __shfl_xor(part, 32, kWave);
-  const float p_self = q_c ? (float)(bf16)silu_rcp(s_self) : 0.f;
 
   // Stage this wavefront's O rows (fp32) in LDS, one tile buffer per wavefront (the key loop
   // ended with a barrier and no loads in flight, so they are free): element r of tile t is row
@@ -363,37 +379,50 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       Os[(8 * (r >> 2) + 4 * hh + (r & 3)) * DH + ((t ^ hh) * 32 + l32)] = o[t][r];
+  float part = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < DH / 16; ++ks)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) part += (float)qf[ks][e] * (float)kr[ks][e];
+  const float s_self = part + __shfl_xor(part, 32, kWave);
+  const float p_self = q_c ? (float)(bf16)silu_rcp(s_self) : 0.f;
   if (hh == 0) Ps[l32] = p_self;
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // y = (O + p_self v) / n (.) u, 8 features per lane step, 16-byte loads and stores.
+  // y = (O + p_self v) / n (.) u, 8 features per lane step, 16-byte loads and stores.  Every
+  // chunk's LDS reads are issued before the first one is used.
   const float inv_n = 1.0f / (float)n;
-  for (int idx = lane; idx < 32 * CPR; idx += 64) {
-    const int ql = idx / CPR, c = idx % CPR;
-    const int q = wq0 + ql;
-    if (q >= n) continue;
+  f32x4 oa[NE][2];
+  float pse[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int idx = lane + 64 * e, ql = idx / CPR, c = idx % CPR;
     const int col = (c * 8) ^ (32 * ((ql >> 2) & 1));
-    const f32x4 a0 = *reinterpret_cast<const f32x4*>(&Os[ql * DH + col]);
-    const f32x4 a1 = *reinterpret_cast<const f32x4*>(&Os[ql * DH + col + 4]);
+    oa[e][0] = *reinterpret_cast<const f32x4*>(&Os[ql * DH + col]);
+    oa[e][1] = *reinterpret_cast<const f32x4*>(&Os[ql * DH + col + 4]);
+    pse[e] = Ps[ql];
+  }
+#pragma unroll
+  for (int e = 0; e < NE; ++e) {
+    const int idx = lane + 64 * e, ql = idx / CPR, c = idx % CPR, q = wq0 + ql;
+    if (q >= n) continue;
     float acc[8];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) { acc[e] = a0[e]; acc[e + 4] = a1[e]; }
-    const float ps = Ps[ql];
-    if (ps != 0.f) {
-      const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(Vp + q * ld + c * 8);
+    for (int i = 0; i < 4; ++i) { acc[i] = oa[e][0][i]; acc[i + 4] = oa[e][1][i]; }
+    const float ps = pse[e];
+    if (ps != 0.f) {   // a candidate row: its V row was loaded above
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += ps * (float)v8[e];
+      for (int i = 0; i < 8; ++i) acc[i] += ps * (float)v8[e][i];
     }
-    const bf16x8 u8 = *reinterpret_cast<const bf16x8*>(Up + q * ld + c * 8);
     bf16x8 out;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) out[e] = (bf16)(acc[e] * inv_n * (float)u8[e]);
+    for (int i = 0; i < 8; ++i) out[i] = (bf16)(acc[i] * inv_n * (float)u8[e][i]);
     if (vt) {   // the ungated V~ (kept for the backward pass)
       bf16x8 o2;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o2[e] = (bf16)(acc[e] * inv_n);
+      for (int i = 0; i < 8; ++i) o2[i] = (bf16)(acc[i] * inv_n);
       *reinterpret_cast<bf16x8*>(vt + (base + q) * (int64_t)d + (int64_t)h * DH + c * 8) = o2;
     }
     *reinterpret_cast<bf16x8*>(y + (base + q) * (int64_t)d + (int64_t)h * DH + c * 8) = out;
