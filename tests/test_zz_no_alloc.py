@@ -76,3 +76,46 @@ def test_noalloc_rejects_batches_beyond_scratch():
     M.mtgr_attention_fwd_noalloc(db, 256, 2, M.MTGR_BF16, 0, qkvu, got)
     torch.cuda.synchronize()
     assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
+def _one_token_users(B):
+    """B users of one long-term-history token each: no candidates, so the allocating entry's
+    workspace query sizes the same tables the no-allocation entry keeps in its scratch"""
+    off = np.arange(B + 1, dtype=np.int64)
+    return synth.Batch(offsets=off, group_ids=np.ones(B, np.uint8), timestamps=np.full(B, -np.inf, np.float32),
+                       x=np.zeros((B, 1), np.float32), n_u=np.zeros(B, np.int64), n_s=np.ones(B, np.int64),
+                       n_r=np.zeros(B, np.int64), k=np.zeros(B, np.int64))
+
+
+@pytest.mark.gpu
+def test_noalloc_at_the_scratch_limit():
+    d, H = 256, 2
+    # the largest user count whose tables fit the 4 MiB scratch, by bisection on the host-only size query
+    def tables(B):
+        off = np.arange(B + 1, dtype=np.int64)
+        hb = M.MtgrBatch(B, B, 0, off.ctypes.data, 0x1000, 0x1000, 0x1000)
+        n = ctypes.c_size_t(0)
+        assert M.lib().mtgr_attention_workspace_size(ctypes.byref(hb), d, H, ctypes.byref(n)) == 0
+        return n.value
+    lo, hi = 1, 1 << 20
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if tables(mid) <= 4 << 20:
+            lo = mid
+        else:
+            hi = mid - 1
+    for B, expect in ((lo, 0), (lo + 1, 7)):
+        print(f"noalloc at the limit: {B} users", flush=True)
+        b = _one_token_users(B)
+        db = M.DeviceBatch(b)
+        if expect:
+            assert M.lib().mtgr_attention_fwd_noalloc(ctypes.byref(db.c), d, H, M.MTGR_BF16, 0, 0x1000, 0x1000, None) == 7
+            continue
+        qkvu = _qkvu(b, d, H, 34, torch.bfloat16)
+        ref = torch.full((B, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+        M.mtgr_attention_fwd(db, d, H, M.MTGR_BF16, 0, qkvu, ref, M.workspace(M.mtgr_attention_workspace_size(db, d, H)))
+        got = torch.full_like(ref, float("nan"))
+        M.mtgr_attention_fwd_noalloc(db, d, H, M.MTGR_BF16, 0, qkvu, got)
+        torch.cuda.synchronize()
+        assert not torch.isnan(ref).any()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
