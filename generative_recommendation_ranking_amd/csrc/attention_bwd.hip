@@ -553,13 +553,28 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
     if (unmasked) scores_t(std::false_type{}, buf, k0);
     else scores_t(std::true_type{}, buf, k0);
   };
-  auto accumulate = [&](int buf) {
+  // The next tile's LDS-direct loads, then dQ += dS K over the current tile.  Both buffers live in
+  // one array, so the compiler cannot tell them apart by name; restrict-qualified views of the
+  // current K tile and of the next buffers tell it the loads do not write what the dQ reads read,
+  // and it no longer waits for those loads before the reads (it did, on every tile).
+  auto dq_phase = [&](const bf16* __restrict__ kcur, bf16* __restrict__ knxt, bf16* __restrict__ vnxt, bool need,
+                      int k0) {
+    if (k0 + BKV < kend) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int i = 0; i < NI; ++i) {
+        lds_dma16(k_rsrc, knxt + (w * NI + i) * 512, st_vo[i], (uint32_t)(k0 + BKV) * row_b);
+        lds_dma16(v_rsrc, vnxt + (w * NI + i) * 512, st_vo[i], (uint32_t)(k0 + BKV) * row_b);
+      }
+      if (MODE == kMaskDynamic && tid < BKV) rt = (k0 + BKV + tid < kend) ? ts[base + k0 + BKV + tid] : INFINITY;
+    }
+    if (need) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const bf16x8 kb = tr_frag<DH>(Ks[buf], ks, t, lane);
-        dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], kb, dq[t], 0, 0, 0);
+      for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const bf16x8 kb = tr_frag<DH>(kcur, ks, t, lane);
+          dq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[ks], kb, dq[t], 0, 0, 0);
+        }
       }
     }
   };
@@ -572,8 +587,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_bwd_dq(
     const int k0 = kt * BKV;
     const bool need = tile_needed(cur, k0);
     if (need) scores(cur, k0);
-    if (kt + 1 < nkt) stage_load(k0 + BKV, cur ^ 1);
-    if (need) accumulate(cur);
+    dq_phase(Ks[cur], Ks[cur ^ 1], Vs[cur ^ 1], need, k0);
     if (kt + 1 < nkt) stage_store(cur ^ 1);
     __syncthreads();
   }
