@@ -6,10 +6,19 @@
 //
 // bf16 path: v_mfma_f32_32x32x16_bf16 with fp32 accumulation, one persistent workgroup of 8
 // wavefronts per CU walking 256 x 256 output tiles (wavefront tile 64 x 128); the K loop stages
-// 64-wide slabs of a and w through LDS (register-staged, double-buffered, rows padded by 16 bytes
-// so 16-byte fragment reads of 32 consecutive rows hit distinct banks) and keeps one software
-// pipeline running across tile boundaries.  Both operands are K-contiguous, so every lane
-// fetches its 8 consecutive k values of a fragment with one 16-byte LDS read.
+// 64-wide slabs of a and w through two LDS buffers and keeps one software pipeline running across
+// tile boundaries.  With both operands K-contiguous the slabs go from global memory straight into
+// LDS (buffer loads with the LDS bit, XOR-swizzled rows) and every lane fetches the 8 consecutive
+// k values of a fragment with one 16-byte LDS read; the k-major variant (weight gradients) stages
+// through registers into padded rows and reads its fragments with transposing LDS reads.
+//
+// Where the time goes (large workload, Q/K/V/U projection 630,293 x 3072 x 768, about 3.0 ms):
+// timing builds that skip one part each ran in 1.85 ms without the global loads, 2.4 ms without
+// the epilogue, 1.6 ms without both, and 2.87 ms without the LDS fragment reads: the MFMA and LDS
+// core runs at about 75% of peak, and the slab loads and the output stores, which every CU issues
+// at the same points of its tile, are what the pipeline does not hide.  Tried without gain: a
+// 2 x 2 wavefront grid (128 x 128 per wavefront, one wavefront per SIMD: 10% slower), the slab
+// DMA spread over the k-steps, and workgroups started up to a few microseconds apart.
 //
 // Workgroup order: MI355X dispatches consecutive workgroup ids round-robin to its 8 XCDs, each
 // with a private L2.  Tiles are numbered so that every XCD walks its own M-tiles and, for each,
@@ -34,6 +43,21 @@ constexpr int kXcd = 8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kBiasLds = 4096;  // bias entries staged in LDS by the persistent bf16 GEMM
+// one slab buffer of the DMA pipeline: 512 rows of 128 bytes plus a gap, 8 x 32 rows of 272 bytes
+constexpr int kDmaBufBytes = 8 * 32 * 272;
+static_assert(kDmaBufBytes >= 512 * 128, "DMA slab buffer");
+
+// 16 bytes per lane from a buffer resource straight into LDS: lane l writes lds + 16 l; lanes
+// past the resource's end write zeros
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+
+// wait until at most N vector memory operations of this wavefront are outstanding
+template <int N> __device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <int EPI, typename TOut>
 __device__ __forceinline__ void store_out(TOut* out, const float* resid, int64_t idx, float v) {
@@ -52,9 +76,11 @@ __device__ __forceinline__ void store_out(TOut* out, const float* resid, int64_t
 //   * WM x WN wavefronts, 256 x 256 tile, BK = 64 (4 MFMA k-steps per slab), two LDS buffers.
 //   * Global loads are buffer loads whose resource starts at the tile's first row and whose size
 //     stops at M (N): rows past the end read as zero, and per-chunk offsets live in SGPRs.
-//   * Per slab: the fragments of k-step ks+1 are read before the MFMAs of k-step ks; the next
-//     slab is written to LDS and the one after it fetched after k-step 1; one barrier after
-//     k-step 2 (LDS traffic only) covers both buffers.
+//   * Per slab: the fragments of k-step ks+1 are read while the MFMAs of k-step ks run, and one
+//     barrier per slab publishes the next slab and frees the buffer of the last one.
+//   * K-contiguous operands: the next slab goes into the free buffer by DMA at the start of a
+//     slab (see the DMA pipeline below).  k-major operands: the slab after next is fetched into
+//     registers after k-step 1 and written to LDS one slab later.
 // KMAJOR: both operands token-major (k-major) for weight gradients, out[m][n] = sum_t A[t][m] W[t][n] over the
 // token axis K (t_rows real rows, the rest read as zero), A and W with row pitches lda and ldb;
 // the slab is staged as [k][m] / [k][n] and the MFMA fragments come from transposing LDS reads.
@@ -72,12 +98,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   constexpr int CA = BM * CPR / NT, CB = BN * CPR / NT;   // 4 and 4 chunks per thread
   constexpr int RSTEP = NT / CPR;                          // rows covered by one chunk index
 
+  // DMA: slabs of a and w go from global memory straight into LDS (K-contiguous operands only).
+  // Buffer b then holds [BM rows of a][BN rows of w], 128-byte rows without padding, the 16-byte
+  // chunk c of row r at position c ^ ((r >> 1) & 7), which keeps 16-byte fragment reads of 32
+  // consecutive rows on distinct banks, followed by a gap that lets the epilogue stage 8 x 32
+  // rows at its padded pitch in the buffer and its gap.
+  constexpr bool DMA = !KMAJOR;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16 (*As)[BM][LP] = reinterpret_cast<bf16 (*)[BM][LP]>(smem);
   bf16 (*Bs)[BN][LP] = reinterpret_cast<bf16 (*)[BN][LP]>(smem + 2 * BM * LP * sizeof(bf16));
   // Bias table in LDS: the whole vector when N <= kBiasLds (staged once), else the current
   // tile's slice (staged at the start of each tile).  It seeds the accumulators.
-  bf16* Bias = reinterpret_cast<bf16*>(smem + 2 * (BM + BN) * LP * sizeof(bf16));
+  constexpr int kSlabBytes = DMA ? kDmaBufBytes : (BM + BN) * LP * (int)sizeof(bf16);
+  bf16* Bias = reinterpret_cast<bf16*>(smem + 2 * kSlabBytes);
   constexpr int TP = BM + 32;   // k-major slabs [BK][BM + 32]: the same bytes as [BM][LP]; a pitch of 16
                                 // (mod 64) dwords keeps the transposing reads conflict-free
   static_assert(BK * TP == BM * LP && BN == BM, "k-major slab layout");
@@ -264,12 +297,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   if (bias_whole) {
     for (int i = tid; i < N; i += NT) Bias[i] = bias[i];
   }
-  issue_loads(r_cur, 0);
-  store_slab(0);
-  issue_loads(r_cur, 1);
   bool have_next = true;   // registers hold a slab still to be written to LDS
-  lds_barrier();
-  read_frags(0, 0, 0);
+  if constexpr (!DMA) {
+    issue_loads(r_cur, 0);
+    store_slab(0);
+    issue_loads(r_cur, 1);
+    lds_barrier();
+    read_frags(0, 0, 0);
+  }
 
   int cur = 0;
   bool more_tiles = next < nslots;
@@ -356,8 +391,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   constexpr int CPS = sizeof(TS) == 2 ? 4 : 2;     // MFMA column tiles per pass: 256 bytes of row
   constexpr int NPASS = FM * FN / CPS;
   constexpr int CW = 16 / (int)sizeof(TS);         // columns per 16-byte staged chunk
-  static_assert(NT == 512 && WM * WN == 8 && 32 * SP <= BM * LP * (int)sizeof(bf16) / 4,
-                "each wavefront stages 32 rows in a quarter of one operand buffer");
+  static_assert(DMA ? WM * WN * 32 * SP <= kDmaBufBytes : (NT == 512 && 32 * SP <= BM * LP * (int)sizeof(bf16) / 4),
+                "each wavefront stages 32 rows in a quarter of one operand buffer, or a share of one DMA buffer");
   // byte offset of this lane's first chunk inside a wavefront tile (row lane/16, 16-byte chunk
   // lane%16)
   const uint32_t lane_off =
@@ -381,11 +416,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
       r_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(resid + m0 * N), (short)0, nbytes, 0x00020000);
     if constexpr (EPI == kEpiSiluBwd)   // the pre-activation a, read and overwritten with silu(a)
       r_rsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(static_cast<bf16*>(aux) + m0 * N), (short)0, nbytes, 0x00020000);
-    // this wavefront's staging region: a quarter of the operand buffer the last slab used
-    char* stage = (wave < 4 ? reinterpret_cast<char*>(&As[cur ^ 1][0][0])
-                            : reinterpret_cast<char*>(&Bs[cur ^ 1][0][0])) + (wave & 3) * (BM * LP * (int)sizeof(bf16) / 4);
+    // this wavefront's staging region in the buffer the last slab used: a quarter of its operand
+    // buffer, or an eighth of the DMA buffer with its gap
+    char* stage = DMA ? reinterpret_cast<char*>(smem) + (cur ^ 1) * kSlabBytes + wave * (32 * SP)
+                      : (wave < 4 ? reinterpret_cast<char*>(&As[cur ^ 1][0][0])
+                                  : reinterpret_cast<char*>(&Bs[cur ^ 1][0][0])) + (wave & 3) * (BM * LP * (int)sizeof(bf16) / 4);
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
+      // (one pass at a time: the accumulators of later passes stay where they are)
+      __builtin_amdgcn_sched_barrier(0);
       const int i = p / (FN / CPS), j0 = (p % (FN / CPS)) * CPS;
       // Chunk it of this lane covers row i*32 + it*4 + lane/16 of the wavefront tile and columns
       // j0*32 + (lane%16)*CW .. +CW-1: a per-lane byte offset (one VGPR, or kDrop when the chunk
@@ -505,20 +544,134 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   // The tile loop is rotated so that each epilogue runs straight into the first slab of the next
   // tile with no control-flow merge between them (a merge would make the compiler's wait before
   // that slab's LDS write conservative again).
-  init_acc();
-  for (int kt = 0; kt < nk; ++kt) slab(kt);
-  while (true) {
-    epilogue();
-    if (!more_tiles) break;
-    slot = next;
-    next = next_slot(slot);
-    r_cur = r_nxt;
-    if (next < nslots) r_nxt = make_rsrc(next);
-    more_tiles = next < nslots;
+  if constexpr (!DMA) {
     init_acc();
-    read_frags(cur, 0, 0);
-    slab(0);
-    for (int kt = 1; kt < nk; ++kt) slab(kt);
+    for (int kt = 0; kt < nk; ++kt) slab(kt);
+    while (true) {
+      epilogue();
+      if (!more_tiles) break;
+      slot = next;
+      next = next_slot(slot);
+      r_cur = r_nxt;
+      if (next < nslots) r_nxt = make_rsrc(next);
+      more_tiles = next < nslots;
+      init_acc();
+      read_frags(cur, 0, 0);
+      slab(0);
+      for (int kt = 1; kt < nk; ++kt) slab(kt);
+    }
+  } else {
+    // DMA pipeline.  Phase kt runs from the barrier that published slab kt to the one that
+    // publishes slab kt+1.  At its start the buffer of slab kt-1 is free (its last fragments were
+    // read before that barrier; in a tile's first phase it is the epilogue's staging area, free
+    // after the epilogue's barrier) and receives slab kt+1 by DMA, or in a tile's last phase the
+    // next tile's slab 0, which then has the whole phase to land; the phase waits for it (vmcnt)
+    // just before its closing barrier.  The buffers are passed to each phase as restrict views,
+    // which tells the compiler that the reads of one buffer do not wait for the DMA into the other.
+    bf16* const buf0 = reinterpret_cast<bf16*>(smem);
+    auto abuf = [&](int b) { return buf0 + b * (kSlabBytes / (int)sizeof(bf16)); };
+    auto bbuf = [&](int b) { return abuf(b) + BM * BK; };
+    // wavefront w moves rows [RW w, RW (w + 1)) of both operands, 8 rows per instruction: lane l
+    // takes row 8i + l/8 and LDS position l%8, i.e. global chunk (l%8) ^ swizzle(row), where the
+    // swizzle of row RW w + 8i + j is 4(i&1) + j/2
+    constexpr int RW = BM / (WM * WN);
+    static_assert(BM == BN && RW % 16 == 0, "DMA row split");
+    const int wu = __builtin_amdgcn_readfirstlane(wave);
+    const int j8 = lane >> 3, c8 = lane & 7;
+    const uint32_t dvo0 = (uint32_t)(j8 * K * 2 + ((c8 ^ (j8 >> 1)) << 4));
+    const uint32_t dvo1 = (uint32_t)(j8 * K * 2 + ((c8 ^ (4 + (j8 >> 1))) << 4));
+    constexpr int NDI = RW / 8;   // DMA instructions per operand and wavefront
+    auto dma_slab = [&](const TileRsrc& r, int kt, bf16* __restrict__ da, bf16* __restrict__ db) {
+#pragma unroll
+      for (int i = 0; i < NDI; ++i) {
+        const int row = wu * RW + i * 8;
+        const uint32_t so = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(kt * BK * 2);
+        lds_dma16(r.a, da + row * BK, (i & 1) ? dvo1 : dvo0, so);
+        lds_dma16(r.w, db + row * BK, (i & 1) ? dvo1 : dvo0, so);
+      }
+    };
+    // rows of a wavefront's fragments are 32-aligned plus l32, so their swizzle is (l32/2) & 7
+    const int f_sw = (l32 >> 1) & 7;
+    auto read_frags_d = [&](const bf16* pa, const bf16* pb, int ks, int fslot, bool fence = true) {
+      const int ch = ((2 * ks + hh) ^ f_sw) * 8;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        fa[fslot][i] = *reinterpret_cast<const bf16x8*>(pa + (wm * TM + i * 32 + l32) * BK + ch);
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        fb[fslot][j] = *reinterpret_cast<const bf16x8*>(pb + (wn * TN + j * 32 + l32) * BK + ch);
+      if (fence) __builtin_amdgcn_sched_barrier(0);
+    };
+    // kind 0: first phase of a tile (its k-step 0 fragments are already in slot 0), 1: a middle
+    // phase, 2: the last phase of a tile
+    auto phase = [&](auto kind, int kt, const bf16* __restrict__ pa, const bf16* __restrict__ pb,
+                     bf16* __restrict__ qa, bf16* __restrict__ qb) {
+      constexpr int KIND = decltype(kind)::value;
+      // Bracket b: the fragments of k-step b are read while the MFMAs of k-step b-1 run (k-step 3
+      // of the previous slab for b = 0), each read issued right after one MFMA; bracket 0 also
+      // sends the next slab by DMA, one instruction after each of its remaining MFMAs.
+      auto bracket = [&](auto bc) {
+        constexpr int B = decltype(bc)::value;
+        constexpr int NV = B == 0 ? 2 * NDI : 0;
+        constexpr int NM = (KIND == 0 && B == 0) ? 0 : FM * FN;
+        constexpr int NR = (KIND == 0 && B == 0) ? 0 : FM + FN;
+        if constexpr (NR > 0) read_frags_d(pa, pb, B, B & 1, false);
+        if constexpr (NM > 0) mfmas((B + 1) & 1);
+        if constexpr (B == 0) {
+          if constexpr (KIND != 2) dma_slab(r_cur, kt + 1, qa, qb);
+          if constexpr (KIND == 2) {
+            if (more_tiles) dma_slab(r_nxt, 0, qa, qb);
+          }
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // one MFMA
+          if (m < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           // one LDS read
+          if (m >= NM - NV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);     // one DMA
+        }
+        if constexpr (NV > NM) __builtin_amdgcn_sched_group_barrier(0x010, NV - NM, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      bracket(std::integral_constant<int, 0>{});
+      bracket(std::integral_constant<int, 1>{});
+      bracket(std::integral_constant<int, 2>{});
+      bracket(std::integral_constant<int, 3>{});
+      if (KIND != 2 || more_tiles) {
+        __builtin_amdgcn_sched_barrier(0);   // the phase's MFMAs issue before the wait
+        wait_vm<0>();
+        lds_barrier();
+      }
+    };
+    auto run_tile = [&] {
+      phase(std::integral_constant<int, 0>{}, 0, abuf(cur), bbuf(cur), abuf(cur ^ 1), bbuf(cur ^ 1));
+      cur ^= 1;
+      for (int kt = 1; kt + 1 < nk; ++kt) {
+        phase(std::integral_constant<int, 1>{}, kt, abuf(cur), bbuf(cur), abuf(cur ^ 1), bbuf(cur ^ 1));
+        cur ^= 1;
+      }
+      phase(std::integral_constant<int, 2>{}, nk - 1, abuf(cur), bbuf(cur), abuf(cur ^ 1), bbuf(cur ^ 1));
+      if (more_tiles) cur ^= 1;
+      mfmas(1);   // k-step 3 of the last slab
+    };
+    // prologue: slab 0 by DMA into buffer 0
+    dma_slab(r_cur, 0, abuf(0), bbuf(0));
+    wait_vm<0>();
+    lds_barrier();
+    init_acc();
+    read_frags_d(abuf(0), bbuf(0), 0, 0);
+    run_tile();
+    while (true) {
+      epilogue();
+      if (!more_tiles) break;
+      slot = next;
+      next = next_slot(slot);
+      r_cur = r_nxt;
+      if (next < nslots) r_nxt = make_rsrc(next);
+      more_tiles = next < nslots;
+      init_acc();
+      read_frags_d(abuf(cur), bbuf(cur), 0, 0);
+      run_tile();
+    }
   }
 }
 
@@ -589,7 +742,8 @@ template <int WM, int WN, int EPI, typename TOut, bool KMAJOR = false>
 hipError_t run_bf16_persistent(int64_t M, int N, int K, const bf16* a, const bf16* w,
                                const bf16* bias, const float* resid, void* out, hipStream_t s,
                                int ksplit = 1, KMajorArgs km = KMajorArgs(), void* aux = nullptr) {
-  constexpr size_t lds = 2 * (size_t)(256 + 256) * (64 + 8) * sizeof(bf16) + kBiasLds * sizeof(bf16);
+  constexpr size_t lds = (!KMAJOR ? 2 * (size_t)kDmaBufBytes : 2 * (size_t)(256 + 256) * (64 + 8) * sizeof(bf16)) +
+                         kBiasLds * sizeof(bf16);
   auto kern = k_gemm_bf16_persistent<WM, WN, EPI, TOut, KMAJOR>;
   static bool attr_set = false;
   if (!attr_set) {
