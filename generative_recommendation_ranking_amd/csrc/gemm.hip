@@ -79,8 +79,9 @@ __device__ __forceinline__ void store_out(TOut* out, const float* resid, int64_t
 //   * Per slab: the fragments of k-step ks+1 are read while the MFMAs of k-step ks run, and one
 //     barrier per slab publishes the next slab and frees the buffer of the last one.
 //   * K-contiguous operands: the next slab goes into the free buffer by DMA at the start of a
-//     slab (see the DMA pipeline below).  k-major operands: the slab after next is fetched into
-//     registers after k-step 1 and written to LDS one slab later.
+//     slab, the activation rows of most slabs through registers two slabs ahead (see the DMA
+//     pipeline below).  k-major operands: the slab after next is fetched into registers after
+//     k-step 1 and written to LDS one slab later.
 // KMAJOR: both operands token-major (k-major) for weight gradients, out[m][n] = sum_t A[t][m] W[t][n] over the
 // token axis K (t_rows real rows, the rest read as zero), A and W with row pitches lda and ldb;
 // the slab is staged as [k][m] / [k][n] and the MFMA fragments come from transposing LDS reads.
@@ -581,14 +582,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     const uint32_t dvo0 = (uint32_t)(j8 * K * 2 + ((c8 ^ (j8 >> 1)) << 4));
     const uint32_t dvo1 = (uint32_t)(j8 * K * 2 + ((c8 ^ (4 + (j8 >> 1))) << 4));
     constexpr int NDI = RW / 8;   // DMA instructions per operand and wavefront
-    auto dma_slab = [&](const TileRsrc& r, int kt, bf16* __restrict__ da, bf16* __restrict__ db) {
+    auto dma_slab = [&](const TileRsrc& r, int kt, bf16* __restrict__ da, bf16* __restrict__ db, bool with_a) {
 #pragma unroll
       for (int i = 0; i < NDI; ++i) {
         const int row = wu * RW + i * 8;
         const uint32_t so = (uint32_t)row * (uint32_t)K * 2u + (uint32_t)(kt * BK * 2);
-        lds_dma16(r.a, da + row * BK, (i & 1) ? dvo1 : dvo0, so);
+        if (with_a) lds_dma16(r.a, da + row * BK, (i & 1) ? dvo1 : dvo0, so);
         lds_dma16(r.w, db + row * BK, (i & 1) ? dvo1 : dvo0, so);
       }
+    };
+    // Activation slabs 2 .. nk-1 of a tile come through registers two phases ahead (register set
+    // s & 1 holds slab s): thread t loads chunk t%8 of rows t/8 + 64i and writes it to its swizzled
+    // position, (t/16) & 7 being the swizzle of those rows.
+    bf16x8 rA[2][CA];
+    const uint32_t a_vo = (uint32_t)((tid >> 3) * K * 2 + (tid & 7) * 16);
+    const int s_row = tid >> 3, s_ch = ((tid & 7) ^ ((tid >> 4) & 7)) * 8;
+    auto load_a = [&](auto set, int kt) {
+      constexpr int S = decltype(set)::value;
+#pragma unroll
+      for (int i = 0; i < CA; ++i)
+        rA[S][i] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  r_cur.a, a_vo, (uint32_t)(i * RSTEP * K * 2 + kt * BK * 2), 0));
+    };
+    auto store_a = [&](auto set, bf16* __restrict__ da) {
+      constexpr int S = decltype(set)::value;
+#pragma unroll
+      for (int i = 0; i < CA; ++i) *reinterpret_cast<bf16x8*>(da + (s_row + i * RSTEP) * BK + s_ch) = rA[S][i];
     };
     // rows of a wavefront's fragments are 32-aligned plus l32, so their swizzle is (l32/2) & 7
     const int f_sw = (l32 >> 1) & 7;
@@ -603,31 +622,35 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
       if (fence) __builtin_amdgcn_sched_barrier(0);
     };
     // kind 0: first phase of a tile (its k-step 0 fragments are already in slot 0), 1: a middle
-    // phase, 2: the last phase of a tile
-    auto phase = [&](auto kind, int kt, const bf16* __restrict__ pa, const bf16* __restrict__ pb,
-                     bf16* __restrict__ qa, bf16* __restrict__ qb) {
-      constexpr int KIND = decltype(kind)::value;
+    // phase, 2: the last phase of a tile; P: the parity of kt (the register set it loads into)
+    auto phase = [&](auto kind, auto par, int kt, const bf16* __restrict__ pa, const bf16* __restrict__ pb,
+                     bf16* __restrict__ qa, bf16* __restrict__ qb) __attribute__((always_inline)) {
+      constexpr int KIND = decltype(kind)::value, P = decltype(par)::value;
+      const bool load_next = KIND != 2 && kt + 2 < nk;   // activation slab kt+2 into registers
       // Bracket b: the fragments of k-step b are read while the MFMAs of k-step b-1 run (k-step 3
       // of the previous slab for b = 0), each read issued right after one MFMA; bracket 0 also
-      // sends the next slab by DMA, one instruction after each of its remaining MFMAs.
+      // issues the phase's global loads, one after each of its remaining MFMAs.
       auto bracket = [&](auto bc) {
         constexpr int B = decltype(bc)::value;
-        constexpr int NV = B == 0 ? 2 * NDI : 0;
+        constexpr int NV = B == 0 ? (KIND == 1 ? NDI : 2 * NDI) + (KIND == 2 ? 0 : CA) : 0;
         constexpr int NM = (KIND == 0 && B == 0) ? 0 : FM * FN;
         constexpr int NR = (KIND == 0 && B == 0) ? 0 : FM + FN;
         if constexpr (NR > 0) read_frags_d(pa, pb, B, B & 1, false);
         if constexpr (NM > 0) mfmas((B + 1) & 1);
         if constexpr (B == 0) {
-          if constexpr (KIND != 2) dma_slab(r_cur, kt + 1, qa, qb);
+          // slab kt+1 by DMA (its activation rows too in a tile's first phase), or the next
+          // tile's slab 0 in its last phase
+          if constexpr (KIND != 2) dma_slab(r_cur, kt + 1, qa, qb, KIND == 0);
           if constexpr (KIND == 2) {
-            if (more_tiles) dma_slab(r_nxt, 0, qa, qb);
+            if (more_tiles) dma_slab(r_nxt, 0, qa, qb, true);
           }
+          if (load_next) load_a(std::integral_constant<int, P>{}, kt + 2);
         }
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // one MFMA
           if (m < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);           // one LDS read
-          if (m >= NM - NV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);     // one DMA
+          if (m >= NM - NV) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);     // one global load
         }
         if constexpr (NV > NM) __builtin_amdgcn_sched_group_barrier(0x010, NV - NM, 0);
         __builtin_amdgcn_sched_barrier(0);
@@ -638,23 +661,46 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
       bracket(std::integral_constant<int, 3>{});
       if (KIND != 2 || more_tiles) {
         __builtin_amdgcn_sched_barrier(0);   // the phase's MFMAs issue before the wait
-        wait_vm<0>();
+        // everything but the activation loads just issued: this phase's DMA and, in a middle
+        // phase, the registers of slab kt+1, which then go to LDS
+        if (load_next) wait_vm<CA>();
+        else wait_vm<0>();
+        if constexpr (KIND == 1) store_a(std::integral_constant<int, P ^ 1>{}, qa);
         lds_barrier();
       }
     };
-    auto run_tile = [&] {
-      phase(std::integral_constant<int, 0>{}, 0, abuf(cur), bbuf(cur), abuf(cur ^ 1), bbuf(cur ^ 1));
+    // the buffer addresses are formed anew in every phase (an opaque copy of `cur`), which keeps
+    // the compiler from holding both buffers' fragment addresses in registers across the loop
+    auto phase_at = [&](auto kind, auto par, int kt) __attribute__((always_inline)) {
+      int c = __builtin_amdgcn_readfirstlane(cur);
+      asm volatile("" : "+s"(c));
+      phase(kind, par, kt, abuf(c), bbuf(c), abuf(c ^ 1), bbuf(c ^ 1));
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    auto run_tile = [&]() __attribute__((always_inline)) {
+      phase_at(I0{}, I0{}, 0);
       cur ^= 1;
-      for (int kt = 1; kt + 1 < nk; ++kt) {
-        phase(std::integral_constant<int, 1>{}, kt, abuf(cur), bbuf(cur), abuf(cur ^ 1), bbuf(cur ^ 1));
+      // middle phases 1 .. nk-2 in pairs (odd kt, then even), so each names its register sets
+      // at compile time
+      int kt = 1;
+      for (; kt + 2 < nk; kt += 2) {
+        phase_at(I1{}, I1{}, kt);
+        cur ^= 1;
+        phase_at(I1{}, I0{}, kt + 1);
         cur ^= 1;
       }
-      phase(std::integral_constant<int, 2>{}, nk - 1, abuf(cur), bbuf(cur), abuf(cur ^ 1), bbuf(cur ^ 1));
+      if (kt + 1 < nk) {
+        phase_at(I1{}, I1{}, kt);
+        cur ^= 1;
+      }
+      phase_at(I2{}, I0{}, nk - 1);
       if (more_tiles) cur ^= 1;
       mfmas(1);   // k-step 3 of the last slab
     };
     // prologue: slab 0 by DMA into buffer 0
-    dma_slab(r_cur, 0, abuf(0), bbuf(0));
+    dma_slab(r_cur, 0, abuf(0), bbuf(0), true);
     wait_vm<0>();
     lds_barrier();
     init_acc();
