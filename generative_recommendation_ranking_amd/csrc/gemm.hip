@@ -385,6 +385,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   // the tile's last valid row; chunks past column N get an offset beyond it and are dropped), so
   // the compiler can also count past them when it waits for the next tile's prefetched slab.
   constexpr uint32_t kDrop = 0x80000000u;   // > any valid byte offset (N <= 2^20, 256 rows)
+  // the output rows are written once and not read again by this kernel: non-temporal stores keep
+  // them from displacing the activation slabs that later column tiles re-read from L2
+  constexpr int kStoreNT = 2;
   constexpr int SP = 272;                    // staging row pitch, bytes (16-byte aligned, 4-bank skew)
   // staged element type: the output type, except the SiLU-backward epilogue, which stages fp32
   // and finishes the product with silu'(a) on the way out
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
       // the store; the compiler omits it when the store's SGPR offset field holds a register, but
       // gfx950 corrupts the stored data without it, so it is inserted here.
       auto store_chunk = [&](u32x4 c, int it) {
-        __builtin_amdgcn_raw_buffer_store_b128(c, o_rsrc, vo_c, s_off(it), 0);
+        __builtin_amdgcn_raw_buffer_store_b128(c, o_rsrc, vo_c, s_off(it), kStoreNT);
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_nop 1");
         __builtin_amdgcn_sched_barrier(0);

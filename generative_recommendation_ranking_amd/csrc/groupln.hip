@@ -12,9 +12,11 @@
 // pieces (4 fp32 or 8 bf16 values), lane l holding pieces l, l+64, ..., so every load instruction
 // covers one contiguous run of the row; the row is read from HBM once and kept in registers; mean
 // and variance are two wavefront reductions (two-pass, fp32).  gamma/beta come through the cache
-// with the same piece layout.  The kernel is HBM-bound: it moves (in_bytes + out_bytes) * d per
-// token.  Measured on the large workload (d = 768): 0.48 ms for fp32 -> bf16 and 0.37 ms for
-// bf16 -> bf16, 5.9 and 5.3 TB/s, against 5.2 TB/s for a device-to-device copy on the same box.
+// with the same piece layout; the rows of x and y go through non-temporal loads and stores.  The
+// kernel is HBM-bound: it moves (in_bytes + out_bytes) * d per token.  Measured on the large
+// workload (d = 768): 0.455 ms for fp32 -> bf16 and 0.348 ms for bf16 -> bf16, 6.4 and 5.6 TB/s
+// (0.48 and 0.36 ms with cached loads and stores), against 5.2 TB/s for a device-to-device copy
+// on the same box.
 #include "kernels.h"
 
 namespace mtgr {
@@ -48,13 +50,35 @@ template <> __device__ __forceinline__ void load_piece<8, float>(const float* p,
 #pragma unroll
   for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[i + 4] = b[i]; }
 }
+// The rows of x and y are touched once: their loads and stores are non-temporal (gamma and beta,
+// read by every row, stay cached).
+template <int E, typename T> __device__ __forceinline__ void load_row_piece(const T* p, float v[E]) {
+  if constexpr (E == 8 && sizeof(T) == 4) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { v[i] = a[i]; v[i + 4] = b[i]; }
+  } else if constexpr (sizeof(T) == 4) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = a[i];
+  } else if constexpr (E == 8) {
+    const bf16x8 a = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(p));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (float)a[i];
+  } else {
+    const bf16x4 a = __builtin_nontemporal_load(reinterpret_cast<const bf16x4*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (float)a[i];
+  }
+}
 template <int E> __device__ __forceinline__ void store_piece(float* p, const float v[E]) {
 #pragma unroll
   for (int h = 0; h < E / 4; ++h) {
     f32x4 a;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = v[4 * h + i];
-    *reinterpret_cast<f32x4*>(p + 4 * h) = a;
+    __builtin_nontemporal_store(a, reinterpret_cast<f32x4*>(p + 4 * h));
   }
 }
 template <int E> __device__ __forceinline__ void store_piece(bf16* p, const float v[E]) {
@@ -62,12 +86,12 @@ template <int E> __device__ __forceinline__ void store_piece(bf16* p, const floa
     bf16x8 a;
 #pragma unroll
     for (int i = 0; i < 8; ++i) a[i] = (bf16)v[i];
-    *reinterpret_cast<bf16x8*>(p) = a;
+    __builtin_nontemporal_store(a, reinterpret_cast<bf16x8*>(p));
   } else {
     bf16x4 a;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a[i] = (bf16)v[i];
-    *reinterpret_cast<bf16x4*>(p) = a;
+    __builtin_nontemporal_store(a, reinterpret_cast<bf16x4*>(p));
   }
 }
 
@@ -97,7 +121,7 @@ __global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __
     for (int k = 0; k < MP; ++k) {
       const int pc = lane + 64 * k;
       if (row < T && pc < np) {
-        load_piece<E>(x + row * d + pc * E, v[r][k]);
+        load_row_piece<E>(x + row * d + pc * E, v[r][k]);
       } else {
 #pragma unroll
         for (int i = 0; i < E; ++i) v[r][k][i] = 0.f;
