@@ -12,13 +12,15 @@
 // k values of a fragment with one 16-byte LDS read; the k-major variant (weight gradients) stages
 // through registers into padded rows and reads its fragments with transposing LDS reads.
 //
-// Where the time goes (large workload, Q/K/V/U projection 630,293 x 3072 x 768, about 3.0 ms):
-// timing builds that skip one part each ran in 1.85 ms without the global loads, 2.4 ms without
-// the epilogue, 1.6 ms without both, and 2.87 ms without the LDS fragment reads: the MFMA and LDS
-// core runs at about 75% of peak, and the slab loads and the output stores, which every CU issues
-// at the same points of its tile, are what the pipeline does not hide.  Tried without gain: a
-// 2 x 2 wavefront grid (128 x 128 per wavefront, one wavefront per SIMD: 10% slower), the slab
-// DMA spread over the k-steps, and workgroups started up to a few microseconds apart.
+// Where the time goes (large workload, Q/K/V/U projection 630,293 x 3072 x 768, about 2.9 ms):
+// timing builds that skip one part each ran in 2.47 ms without the epilogue (2.55 ms without just
+// its global stores), 2.32 ms without the weight DMA, 2.45 ms without the activation loads and
+// 1.84 ms without both loads: the MFMA and LDS core runs at about 75% of peak, and the operand
+// feed and the output stores are what the pipeline does not hide.  Tried without gain: a 2 x 2
+// wavefront grid (128 x 128 per wavefront, one wavefront per SIMD: 10% slower), the slab DMA
+// spread over the k-steps, workgroups started up to a few microseconds apart, the weights
+// (instead of the activations) through registers, and each tile's slab 1 sent before the
+// previous tile's epilogue with the staging moved out of the slab buffers.
 //
 // Workgroup order: MI355X dispatches consecutive workgroup ids round-robin to its 8 XCDs, each
 // with a private L2.  Tiles are numbered so that every XCD walks its own M-tiles and, for each,
