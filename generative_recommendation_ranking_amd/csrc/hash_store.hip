@@ -114,10 +114,28 @@ __device__ int64_t claim(const View& v, int64_t key, int lane) {
   return -1;
 }
 
+// Slot index of `key`, or -1 (no concurrent writers: plain loads), probing from line `line` on,
+// `probe0` lines of the sequence already seen.
+__device__ int64_t find_from(const View& v, int64_t key, int64_t line, int64_t probe0, int lane) {
+  const int sub = lane & (kTeam - 1);
+  for (int64_t probe = probe0; probe <= v.lmask; ++probe) {
+    const int64_t k = v.slots[line * kTeam + sub].key;
+    const uint32_t m = team_ballot(k == key, lane);
+    if (m) return line * kTeam + (__ffs(m) - 1);
+    if (team_ballot(k == kEmpty, lane)) return -1;
+    line = (line + 1) & v.lmask;
+  }
+  return -1;
+}
+
+__device__ __forceinline__ int64_t home_line(const View& v, int64_t key) {
+  return (int64_t)(mix64((uint64_t)key) >> 3) & v.lmask;
+}
+
 // Slot index of `key`, or -1 (no concurrent writers: plain loads).
 __device__ int64_t find(const View& v, int64_t key, int lane) {
   const int sub = lane & (kTeam - 1);
-  int64_t line = (int64_t)(mix64((uint64_t)key) >> 3) & v.lmask;
+  int64_t line = home_line(v, key);
   for (int64_t probe = 0; probe <= v.lmask; ++probe) {
     const int64_t k = v.slots[line * kTeam + sub].key;
     const uint32_t m = team_ballot(k == key, lane);
@@ -264,6 +282,8 @@ __global__ __launch_bounds__(256) void k_resolve(View v, int64_t n, const int64_
   }
 }
 
+// Each team looks up two keys per iteration (i and i + teams) and requests the two keys' index
+// lines, slot rows and value rows side by side, so it has two dependent chains of loads in flight.
 __global__ __launch_bounds__(256) void k_lookup(View v, int64_t n, const int64_t* __restrict__ keys, int32_t step,
                                                 char* __restrict__ out, int32_t* __restrict__ rows_out,
                                                 const int64_t* __restrict__ n_dev) {
@@ -271,14 +291,46 @@ __global__ __launch_bounds__(256) void k_lookup(View v, int64_t n, const int64_t
   if (n_dev) n = min(n, *n_dev);
   const int64_t team = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kTeam;
   const int64_t teams = (int64_t)gridDim.x * blockDim.x / kTeam;
-  for (int64_t i = team; i < n; i += teams) {
-    const int64_t key = keys[i];
-    const int64_t slot = key >= 0 ? find(v, key, lane) : -1;
-    const int32_t row = slot >= 0 ? v.slots[slot].row : -1;
-    if (out) team_copy(out + i * v.row_bytes, row >= 0 ? v.values + (int64_t)row * v.row_bytes : nullptr, v.row_bytes, sub);
+  for (int64_t i0 = team; i0 < n; i0 += 2 * teams) {
+    const int64_t i1 = i0 + teams;
+    const bool has1 = i1 < n;
+    const int64_t key0 = keys[i0];
+    const int64_t key1 = has1 ? keys[i1] : kEmpty;
+    // first probe of both keys' sequences
+    const int64_t line0 = key0 >= 0 ? home_line(v, key0) : 0;
+    const int64_t line1 = key1 >= 0 ? home_line(v, key1) : 0;
+    const int64_t k0 = key0 >= 0 ? v.slots[line0 * kTeam + sub].key : kEmpty;
+    const int64_t k1 = key1 >= 0 ? v.slots[line1 * kTeam + sub].key : kEmpty;
+    const uint32_t m0 = team_ballot(key0 >= 0 && k0 == key0, lane), e0 = team_ballot(k0 == kEmpty, lane);
+    const uint32_t m1 = team_ballot(key1 >= 0 && k1 == key1, lane), e1 = team_ballot(k1 == kEmpty, lane);
+    int64_t slot0 = m0 ? line0 * kTeam + (__ffs(m0) - 1) : -1;
+    int64_t slot1 = m1 ? line1 * kTeam + (__ffs(m1) - 1) : -1;
+    // a full home line without the key: keep probing (rare at the store's load factors)
+    if (key0 >= 0 && !m0 && !e0) slot0 = find_from(v, key0, (line0 + 1) & v.lmask, 1, lane);
+    if (key1 >= 0 && !m1 && !e1) slot1 = find_from(v, key1, (line1 + 1) & v.lmask, 1, lane);
+    const int32_t row0 = slot0 >= 0 ? v.slots[slot0].row : -1;
+    const int32_t row1 = slot1 >= 0 ? v.slots[slot1].row : -1;
+    if (out) {
+      const char* src0 = row0 >= 0 ? v.values + (int64_t)row0 * v.row_bytes : nullptr;
+      const char* src1 = row1 >= 0 ? v.values + (int64_t)row1 * v.row_bytes : nullptr;
+      char* dst0 = out + i0 * v.row_bytes;
+      char* dst1 = out + i1 * v.row_bytes;
+      for (int c = sub * 16; c < v.row_bytes; c += kTeam * 16) {
+        const uint4 a = src0 ? *reinterpret_cast<const uint4*>(src0 + c) : make_uint4(0, 0, 0, 0);
+        const uint4 b = (has1 && src1) ? *reinterpret_cast<const uint4*>(src1 + c) : make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(dst0 + c) = a;
+        if (has1) *reinterpret_cast<uint4*>(dst1 + c) = b;
+      }
+    }
     if (sub == 0) {
-      if (rows_out) rows_out[i] = row;
-      if (row >= 0 && step >= 0) v.last_seen[row] = step;
+      if (rows_out) {
+        rows_out[i0] = row0;
+        if (has1) rows_out[i1] = row1;
+      }
+      if (step >= 0) {
+        if (row0 >= 0) v.last_seen[row0] = step;
+        if (has1 && row1 >= 0) v.last_seen[row1] = step;
+      }
     }
   }
 }
