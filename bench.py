@@ -149,7 +149,7 @@ def host_cpu():
     return {"model": model, "logical_cpus": os.cpu_count()}
 
 
-def survey_user_order(b):
+def baseline_user_order(b):
     """users in the order the baseline samples them: the first user whose long-term history sits at
     the workload's 3000-item cap (when there is one), then users 0, 1, 2, ..."""
     tail = np.flatnonzero(np.asarray(b.n_s) == 3000)
@@ -174,7 +174,7 @@ def cpu_baseline(b, p, mask="dynamic", norm="group", budget_s=20.0, max_s=30.0):
     from oracle import mtgr_oracle as O
     layers, head = O.params_layers(p), O.params_head(p)
     done, users, t0 = 0, [], time.perf_counter()
-    for u in survey_user_order(b):
+    for u in baseline_user_order(b):
         s = synth.subset(b, [u])
         O.encoder_forward(s.offsets, s.group_ids, s.timestamps, s.x, layers, head, p.H, p.ln_eps,
                           mask_mode=mask, shared_norm=(norm == "shared"))

@@ -340,10 +340,10 @@ def elem_err(g, r):
     return float(e.max()), float(np.percentile(e, 99.9))
 
 
-def _sample_users(b, k_extra, survey_subset=False):
-    """the longest and the shortest user plus users 0 .. k_extra-1; with survey_subset instead
+def _sample_users(b, k_extra, capped_history_subset=False):
+    """the longest and the shortest user plus users 0 .. k_extra-1; with capped_history_subset instead
     users 0-7 and the first user whose long-term history is at the workload's cap of 3000 items"""
-    if survey_subset:
+    if capped_history_subset:
         return sorted(set(range(8)) | {int(np.flatnonzero(b.n_s == 3000)[0])})
     n = b.offsets[1:] - b.offsets[:-1]
     return sorted({int(np.argmax(n)), int(np.argmin(n))} | set(range(k_extra)))
@@ -360,7 +360,7 @@ def test_encoder_workload_sampled_users(name, k_extra, mask, norm):
     history cap (about 24k tokens, a minute or two of the oracle on the host)."""
     b, p = workload(name)
     hid, logit = run_encoder(b, p, mask, norm)
-    users = _sample_users(b, k_extra, survey_subset=(name == "large-bf16" and mask == "dynamic"))
+    users = _sample_users(b, k_extra, capped_history_subset=(name == "large-bf16" and mask == "dynamic"))
     rh, rl = oracle_subset(b, p, users, mask, norm)
     gh = hid[synth.user_rows(b, users)]
     gl = logit[synth.candidate_rows(b, users)]
