@@ -41,6 +41,19 @@ template <typename Op> __device__ __forceinline__ float wave_reduce(float v, flo
 __device__ __forceinline__ float wave_sum(float v) {
   return wave_reduce(v, 0.f, [](float a, float b) { return a + b; });
 }
+// Sum over each half of the wavefront (lanes 0-31 and 32-63), every lane getting its own half's
+// sum: the same steps as wave_reduce up to the broadcast of lane 15 into rows 1 and 3, after which
+// lanes 31 and 63 hold the two halves' sums.
+__device__ __forceinline__ float half_wave_sum(float v) {
+  v += dpp_mov<0xB1, 0xF>(v, 0.f);
+  v += dpp_mov<0x4E, 0xF>(v, 0.f);
+  v += dpp_mov<0x141, 0xF>(v, 0.f);
+  v += dpp_mov<0x140, 0xF>(v, 0.f);
+  v += dpp_mov<0x142, 0xA>(v, 0.f);
+  const float lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  const float hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  return (threadIdx.x & 32) ? hi : lo;
+}
 __device__ __forceinline__ float wave_max(float v) {
   return wave_reduce(v, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
 }

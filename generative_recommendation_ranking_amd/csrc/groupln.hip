@@ -7,16 +7,18 @@
 // With `shared` set every token takes gamma[0], beta[0]: one plain LayerNorm, the ablation
 // without GroupLN (marovi.ai MTGR page, 方法, GLN paragraph).
 //
-// Mapping: four wavefronts per 256-thread workgroup, one token row per wavefront for fp32 input
-// and two rows (both rows' loads in flight together) for bf16 input.  A row is split into 16-byte
-// pieces (4 fp32 or 8 bf16 values), lane l holding pieces l, l+64, ..., so every load instruction
-// covers one contiguous run of the row; the row is read from HBM once and kept in registers; mean
-// and variance are two wavefront reductions (two-pass, fp32).  gamma/beta come through the cache
-// with the same piece layout; the rows of x and y go through non-temporal loads and stores.  The
-// kernel is HBM-bound: it moves (in_bytes + out_bytes) * d per token.  Measured on the large
-// workload (d = 768): 0.455 ms for fp32 -> bf16 and 0.348 ms for bf16 -> bf16, 6.4 and 5.6 TB/s
-// (0.48 and 0.36 ms with cached loads and stores), against 5.2 TB/s for a device-to-device copy
-// on the same box.
+// Mapping: four wavefronts per 256-thread workgroup.  A row is split into 16-byte pieces (4 fp32
+// or 8 bf16 values).  fp32 input: one row per wavefront, lane l holding pieces l, l+64, ...;
+// bf16 input: two rows per wavefront, lanes 0-31 holding pieces l, l+32, ... of the first row and
+// lanes 32-63 those of the second.  At d = 768 every lane then holds three pieces of its row.
+// Every load instruction covers contiguous runs of a row; the rows are read from HBM once and
+// kept in registers; mean and variance are two reductions over the lanes of a row (two-pass,
+// fp32).  gamma/beta come through the cache with the same piece layout; the rows of x and y go
+// through non-temporal loads and stores.  The kernel is HBM-bound: it moves
+// (in_bytes + out_bytes) * d per token.  Measured on the large workload (d = 768, 630,293 rows,
+// inside the encoder step): fp32 -> bf16 0.46-0.48 ms (6.1-6.3 TB/s); bf16 -> bf16 0.32 ms
+// (6.0 TB/s), 0.36 ms with whole-wavefront rows.  A plain non-temporal 16-byte copy of the same
+// bf16 rows runs at 6.6 TB/s on that box (read-only 7.1, write-only 6.8).
 #include "kernels.h"
 
 namespace mtgr {
@@ -95,7 +97,21 @@ template <int E> __device__ __forceinline__ void store_piece(bf16* p, const floa
   }
 }
 
-template <typename Tin> constexpr int rows_per_wave() { return sizeof(Tin) == 4 ? 1 : 2; }
+// Rows per wavefront and lanes per row.  fp32 input: one row per wavefront (a row of 768 fp32 is
+// 192 pieces, three per lane).  bf16 input: lanes 0-31 take the first row and lanes 32-63 the
+// second (768 bf16 are 96 pieces, three per lane of a half); with whole-wavefront rows half the
+// lanes had a third fewer pieces.
+template <typename Tin> struct RowMap {
+  static constexpr int LPR = sizeof(Tin) == 4 ? 64 : 32;   // lanes per row
+  static constexpr int RPW = sizeof(Tin) == 4 ? 1 : 2;     // rows per wavefront
+  static constexpr int RPL = RPW * LPR / 64;               // rows per lane
+};
+
+// sum over the lanes that share this lane's row
+template <int LPR> __device__ __forceinline__ float row_sum(float v) {
+  if constexpr (LPR == 64) return wave_sum(v);
+  else return half_wave_sum(v);
+}
 
 template <typename Tin, typename Tout, typename Tp>
 __global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __restrict__ x,
@@ -103,23 +119,27 @@ __global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __
                                                  const Tp* __restrict__ gamma,
                                                  const Tp* __restrict__ beta, float eps,
                                                  int gmask, Tout* __restrict__ y) {
+  using RM = RowMap<Tin>;
   constexpr int E = Piece<Tin>::E;            // values per piece
-  constexpr int MP = 1024 / E / 64;           // pieces per lane at the largest d (1024)
-  constexpr int RPW = rows_per_wave<Tin>();
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW;
+  constexpr int LPR = RM::LPR, RPL = RM::RPL;
+  constexpr int MP = 1024 / E / LPR;          // pieces per lane and row at the largest d (1024)
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RM::RPW;
   const int lane = threadIdx.x & 63;
+  const int rl = lane % LPR;                  // lane within its row
   if (row0 >= T) return;
   const int np = d / E;                       // pieces per row (d is a multiple of 8)
+  // lane's rows: row0 + r (fp32 input) or row0 + lane / 32 (bf16 input)
+  auto row_of = [&](int r) { return row0 + r + lane / LPR; };
   // every row's loads are issued before the first reduction; pieces past the row end hold zeros
-  float v[RPW][MP][E];
-  int grp[RPW];
+  float v[RPL][MP][E];
+  int grp[RPL];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int64_t row = row0 + r;
+  for (int r = 0; r < RPL; ++r) {
+    const int64_t row = row_of(r);
     grp[r] = 0;
 #pragma unroll
     for (int k = 0; k < MP; ++k) {
-      const int pc = lane + 64 * k;
+      const int pc = rl + LPR * k;
       if (row < T && pc < np) {
         load_row_piece<E>(x + row * d + pc * E, v[r][k]);
       } else {
@@ -132,22 +152,22 @@ __global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __
     if (row < T) grp[r] = g[row] & gmask;
   }
   const float inv_d = 1.0f / (float)d;
-  float mean[RPW], rstd[RPW];
+  float mean[RPL], rstd[RPL];
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
+  for (int r = 0; r < RPL; ++r) {
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < MP; ++k)
 #pragma unroll
       for (int i = 0; i < E; ++i) s += v[r][k][i];
-    mean[r] = wave_sum(s) * inv_d;
+    mean[r] = row_sum<LPR>(s) * inv_d;
   }
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
+  for (int r = 0; r < RPL; ++r) {
     float q = 0.f;
 #pragma unroll
     for (int k = 0; k < MP; ++k) {
-      if (lane + 64 * k < np) {
+      if (rl + LPR * k < np) {
 #pragma unroll
         for (int i = 0; i < E; ++i) {
           const float e = v[r][k][i] - mean[r];
@@ -155,17 +175,17 @@ __global__ __launch_bounds__(256) void k_groupln(int64_t T, int d, const Tin* __
         }
       }
     }
-    rstd[r] = 1.0f / sqrtf(wave_sum(q) * inv_d + eps);
+    rstd[r] = 1.0f / sqrtf(row_sum<LPR>(q) * inv_d + eps);
   }
 #pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const int64_t row = row0 + r;
+  for (int r = 0; r < RPL; ++r) {
+    const int64_t row = row_of(r);
     if (row >= T) break;
     const Tp* gr = gamma + (int64_t)grp[r] * d;
     const Tp* br = beta + (int64_t)grp[r] * d;
 #pragma unroll
     for (int k = 0; k < MP; ++k) {
-      const int pc = lane + 64 * k;
+      const int pc = rl + LPR * k;
       if (pc < np) {
         float ga[E], be[E], o[E];
         load_piece<E>(gr + pc * E, ga);
@@ -183,7 +203,7 @@ hipError_t run(int64_t T, int d, const void* x, const uint8_t* g, const void* ga
                const void* beta, float eps, int gmask, void* y, hipStream_t s) {
   if (T == 0) return hipSuccess;
   if (d % 8 != 0 || d > 1024) return hipErrorInvalidValue;
-  const int64_t rows_per_block = 4 * rows_per_wave<Tin>();
+  const int64_t rows_per_block = 4 * RowMap<Tin>::RPW;
   const int64_t blocks = (T + rows_per_block - 1) / rows_per_block;
   k_groupln<Tin, Tout, Tp><<<(unsigned)blocks, 256, 0, s>>>(
       T, d, static_cast<const Tin*>(x), g, static_cast<const Tp*>(gamma),
