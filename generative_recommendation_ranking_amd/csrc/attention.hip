@@ -257,12 +257,28 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
     // sc[mt][r]: key k0 + mt*32 + 8*(r/4) + 4*hh + r%4, query qi
     // tiles every key of which is visible to every row of the wavefront skip the mask
     const bool unmasked = MODE == kMaskFull || (MODE == kMaskCausal ? k0 + BKV <= wq0 + 1 : k0 + BKV <= ns);
+    // silu(z) = z * rcp(1 + e^-z) (silu_rcp), computed 16 scores at a time with the steps of the
+    // 16 chains issued side by side (exponentials, sums, reciprocals), not chain after chain
+    auto silu16 = [&](int mt, float (&p)[16]) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __expf(-sc[mt][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = __builtin_amdgcn_rcpf(1.0f + p[r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) p[r] = sc[mt][r] * p[r];
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);   // the products -z log2(e)
+      __builtin_amdgcn_sched_group_barrier(0x400, 16, 0);   // 16 exponentials
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);   // 16 sums
+      __builtin_amdgcn_sched_group_barrier(0x400, 16, 0);   // 16 reciprocals
+    };
     if (unmasked) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 2; ++mt) {
+        float p[16];
+        silu16(mt, p);
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          pa[mt * 2 + (r >> 3)][r & 7] = (bf16)silu_rcp(sc[mt][r]);
+        for (int r = 0; r < 16; ++r) pa[mt * 2 + (r >> 3)][r & 7] = (bf16)p[r];
+      }
     } else {
       // Mask.  With jb = k0 + 4*hh this lane's keys are jb + dk, dk = mt*32 + 8*(r/4) + r%4 a
       // compile-time constant, so the visibility rule (the same as mtgr_visible) becomes three
@@ -273,6 +289,8 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
       const int lim_static = ns - jb, lim_rc = rc_end - jb, self = qi - jb;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
+        float ps[16];
+        silu16(mt, ps);
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
           const f32x4 t4 = *reinterpret_cast<const f32x4*>(&Tb[mt * 32 + 8 * g4 + 4 * hh]);
@@ -280,7 +298,7 @@ __global__ __launch_bounds__(64 * NW, 8 / NW) void k_attn_bf16(
           for (int c = 0; c < 4; ++c) {
             const int r = g4 * 4 + c;
             const int dk = mt * 32 + 8 * g4 + c;
-            const float p = silu_rcp(sc[mt][r]);
+            const float p = ps[r];
             const bool vis = MODE == kMaskCausal
                                  ? dk <= self
                                  : (dk < lim_static) | (dk == self) | (q_rc & (dk < lim_rc) & (t4[c] < tq));
