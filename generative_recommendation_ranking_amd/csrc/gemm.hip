@@ -427,6 +427,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
     char* stage = DMA ? reinterpret_cast<char*>(smem) + (cur ^ 1) * kSlabBytes + wave * (32 * SP)
                       : (wave < 4 ? reinterpret_cast<char*>(&As[cur ^ 1][0][0])
                                   : reinterpret_cast<char*>(&Bs[cur ^ 1][0][0])) + (wave & 3) * (BM * LP * (int)sizeof(bf16) / 4);
+    // fp32 residual chunks of pass pp (the same layout as the pass's stores), requested one pass
+    // ahead: a pass's residual loads then precede the previous pass's stores, so waiting for them
+    // does not wait for those stores
+    auto load_resid = [&](int pp, f32x4 (&dst)[8]) {
+      const int ip = pp / (FN / CPS), jp = (pp % (FN / CPS)) * CPS;
+      const bool ok = n0 + wn * TN + jp * 32 + (lane & 15) * CW < N;
+#pragma unroll
+      for (int it = 0; it < 8; ++it)
+        dst[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+            r_rsrc, ok ? lane_off : kDrop, (uint32_t)((ip * 32 + it * 4) * N + n0 + jp * 32) * (uint32_t)sizeof(TOut), 0));
+    };
+    f32x4 rq_next[8];
+    if constexpr (EPI == MTGR_EPI_RESIDUAL_F32) load_resid(0, rq_next);
 #pragma unroll
     for (int p = 0; p < NPASS; ++p) {
       // (one pass at a time: the accumulators of later passes stay where they are)
@@ -452,8 +465,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
       f32x4 rq[8];
       if constexpr (EPI == MTGR_EPI_RESIDUAL_F32) {
 #pragma unroll
-        for (int it = 0; it < 8; ++it)
-          rq[it] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r_rsrc, vo_c, s_off(it), 0));
+        for (int it = 0; it < 8; ++it) rq[it] = rq_next[it];
+        if (p + 1 < NPASS) load_resid(p + 1, rq_next);
       }
       u32x2 za[8];
       if constexpr (EPI == kEpiSiluBwd) {
