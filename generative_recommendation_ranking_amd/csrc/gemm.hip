@@ -381,11 +381,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_bf16_persistent(
   // tile does not use yet, 32 rows at a time, and writes whole 256-byte row segments with 16-byte
   // stores (the residual rows of the fp32 variant are read the same way).  Vector memory
   // operations retire in order, so a wait for a load also waits for every store issued before it:
-  // the bias is already in the accumulators, the residual chunks of a pass are requested before
-  // the pass's stores, and every
-  // lane issues the same fixed number of stores whatever the tile's edges (the resource ends at
-  // the tile's last valid row; chunks past column N get an offset beyond it and are dropped), so
-  // the compiler can also count past them when it waits for the next tile's prefetched slab.
+  // the bias is already in the accumulators, the residual chunks of a pass are requested one pass
+  // ahead (before the previous pass's stores), and every lane issues the same fixed number of
+  // stores whatever the tile's edges (the resource ends at the tile's last valid row; chunks past
+  // column N get an offset beyond it and are dropped), so the compiler can also count past them
+  // when it waits for the next tile's prefetched slab.
   constexpr uint32_t kDrop = 0x80000000u;   // > any valid byte offset (N <= 2^20, 256 rows)
   // the output rows are written once and not read again by this kernel: non-temporal stores keep
   // them from displacing the activation slabs that later column tiles re-read from L2
