@@ -136,9 +136,12 @@ def test_onehot_probe_reproduces_mask_through_fused_kernel(dtype, d, H, mode):
 # ---------------------------------------------------------------------------------------------
 # kernels
 # ---------------------------------------------------------------------------------------------
+# bf16 input gives each half-wavefront a row of its own: d = 40 leaves all but 5 lanes of each half
+# without a piece, d = 1024 gives every lane of a half its 4 pieces
 @pytest.mark.parametrize("kin,kout,d,shared", [(0, 0, 64, False), (0, 1, 256, False), (1, 1, 768, False),
                                                (0, 1, 1024, False), (0, 0, 40, False), (0, 0, 64, True),
-                                               (0, 1, 768, True), (1, 1, 256, True)])
+                                               (0, 1, 768, True), (1, 1, 256, True), (1, 1, 40, False),
+                                               (1, 1, 1024, False)])
 def test_groupln_parity(kin, kout, d, shared):
     b = custom_batch(EDGE_LENGTHS, d, 2, "f32")
     db = M.DeviceBatch(b)
@@ -162,8 +165,8 @@ def test_groupln_parity(kin, kout, d, shared):
     assert rel_err(to_np(y), ref) < tol
 
 
-# a token count that is not a multiple of the rows one workgroup normalises (8: two per wavefront),
-# so the last wavefront holds a single row
+# a token count that is not a multiple of the rows one workgroup normalises (bf16 rows: 8, two per
+# wavefront; fp32 rows: 4), so the last bf16 wavefront holds a single row and one half idles
 @pytest.mark.parametrize("kin,kout,d", [(0, 1, 768), (1, 1, 768), (0, 0, 64)])
 def test_groupln_ragged_rows(kin, kout, d):
     b = custom_batch(EDGE_LENGTHS + [(0, 3, 0, 0)], d, 2, "f32")
