@@ -687,7 +687,10 @@ hipError_t launch_attention_bwd_bf16(int32_t B, int64_t T, int64_t grid_slots, i
                                      const bf16* vt, const bf16* dy, bf16* g, bf16* dqkvu, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const int64_t chunks = T * (d / 8);
-  k_gate_bwd<<<(unsigned)std::min<int64_t>((chunks + 255) / 256, 16384), 256, 0, s>>>(T, d, qkvu, vt, dy, g, dqkvu);
+  // one 16-byte chunk per thread (the loop in the kernel only matters past 2^38 chunks): a thread
+  // that looped over several would wait, at each chunk's loads, for its previous chunk's stores
+  // (vector memory operations retire in order)
+  k_gate_bwd<<<(unsigned)std::min<int64_t>((chunks + 255) / 256, int64_t(1) << 30), 256, 0, s>>>(T, d, qkvu, vt, dy, g, dqkvu);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || grid_slots == 0) return e;
   const unsigned grid = (unsigned)(grid_slots * kXcdCount);
