@@ -111,9 +111,11 @@ __global__ __launch_bounds__(256) void k_gate_bwd(int64_t T, int d, const bf16* 
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t t = i / cpr;
     const int c = (int)(i - t * cpr);
-    const bf16x8 y8 = *reinterpret_cast<const bf16x8*>(dy + t * d + c * 8);
-    const bf16x8 u8 = *reinterpret_cast<const bf16x8*>(qkvu + t * 4 * d + 3 * d + c * 8);
-    const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(vt + t * d + c * 8);
+    // dy, U and V~ are read once here and dU written once: non-temporal; G is read again by the
+    // dK/dV and dQ passes and goes through the caches
+    const bf16x8 y8 = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(dy + t * d + c * 8));
+    const bf16x8 u8 = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(qkvu + t * 4 * d + 3 * d + c * 8));
+    const bf16x8 v8 = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(vt + t * d + c * 8));
     bf16x8 g8, du8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -121,7 +123,7 @@ __global__ __launch_bounds__(256) void k_gate_bwd(int64_t T, int d, const bf16* 
       du8[e] = (bf16)((float)y8[e] * (float)v8[e]);
     }
     *reinterpret_cast<bf16x8*>(g + t * d + c * 8) = g8;
-    *reinterpret_cast<bf16x8*>(dqkvu + t * 4 * d + 3 * d + c * 8) = du8;
+    __builtin_nontemporal_store(du8, reinterpret_cast<bf16x8*>(dqkvu + t * 4 * d + 3 * d + c * 8));
   }
 }
 
