@@ -493,20 +493,36 @@ __global__ __launch_bounds__(256) void k_convert_colsum(int64_t T, int M, int64_
   const int c0 = blockIdx.y * 512 + lane * 8;
   const int64_t r0 = (int64_t)blockIdx.x * rpb, r1 = min(T, r0 + rpb);
   float acc[8] = {};
-  if (c0 < M) {
-    for (int64_t r = r0 + w; r < r1; r += 4) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(src + r * M + c0);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(src + r * M + c0 + 4);
-      bf16x8 o;
+  // one row: accumulate its 8 columns and store them rounded to bf16
+  auto put = [&](int64_t r, const f32x4& a, const f32x4& b) {
+    bf16x8 o;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc[e] += a[e];
-        acc[e + 4] += b[e];
-        o[e] = (bf16)a[e];
-        o[e + 4] = (bf16)b[e];
-      }
-      *reinterpret_cast<bf16x8*>(dst + r * M + c0) = o;
+    for (int e = 0; e < 4; ++e) {
+      acc[e] += a[e];
+      acc[e + 4] += b[e];
+      o[e] = (bf16)a[e];
+      o[e + 4] = (bf16)b[e];
     }
+    *reinterpret_cast<bf16x8*>(dst + r * M + c0) = o;
+  };
+  if (c0 < M) {
+    // four rows' loads before their stores: vector memory operations retire in order, so a row's
+    // loads issued after the previous row's store would wait for it.  The fp32 rows are read once
+    // (non-temporal); the bf16 copy is read again by the weight-gradient GEMMs.
+    int64_t r = r0 + w;
+    for (; r + 12 < r1; r += 16) {
+      f32x4 a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (r + 4 * u) * M + c0));
+        b[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + (r + 4 * u) * M + c0 + 4));
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) put(r + 4 * u, a[u], b[u]);
+    }
+    for (; r < r1; r += 4)
+      put(r, __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + r * M + c0)),
+          __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + r * M + c0 + 4)));
   }
   if (!part) return;                                   // block-uniform
 #pragma unroll
