@@ -205,6 +205,32 @@ __global__ __launch_bounds__(256) void k_reduce_wb(int M, int K, int Kx, int nsp
   }
 }
 
+// The split-K slices without a bias column (Kx == K, db absent) are nsplit contiguous arrays of
+// M*K values: four consecutive values per thread, the slices added in split order (the same order,
+// so the same sums, as k_reduce_wb), eight slices' loads issued before their adds.
+__global__ __launch_bounds__(256) void k_reduce_wb4(int64_t n4, int nsplit, int64_t stride4,
+                                                    const f32x4* __restrict__ part, f32x4* __restrict__ dw) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int sp = 0;
+  for (; sp + 8 <= nsplit; sp += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(part + (int64_t)(sp + u) * stride4 + i);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += v[u][e];
+  }
+  for (; sp < nsplit; ++sp) {
+    const f32x4 v = __builtin_nontemporal_load(part + (int64_t)sp * stride4 + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += v[e];
+  }
+  dw[i] = acc;
+}
+
 // ---- GroupLN backward -------------------------------------------------------------------------
 // One wavefront per token row, as in the forward; each wavefront takes a contiguous run of rows.
 // dx = (dxh - mean(dxh) - xh mean(dxh xh)) / s; with resid, dx += resid (the residual path of the
@@ -603,6 +629,14 @@ hipError_t launch_reduce_wb(int M, int K, int Kx, int nsplit, const float* part,
                             hipStream_t s) {
   const int64_t n = (int64_t)M * (K + 1);
   if (M == 0) return hipSuccess;
+  const int64_t mk = (int64_t)M * K;
+  if (!db && Kx == K && mk % 4 == 0 && nsplit > 0 &&
+      reinterpret_cast<uintptr_t>(part) % 16 == 0 && reinterpret_cast<uintptr_t>(dw) % 16 == 0) {
+    const int64_t n4 = mk / 4;
+    k_reduce_wb4<<<(unsigned)((n4 + 255) / 256), 256, 0, s>>>(n4, nsplit, n4, reinterpret_cast<const f32x4*>(part),
+                                                               reinterpret_cast<f32x4*>(dw));
+    return hipGetLastError();
+  }
   k_reduce_wb<<<ew_grid(n), 256, 0, s>>>(M, K, Kx, nsplit, part, dw, db);
   return hipGetLastError();
 }
